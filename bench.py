@@ -1,0 +1,312 @@
+#!/usr/bin/env python3
+"""Throughput of the CacheBlend KV-fusion step on one MI355X.
+
+A step is one pass of the whole hot path -- for every layer of the workload:
+re-rotate the cached keys, score and select the candidates, fuse the
+recomputed rows, and run the selected rows' causal GQA attention -- over one
+batch of seeded synthetic input already resident in HBM.  Every step gets its
+own copy of the inputs (the blend works in place), so nothing is restored
+inside the timed region and no step is served from the 256 MB Infinity Cache.
+
+Metric: blended context tokens per second per layer = tokens * layers / time.
+
+Printed: one JSON line with the metric, a roofline entry for the dominant
+kernel (algorithmic work per launch / its average launch time, measured with
+HIP events on the launch stream), per-kernel figures and the CPU oracle timed
+on the host as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3       # fp32 vector
+DEFAULT_STEPS = {"c0": (200, 20), "c1": (200, 20), "c2": (20, 3), "c3": (4, 1), "c4": (2, 1)}
+STAGES = ("rerotate", "deviation_topk", "fuse_scatter", "partial_attn")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="c1", choices=["c0", "c1", "c2", "c3", "c4"])
+    ap.add_argument("--schedule", default="pool", choices=["pool", "chain"])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="budget of the CPU oracle baseline (0 disables it)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_work(wl, runner, planted_per_layer):
+    """Per-layer algorithmic bytes / flops of each stage (what the method must
+    move or compute), from the selection actually made."""
+    import numpy as np
+    elem = 2 if wl.dtype == "bf16" else 4
+    row = wl.n_kv_heads * wl.head_dim * elem
+    t_count = wl.n_tokens
+    nz = int(np.count_nonzero(wl.delta()))
+    tok_off = wl.tok_off
+    work = []
+    for layer in range(wl.n_layers):
+        m = runner.batches[layer].n_cand
+        sel = planted_per_layer[layer]
+        k = len(sel)
+        req = np.searchsorted(tok_off, sel, side="right") - 1
+        pos = sel - tok_off[req]
+        flops = 4.0 * wl.head_dim * wl.n_q_heads * float(np.sum(pos + 1))
+        work.append({
+            "rerotate": 2.0 * row * nz + 4.0 * t_count,
+            "deviation_topk": 2.0 * row * m + 8.0 * m,
+            "fuse_scatter": 4.0 * row * k + 8.0 * k,
+            "partial_attn": flops,
+        })
+    return work
+
+
+def cpu_baseline(wl, seconds):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from oracle import cacheblend_oracle as O
+    from selective_recompute_amd import workloads as W
+
+    sets = W.PlantedSets(wl)
+    x = W.layer_inputs(wl, sets, 0, device="cpu")
+    f64 = lambda t: t.to(torch.float64).numpy()
+    args = dict(k_old=f64(x["k_old"]), v_old=f64(x["v_old"]), delta=wl.delta(),
+                k_new_c=f64(x["k_new_c"]), v_new_c=f64(x["v_new_c"]), q_c=f64(x["q_c"]),
+                cand_idx=x["cand_idx"].numpy(), tok_off=wl.tok_off, cand_off=x["h_cand_off"],
+                sel_counts=[(wl.r1_pct * n + 99) // 100 for n in wl.request_lengths],
+                n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads, theta=wl.rope_theta,
+                scale=1.0 / math.sqrt(wl.head_dim))
+    # Large layers: time re-rotation/deviation/top-k/fuse in full and the
+    # attention on an evenly spaced 1/frac of the selected rows, then scale.
+    frac = 1 if wl.n_tokens <= 8192 else 16
+    reps, t_total = 0, 0.0
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        res = O.blend_layer(**args, attend=(frac == 1))
+        t1 = time.perf_counter()
+        t_layer = t1 - t0
+        if frac > 1:
+            rows = np.arange(0, len(res["sel_global"]), frac)
+            O.attention_rows(args["q_c"], res["sel_local"][rows], res["sel_global"][rows],
+                             res["row_start"][rows], res["k_fused"], res["v_fused"],
+                             wl.n_q_heads, wl.n_kv_heads, args["scale"])
+            t_layer += (time.perf_counter() - t1) * frac
+        t_total += t_layer
+        reps += 1
+        if time.perf_counter() - t_start >= seconds:
+            break
+    blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+    cores = max(blas) if blas else 1
+    sample = (f"layer 1 of {wl.name} ({wl.n_tokens} tokens, {sum(args['sel_counts'])} selected), "
+              f"{reps} repetition(s) of the full oracle pipeline in float64 numpy")
+    if frac > 1:
+        sample += f"; attention timed on every {frac}th selected row and scaled by {frac}"
+    sample += "; element-wise numpy runs on one thread, matrix-vector products on the BLAS pool"
+    return {"value": wl.n_tokens * reps / t_total, "unit": "tokens/s/layer", "cores": cores,
+            "kind": "oracle", "sample": sample}
+
+
+def main():
+    a = parse_args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported by this "
+              "single-GPU build (no multi-GPU path exists).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from selective_recompute_amd import binding as B
+    from selective_recompute_amd import pipeline as PL
+    from selective_recompute_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    B.lib()
+    wl = W.make_workload(a.workload)
+    steps, warmup = DEFAULT_STEPS[wl.name]
+    steps = a.steps if a.steps is not None else steps
+    warmup = a.warmup if a.warmup is not None else warmup
+    L = wl.n_layers
+    sets = W.PlantedSets(wl, a.schedule)
+    runner = PL.BlendRunner(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.torch_dtype,
+                            wl.request_lengths, wl.r1_pct, wl.r2_pct, L, wl.rope_theta,
+                            schedule=a.schedule, device="cuda")
+    stream = torch.cuda.Stream()
+    h = stream.cuda_stream
+
+    def make_copies(n, first_draw):
+        cps = []
+        for c in range(n):
+            cps.append([W.layer_inputs(wl, sets, l, device="cuda", draw=first_draw + c)
+                        for l in range(L)])
+        torch.cuda.synchronize()
+        return cps
+
+    # ---- timed pass: whole layers through cb_blend_layer --------------------
+    log(f"[bench] {wl.name}: generating {steps + warmup} input copies")
+    copies = make_copies(steps + warmup, 0)
+    prepared = []
+    for cp in copies:
+        row = []
+        for l, x in enumerate(cp):
+            o = runner.outs[l]
+            row.append(B.PreparedLayer(runner.geom, runner.batches[l], k=x["k_old"], v=x["v_old"],
+                                       k_new_c=x["k_new_c"], v_new_c=x["v_new_c"], q_c=x["q_c"],
+                                       delta=x["delta"], cand_idx=runner.candidates(l),
+                                       rope_theta=wl.rope_theta, rope_style=B.ROPE_HALF,
+                                       softmax_scale=runner.scale, dev=o["dev"],
+                                       sel_local=o["sel_local"], sel_global=o["sel_global"],
+                                       out=o["out"]))
+        prepared.append(row)
+    with torch.cuda.stream(stream):
+        for c in range(warmup):
+            for p in prepared[c]:
+                p.launch(h)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for c in range(warmup, warmup + steps):
+            for p in prepared[c]:
+                p.launch(h)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    ms_per_step = ev0.elapsed_time(ev1) / steps
+    wall_ms_per_step = (t1 - t0) * 1e3 / steps
+    log(f"[bench] timed {steps} steps: {ms_per_step:.4f} ms/step (wall {wall_ms_per_step:.4f})")
+    planted = [sets.layer(l).planted for l in range(L)]
+    for l in range(L):
+        got = runner.outs[l]["sel_global"].cpu().numpy()
+        if not np.array_equal(got, planted[l]):
+            raise RuntimeError(f"layer {l}: selection differs from the planted set")
+    del prepared, copies
+    torch.cuda.empty_cache()
+
+    # ---- attribution pass: each entry point timed over all its launches -----
+    lib = B.lib()
+    copies = make_copies(steps, 10_000)
+    gref = ctypes.byref(runner.geom)
+    rgs = [rb.struct() for rb in runner.batches]
+    stage_calls = {s: [[] for _ in range(L)] for s in STAGES}
+    keep = []
+    for cp in copies:
+        sels = []
+        for l, x in enumerate(cp):
+            rb = runner.batches[l]
+            dev_t = torch.empty(rb.n_cand, dtype=torch.float32, device="cuda")
+            sl = torch.empty(rb.n_sel, dtype=torch.int32, device="cuda")
+            sg = torch.empty(rb.n_sel, dtype=torch.int32, device="cuda")
+            sels.append(sg)
+            src = runner.filter.cand_source(l)
+            cand = runner.all_tokens if src is None else sels[src]
+            keep += [dev_t, sl, sg]
+            k_ptr, v_ptr = x["k_old"].data_ptr(), x["v_old"].data_ptr()
+            stage_calls["rerotate"][l].append(
+                (lib.cb_rerotate, (gref, k_ptr, k_ptr, x["delta"].data_ptr(), wl.n_tokens, 1,
+                                   wl.rope_theta, B.ROPE_HALF, h)))
+            stage_calls["deviation_topk"][l].append(
+                (lib.cb_deviation_topk, (gref, ctypes.byref(rgs[l]), x["v_new_c"].data_ptr(),
+                                         v_ptr, cand.data_ptr(), dev_t.data_ptr(), sl.data_ptr(),
+                                         sg.data_ptr(), h)))
+            stage_calls["fuse_scatter"][l].append(
+                (lib.cb_fuse_scatter, (gref, k_ptr, v_ptr, x["k_new_c"].data_ptr(),
+                                       x["v_new_c"].data_ptr(), sl.data_ptr(), sg.data_ptr(),
+                                       rb.n_sel, h)))
+            stage_calls["partial_attn"][l].append(
+                (lib.cb_partial_attn, (gref, ctypes.byref(rgs[l]),
+                                       runner.outs[l]["out"].data_ptr(), x["q_c"].data_ptr(),
+                                       sl.data_ptr(), sg.data_ptr(), k_ptr, v_ptr,
+                                       runner.scale, h)))
+    events = {}
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        for l in range(L):
+            for s in STAGES:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for fn, args in stage_calls[s][l]:
+                    st = fn(*args)
+                    if st != 0:
+                        B.check(st)
+                e1.record(stream)
+                events[(l, s)] = (e0, e1)
+        torch.cuda.synchronize()
+    stage_ms = {s: sum(events[(l, s)][0].elapsed_time(events[(l, s)][1]) for l in range(L))
+                for s in STAGES}
+    launches = steps * L
+    work = algorithmic_work(wl, runner, planted)
+    stage_work = {s: sum(w[s] for w in work) for s in STAGES}
+    kernels = {}
+    for s in STAGES:
+        avg_us = stage_ms[s] * 1e3 / launches
+        if s == "partial_attn":
+            rate = stage_work[s] / (stage_ms[s] * 1e-3) / 1e12
+            kernels[s] = {"avg_us": round(avg_us, 3), "tflops": round(rate, 3),
+                          "gflop_per_launch": round(stage_work[s] / launches / 1e9, 4)}
+        else:
+            rate = stage_work[s] / (stage_ms[s] * 1e-3) / 1e9
+            kernels[s] = {"avg_us": round(avg_us, 3), "gbs": round(rate, 1),
+                          "mb_per_launch": round(stage_work[s] / launches / 1e6, 4)}
+    dominant = max(STAGES, key=lambda s: stage_ms[s])
+    if dominant == "partial_attn":
+        bf16 = wl.dtype == "bf16"
+        peak = BF16_PEAK_TFLOPS if bf16 else FP32_PEAK_TFLOPS
+        achieved = kernels[dominant]["tflops"]
+        roof = {"kernel": "partial_attn", "bound": "mfma" if bf16 else "alu",
+                "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 5), "traffic": None}
+    else:
+        achieved = kernels[dominant]["gbs"]
+        roof = {"kernel": dominant, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None}
+    del stage_calls, copies, keep
+    torch.cuda.empty_cache()
+
+    cpu = None
+    if a.cpu_seconds > 0:
+        log("[bench] timing the CPU oracle")
+        cpu = cpu_baseline(wl, a.cpu_seconds)
+
+    value = wl.n_tokens * L / (ms_per_step * 1e-3)
+    ratio = {"c0": "r=15%", "c1": "r=15%"}.get(wl.name, f"r1={wl.r1_pct}% -> r2={wl.r2_pct}%")
+    line = {
+        "metric": "blended context tokens/s per layer (1 GPU) + % HBM / MFMA roofline",
+        "value": round(value, 1), "unit": "tokens/s/layer", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.description}", "tokens": wl.n_tokens,
+                   "layers": L, "requests": wl.n_requests, "q_heads": wl.n_q_heads,
+                   "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "selection": ratio,
+                   "hkvd_pct": wl.hkvd_pct, "schedule": a.schedule},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "wall_ms_per_step": round(wall_ms_per_step, 5),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

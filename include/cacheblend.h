@@ -1,0 +1,216 @@
+/*
+ * cacheblend.h -- C ABI of the MI355X (gfx950) CacheBlend KV-fusion library.
+ *
+ * One layer of the blend joins separately prefilled chunk caches of a request:
+ *   1. cached keys are moved to their new positions by re-rotation,
+ *   2. each candidate token is scored by the squared deviation of its V row,
+ *   3. the top-k tokens per request are selected,
+ *   4. their recomputed K/V rows replace the cached rows,
+ *   5. the selected query rows run causal GQA attention over the fused cache.
+ *
+ * Pages cited:
+ *   [Derivations] the page "数学推导" (math derivations) of the CacheBlend
+ *                 documentation, inference.lei6393.com/cacheblend/appendix/
+ *                 c-math-derivations/
+ *   [KV-blog]     the blog page "rag的kvcache问题" (zxj-2023.github.io)
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless the argument says [host].
+ *   - Tensors are dense, row-major and token-major: [token][head][dim].
+ *     Element type is cb_geom.dtype (fp32 or bf16); every base pointer of a
+ *     tensor must be 16-byte aligned.  Index arrays are int32.
+ *   - "Packed" rows: the tokens of all requests of a ragged batch are
+ *     concatenated; request r owns rows [tok_off[r], tok_off[r+1]).  Positions
+ *     inside a request start at 0.
+ *   - Candidate rows: request r's candidates are cand_idx[cand_off[r] ..
+ *     cand_off[r+1]), packed row numbers in ascending order; the recomputed
+ *     tensors (k_new_c, v_new_c, q_c) hold one row per candidate in that order.
+ *   - Ownership: the caller allocates and frees every buffer.  The library
+ *     never allocates, frees or synchronizes, and keeps no mutable global state.
+ *   - Ordering: every call enqueues its kernels on `stream` (a hipStream_t;
+ *     NULL = the default stream) and returns without waiting.  Calls are
+ *     thread-safe.
+ *   - Errors: argument errors are detected on the host before any HIP call and
+ *     return CB_ERR_INVALID_ARG or CB_ERR_UNSUPPORTED with nothing enqueued.
+ *     A failed launch returns CB_ERR_HIP.  cb_last_error() gives the detail
+ *     text of the calling thread's last failure.  Device-side preconditions
+ *     that the host cannot see (index values in range, ascending order) are
+ *     the caller's responsibility.
+ */
+#ifndef CACHEBLEND_H
+#define CACHEBLEND_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum cb_status {
+  CB_OK = 0,
+  CB_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size or offsets */
+  CB_ERR_UNSUPPORTED = 2, /* valid request outside what the kernels implement */
+  CB_ERR_HIP = 3          /* the HIP runtime reported an error */
+} cb_status;
+
+typedef enum cb_dtype { CB_DTYPE_F32 = 0, CB_DTYPE_BF16 = 1 } cb_dtype;
+
+/* Pairing of the coordinates that one RoPE 2x2 block rotates. */
+typedef enum cb_rope_style {
+  CB_ROPE_HALF = 0,        /* pairs (j, j + D/2), j < D/2 */
+  CB_ROPE_INTERLEAVED = 1  /* pairs (2j, 2j + 1) */
+} cb_rope_style;
+
+/* Head geometry.  n_q_heads % n_kv_heads == 0; query head h reads KV head
+ * h / (n_q_heads / n_kv_heads).  head_dim in {16, 32, 64, 128}. */
+typedef struct cb_geom {
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t dtype; /* cb_dtype */
+} cb_geom;
+
+/* A ragged batch of n_req independent requests.  The three offset arrays have
+ * n_req + 1 entries, start at 0 and never decrease.  The device copies feed
+ * the kernels; the [host] mirrors (same values) serve validation and grid
+ * sizing, so no call ever reads device memory back. */
+typedef struct cb_ragged {
+  int32_t n_req;
+  const int32_t *tok_off;    /* packed token rows of each request */
+  const int32_t *cand_off;   /* candidate slice of each request */
+  const int32_t *sel_off;    /* selected slice: k_r = sel_off[r+1] - sel_off[r] */
+  const int32_t *h_tok_off;  /* [host] */
+  const int32_t *h_cand_off; /* [host] */
+  const int32_t *h_sel_off;  /* [host] */
+} cb_ragged;
+
+/*
+ * cb_rerotate -- move cached keys to their new positions.
+ * [Derivations, "CacheBlend 中的应用"]: a key cached at p_old is taken to
+ * p_new by the rotation R_{p_new - p_old}; R is the block-diagonal matrix of
+ * 2x2 rotations of [Derivations, "RoPE 位置编码的相对位置不变性证明"], pair j
+ * turning by delta * theta^(-2j/D) (the RoFormer schedule).  V is not rotated.
+ *
+ *   k_in, k_out : [n_layers][n_tok][n_kv_heads][head_dim], dtype.  k_out may
+ *                 equal k_in (in place); any other overlap is invalid.  In place,
+ *                 rows whose delta is 0 are not touched; out of place they are
+ *                 copied unchanged.
+ *   delta       : [n_tok] int32, p_new - p_old of each packed row (shared by
+ *                 all layers).
+ *   rope_theta  : frequency base (> 0, finite).
+ * Angles are reduced in double precision, the rotation is applied in fp32 and
+ * stored with round-to-nearest-even.
+ */
+cb_status cb_rerotate(const cb_geom *geom, void *k_out, const void *k_in,
+                      const int32_t *delta, int64_t n_tok, int32_t n_layers,
+                      double rope_theta, int32_t rope_style, void *stream);
+
+/*
+ * cb_deviation_topk -- score candidates and select the high-deviation tokens.
+ * [Derivations, "近似解"]: S = TopK_i ||V_new[i] - V_old[i]||_2^2, summed
+ * over every KV head and dimension of the token; [KV-blog, "渐进式过滤机制"]:
+ * the candidate pool is all tokens at layer 1 and the survivors afterwards.
+ *
+ *   v_new_c  : [M][n_kv_heads][head_dim]  recomputed V of the candidates
+ *   v_old    : [T][n_kv_heads][head_dim]  cached V (T = h_tok_off[n_req])
+ *   cand_idx : [M] candidate packed rows (M = h_cand_off[n_req])
+ *   dev      : [M] fp32 out, the deviation of each candidate (fp32 accumulation)
+ *   sel_local, sel_global : [K] int32 out (K = h_sel_off[n_req]).  For request
+ *              r, the k_r candidates with the largest deviation (NaN above
+ *              +inf; ties to the lower packed row), in ascending order:
+ *              sel_local = index into the candidate arrays (0 .. M-1),
+ *              sel_global = cand_idx[sel_local].
+ * Requires k_r <= M_r <= N_r for every request.
+ */
+cb_status cb_deviation_topk(const cb_geom *geom, const cb_ragged *rg,
+                            const void *v_new_c, const void *v_old,
+                            const int32_t *cand_idx, float *dev,
+                            int32_t *sel_local, int32_t *sel_global,
+                            void *stream);
+
+/*
+ * cb_topk -- the selection half of cb_deviation_topk on given fp32 scores:
+ * same ordering, tie and output rules.  dev: [M] fp32.
+ */
+cb_status cb_topk(const cb_ragged *rg, const float *dev, const int32_t *cand_idx,
+                  int32_t *sel_local, int32_t *sel_global, void *stream);
+
+/*
+ * cb_fuse_scatter -- splice the recomputed rows into the cache, in place.
+ * [Derivations, "形式化"]: K_fused[i] = K_new[i] for i in S, else the cached
+ * row; V likewise.  [KV-blog, "渐进式过滤机制"]: the recomputed rows are
+ * joined with the reused cache before attention.
+ *
+ *   k_fused, v_fused : [T][n_kv_heads][head_dim], in/out (hold K_rot / V_old)
+ *   k_new_c, v_new_c : [M][n_kv_heads][head_dim]
+ *   sel_local, sel_global : [k_total]; row sel_local[s] of the new tensors is
+ *                    copied bit for bit to row sel_global[s] of the fused ones.
+ */
+cb_status cb_fuse_scatter(const cb_geom *geom, void *k_fused, void *v_fused,
+                          const void *k_new_c, const void *v_new_c,
+                          const int32_t *sel_local, const int32_t *sel_global,
+                          int64_t k_total, void *stream);
+
+/*
+ * cb_partial_attn -- causal GQA attention of the selected rows only.
+ * [Derivations, "形式化"]: Attention(Q, K_fused, V_fused); [KV-blog, "阶段二：
+ * 注意力分数计算阶段"]: every query row is computed independently;
+ * [KV-blog, "transformer训练与推理并行计算的差异"]: causal mask.
+ *
+ * For selected row s of request r (packed row p = sel_global[s]) and query
+ * head h, with g = h / (n_q_heads / n_kv_heads):
+ *   out[s][h] = sum_{u = tok_off[r]}^{p} softmax_u(<q, K_fused[u][g]> * scale)
+ *               * V_fused[u][g],   q = q_c[sel_local[s]][h].
+ *   out    : [K][n_q_heads][head_dim] dtype, K = h_sel_off[n_req]
+ *   q_c    : [M][n_q_heads][head_dim], already rotated at the new positions
+ * bf16 uses MFMA products with fp32 accumulation and an fp32 online softmax.
+ */
+cb_status cb_partial_attn(const cb_geom *geom, const cb_ragged *rg, void *out,
+                          const void *q_c, const int32_t *sel_local,
+                          const int32_t *sel_global, const void *k_fused,
+                          const void *v_fused, float softmax_scale,
+                          void *stream);
+
+/* Every argument of one layer of the blend. */
+typedef struct cb_layer_args {
+  cb_geom geom;
+  cb_ragged rg;
+  void *k;              /* [T][Hkv][D] cached K: re-rotated, then fused, in place */
+  void *v;              /* [T][Hkv][D] cached V: fused in place */
+  const void *k_new_c;  /* [M][Hkv][D] */
+  const void *v_new_c;  /* [M][Hkv][D] */
+  const void *q_c;      /* [M][Hq][D] */
+  const int32_t *delta; /* [T] p_new - p_old; NULL = keys already at p_new */
+  const int32_t *cand_idx; /* [M] */
+  double rope_theta;
+  int32_t rope_style;
+  float softmax_scale;
+  float *dev;           /* [M] out */
+  int32_t *sel_local;   /* [K] out */
+  int32_t *sel_global;  /* [K] out */
+  void *out;            /* [K][Hq][D] out */
+} cb_layer_args;
+
+/*
+ * cb_blend_layer -- one layer: cb_rerotate (in place, when delta != NULL) ->
+ * cb_deviation_topk -> cb_fuse_scatter -> cb_partial_attn, all on `stream`.
+ * [KV-blog, "渐进式过滤机制"]: the caller runs it per layer, passing all
+ * tokens as candidates at layer 1 and the surviving rows afterwards.
+ */
+cb_status cb_blend_layer(const cb_layer_args *args, void *stream);
+
+/* Static description of a status code. */
+const char *cb_status_str(cb_status status);
+/* Detail text of the calling thread's last failing call ("" if none). */
+const char *cb_last_error(void);
+/* ABI revision of this header (bumped on any incompatible change). */
+int32_t cb_abi_version(void);
+
+#define CB_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CACHEBLEND_H */

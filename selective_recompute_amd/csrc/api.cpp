@@ -1,0 +1,358 @@
+// extern "C" entry points of libcacheblend: host-side validation, then the
+// kernel launches.  Validation makes no HIP call, so every argument error is
+// reported synchronously with nothing enqueued.
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "cacheblend.h"
+#include "cb_launch.hpp"
+
+#define CB_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+cb_status fail(cb_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_size(int32_t dtype) { return dtype == CB_DTYPE_BF16 ? 2 : 4; }
+
+#define CB_TRY(expr)                 \
+  do {                               \
+    cb_status _st = (expr);          \
+    if (_st != CB_OK) return _st;    \
+  } while (0)
+
+cb_status check_geom(const cb_geom *g) {
+  if (!g) return fail(CB_ERR_INVALID_ARG, "geom is NULL");
+  if (g->dtype != CB_DTYPE_F32 && g->dtype != CB_DTYPE_BF16)
+    return fail(CB_ERR_UNSUPPORTED, "dtype %d is not CB_DTYPE_F32 or CB_DTYPE_BF16", g->dtype);
+  if (g->n_kv_heads < 1 || g->n_q_heads < 1)
+    return fail(CB_ERR_INVALID_ARG, "head counts must be >= 1 (q %d, kv %d)", g->n_q_heads,
+                g->n_kv_heads);
+  if (g->n_q_heads % g->n_kv_heads != 0)
+    return fail(CB_ERR_INVALID_ARG, "n_q_heads %d is not a multiple of n_kv_heads %d",
+                g->n_q_heads, g->n_kv_heads);
+  if (g->head_dim != 16 && g->head_dim != 32 && g->head_dim != 64 && g->head_dim != 128)
+    return fail(CB_ERR_UNSUPPORTED, "head_dim %d not in {16, 32, 64, 128}", g->head_dim);
+  // one rerotate unit per 16 bytes of half a head; a row must fit a workgroup
+  const int pairs_per_unit = 16 / elem_size(g->dtype);
+  const int64_t units = (int64_t)g->n_kv_heads * (g->head_dim / 2) / pairs_per_unit;
+  if (units > 1024)
+    return fail(CB_ERR_UNSUPPORTED, "n_kv_heads %d too large for head_dim %d", g->n_kv_heads,
+                g->head_dim);
+  if (g->n_q_heads > 65535) return fail(CB_ERR_UNSUPPORTED, "n_q_heads too large");
+  return CB_OK;
+}
+
+cb_status need_ptr(const void *p, const char *name, bool needed) {
+  if (!needed) return CB_OK;
+  if (!p) return fail(CB_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(CB_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return CB_OK;
+}
+
+cb_status need_idx(const void *p, const char *name, bool needed) {
+  if (!needed) return CB_OK;
+  if (!p) return fail(CB_ERR_INVALID_ARG, "%s is NULL", name);
+  if ((reinterpret_cast<uintptr_t>(p) & 3u) != 0)
+    return fail(CB_ERR_INVALID_ARG, "%s is not 4-byte aligned", name);
+  return CB_OK;
+}
+
+cb_status check_offsets(const int32_t *h, int32_t n, const char *name) {
+  if (!h) return fail(CB_ERR_INVALID_ARG, "host mirror %s is NULL", name);
+  if (h[0] != 0) return fail(CB_ERR_INVALID_ARG, "%s[0] = %d, expected 0", name, h[0]);
+  for (int32_t r = 0; r < n; ++r)
+    if (h[r + 1] < h[r])
+      return fail(CB_ERR_INVALID_ARG, "%s decreases at request %d", name, r);
+  return CB_OK;
+}
+
+// Ragged batch checks.  want_tok/want_cand/want_sel: which offsets the call uses.
+cb_status check_ragged(const cb_ragged *rg, bool want_tok, bool want_cand, bool want_sel) {
+  if (!rg) return fail(CB_ERR_INVALID_ARG, "ragged descriptor is NULL");
+  if (rg->n_req < 1) return fail(CB_ERR_INVALID_ARG, "n_req %d < 1", rg->n_req);
+  if (want_tok) {
+    CB_TRY(need_idx(rg->tok_off, "tok_off", true));
+    CB_TRY(check_offsets(rg->h_tok_off, rg->n_req, "h_tok_off"));
+  }
+  if (want_cand) {
+    CB_TRY(need_idx(rg->cand_off, "cand_off", true));
+    CB_TRY(check_offsets(rg->h_cand_off, rg->n_req, "h_cand_off"));
+  }
+  if (want_sel) {
+    CB_TRY(need_idx(rg->sel_off, "sel_off", true));
+    CB_TRY(check_offsets(rg->h_sel_off, rg->n_req, "h_sel_off"));
+  }
+  for (int32_t r = 0; r < rg->n_req; ++r) {
+    const int64_t n = want_tok ? (int64_t)rg->h_tok_off[r + 1] - rg->h_tok_off[r] : -1;
+    const int64_t m = want_cand ? (int64_t)rg->h_cand_off[r + 1] - rg->h_cand_off[r] : -1;
+    const int64_t k = want_sel ? (int64_t)rg->h_sel_off[r + 1] - rg->h_sel_off[r] : -1;
+    if (want_cand && want_sel && k > m)
+      return fail(CB_ERR_INVALID_ARG, "request %d selects %lld of %lld candidates", r,
+                  (long long)k, (long long)m);
+    if (want_tok && want_cand && m > n)
+      return fail(CB_ERR_INVALID_ARG, "request %d has %lld candidates for %lld tokens", r,
+                  (long long)m, (long long)n);
+    if (want_tok && want_sel && k > n)
+      return fail(CB_ERR_INVALID_ARG, "request %d selects %lld rows of %lld tokens", r,
+                  (long long)k, (long long)n);
+  }
+  return CB_OK;
+}
+
+cb_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return CB_OK;
+  return fail(CB_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t row_elems(const cb_geom *g) { return (int64_t)g->n_kv_heads * g->head_dim; }
+
+cb_status validate_rerotate(const cb_geom *geom, void *k_out, const void *k_in,
+                            const int32_t *delta, int64_t n_tok, int32_t n_layers,
+                            double rope_theta, int32_t rope_style) {
+  CB_TRY(check_geom(geom));
+  if (n_tok < 0 || n_tok >= INT32_MAX) return fail(CB_ERR_INVALID_ARG, "n_tok %lld out of range", (long long)n_tok);
+  if (n_layers < 1) return fail(CB_ERR_INVALID_ARG, "n_layers %d < 1", n_layers);
+  if (!(rope_theta > 0.0) || !std::isfinite(rope_theta))
+    return fail(CB_ERR_INVALID_ARG, "rope_theta must be positive and finite");
+  if (rope_style != CB_ROPE_HALF && rope_style != CB_ROPE_INTERLEAVED)
+    return fail(CB_ERR_INVALID_ARG, "rope_style %d unknown", rope_style);
+  const bool any = n_tok > 0;
+  CB_TRY(need_ptr(k_in, "k_in", any));
+  CB_TRY(need_ptr(k_out, "k_out", any));
+  CB_TRY(need_idx(delta, "delta", any));
+  if (any && k_out != k_in) {
+    const int64_t bytes = (int64_t)n_layers * n_tok * row_elems(geom) * elem_size(geom->dtype);
+    const char *a = static_cast<const char *>(k_in), *b = static_cast<const char *>(k_out);
+    if (a < b + bytes && b < a + bytes)
+      return fail(CB_ERR_INVALID_ARG, "k_out partially overlaps k_in");
+  }
+  return CB_OK;
+}
+
+cb::RopeTable rope_table(int head_dim, double theta) {
+  cb::RopeTable t{};
+  const double two_pi = 6.283185307179586476925;
+  for (int j = 0; j < head_dim / 2; ++j)
+    t.rev_per_pos[j] = std::pow(theta, -2.0 * j / head_dim) / two_pi;
+  return t;
+}
+
+cb_status validate_devtopk(const cb_geom *geom, const cb_ragged *rg, const void *v_new_c,
+                           const void *v_old, const int32_t *cand_idx, const float *dev,
+                           const int32_t *sel_local, const int32_t *sel_global) {
+  CB_TRY(check_geom(geom));
+  CB_TRY(check_ragged(rg, true, true, true));
+  const int32_t m = rg->h_cand_off[rg->n_req], k = rg->h_sel_off[rg->n_req];
+  CB_TRY(need_ptr(v_new_c, "v_new_c", m > 0));
+  CB_TRY(need_ptr(v_old, "v_old", m > 0));
+  CB_TRY(need_idx(cand_idx, "cand_idx", m > 0));
+  CB_TRY(need_idx(dev, "dev", m > 0));
+  CB_TRY(need_idx(sel_local, "sel_local", k > 0));
+  CB_TRY(need_idx(sel_global, "sel_global", k > 0));
+  return CB_OK;
+}
+
+cb_status validate_topk(const cb_ragged *rg, const float *dev, const int32_t *cand_idx,
+                        const int32_t *sel_local, const int32_t *sel_global) {
+  CB_TRY(check_ragged(rg, false, true, true));
+  const int32_t m = rg->h_cand_off[rg->n_req], k = rg->h_sel_off[rg->n_req];
+  CB_TRY(need_idx(dev, "dev", m > 0));
+  CB_TRY(need_idx(cand_idx, "cand_idx", m > 0));
+  CB_TRY(need_idx(sel_local, "sel_local", k > 0));
+  CB_TRY(need_idx(sel_global, "sel_global", k > 0));
+  return CB_OK;
+}
+
+cb_status validate_fuse(const cb_geom *geom, void *k_fused, void *v_fused, const void *k_new_c,
+                        const void *v_new_c, const int32_t *sel_local, const int32_t *sel_global,
+                        int64_t k_total) {
+  CB_TRY(check_geom(geom));
+  if (k_total < 0 || k_total >= INT32_MAX) return fail(CB_ERR_INVALID_ARG, "k_total out of range");
+  const bool any = k_total > 0;
+  CB_TRY(need_ptr(k_fused, "k_fused", any));
+  CB_TRY(need_ptr(v_fused, "v_fused", any));
+  CB_TRY(need_ptr(k_new_c, "k_new_c", any));
+  CB_TRY(need_ptr(v_new_c, "v_new_c", any));
+  CB_TRY(need_idx(sel_local, "sel_local", any));
+  CB_TRY(need_idx(sel_global, "sel_global", any));
+  return CB_OK;
+}
+
+cb_status validate_attn(const cb_geom *geom, const cb_ragged *rg, void *out, const void *q_c,
+                        const int32_t *sel_local, const int32_t *sel_global, const void *k_fused,
+                        const void *v_fused, float softmax_scale) {
+  CB_TRY(check_geom(geom));
+  CB_TRY(check_ragged(rg, true, false, true));
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+    return fail(CB_ERR_INVALID_ARG, "softmax_scale must be positive and finite");
+  const int32_t k = rg->h_sel_off[rg->n_req];
+  const bool any = k > 0;
+  CB_TRY(need_ptr(out, "out", any));
+  CB_TRY(need_ptr(q_c, "q_c", any));
+  CB_TRY(need_ptr(k_fused, "k_fused", any));
+  CB_TRY(need_ptr(v_fused, "v_fused", any));
+  CB_TRY(need_idx(sel_local, "sel_local", any));
+  CB_TRY(need_idx(sel_global, "sel_global", any));
+  if ((int64_t)k * geom->n_q_heads > INT32_MAX)
+    return fail(CB_ERR_UNSUPPORTED, "k_total * n_q_heads exceeds the grid limit");
+  return CB_OK;
+}
+
+cb_status run_attn(const cb_geom *geom, const cb_ragged *rg, void *out, const void *q_c,
+                   const int32_t *sel_local, const int32_t *sel_global, const void *k_fused,
+                   const void *v_fused, float softmax_scale, hipStream_t stream) {
+  cb::AttnArgs a;
+  a.out = out; a.q_c = q_c; a.sel_local = sel_local; a.sel_global = sel_global;
+  a.k_fused = k_fused; a.v_fused = v_fused; a.tok_off = rg->tok_off; a.sel_off = rg->sel_off;
+  a.n_req = rg->n_req; a.k_total = rg->h_sel_off[rg->n_req];
+  a.n_q_heads = geom->n_q_heads; a.n_kv_heads = geom->n_kv_heads; a.head_dim = geom->head_dim;
+  a.softmax_scale = softmax_scale;
+  if (a.k_total == 0) return CB_OK;
+  const int rows = cb::attn_mfma_rows_per_tile(geom->dtype, geom->n_q_heads, geom->n_kv_heads,
+                                               geom->head_dim);
+  if (rows > 0) {
+    int64_t tiles = 0;
+    for (int32_t r = 0; r < rg->n_req; ++r) {
+      const int64_t kr = rg->h_sel_off[r + 1] - rg->h_sel_off[r];
+      tiles += (kr + rows - 1) / rows;
+    }
+    if (tiles * geom->n_kv_heads > INT32_MAX)
+      return fail(CB_ERR_UNSUPPORTED, "too many attention tiles");
+    return hip_status(cb::launch_attn_mfma(a, rows, (int32_t)tiles, stream), "partial_attn");
+  }
+  return hip_status(cb::launch_attn_simple(geom->dtype, a, stream), "partial_attn");
+}
+
+}  // namespace
+
+CB_EXPORT cb_status cb_rerotate(const cb_geom *geom, void *k_out, const void *k_in,
+                                const int32_t *delta, int64_t n_tok, int32_t n_layers,
+                                double rope_theta, int32_t rope_style, void *stream) {
+  g_last_error.clear();
+  CB_TRY(validate_rerotate(geom, k_out, k_in, delta, n_tok, n_layers, rope_theta, rope_style));
+  if (n_tok == 0) return CB_OK;
+  return hip_status(cb::launch_rerotate(geom->dtype, rope_style, k_out, k_in, delta, n_tok,
+                                        n_layers, geom->n_kv_heads, geom->head_dim,
+                                        rope_table(geom->head_dim, rope_theta),
+                                        (hipStream_t)stream),
+                    "rerotate");
+}
+
+CB_EXPORT cb_status cb_deviation_topk(const cb_geom *geom, const cb_ragged *rg,
+                                      const void *v_new_c, const void *v_old,
+                                      const int32_t *cand_idx, float *dev, int32_t *sel_local,
+                                      int32_t *sel_global, void *stream) {
+  g_last_error.clear();
+  CB_TRY(validate_devtopk(geom, rg, v_new_c, v_old, cand_idx, dev, sel_local, sel_global));
+  const int32_t m = rg->h_cand_off[rg->n_req];
+  CB_TRY(hip_status(cb::launch_deviation(geom->dtype, v_new_c, v_old, cand_idx, dev, m,
+                                         (int32_t)row_elems(geom), (hipStream_t)stream),
+                    "deviation"));
+  if (rg->h_sel_off[rg->n_req] == 0) return CB_OK;
+  return hip_status(cb::launch_topk(rg->n_req, dev, cand_idx, rg->cand_off, rg->sel_off,
+                                    sel_local, sel_global, (hipStream_t)stream),
+                    "topk");
+}
+
+CB_EXPORT cb_status cb_topk(const cb_ragged *rg, const float *dev, const int32_t *cand_idx,
+                            int32_t *sel_local, int32_t *sel_global, void *stream) {
+  g_last_error.clear();
+  CB_TRY(validate_topk(rg, dev, cand_idx, sel_local, sel_global));
+  if (rg->h_sel_off[rg->n_req] == 0) return CB_OK;
+  return hip_status(cb::launch_topk(rg->n_req, dev, cand_idx, rg->cand_off, rg->sel_off,
+                                    sel_local, sel_global, (hipStream_t)stream),
+                    "topk");
+}
+
+CB_EXPORT cb_status cb_fuse_scatter(const cb_geom *geom, void *k_fused, void *v_fused,
+                                    const void *k_new_c, const void *v_new_c,
+                                    const int32_t *sel_local, const int32_t *sel_global,
+                                    int64_t k_total, void *stream) {
+  g_last_error.clear();
+  CB_TRY(validate_fuse(geom, k_fused, v_fused, k_new_c, v_new_c, sel_local, sel_global, k_total));
+  if (k_total == 0) return CB_OK;
+  return hip_status(cb::launch_fuse(k_fused, v_fused, k_new_c, v_new_c, sel_local, sel_global,
+                                    k_total, (int32_t)(row_elems(geom) * elem_size(geom->dtype)),
+                                    (hipStream_t)stream),
+                    "fuse_scatter");
+}
+
+CB_EXPORT cb_status cb_partial_attn(const cb_geom *geom, const cb_ragged *rg, void *out,
+                                    const void *q_c, const int32_t *sel_local,
+                                    const int32_t *sel_global, const void *k_fused,
+                                    const void *v_fused, float softmax_scale, void *stream) {
+  g_last_error.clear();
+  CB_TRY(validate_attn(geom, rg, out, q_c, sel_local, sel_global, k_fused, v_fused,
+                       softmax_scale));
+  return run_attn(geom, rg, out, q_c, sel_local, sel_global, k_fused, v_fused, softmax_scale,
+                  (hipStream_t)stream);
+}
+
+CB_EXPORT cb_status cb_blend_layer(const cb_layer_args *a, void *stream) {
+  g_last_error.clear();
+  if (!a) return fail(CB_ERR_INVALID_ARG, "args is NULL");
+  const cb_geom *geom = &a->geom;
+  const cb_ragged *rg = &a->rg;
+  // Validate every stage before enqueuing any of them.
+  CB_TRY(check_ragged(rg, true, true, true));
+  const int64_t n_tok = rg->h_tok_off[rg->n_req];
+  if (a->delta)
+    CB_TRY(validate_rerotate(geom, a->k, a->k, a->delta, n_tok, 1, a->rope_theta, a->rope_style));
+  CB_TRY(validate_devtopk(geom, rg, a->v_new_c, a->v, a->cand_idx, a->dev, a->sel_local,
+                          a->sel_global));
+  const int32_t k_total = rg->h_sel_off[rg->n_req];
+  CB_TRY(validate_fuse(geom, a->k, a->v, a->k_new_c, a->v_new_c, a->sel_local, a->sel_global,
+                       k_total));
+  CB_TRY(validate_attn(geom, rg, a->out, a->q_c, a->sel_local, a->sel_global, a->k, a->v,
+                       a->softmax_scale));
+  const hipStream_t s = (hipStream_t)stream;
+  if (a->delta && n_tok > 0)
+    CB_TRY(hip_status(cb::launch_rerotate(geom->dtype, a->rope_style, a->k, a->k, a->delta, n_tok,
+                                          1, geom->n_kv_heads, geom->head_dim,
+                                          rope_table(geom->head_dim, a->rope_theta), s),
+                      "rerotate"));
+  const int32_t m = rg->h_cand_off[rg->n_req];
+  CB_TRY(hip_status(cb::launch_deviation(geom->dtype, a->v_new_c, a->v, a->cand_idx, a->dev, m,
+                                         (int32_t)row_elems(geom), s),
+                    "deviation"));
+  if (k_total == 0) return CB_OK;
+  CB_TRY(hip_status(cb::launch_topk(rg->n_req, a->dev, a->cand_idx, rg->cand_off, rg->sel_off,
+                                    a->sel_local, a->sel_global, s),
+                    "topk"));
+  CB_TRY(hip_status(cb::launch_fuse(a->k, a->v, a->k_new_c, a->v_new_c, a->sel_local,
+                                    a->sel_global, k_total,
+                                    (int32_t)(row_elems(geom) * elem_size(geom->dtype)), s),
+                    "fuse_scatter"));
+  return run_attn(geom, rg, a->out, a->q_c, a->sel_local, a->sel_global, a->k, a->v,
+                  a->softmax_scale, s);
+}
+
+CB_EXPORT const char *cb_status_str(cb_status status) {
+  switch (status) {
+    case CB_OK: return "CB_OK";
+    case CB_ERR_INVALID_ARG: return "CB_ERR_INVALID_ARG";
+    case CB_ERR_UNSUPPORTED: return "CB_ERR_UNSUPPORTED";
+    case CB_ERR_HIP: return "CB_ERR_HIP";
+  }
+  return "unknown cb_status";
+}
+
+CB_EXPORT const char *cb_last_error(void) { return g_last_error.c_str(); }
+
+CB_EXPORT int32_t cb_abi_version(void) { return CB_ABI_VERSION; }

@@ -1,0 +1,67 @@
+// Internal launcher interface between the C ABI (api.cpp) and the kernels.
+// Every launcher enqueues on `stream` and returns the launch status; none of
+// them validates arguments (api.cpp does that before calling).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cb {
+
+// Turning speed of each RoPE pair in revolutions per position:
+// omega_j / (2 pi), omega_j = theta^(-2j/D), computed on the host in double.
+struct RopeTable {
+  double rev_per_pos[64];
+};
+
+enum : int { kF32 = 0, kBF16 = 1 };
+
+hipError_t launch_rerotate(int dtype, int style, void *k_out, const void *k_in,
+                           const int32_t *delta, int64_t n_tok, int32_t n_layers,
+                           int32_t n_kv_heads, int32_t head_dim,
+                           const RopeTable &tab, hipStream_t stream);
+
+hipError_t launch_deviation(int dtype, const void *v_new_c, const void *v_old,
+                            const int32_t *cand_idx, float *dev, int64_t m,
+                            int32_t row_elems, hipStream_t stream);
+
+hipError_t launch_topk(int32_t n_req, const float *dev, const int32_t *cand_idx,
+                       const int32_t *cand_off, const int32_t *sel_off,
+                       int32_t *sel_local, int32_t *sel_global,
+                       hipStream_t stream);
+
+hipError_t launch_fuse(void *k_fused, void *v_fused, const void *k_new_c,
+                       const void *v_new_c, const int32_t *sel_local,
+                       const int32_t *sel_global, int64_t k_total,
+                       int32_t row_bytes, hipStream_t stream);
+
+// Partial attention.  `tiles` is the number of query tiles over all requests
+// for the MFMA kernel (computed by the host from the selected counts).
+struct AttnArgs {
+  void *out;
+  const void *q_c;
+  const int32_t *sel_local;
+  const int32_t *sel_global;
+  const void *k_fused;
+  const void *v_fused;
+  const int32_t *tok_off;
+  const int32_t *sel_off;
+  int32_t n_req;
+  int32_t k_total;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  float softmax_scale;
+};
+
+// Rows of one MFMA query tile (64 query vectors = rows x group heads), or 0
+// if the MFMA kernel does not cover this geometry.
+int attn_mfma_rows_per_tile(int dtype, int32_t n_q_heads, int32_t n_kv_heads,
+                            int32_t head_dim);
+
+hipError_t launch_attn_mfma(const AttnArgs &a, int32_t rows_per_tile,
+                            int32_t n_tiles, hipStream_t stream);
+
+hipError_t launch_attn_simple(int dtype, const AttnArgs &a, hipStream_t stream);
+
+}  // namespace cb

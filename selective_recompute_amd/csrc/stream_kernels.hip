@@ -1,0 +1,352 @@
+// Bandwidth-bound kernels of the blend: key re-rotation, V deviation, the
+// per-request top-k selection and the row scatter that fuses the caches.
+//
+// Pages: [Derivations] = "数学推导" (CacheBlend math derivations page);
+// [KV-blog] = "rag的kvcache问题".
+#include <climits>
+
+#include "cb_device.hpp"
+#include "cb_launch.hpp"
+
+namespace cb {
+
+// ---------------------------------------------------------------------------
+// Re-rotation, [Derivations, "CacheBlend 中的应用"]: K_rot = R_delta K_old,
+// applied to each D/2 coordinate pairs of every KV head with the 2x2 block of
+// [Derivations, "RoPE 位置编码的相对位置不变性证明"].
+//
+// A thread owns one "unit": VP consecutive pairs of one head (VP = 8 for
+// bf16, 4 for fp32 so that each half is one 16-byte access).  Its pairs are
+// fixed for the whole kernel, so the cos/sin of its VP angles are computed
+// only when delta changes between the tokens it visits (a token's delta is
+// the start of its chunk, so that happens once per chunk) and are reused
+// across all layers.  Angles are reduced in double precision to a fraction
+// of a turn before the fp32 sincos, so |delta| up to 2^31 keeps ~1e-7 rad.
+// ---------------------------------------------------------------------------
+template <typename T, int STYLE>
+__global__ __launch_bounds__(1024) void rerotate_kernel(
+    T *__restrict__ k_out, const T *__restrict__ k_in,
+    const int32_t *__restrict__ delta, int64_t n_tok, int32_t n_layers,
+    int32_t head_dim, int32_t units_per_head, int32_t units_per_row,
+    int32_t tok_per_iter, int32_t tok_per_block, RopeTable tab) {
+  constexpr int VP = Vec16<T>::N;  // pairs per unit
+  const int tid = threadIdx.x;
+  const int unit = tid % units_per_row;
+  const int slot = tid / units_per_row;
+  const int head = unit / units_per_head;
+  const int j0 = (unit % units_per_head) * VP;
+  const int64_t row_elems = (int64_t)(units_per_row / units_per_head) * head_dim;
+  const bool in_place = (k_out == k_in);
+
+  double rev[VP];
+#pragma unroll
+  for (int i = 0; i < VP; ++i) rev[i] = tab.rev_per_pos[j0 + i];
+  float cs[VP], sn[VP];
+  int cur = INT_MIN;
+
+  const int64_t t_begin = (int64_t)blockIdx.x * tok_per_block;
+  const int64_t t_end = t_begin + tok_per_block < n_tok ? t_begin + tok_per_block : n_tok;
+  for (int64_t t = t_begin + slot; t < t_end; t += tok_per_iter) {
+    const int d = delta[t];
+    if (d == 0 && in_place) continue;  // R_0 = I
+    if (d != cur && d != 0) {
+      cur = d;
+#pragma unroll
+      for (int i = 0; i < VP; ++i) {
+        const double turns = (double)d * rev[i];
+        const double frac = turns - rint(turns);            // in [-1/2, 1/2]
+        const float ang = (float)(frac * 6.283185307179586476925);
+        sincosf(ang, &sn[i], &cs[i]);
+      }
+    }
+    for (int l = 0; l < n_layers; ++l) {
+      const int64_t off = ((int64_t)l * n_tok + t) * row_elems + (int64_t)head * head_dim;
+      const T *src = k_in + off;
+      T *dst = k_out + off;
+      float a[VP], b[VP];
+      if (STYLE == 0) {  // pairs (j, j + D/2)
+        Vec16<T>::load(src + j0, a);
+        Vec16<T>::load(src + head_dim / 2 + j0, b);
+      } else {           // pairs (2j, 2j + 1)
+        float x0[VP], x1[VP];
+        Vec16<T>::load(src + 2 * j0, x0);
+        Vec16<T>::load(src + 2 * j0 + VP, x1);
+#pragma unroll
+        for (int i = 0; i < VP / 2; ++i) {
+          a[i] = x0[2 * i]; b[i] = x0[2 * i + 1];
+          a[VP / 2 + i] = x1[2 * i]; b[VP / 2 + i] = x1[2 * i + 1];
+        }
+      }
+      if (d != 0) {
+#pragma unroll
+        for (int i = 0; i < VP; ++i) {
+          const float x = a[i], y = b[i];
+          a[i] = fmaf(x, cs[i], -y * sn[i]);
+          b[i] = fmaf(x, sn[i], y * cs[i]);
+        }
+      }
+      if (STYLE == 0) {
+        Vec16<T>::store(dst + j0, a);
+        Vec16<T>::store(dst + head_dim / 2 + j0, b);
+      } else {
+        float x0[VP], x1[VP];
+#pragma unroll
+        for (int i = 0; i < VP / 2; ++i) {
+          x0[2 * i] = a[i]; x0[2 * i + 1] = b[i];
+          x1[2 * i] = a[VP / 2 + i]; x1[2 * i + 1] = b[VP / 2 + i];
+        }
+        Vec16<T>::store(dst + 2 * j0, x0);
+        Vec16<T>::store(dst + 2 * j0 + VP, x1);
+      }
+    }
+  }
+}
+
+template <typename T, int STYLE>
+static hipError_t rerotate_typed(void *k_out, const void *k_in, const int32_t *delta,
+                                 int64_t n_tok, int32_t n_layers, int32_t n_kv_heads,
+                                 int32_t head_dim, const RopeTable &tab, hipStream_t stream) {
+  constexpr int VP = Vec16<T>::N;
+  const int units_per_head = (head_dim / 2) / VP;
+  const int units_per_row = units_per_head * n_kv_heads;
+  const int tok_per_iter = units_per_row >= 256 ? 1 : 256 / units_per_row;
+  const int threads = units_per_row * tok_per_iter;
+  // Enough blocks to fill the chip; each block then walks a short contiguous
+  // token range so the cached trig is reused within a chunk.
+  int64_t iters = (n_tok + (int64_t)tok_per_iter * 2048 - 1) / ((int64_t)tok_per_iter * 2048);
+  if (iters < 1) iters = 1;
+  if (iters > 16) iters = 16;
+  const int tok_per_block = (int)(tok_per_iter * iters);
+  const int64_t blocks = (n_tok + tok_per_block - 1) / tok_per_block;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((rerotate_kernel<T, STYLE>), dim3((unsigned)blocks), dim3(threads), 0, stream,
+                     (T *)k_out, (const T *)k_in, delta, n_tok, n_layers, head_dim,
+                     units_per_head, units_per_row, tok_per_iter, tok_per_block, tab);
+  return hipGetLastError();
+}
+
+hipError_t launch_rerotate(int dtype, int style, void *k_out, const void *k_in,
+                           const int32_t *delta, int64_t n_tok, int32_t n_layers,
+                           int32_t n_kv_heads, int32_t head_dim, const RopeTable &tab,
+                           hipStream_t stream) {
+  if (dtype == kBF16)
+    return style == 0 ? rerotate_typed<bf16, 0>(k_out, k_in, delta, n_tok, n_layers, n_kv_heads, head_dim, tab, stream)
+                      : rerotate_typed<bf16, 1>(k_out, k_in, delta, n_tok, n_layers, n_kv_heads, head_dim, tab, stream);
+  return style == 0 ? rerotate_typed<float, 0>(k_out, k_in, delta, n_tok, n_layers, n_kv_heads, head_dim, tab, stream)
+                    : rerotate_typed<float, 1>(k_out, k_in, delta, n_tok, n_layers, n_kv_heads, head_dim, tab, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Deviation, [Derivations, "近似解"]: dev[j] = ||V_new_c[j] - V_old[cand[j]]||^2
+// over all KV heads and dims.  One wave per candidate row, 16-byte loads,
+// fp32 fused multiply-add accumulation, butterfly reduction across the wave.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void deviation_kernel(
+    const T *__restrict__ v_new_c, const T *__restrict__ v_old,
+    const int32_t *__restrict__ cand_idx, float *__restrict__ dev, int64_t m,
+    int32_t row_elems) {
+  constexpr int V = Vec16<T>::N;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+  const int64_t n_waves = ((int64_t)gridDim.x * blockDim.x) / kWave;
+  const int nvec = row_elems / V;
+  for (int64_t j = wave; j < m; j += n_waves) {
+    const T *a = v_new_c + j * row_elems;
+    const T *b = v_old + (int64_t)cand_idx[j] * row_elems;
+    float acc = 0.f;
+    for (int v = lane; v < nvec; v += kWave) {
+      float x[V], y[V];
+      Vec16<T>::load(a + v * V, x);
+      Vec16<T>::load(b + v * V, y);
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const float df = x[i] - y[i];
+        acc = fmaf(df, df, acc);
+      }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) dev[j] = acc;
+  }
+}
+
+hipError_t launch_deviation(int dtype, const void *v_new_c, const void *v_old,
+                            const int32_t *cand_idx, float *dev, int64_t m,
+                            int32_t row_elems, hipStream_t stream) {
+  if (m == 0) return hipSuccess;
+  int64_t blocks = (m + 3) / 4;  // 4 waves per block, one row per wave
+  if (blocks > 8192) blocks = 8192;
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(deviation_kernel<bf16>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const bf16 *)v_new_c, (const bf16 *)v_old, cand_idx, dev, m, row_elems);
+  else
+    hipLaunchKernelGGL(deviation_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const float *)v_new_c, (const float *)v_old, cand_idx, dev, m, row_elems);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Top-k, [Derivations, "近似解"] (greedy TopK of the deviation) with ties to
+// the lower index and NaN above +inf.  One 1024-thread workgroup per request:
+//   1. MSB-first radix select over the order-preserving uint32 key of each
+//      fp32 score (4 passes of 8 bits, LDS histogram) finds the exact key tau
+//      of the k-th largest score and how many keys equal to tau to keep;
+//   2. an ordered compaction emits, in candidate order (= ascending packed
+//      row), every key > tau and the first `keep_eq` keys == tau.
+// ---------------------------------------------------------------------------
+__device__ inline uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (x != x) return 0xFFFFFFFFu;          // NaN ranks first
+  if (u == 0x80000000u) u = 0u;            // -0 ranks with +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkWaves = kTopkThreads / kWave;
+
+// Exclusive block-wide prefix of two per-thread counts.
+__device__ inline void block_excl_scan2(uint32_t a, uint32_t b, uint32_t &a_excl, uint32_t &b_excl,
+                                        uint32_t (*wave_tot)[kTopkWaves]) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int ai = wave_incl_scan((int)a), bi = wave_incl_scan((int)b);
+  if (lane == kWave - 1) { wave_tot[0][wave] = ai; wave_tot[1][wave] = bi; }
+  __syncthreads();
+  uint32_t a_before = 0, b_before = 0;
+  for (int w = 0; w < wave; ++w) { a_before += wave_tot[0][w]; b_before += wave_tot[1][w]; }
+  a_excl = a_before + ai - a;
+  b_excl = b_before + bi - b;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(
+    const float *__restrict__ dev, const int32_t *__restrict__ cand_idx,
+    const int32_t *__restrict__ cand_off, const int32_t *__restrict__ sel_off,
+    int32_t *__restrict__ sel_local, int32_t *__restrict__ sel_global) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh_digit, sh_above;
+  __shared__ uint32_t wave_tot[2][kTopkWaves];
+
+  const int r = blockIdx.x;
+  const int c0 = cand_off[r];
+  const int m = cand_off[r + 1] - c0;
+  const int s0 = sel_off[r];
+  const int k = sel_off[r + 1] - s0;
+  const int tid = threadIdx.x;
+  if (k <= 0) return;
+  if (k >= m) {  // every candidate is selected
+    for (int j = tid; j < m; j += kTopkThreads) {
+      sel_local[s0 + j] = c0 + j;
+      sel_global[s0 + j] = cand_idx[c0 + j];
+    }
+    return;
+  }
+
+  uint32_t prefix = 0, mask = 0, krem = (uint32_t)k;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0;
+    __syncthreads();
+    for (int j = tid; j < m; j += kTopkThreads) {
+      const uint32_t key = order_key(dev[c0 + j]);
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid < kWave) {
+      uint32_t h[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) h[q] = hist[4 * tid + q];
+      const uint32_t tot = h[0] + h[1] + h[2] + h[3];
+      uint32_t suf = tot;  // sum over this lane's bins and every higher lane's
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t t = __shfl_down(suf, off, kWave);
+        if (tid + off < kWave) suf += t;
+      }
+      uint32_t above = suf - tot;
+      if (above < krem && suf >= krem) {
+        for (int q = 3; q >= 0; --q) {
+          if (above + h[q] >= krem) { sh_digit = 4 * tid + q; sh_above = above; break; }
+          above += h[q];
+        }
+      }
+    }
+    __syncthreads();
+    prefix |= sh_digit << shift;
+    mask |= 255u << shift;
+    krem -= sh_above;
+    __syncthreads();
+  }
+  const uint32_t tau = prefix;   // key of the k-th largest score
+  const uint32_t keep_eq = krem; // how many keys equal to tau are selected
+
+  // Ordered compaction over contiguous per-thread segments.
+  const int seg = (m + kTopkThreads - 1) / kTopkThreads;
+  const int jb = tid * seg < m ? tid * seg : m;
+  const int je = jb + seg < m ? jb + seg : m;
+  uint32_t n_gt = 0, n_eq = 0;
+  for (int j = jb; j < je; ++j) {
+    const uint32_t key = order_key(dev[c0 + j]);
+    n_gt += key > tau;
+    n_eq += key == tau;
+  }
+  uint32_t gt_before, eq_before;
+  block_excl_scan2(n_gt, n_eq, gt_before, eq_before, wave_tot);
+  for (int j = jb; j < je; ++j) {
+    const uint32_t key = order_key(dev[c0 + j]);
+    const bool gt = key > tau, eq = key == tau;
+    const bool take = gt || (eq && eq_before < keep_eq);
+    if (take) {
+      const uint32_t pos = gt_before + (eq_before < keep_eq ? eq_before : keep_eq);
+      sel_local[s0 + pos] = c0 + j;
+      sel_global[s0 + pos] = cand_idx[c0 + j];
+    }
+    gt_before += gt;
+    eq_before += eq;
+  }
+}
+
+hipError_t launch_topk(int32_t n_req, const float *dev, const int32_t *cand_idx,
+                       const int32_t *cand_off, const int32_t *sel_off, int32_t *sel_local,
+                       int32_t *sel_global, hipStream_t stream) {
+  if (n_req == 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_kernel, dim3(n_req), dim3(kTopkThreads), 0, stream, dev, cand_idx,
+                     cand_off, sel_off, sel_local, sel_global);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fuse, [Derivations, "形式化"]: row sel_global[s] of K/V takes row
+// sel_local[s] of the recomputed tensors.  16-byte copies; a row is covered
+// by consecutive threads so every access is a contiguous run.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fuse_kernel(
+    uint4 *__restrict__ k_fused, uint4 *__restrict__ v_fused,
+    const uint4 *__restrict__ k_new_c, const uint4 *__restrict__ v_new_c,
+    const int32_t *__restrict__ sel_local, const int32_t *__restrict__ sel_global,
+    int64_t k_total, int32_t row_vec) {
+  const int64_t total = k_total * row_vec;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int64_t s = i / row_vec;
+    const int c = (int)(i - s * row_vec);
+    const int64_t src = (int64_t)sel_local[s] * row_vec + c;
+    const int64_t dst = (int64_t)sel_global[s] * row_vec + c;
+    k_fused[dst] = k_new_c[src];
+    v_fused[dst] = v_new_c[src];
+  }
+}
+
+hipError_t launch_fuse(void *k_fused, void *v_fused, const void *k_new_c, const void *v_new_c,
+                       const int32_t *sel_local, const int32_t *sel_global, int64_t k_total,
+                       int32_t row_bytes, hipStream_t stream) {
+  const int32_t row_vec = row_bytes / 16;
+  const int64_t total = k_total * row_vec;
+  if (total == 0) return hipSuccess;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(fuse_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (uint4 *)k_fused,
+                     (uint4 *)v_fused, (const uint4 *)k_new_c, (const uint4 *)v_new_c, sel_local,
+                     sel_global, k_total, row_vec);
+  return hipGetLastError();
+}
+
+}  // namespace cb

@@ -1,0 +1,325 @@
+"""GPU parity: every HIP kernel, called through the C ABI, against the CPU oracle.
+
+Bars (floating point against the oracle's unrounded fp64 values):
+* re-rotated K: |err| <= max(1e-2, half a bf16 ulp of the reference + 1e-5)
+  (for |k| >= 4 a bf16 half-ulp alone exceeds 1e-2, so the widening is the
+  least any bf16 result can meet);
+* deviation: relative error <= 1e-4;
+* attention output: |err| <= 2e-2;
+* selected index sets and fused rows: bit-exact.
+Inputs come from the seeded generator; the planted tiers keep a relative gap
+far above 1e-3 at every selection boundary (checked on the oracle side).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import cacheblend_oracle as O
+from selective_recompute_amd import binding as B
+from selective_recompute_amd import pipeline as PL
+from selective_recompute_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+K_ABS = 1e-2
+DEV_REL = 1e-4
+ATTN_ABS = 2e-2
+
+
+def np64(t):
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def npi(t):
+    return t.detach().to("cpu").numpy().astype(np.int64)
+
+
+def say(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def assert_k_close(gpu, ref, dtype, what="K"):
+    err = np.abs(gpu - ref)
+    if dtype == torch.bfloat16:
+        mag = np.maximum(np.abs(ref), 1e-30)
+        ulp = 2.0 ** (np.floor(np.log2(mag)) - 7)
+        tol = np.maximum(K_ABS, 0.5 * ulp + 1e-5)
+    else:
+        tol = np.full_like(ref, K_ABS)
+    bad = err > tol
+    assert not bad.any(), f"{what}: {bad.sum()} elements out of tolerance, max err {err.max()}"
+
+
+def assert_dev_close(gpu, ref):
+    rel = np.abs(gpu - ref) / np.maximum(ref, 1e-30)
+    assert np.all((ref == 0) == (gpu == 0))
+    assert rel.max() <= DEV_REL, f"deviation rel err {rel.max()}"
+
+
+# ------------------------------------------------------------------ rerotate --
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("style", [B.ROPE_HALF, B.ROPE_INTERLEAVED])
+@pytest.mark.parametrize("hkv,d", [(2, 16), (1, 32), (8, 128), (3, 64), (16, 128)])
+@pytest.mark.parametrize("in_place", [True, False])
+def test_rerotate_parity(dtype, style, hkv, d, in_place):
+    say(f"rerotate dtype={dtype} style={style} hkv={hkv} d={d} in_place={in_place}")
+    rng = np.random.default_rng(hkv * 1000 + d + style)
+    chunks = [37, 64, 200, 3]
+    n_layers = 3
+    delta = np.concatenate([np.full(n, s) for n, s in
+                            zip(chunks, [0, 37, 60000, 101])]).astype(np.int32)
+    t_count = len(delta)
+    k = torch.from_numpy(rng.standard_normal((n_layers, t_count, hkv, d)).astype(np.float32)).to(dtype)
+    k_np = np64(k)
+    k_in = k.to(DEV)
+    k_out = k_in if in_place else torch.full_like(k_in, float("nan"))
+    g = B.geom(hkv, hkv, d, dtype)
+    B.rerotate(g, k_out, k_in, torch.from_numpy(delta).to(DEV), t_count, n_layers, 10000.0, style)
+    torch.cuda.synchronize()
+    got = np64(k_out)
+    for layer in range(n_layers):
+        ref = O.rerotate(k_np[layer], delta, 10000.0, style)
+        assert_k_close(got[layer], ref, dtype)
+        # rows with delta 0 are bit-identical to the input
+        zero = delta == 0
+        assert np.array_equal(got[layer][zero], k_np[layer][zero])
+
+
+# --------------------------------------------------------- deviation + top-k --
+def _gpu_devtopk(wl, x, k_counts):
+    g = B.geom(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.torch_dtype)
+    sel_off = PL.offsets(k_counts)
+    rb = B.RaggedBatch(x["h_tok_off"], x["h_cand_off"], sel_off, DEV)
+    m, k = rb.n_cand, rb.n_sel
+    dev = torch.empty(m, dtype=torch.float32, device=DEV)
+    sl = torch.empty(k, dtype=torch.int32, device=DEV)
+    sg = torch.empty(k, dtype=torch.int32, device=DEV)
+    B.deviation_topk(g, rb, x["v_new_c"].to(DEV), x["v_old"].to(DEV), x["cand_idx"].to(DEV),
+                     dev, sl, sg)
+    torch.cuda.synchronize()
+    return dev.cpu().numpy().astype(np.float64), npi(sl), npi(sg)
+
+
+@pytest.mark.parametrize("name,layer", [("c0", 0), ("c1", 0), ("c2", 0), ("c2", 1), ("c2", 4)])
+def test_deviation_topk_parity(name, layer):
+    say(f"deviation_topk {name} layer {layer}")
+    wl = W.make_workload(name)
+    x = W.layer_inputs(wl, W.PlantedSets(wl), layer)
+    counts = PL.GradualFilter(wl.request_lengths, wl.r1_pct, wl.r2_pct).counts(layer)
+    dev, sl, sg = _gpu_devtopk(wl, x, counts)
+    cand = npi(x["cand_idx"])
+    ref_dev = O.deviation(np64(x["v_new_c"]), np64(x["v_old"]), cand)
+    assert_dev_close(dev, ref_dev)
+    off = x["h_cand_off"]
+    sel_off = PL.offsets(counts)
+    for r in range(wl.n_requests):
+        loc, glob = O.topk_select(ref_dev[off[r]:off[r + 1]], cand[off[r]:off[r + 1]], counts[r])
+        assert np.array_equal(sg[sel_off[r]:sel_off[r + 1]], glob)
+        assert np.array_equal(sl[sel_off[r]:sel_off[r + 1]], loc + off[r])
+
+
+def test_topk_exact_ties_and_specials():
+    say("topk ties / NaN / inf / k in {0, M} / ragged")
+    rng = np.random.default_rng(42)
+    lens = [1, 7, 300, 2048, 5000, 33, 0]
+    ks = [1, 0, 150, 2048, 1234, 17, 0]
+    devs, cands = [], []
+    base = 0
+    for n in lens:
+        d = rng.integers(0, 4, size=n).astype(np.float32)     # exact ties everywhere
+        devs.append(d)
+        cands.append(np.sort(rng.choice(10 ** 6, size=n, replace=False)) + base)
+        base += 10 ** 6
+    devs[3][[5, 900]] = np.nan
+    devs[3][[7, 8]] = np.inf
+    devs[4][::7] = -0.0
+    devs[4][::11] = 0.0
+    dev = np.concatenate(devs)
+    cand = np.concatenate(cands).astype(np.int32)
+    cand_off = PL.offsets(lens)
+    sel_off = PL.offsets(ks)
+    rb = B.RaggedBatch(cand_off, cand_off, sel_off, DEV)
+    sl = torch.empty(rb.n_sel, dtype=torch.int32, device=DEV)
+    sg = torch.empty(rb.n_sel, dtype=torch.int32, device=DEV)
+    B.topk(rb, torch.from_numpy(dev).to(DEV), torch.from_numpy(cand).to(DEV), sl, sg)
+    torch.cuda.synchronize()
+    sl, sg = npi(sl), npi(sg)
+    for r in range(len(lens)):
+        loc, glob = O.topk_select(dev[cand_off[r]:cand_off[r + 1]].astype(np.float64),
+                                  cand[cand_off[r]:cand_off[r + 1]], ks[r])
+        assert np.array_equal(sg[sel_off[r]:sel_off[r + 1]], glob), r
+        assert np.array_equal(sl[sel_off[r]:sel_off[r + 1]], loc + cand_off[r]), r
+
+
+# ---------------------------------------------------------------------- fuse --
+@pytest.mark.parametrize("dtype,hkv,d", [(torch.float32, 2, 16), (torch.bfloat16, 8, 128)])
+def test_fuse_scatter_bit_exact(dtype, hkv, d):
+    say(f"fuse dtype={dtype} hkv={hkv} d={d}")
+    rng = np.random.default_rng(1)
+    t_count, m, k = 1000, 400, 123
+    kf = torch.randn(t_count, hkv, d).to(dtype)
+    vf = torch.randn(t_count, hkv, d).to(dtype)
+    kn = torch.randn(m, hkv, d).to(dtype)
+    vn = torch.randn(m, hkv, d).to(dtype)
+    loc = np.sort(rng.choice(m, k, replace=False)).astype(np.int32)
+    glob = np.sort(rng.choice(t_count, k, replace=False)).astype(np.int32)
+    kg, vg = kf.to(DEV), vf.to(DEV)
+    B.fuse_scatter(B.geom(hkv, hkv, d, dtype), kg, vg, kn.to(DEV), vn.to(DEV),
+                   torch.from_numpy(loc).to(DEV), torch.from_numpy(glob).to(DEV), k)
+    torch.cuda.synchronize()
+    kr, vr = kf.clone(), vf.clone()
+    kr[glob] = kn[loc]
+    vr[glob] = vn[loc]
+    assert torch.equal(kg.cpu(), kr) and torch.equal(vg.cpu(), vr)
+
+
+# ----------------------------------------------------------------- attention --
+ATTN_CASES = [
+    # (dtype, hq, hkv, d, request lengths, selected per request)
+    (torch.bfloat16, 32, 8, 128, [2048], [308]),
+    (torch.bfloat16, 64, 8, 128, [700, 1500, 33], [100, 257, 33]),
+    (torch.bfloat16, 8, 8, 64, [500, 90], [64, 1]),
+    (torch.bfloat16, 16, 1, 32, [1000], [77]),
+    (torch.bfloat16, 4, 2, 128, [129, 64, 1], [65, 64, 1]),
+    (torch.bfloat16, 6, 2, 64, [300], [40]),          # group 3: plain kernel
+    (torch.bfloat16, 4, 2, 16, [200], [30]),          # head_dim 16: plain kernel
+    (torch.float32, 4, 2, 16, [64, 64], [10, 10]),
+    (torch.float32, 32, 8, 128, [1000], [50]),
+    (torch.bfloat16, 128, 2, 128, [300, 0, 200], [40, 0, 9]),  # group 64, empty request
+]
+
+
+@pytest.mark.parametrize("case", ATTN_CASES, ids=[f"a{i}" for i in range(len(ATTN_CASES))])
+def test_partial_attention_parity(case):
+    dtype, hq, hkv, d, lens, ks = case
+    say(f"attention {case}")
+    rng = np.random.default_rng(sum(lens) + hq)
+    t_count = sum(lens)
+    tok_off = PL.offsets(lens)
+    sel_off = PL.offsets(ks)
+    sel_g, row_start = [], []
+    for r, (n, k) in enumerate(zip(lens, ks)):
+        rows = np.sort(rng.choice(n, k, replace=False)) if k else np.zeros(0, np.int64)
+        if k and k < n:
+            rows[-1] = n - 1                                  # exercise the longest row
+            rows = np.unique(rows)
+            while len(rows) < k:
+                rows = np.unique(np.concatenate([rows, rng.choice(n, 1)]))
+        sel_g.append(rows + tok_off[r])
+        row_start.append(np.full(k, tok_off[r]))
+    sel_g = np.concatenate(sel_g).astype(np.int32)
+    row_start = np.concatenate(row_start)
+    m = t_count
+    sel_l = sel_g.copy()                                      # candidates = all tokens
+    q = torch.randn(m, hq, d).to(dtype)
+    kf = torch.randn(t_count, hkv, d).to(dtype)
+    vf = torch.randn(t_count, hkv, d).to(dtype)
+    rb = B.RaggedBatch(tok_off, tok_off, sel_off, DEV)
+    out = torch.full((rb.n_sel, hq, d), float("nan"), dtype=dtype, device=DEV)
+    scale = 1.0 / math.sqrt(d)
+    B.partial_attn(B.geom(hq, hkv, d, dtype), rb, out, q.to(DEV), torch.from_numpy(sel_l).to(DEV),
+                   torch.from_numpy(sel_g).to(DEV), kf.to(DEV), vf.to(DEV), scale)
+    torch.cuda.synchronize()
+    ref = O.attention_rows(np64(q), sel_l, sel_g, row_start, np64(kf), np64(vf), hq, hkv, scale)
+    got = np64(out)
+    err = np.abs(got - ref)
+    assert np.isfinite(got).all()
+    assert err.max() <= ATTN_ABS, f"max err {err.max()}"
+
+
+# ------------------------------------------------------------- end to end ----
+def _oracle_layer(wl, x, cand, counts, attend_rows=None):
+    """Oracle for one layer on the exact stored inputs; attention only for the
+    selected positions listed in attend_rows (None = all)."""
+    k_old, v_old = np64(x["k_old"]), np64(x["v_old"])
+    k_rot = O.rerotate(k_old, wl.delta(), wl.rope_theta)
+    dev = O.deviation(np64(x["v_new_c"]), v_old, cand)
+    cand_off = x["h_cand_off"]
+    sel_l, sel_g, row_start = [], [], []
+    tok_off = wl.tok_off
+    for r in range(wl.n_requests):
+        a, b = cand_off[r], cand_off[r + 1]
+        loc, glob = O.topk_select(dev[a:b], cand[a:b], counts[r])
+        sel_l.append(loc + a)
+        sel_g.append(glob)
+        row_start.append(np.full(len(glob), tok_off[r]))
+    sel_l, sel_g, row_start = map(np.concatenate, (sel_l, sel_g, row_start))
+    k_fused, v_fused = O.fuse(k_rot, v_old, np64(x["k_new_c"]), np64(x["v_new_c"]), sel_l, sel_g)
+    rows = np.arange(len(sel_g)) if attend_rows is None else attend_rows
+    q_rows = np64(x["q_c"][torch.from_numpy(sel_l[rows])])
+    out = O.attention_rows(q_rows, np.arange(len(rows)), sel_g[rows], row_start[rows], k_fused,
+                           v_fused, wl.n_q_heads, wl.n_kv_heads, 1.0 / math.sqrt(wl.head_dim))
+    return dict(k_rot=k_rot, dev=dev, sel_local=sel_l, sel_global=sel_g, k_fused=k_fused,
+                v_fused=v_fused, out=out, rows=rows)
+
+
+E2E = [("c0", [0], None), ("c1", [0], None), ("c2", [0, 1, 2], 96),
+       ("c3", [0, 1], 24), ("c4", [0, 1], 24)]
+
+
+@pytest.mark.parametrize("name,layers,n_rows", E2E, ids=[e[0] for e in E2E])
+def test_blend_layers_end_to_end(name, layers, n_rows):
+    wl = W.make_workload(name)
+    sets = W.PlantedSets(wl)
+    gen_dev = "cpu" if wl.n_tokens <= 8192 else DEV
+    runner = PL.BlendRunner(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.torch_dtype,
+                            wl.request_lengths, wl.r1_pct, wl.r2_pct, max(layers) + 1,
+                            wl.rope_theta)
+    for layer in layers:
+        say(f"blend {name} layer {layer}")
+        x = W.layer_inputs(wl, sets, layer, device=gen_dev)
+        xg = {k: (v.to(DEV) if torch.is_tensor(v) else v) for k, v in x.items()}
+        k_pristine = x["k_old"].cpu() if gen_dev == "cpu" else x["k_old"].clone().cpu()
+        x_cpu = dict(x)
+        x_cpu["k_old"], x_cpu["v_old"] = k_pristine, x["v_old"].clone().cpu()
+        x_cpu["v_new_c"], x_cpu["k_new_c"] = x["v_new_c"].cpu(), x["k_new_c"].cpu()
+        x_cpu["q_c"] = x["q_c"].cpu()
+        if layer > 0:
+            # the device keeps layer 1's selection as this layer's candidates
+            assert np.array_equal(npi(runner.candidates(layer)), npi(x["cand_idx"]))
+        o = runner.run_layer(layer, xg)
+        torch.cuda.synchronize()
+        counts = runner.filter.counts(layer)
+        cand = npi(x["cand_idx"])
+        n_sel = int(np.sum(counts))
+        rows = None
+        if n_rows is not None and n_rows < n_sel:
+            rng = np.random.default_rng(layer)
+            rows = np.unique(np.concatenate([[0, n_sel - 1], rng.choice(n_sel, n_rows, replace=False)]))
+        ref = _oracle_layer(wl, x_cpu, cand, counts, rows)
+        assert_dev_close(o["dev"].cpu().numpy().astype(np.float64), ref["dev"])
+        assert np.array_equal(npi(o["sel_global"]), ref["sel_global"])
+        assert np.array_equal(npi(o["sel_local"]), ref["sel_local"])
+        assert np.array_equal(ref["sel_global"], x["planted"])
+        # fused cache: selected rows bit-exact new rows, others the rotated keys
+        kf, vf = np64(xg["k_old"]), np64(xg["v_old"])
+        sel = ref["sel_global"]
+        assert np.array_equal(kf[sel], np64(x_cpu["k_new_c"])[ref["sel_local"]])
+        assert np.array_equal(vf, ref["v_fused"])
+        mask = np.ones(wl.n_tokens, bool)
+        mask[sel] = False
+        assert_k_close(kf[mask], ref["k_rot"][mask], wl.torch_dtype, "fused K")
+        got = np64(o["out"])[ref["rows"]]
+        err = np.abs(got - ref["out"])
+        assert err.max() <= ATTN_ABS, f"attention max err {err.max()}"
+
+
+def test_blend_is_deterministic():
+    say("determinism c1")
+    wl = W.make_workload("c1")
+    sets = W.PlantedSets(wl)
+    outs = []
+    for _ in range(2):
+        x = {k: (v.to(DEV) if torch.is_tensor(v) else v)
+             for k, v in W.layer_inputs(wl, sets, 0).items()}
+        runner = PL.BlendRunner(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.torch_dtype,
+                                wl.request_lengths, wl.r1_pct, wl.r2_pct, 1, wl.rope_theta)
+        o = runner.run_layer(0, x)
+        torch.cuda.synchronize()
+        outs.append((x["k_old"].cpu(), x["v_old"].cpu(), o["dev"].cpu(), o["sel_global"].cpu(),
+                     o["out"].cpu()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)

@@ -1,0 +1,82 @@
+"""Generator tests (CPU): determinism, planted structure, and the selection gap.
+
+The gap and the planted selection are checked with the CPU oracle's own
+deviation and top-k, on the exact stored values.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import cacheblend_oracle as O
+from selective_recompute_amd import workloads as W
+
+
+def _np64(t):
+    return t.to(torch.float64).cpu().numpy()
+
+
+def test_presets_shapes():
+    c0, c1 = W.make_workload("c0"), W.make_workload("c1")
+    assert c0.n_tokens == 128 and c0.head_dim == 16 and c0.dtype == "f32"
+    assert c1.n_tokens == 2048 and (c1.n_q_heads, c1.n_kv_heads) == (32, 8)
+    c2, c3, c4 = (W.make_workload(n) for n in ("c2", "c3", "c4"))
+    assert (c2.n_tokens, c2.n_layers) == (6144, 32)
+    assert (c3.n_tokens, c3.n_layers) == (32768, 32)
+    assert c4.n_requests == 8 and c4.n_layers == 80 and 57344 <= c4.n_tokens <= 73728
+    for chunk_lens in c4.chunks:
+        assert 2 <= len(chunk_lens) <= 16
+        assert all(256 <= n <= 4096 for n in chunk_lens)
+    # deterministic draw
+    assert W.make_workload("c4").chunks == c4.chunks
+
+
+def test_delta_is_chunk_start():
+    wl = W.make_workload("c0")
+    d = wl.delta()
+    assert list(d[:64]) == [0] * 64 and list(d[64:]) == [64] * 64
+    assert np.array_equal(wl.positions() - d, np.tile(np.arange(64), 2))   # chunk-local p_old
+
+
+def test_generation_is_deterministic():
+    wl = W.make_workload("c0")
+    a = W.layer_inputs(wl, W.PlantedSets(wl), 0)
+    b = W.layer_inputs(wl, W.PlantedSets(wl), 0)
+    for key in ("k_old", "v_old", "k_new_c", "v_new_c", "q_c", "cand_idx"):
+        assert torch.equal(a[key], b[key])
+    c = W.layer_inputs(wl, W.PlantedSets(wl), 0, draw=1)
+    assert not torch.equal(a["k_old"], c["k_old"])
+
+
+@pytest.mark.parametrize("name,layers", [("c0", [0]), ("c1", [0]), ("c2", [0, 1, 2, 5])])
+@pytest.mark.parametrize("schedule", ["pool", "chain"])
+def test_planted_selection_has_gap(name, layers, schedule):
+    wl = W.make_workload(name)
+    sets = W.PlantedSets(wl, schedule)
+    for layer in layers:
+        x = W.layer_inputs(wl, sets, layer)
+        cand = x["cand_idx"].numpy().astype(np.int64)
+        dev = O.deviation(_np64(x["v_new_c"]), _np64(x["v_old"]), cand)
+        offs = x["h_cand_off"]
+        for r in range(wl.n_requests):
+            n = wl.request_lengths[r]
+            _, k = O.layer_plan(layer + 1, n, wl.r1_pct, wl.r2_pct)
+            d_r = dev[offs[r]:offs[r + 1]]
+            _, glob = O.topk_select(d_r, cand[offs[r]:offs[r + 1]], k)
+            planted = x["planted"][x["planted_off"][r]:x["planted_off"][r + 1]]
+            assert np.array_equal(glob, planted)
+            srt = np.sort(d_r)[::-1]
+            if k < len(srt):
+                assert (srt[k - 1] - srt[k]) / srt[k - 1] > 1e-3, (name, layer, r)
+
+
+def test_persistence_and_pool():
+    wl = W.make_workload("c2")
+    sets = W.PlantedSets(wl)
+    l0, l1, l2 = sets.layer(0), sets.layer(1), sets.layer(2)
+    assert l0.hot.sum() == 922 and len(l0.planted) == 1844
+    assert np.array_equal(l1.cand_idx, l0.planted) and np.array_equal(l2.cand_idx, l0.planted)
+    assert np.sum(l0.hot & l1.hot) == 738 and np.sum(l1.hot & l2.hot) == 738
+    assert len(l1.planted) == 922 and len(l2.planted) == 922
+    chain = W.PlantedSets(wl, "chain")
+    assert np.array_equal(chain.layer(1).cand_idx, l0.planted)
+    assert np.array_equal(chain.layer(2).cand_idx, chain.layer(1).planted)
