@@ -177,7 +177,7 @@ def main():
                                        rope_theta=wl.rope_theta, rope_style=B.ROPE_HALF,
                                        softmax_scale=runner.scale, dev=o["dev"],
                                        sel_local=o["sel_local"], sel_global=o["sel_global"],
-                                       out=o["out"]))
+                                       out=o["out"], workspace=runner.workspace))
         prepared.append(row)
     with torch.cuda.stream(stream):
         for c in range(warmup):
@@ -211,6 +211,7 @@ def main():
     rgs = [rb.struct() for rb in runner.batches]
     stage_calls = {s: [[] for _ in range(L)] for s in STAGES}
     keep = []
+    ws_ptr, ws_bytes = B._ws(runner.workspace)
     for cp in copies:
         sels = []
         for l, x in enumerate(cp):
@@ -238,7 +239,7 @@ def main():
                 (lib.cb_partial_attn, (gref, ctypes.byref(rgs[l]),
                                        runner.outs[l]["out"].data_ptr(), x["q_c"].data_ptr(),
                                        sl.data_ptr(), sg.data_ptr(), k_ptr, v_ptr,
-                                       runner.scale, h)))
+                                       runner.scale, ws_ptr, ws_bytes, h)))
     events = {}
     with torch.cuda.stream(stream):
         torch.cuda.synchronize()
@@ -257,7 +258,8 @@ def main():
                 for s in STAGES}
     launches = steps * L
     work = algorithmic_work(wl, runner, planted)
-    stage_work = {s: sum(w[s] for w in work) for s in STAGES}
+    # every layer of every step was launched once
+    stage_work = {s: steps * sum(w[s] for w in work) for s in STAGES}
     kernels = {}
     for s in STAGES:
         avg_us = stage_ms[s] * 1e3 / launches

@@ -164,13 +164,25 @@ cb_status cb_fuse_scatter(const cb_geom *geom, void *k_fused, void *v_fused,
  *               * V_fused[u][g],   q = q_c[sel_local[s]][h].
  *   out    : [K][n_q_heads][head_dim] dtype, K = h_sel_off[n_req]
  *   q_c    : [M][n_q_heads][head_dim], already rotated at the new positions
+ *   workspace, workspace_bytes : optional device scratch owned by the caller
+ *            (NULL/0 allowed).  When the query tiles are too few to fill the
+ *            GPU, long rows are split over key ranges whose fp32 partials
+ *            live here; cb_partial_attn_workspace_size() gives the size that
+ *            enables the split.  A smaller workspace only disables the split.
+ *            Calls that share a workspace must be ordered on one stream.
  * bf16 uses MFMA products with fp32 accumulation and an fp32 online softmax.
  */
 cb_status cb_partial_attn(const cb_geom *geom, const cb_ragged *rg, void *out,
                           const void *q_c, const int32_t *sel_local,
                           const int32_t *sel_global, const void *k_fused,
                           const void *v_fused, float softmax_scale,
+                          void *workspace, size_t workspace_bytes,
                           void *stream);
+
+/* Workspace (bytes) with which cb_partial_attn can split long rows for this
+ * geometry and batch; 0 when no split is used.  Reads host mirrors only. */
+cb_status cb_partial_attn_workspace_size(const cb_geom *geom,
+                                         const cb_ragged *rg, size_t *bytes);
 
 /* Every argument of one layer of the blend. */
 typedef struct cb_layer_args {
@@ -190,6 +202,8 @@ typedef struct cb_layer_args {
   int32_t *sel_local;   /* [K] out */
   int32_t *sel_global;  /* [K] out */
   void *out;            /* [K][Hq][D] out */
+  void *workspace;      /* optional attention workspace (see cb_partial_attn) */
+  size_t workspace_bytes;
 } cb_layer_args;
 
 /*
@@ -207,7 +221,7 @@ const char *cb_last_error(void);
 /* ABI revision of this header (bumped on any incompatible change). */
 int32_t cb_abi_version(void);
 
-#define CB_ABI_VERSION 1
+#define CB_ABI_VERSION 2
 
 #ifdef __cplusplus
 }

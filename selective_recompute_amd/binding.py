@@ -13,7 +13,9 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcacheblend.so")
+# The in-tree build; CB_LIBRARY may name another build of the same library.
+LIB_PATH = os.environ.get("CB_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libcacheblend.so")
 
 CB_OK, CB_ERR_INVALID_ARG, CB_ERR_UNSUPPORTED, CB_ERR_HIP = 0, 1, 2, 3
 CB_DTYPE_F32, CB_DTYPE_BF16 = 0, 1
@@ -42,7 +44,8 @@ class LayerArgs(ctypes.Structure):
                 ("cand_idx", ctypes.c_void_p), ("rope_theta", ctypes.c_double),
                 ("rope_style", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
                 ("dev", ctypes.c_void_p), ("sel_local", ctypes.c_void_p),
-                ("sel_global", ctypes.c_void_p), ("out", ctypes.c_void_p)]
+                ("sel_global", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class CbError(RuntimeError):
@@ -67,7 +70,10 @@ _SIGNATURES = {
                         ctypes.c_void_p],
     "cb_partial_attn": [ctypes.POINTER(Geom), ctypes.POINTER(Ragged), ctypes.c_void_p,
                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                        ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p],
+                        ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t,
+                        ctypes.c_void_p],
+    "cb_partial_attn_workspace_size": [ctypes.POINTER(Geom), ctypes.POINTER(Ragged),
+                                       ctypes.POINTER(ctypes.c_size_t)],
     "cb_blend_layer": [ctypes.POINTER(LayerArgs), ctypes.c_void_p],
 }
 
@@ -192,21 +198,43 @@ def fuse_scatter(g: Geom, k_fused, v_fused, k_new_c, v_new_c, sel_local, sel_glo
                                 _dev(sel_global, torch.int32), k_total, _stream(stream)))
 
 
-def partial_attn(g: Geom, rb: RaggedBatch, out, q_c, sel_local, sel_global, k_fused, v_fused,
-                 softmax_scale: float, stream=None):
+def attn_workspace_bytes(g: Geom, rb: RaggedBatch) -> int:
+    """Workspace with which cb_partial_attn may split long rows (0 = none)."""
+    n = ctypes.c_size_t(0)
     rg = rb.struct()
+    check(lib().cb_partial_attn_workspace_size(ctypes.byref(g), ctypes.byref(rg), ctypes.byref(n)))
+    return int(n.value)
+
+
+def workspace_tensor(nbytes: int, device="cuda") -> Optional[torch.Tensor]:
+    """A device buffer of at least nbytes (16-byte aligned), or None for 0."""
+    if nbytes <= 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _ws(ws: Optional[torch.Tensor]):
+    return (None, 0) if ws is None else (_dev(ws), ws.numel() * ws.element_size())
+
+
+def partial_attn(g: Geom, rb: RaggedBatch, out, q_c, sel_local, sel_global, k_fused, v_fused,
+                 softmax_scale: float, workspace: Optional[torch.Tensor] = None, stream=None):
+    rg = rb.struct()
+    ws_ptr, ws_bytes = _ws(workspace)
     check(lib().cb_partial_attn(ctypes.byref(g), ctypes.byref(rg), _dev(out), _dev(q_c),
                                 _dev(sel_local, torch.int32), _dev(sel_global, torch.int32),
-                                _dev(k_fused), _dev(v_fused), softmax_scale, _stream(stream)))
+                                _dev(k_fused), _dev(v_fused), softmax_scale, ws_ptr, ws_bytes,
+                                _stream(stream)))
 
 
 def blend_layer(g: Geom, rb: RaggedBatch, *, k, v, k_new_c, v_new_c, q_c, delta, cand_idx,
                 rope_theta: float, rope_style: int, softmax_scale: float, dev, sel_local,
-                sel_global, out, stream=None):
+                sel_global, out, workspace: Optional[torch.Tensor] = None, stream=None):
     args = LayerArgs(g, rb.struct(), _dev(k), _dev(v), _dev(k_new_c), _dev(v_new_c), _dev(q_c),
                      _dev(delta, torch.int32), _dev(cand_idx, torch.int32), rope_theta,
                      rope_style, softmax_scale, _dev(dev, torch.float32),
-                     _dev(sel_local, torch.int32), _dev(sel_global, torch.int32), _dev(out))
+                     _dev(sel_local, torch.int32), _dev(sel_global, torch.int32), _dev(out),
+                     *_ws(workspace))
     check(lib().cb_blend_layer(ctypes.byref(args), _stream(stream)))
 
 
@@ -216,14 +244,14 @@ class PreparedLayer:
 
     def __init__(self, g: Geom, rb: RaggedBatch, *, k, v, k_new_c, v_new_c, q_c, delta,
                  cand_idx, rope_theta, rope_style, softmax_scale, dev, sel_local, sel_global,
-                 out):
+                 out, workspace: Optional[torch.Tensor] = None):
         self._keep = (rb, k, v, k_new_c, v_new_c, q_c, delta, cand_idx, dev, sel_local,
-                      sel_global, out)
+                      sel_global, out, workspace)
         self.args = LayerArgs(g, rb.struct(), _dev(k), _dev(v), _dev(k_new_c), _dev(v_new_c),
                               _dev(q_c), _dev(delta, torch.int32), _dev(cand_idx, torch.int32),
                               rope_theta, rope_style, softmax_scale, _dev(dev, torch.float32),
                               _dev(sel_local, torch.int32), _dev(sel_global, torch.int32),
-                              _dev(out))
+                              _dev(out), *_ws(workspace))
         self.ref = ctypes.byref(self.args)
 
     def launch(self, stream_handle: int):

@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
+#include <algorithm>
 #include <cstdio>
 #include <string>
 
@@ -214,27 +215,78 @@ cb_status validate_attn(const cb_geom *geom, const cb_ragged *rg, void *out, con
   return CB_OK;
 }
 
+constexpr int kNoSplit = 1 << 30;
+
+// Tile and key-chunk decomposition of the MFMA attention, from host mirrors
+// only.  Long rows are split over key chunks when the query tiles alone give
+// fewer than 1024 workgroups, aiming at ~2048 units; a split needs
+// `ws_bytes` of workspace and is dropped when `ws_avail` is smaller.
+cb::AttnPlan plan_attn(const cb_geom *g, const cb_ragged *rg, size_t ws_avail) {
+  cb::AttnPlan pl{};
+  // One 16-query block per wave: with 32 queries per wave the head_dim-128
+  // kernel needs more than 256 registers and drops to one wave per SIMD,
+  // which measured slower.
+  pl.qb = 1;
+  pl.rows_per_tile = cb::attn_mfma_rows_per_tile(g->dtype, g->n_q_heads, g->n_kv_heads,
+                                                 g->head_dim, 1);
+  pl.key_chunk = kNoSplit;
+  if (pl.rows_per_tile == 0) return pl;
+  const int rows = pl.rows_per_tile;
+  int64_t max_n = 0;
+  for (int32_t r = 0; r < rg->n_req; ++r) {
+    const int64_t kr = rg->h_sel_off[r + 1] - rg->h_sel_off[r];
+    pl.tiles += (kr + rows - 1) / rows;
+    if (kr > 0) max_n = std::max<int64_t>(max_n, rg->h_tok_off[r + 1] - rg->h_tok_off[r]);
+  }
+  const int64_t blocks = pl.tiles * g->n_kv_heads;
+  if (blocks > 0 && blocks < 1024) {
+    const int64_t want = (2048 + blocks - 1) / blocks;
+    int64_t kc = (max_n + want - 1) / want;
+    kc = std::max<int64_t>(256, (kc + 63) / 64 * 64);
+    if (kc < max_n) pl.key_chunk = (int)kc;
+  }
+  auto count_units = [&](int kc, bool &split) {
+    int64_t units = 0;
+    split = false;
+    for (int32_t r = 0; r < rg->n_req; ++r) {
+      const int64_t kr = rg->h_sel_off[r + 1] - rg->h_sel_off[r];
+      const int64_t n = rg->h_tok_off[r + 1] - rg->h_tok_off[r];
+      const int64_t tr = (kr + rows - 1) / rows;
+      const int64_t cr = (n + kc - 1) / kc;
+      units += tr * cr;
+      if (tr > 0 && cr > 1) split = true;
+    }
+    return units;
+  };
+  pl.units = count_units(pl.key_chunk, pl.split);
+  if (pl.split) {
+    pl.ws_bytes = (size_t)pl.units * g->n_kv_heads * cb::attn_unit_bytes(g->head_dim, pl.qb);
+    if (pl.ws_bytes > ws_avail) {
+      pl.key_chunk = kNoSplit;
+      pl.units = count_units(pl.key_chunk, pl.split);
+      pl.ws_bytes = 0;
+    }
+  }
+  return pl;
+}
+
 cb_status run_attn(const cb_geom *geom, const cb_ragged *rg, void *out, const void *q_c,
                    const int32_t *sel_local, const int32_t *sel_global, const void *k_fused,
-                   const void *v_fused, float softmax_scale, hipStream_t stream) {
+                   const void *v_fused, float softmax_scale, void *workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
   cb::AttnArgs a;
   a.out = out; a.q_c = q_c; a.sel_local = sel_local; a.sel_global = sel_global;
   a.k_fused = k_fused; a.v_fused = v_fused; a.tok_off = rg->tok_off; a.sel_off = rg->sel_off;
+  a.workspace = workspace;
   a.n_req = rg->n_req; a.k_total = rg->h_sel_off[rg->n_req];
   a.n_q_heads = geom->n_q_heads; a.n_kv_heads = geom->n_kv_heads; a.head_dim = geom->head_dim;
   a.softmax_scale = softmax_scale;
   if (a.k_total == 0) return CB_OK;
-  const int rows = cb::attn_mfma_rows_per_tile(geom->dtype, geom->n_q_heads, geom->n_kv_heads,
-                                               geom->head_dim);
-  if (rows > 0) {
-    int64_t tiles = 0;
-    for (int32_t r = 0; r < rg->n_req; ++r) {
-      const int64_t kr = rg->h_sel_off[r + 1] - rg->h_sel_off[r];
-      tiles += (kr + rows - 1) / rows;
-    }
-    if (tiles * geom->n_kv_heads > INT32_MAX)
-      return fail(CB_ERR_UNSUPPORTED, "too many attention tiles");
-    return hip_status(cb::launch_attn_mfma(a, rows, (int32_t)tiles, stream), "partial_attn");
+  const cb::AttnPlan plan = plan_attn(geom, rg, workspace ? workspace_bytes : 0);
+  if (plan.rows_per_tile > 0) {
+    if (plan.units * geom->n_kv_heads > INT32_MAX)
+      return fail(CB_ERR_UNSUPPORTED, "too many attention work units");
+    return hip_status(cb::launch_attn_mfma(a, plan, stream), "partial_attn");
   }
   return hip_status(cb::launch_attn_simple(geom->dtype, a, stream), "partial_attn");
 }
@@ -296,12 +348,25 @@ CB_EXPORT cb_status cb_fuse_scatter(const cb_geom *geom, void *k_fused, void *v_
 CB_EXPORT cb_status cb_partial_attn(const cb_geom *geom, const cb_ragged *rg, void *out,
                                     const void *q_c, const int32_t *sel_local,
                                     const int32_t *sel_global, const void *k_fused,
-                                    const void *v_fused, float softmax_scale, void *stream) {
+                                    const void *v_fused, float softmax_scale, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
   g_last_error.clear();
   CB_TRY(validate_attn(geom, rg, out, q_c, sel_local, sel_global, k_fused, v_fused,
                        softmax_scale));
+  CB_TRY(need_ptr(workspace, "workspace", workspace_bytes > 0));
   return run_attn(geom, rg, out, q_c, sel_local, sel_global, k_fused, v_fused, softmax_scale,
-                  (hipStream_t)stream);
+                  workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+CB_EXPORT cb_status cb_partial_attn_workspace_size(const cb_geom *geom, const cb_ragged *rg,
+                                                   size_t *bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(CB_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = 0;
+  CB_TRY(check_geom(geom));
+  CB_TRY(check_ragged(rg, true, false, true));
+  *bytes = plan_attn(geom, rg, SIZE_MAX).ws_bytes;
+  return CB_OK;
 }
 
 CB_EXPORT cb_status cb_blend_layer(const cb_layer_args *a, void *stream) {
@@ -321,6 +386,7 @@ CB_EXPORT cb_status cb_blend_layer(const cb_layer_args *a, void *stream) {
                        k_total));
   CB_TRY(validate_attn(geom, rg, a->out, a->q_c, a->sel_local, a->sel_global, a->k, a->v,
                        a->softmax_scale));
+  CB_TRY(need_ptr(a->workspace, "workspace", a->workspace_bytes > 0));
   const hipStream_t s = (hipStream_t)stream;
   if (a->delta && n_tok > 0)
     CB_TRY(hip_status(cb::launch_rerotate(geom->dtype, a->rope_style, a->k, a->k, a->delta, n_tok,
@@ -340,7 +406,7 @@ CB_EXPORT cb_status cb_blend_layer(const cb_layer_args *a, void *stream) {
                                     (int32_t)(row_elems(geom) * elem_size(geom->dtype)), s),
                     "fuse_scatter"));
   return run_attn(geom, rg, a->out, a->q_c, a->sel_local, a->sel_global, a->k, a->v,
-                  a->softmax_scale, s);
+                  a->softmax_scale, a->workspace, a->workspace_bytes, s);
 }
 
 CB_EXPORT const char *cb_status_str(cb_status status) {

@@ -15,222 +15,371 @@ namespace cb {
 // ---------------------------------------------------------------------------
 // MFMA kernel (bf16, head_dim HD in {32, 64, 128}).
 //
-// A workgroup of 4 waves owns one query tile of 64 query vectors (R selected
-// rows x G query heads of one KV group g, R = 64 / G) and streams the keys
-// [request start, last row of the tile] through LDS in tiles of 64 keys.
-// Each wave owns 16 query vectors.  Scores are computed transposed,
-// S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (keys on the M side, queries on
-// the N side), so a lane's accumulators all belong to one query column: the
-// online-softmax statistics of that query live in the lane (and its three
-// partner lanes l^16, l^32, l^48), and the probabilities feed the second
-// product O^T = V^T P^T directly as the B operand with no shuffle.  V is
-// transposed on its way into LDS (pairs of keys packed per 32-bit store).
-// Blocks are ordered so that blockIdx % Hkv is the KV head: the round-robin
-// dispatch over the 8 XCDs then keeps each head's K/V in one XCD's L2 when
-// Hkv = 8, and the latest (longest) tiles start first.
+// Work unit = (query tile, KV head g, key chunk).  A query tile holds
+// QT = 64*QB query vectors: rows_per_tile selected rows of one request times
+// the G = Hq/Hkv query heads that read KV head g, so one K/V stream serves
+// all of them.  A workgroup of 4 waves owns a unit; each wave owns 16*QB
+// query vectors.  Keys are streamed through LDS in tiles of 64:
+//
+//  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (keys on the M side, queries
+//    on the N side): a lane's accumulators all belong to one query column,
+//    so the online-softmax statistics stay in the lane (plus its partners
+//    l^16, l^32, l^48) and the probabilities are already laid out as the B
+//    operand of the second product.
+//  * O^T += V^T P^T.  V is stored row-major in LDS; the A operand (8 keys of
+//    one head dimension per lane) is read with gfx950's ds_read_b64_tr_b16:
+//    in each 16-lane group, lane j points at V[key0 + j/4][d0 + 4(j%4)] and
+//    lane i receives V[key0 .. key0+3][d0 + i].
+//  * The next tile's K/V are loaded into registers while the current one is
+//    multiplied, then stored to LDS.
+//  * Each K (A operand) and V^T read from LDS feeds QB MFMAs, one per block
+//    of 16 query vectors.
+//
+// Long rows with too few tiles to fill the chip are split over key chunks of
+// `key_chunk` keys (a multiple of 64); every chunk writes its unnormalised
+// fp32 partial (O, running max, running sum) to the workspace and
+// attn_combine_kernel merges them.  Unsplit units write the output directly.
+// Block order: blockIdx % Hkv is the KV head, so with Hkv = 8 the round-robin
+// dispatch over the 8 XCDs keeps each head's K/V stream in one XCD's L2.
 // ---------------------------------------------------------------------------
-constexpr int kKeyTile = 64;
+struct AttnParams {
+  bf16 *out;
+  const bf16 *q_c;
+  const int32_t *sel_local;
+  const int32_t *sel_global;
+  const bf16 *k_fused;
+  const bf16 *v_fused;
+  const int32_t *tok_off;
+  const int32_t *sel_off;
+  float *ws;
+  int32_t n_req, hq, hkv, group, rows_per_tile, key_chunk;
+  float scale_log2;
+};
 
-template <int HD>
-__global__ __launch_bounds__(256) void attn_mfma_kernel(
-    bf16 *__restrict__ out, const bf16 *__restrict__ q_c,
-    const int32_t *__restrict__ sel_local, const int32_t *__restrict__ sel_global,
-    const bf16 *__restrict__ k_fused, const bf16 *__restrict__ v_fused,
-    const int32_t *__restrict__ tok_off, const int32_t *__restrict__ sel_off,
-    int32_t n_req, int32_t hq, int32_t hkv, int32_t group, int32_t rows_per_tile,
-    int32_t n_tiles, float scale_log2) {
-  constexpr int KS = HD + 8;         // LDS row stride of the K tile (elements)
-  constexpr int VS = kKeyTile + 8;   // LDS row stride of the V^T tile
-  constexpr int NST = HD / 32;       // 32-wide contraction steps over head_dim
-  constexpr int NDT = HD / 16;       // 16-row output tiles over head_dim
-  __shared__ __attribute__((aligned(16))) bf16 ks[kKeyTile * KS];
-  __shared__ __attribute__((aligned(16))) bf16 vt[HD * VS];
+constexpr int kKeyTile = 64;
+constexpr float kNegFloor = -1.0e30f;  // finite start of the running max
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+__device__ inline bf16x4 lds_read_tr(const bf16 *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p));
+}
+
+// Which (request, tile, chunk) unit `u` is; returns false if u is out of range.
+__device__ inline bool locate_unit(const AttnParams &p, int u, int &r, int &tile, int &chunk,
+                                   int &nchunks, int64_t &ubase) {
+  ubase = 0;
+  for (r = 0; r < p.n_req; ++r) {
+    const int kr = p.sel_off[r + 1] - p.sel_off[r];
+    const int n = p.tok_off[r + 1] - p.tok_off[r];
+    const int tr = (kr + p.rows_per_tile - 1) / p.rows_per_tile;
+    const int cr = (int)(((int64_t)n + p.key_chunk - 1) / p.key_chunk);
+    const int64_t nu = (int64_t)tr * cr;
+    if (u < ubase + nu) {
+      const int ul = (int)(u - ubase);
+      tile = ul / cr;
+      chunk = ul - tile * cr;
+      nchunks = cr;
+      return true;
+    }
+    ubase += nu;
+  }
+  return false;
+}
+
+template <int HD, int QB>
+__global__ __launch_bounds__(256) void attn_mfma_kernel(const AttnParams p) {
+  constexpr int LS = HD + 8;            // LDS row stride (elements) of the K and V tiles
+  constexpr int NST = HD / 32;          // 32-wide contraction steps over head_dim
+  constexpr int NDT = HD / 16;          // 16-row output tiles over head_dim
+  constexpr int QT = 64 * QB;           // query vectors per unit
+  constexpr int CPR = HD / 8;           // 16-byte chunks per key row
+  constexpr int CPT = kKeyTile * CPR / 256;  // chunks per thread per tensor
+  __shared__ __attribute__((aligned(16))) bf16 ks[kKeyTile * LS];
+  __shared__ __attribute__((aligned(16))) bf16 vs[kKeyTile * LS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = blockIdx.x % hkv;
-  const int tile_rank = n_tiles - 1 - (int)(blockIdx.x / hkv);
-
-  // Locate this tile's request and first selected row.
-  int r = 0, base = 0, s0 = 0, ns = 0;
-  for (r = 0; r < n_req; ++r) {
-    const int kr = sel_off[r + 1] - sel_off[r];
-    const int nt = (kr + rows_per_tile - 1) / rows_per_tile;
-    if (tile_rank < base + nt) {
-      s0 = sel_off[r] + (tile_rank - base) * rows_per_tile;
-      ns = min(rows_per_tile, sel_off[r + 1] - s0);
-      break;
-    }
-    base += nt;
-  }
-  const int lo = tok_off[r];
-  const int p_last = sel_global[s0 + ns - 1];
-
-  // This lane's query column.
   const int col = lane & 15, grp = lane >> 4;
-  const int qv = wave * 16 + col;
-  const int row = qv / group, hh = qv - row * group;
-  const bool qvalid = row < ns;
-  const int s = s0 + (qvalid ? row : 0);
-  const int p_q = qvalid ? sel_global[s] : lo;  // padding columns see one key
-  const int h = g * group + hh;
+  const int g = blockIdx.x % p.hkv;
+  int r, tile, chunk, nchunks;
+  int64_t ubase;
+  if (!locate_unit(p, (int)(blockIdx.x / p.hkv), r, tile, chunk, nchunks, ubase)) return;
+  const int s0 = p.sel_off[r] + tile * p.rows_per_tile;
+  const int ns = min(p.rows_per_tile, p.sel_off[r + 1] - s0);
+  const int lo = p.tok_off[r];
+  const int p_last = p.sel_global[s0 + ns - 1];
+  const int64_t kb = (int64_t)lo + (int64_t)chunk * p.key_chunk;
+  if (kb > p_last) return;  // whole chunk after the tile's last row (uniform)
+  const int k_begin = (int)kb;
+  const int k_end = (int)min((int64_t)p_last + 1, kb + p.key_chunk);
 
-  bf16x8 qreg[NST];
-  {
-    const bf16 *qp = q_c + ((int64_t)sel_local[s] * hq + h) * HD + 8 * grp;
+  // Query columns of this lane: one per block of 16.
+  int p_q[QB];
+  bf16x8 qreg[QB][NST];
 #pragma unroll
-    for (int st = 0; st < NST; ++st) qreg[st] = *reinterpret_cast<const bf16x8 *>(qp + 32 * st);
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qv = wave * 16 * QB + qb * 16 + col;
+    const int row = qv / p.group, hh = qv - row * p.group;
+    const bool valid = row < ns;
+    const int s = s0 + (valid ? row : 0);
+    p_q[qb] = valid ? p.sel_global[s] : lo;
+    const bf16 *qp = p.q_c + ((int64_t)p.sel_local[s] * p.hq + g * p.group + hh) * HD + 8 * grp;
+#pragma unroll
+    for (int st = 0; st < NST; ++st) qreg[qb][st] = *reinterpret_cast<const bf16x8 *>(qp + 32 * st);
   }
 
-  f32x4 o[NDT];
+  f32x4 o[QB][NDT];
+  float m_run[QB], l_run[QB];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  const int64_t rs = (int64_t)hkv * HD;  // packed row stride of K/V
-  const bf16 *kbase = k_fused + (int64_t)g * HD;
-  const bf16 *vbase = v_fused + (int64_t)g * HD;
-  const int n_kt = (p_last - lo + kKeyTile) / kKeyTile;
-
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int k0 = lo + kt * kKeyTile;
-    // Stage K[k0 .. k0+63][g][:] row-major (zeros past the last key).
-    for (int c = tid; c < kKeyTile * HD / 8; c += 256) {
-      const int key = c / (HD / 8), c8 = c - key * (HD / 8);
-      bf16x8 val = {};
-      if (k0 + key <= p_last)
-        val = *reinterpret_cast<const bf16x8 *>(kbase + (int64_t)(k0 + key) * rs + c8 * 8);
-      *reinterpret_cast<bf16x8 *>(ks + key * KS + c8 * 8) = val;
-    }
-    // Stage V^T: two keys per thread, packed as 32-bit (key, key+1) pairs.
-    for (int c = tid; c < (kKeyTile / 2) * (HD / 8); c += 256) {
-      const int kp = c / (HD / 8), c8 = c - kp * (HD / 8);
-      const int key0 = 2 * kp;
-      bf16x8 a = {}, b = {};
-      if (k0 + key0 <= p_last)
-        a = *reinterpret_cast<const bf16x8 *>(vbase + (int64_t)(k0 + key0) * rs + c8 * 8);
-      if (k0 + key0 + 1 <= p_last)
-        b = *reinterpret_cast<const bf16x8 *>(vbase + (int64_t)(k0 + key0 + 1) * rs + c8 * 8);
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = kNegFloor;
+    l_run[qb] = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        bf16x2 pr = {a[e], b[e]};
-        *reinterpret_cast<bf16x2 *>(vt + (c8 * 8 + e) * VS + key0) = pr;
+    for (int dt = 0; dt < NDT; ++dt) o[qb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int64_t rs = (int64_t)p.hkv * HD;
+  const bf16 *kbase = p.k_fused + (int64_t)g * HD;
+  const bf16 *vbase = p.v_fused + (int64_t)g * HD;
+  bf16x8 kpre[CPT], vpre[CPT];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + 256 * i, key = c / CPR, c8 = c - key * CPR;
+      if (k0 + key <= p_last) {
+        const int64_t off = (int64_t)(k0 + key) * rs + c8 * 8;
+        kpre[i] = *reinterpret_cast<const bf16x8 *>(kbase + off);
+        vpre[i] = *reinterpret_cast<const bf16x8 *>(vbase + off);
+      } else {
+        kpre[i] = bf16x8{};
+        vpre[i] = bf16x8{};
       }
     }
-    __syncthreads();
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + 256 * i, key = c / CPR, c8 = c - key * CPR;
+      *reinterpret_cast<bf16x8 *>(ks + key * LS + c8 * 8) = kpre[i];
+      *reinterpret_cast<bf16x8 *>(vs + key * LS + c8 * 8) = vpre[i];
+    }
+  };
 
-    // S^T tile: sacc[t][i] = score(key k0 + 16t + 4grp + i, query col).
-    f32x4 sacc[4];
+  const int n_kt = (k_end - k_begin + kKeyTile - 1) / kKeyTile;
+  load_tile(k_begin);
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int k0 = k_begin + kt * kKeyTile;
+    store_tile();
+    __syncthreads();
+    if (kt + 1 < n_kt) load_tile(k0 + kKeyTile);
+
+    // S^T: sacc[qb][t][i] = score(key k0 + 16t + 4grp + i, query column qb).
+    f32x4 sacc[QB][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sacc[qb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < NST; ++st) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(ks + (16 * t + col) * KS + 32 * st + 8 * grp);
-        sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[st], sacc[t], 0, 0, 0);
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(ks + (16 * t + col) * LS + 32 * st + 8 * grp);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          sacc[qb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[qb][st], sacc[qb][t], 0, 0, 0);
       }
     }
 
-    // Scale (base-2 logits), causal mask, online softmax.
-    float mx = -INFINITY;
+    // Online softmax in base 2, per query column.
+    bf16x8 bp[QB][2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = k0 + 16 * t + 4 * grp + i;
-        float v = sacc[t][i] * scale_log2;
-        if (key > p_q) v = -INFINITY;
-        sacc[t][i] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float m_new = fmaxf(m_run, mx);  // finite: key `lo` is visible to every column
-    const float alpha = exp2f(m_run - m_new);
-    float psum = 0.f;
-    bf16 pb[16];
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+        for (int i = 0; i < 4; ++i) {
+          const int key = k0 + 16 * t + 4 * grp + i;
+          float v = sacc[qb][t][i] * p.scale_log2;
+          if (key > p_q[qb]) v = -INFINITY;
+          sacc[qb][t][i] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float m_new = fmaxf(m_run[qb], mx);
+      const float alpha = exp2f(m_run[qb] - m_new);
+      float psum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(sacc[t][i] - m_new);
-        psum += p;
-        pb[4 * t + i] = (bf16)p;
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+        for (int i = 0; i < 4; ++i) {
+          const float pv = exp2f(sacc[qb][t][i] - m_new);
+          psum += pv;
+          bp[qb][t >> 1][4 * (t & 1) + i] = (bf16)pv;
+        }
+      l_run[qb] = l_run[qb] * alpha + psum;
+      m_run[qb] = m_new;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[qb][dt] *= alpha;
+    }
 
-    // O^T += V^T P^T over two 32-key halves.
+    // O^T += V^T P^T over two 32-key halves; V^T comes from transpose reads.
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
-      bf16x8 bp;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        bp[i] = pb[4 * (2 * kh) + i];
-        bp[4 + i] = pb[4 * (2 * kh + 1) + i];
-      }
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const bf16 *vrow = vt + (16 * dt + col) * VS + 32 * kh + 4 * grp;
-        const bf16x4 lo4 = *reinterpret_cast<const bf16x4 *>(vrow);
-        const bf16x4 hi4 = *reinterpret_cast<const bf16x4 *>(vrow + 16);
-        bf16x8 a;
+        const bf16 *a0 = vs + (32 * kh + 4 * grp + (col >> 2)) * LS + 16 * dt + 4 * (col & 3);
+        const bf16x4 lo4 = lds_read_tr(a0);
+        const bf16x4 hi4 = lds_read_tr(a0 + 16 * LS);
+        const bf16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { a[i] = lo4[i]; a[4 + i] = hi4[i]; }
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bp, o[dt], 0, 0, 0);
+        for (int qb = 0; qb < QB; ++qb)
+          o[qb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bp[qb][kh], o[qb][dt], 0, 0, 0);
       }
     }
     __syncthreads();
   }
 
-  l_run += __shfl_xor(l_run, 16, kWave);
-  l_run += __shfl_xor(l_run, 32, kWave);
-  if (qvalid) {
-    const float inv = 1.f / l_run;
-    bf16 *op = out + ((int64_t)s * hq + h) * HD;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      bf16x4 w;
+  for (int qb = 0; qb < QB; ++qb) {
+    float l = l_run[qb];
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    const int qv = wave * 16 * QB + qb * 16 + col;
+    if (nchunks == 1) {
+      const int row = qv / p.group, hh = qv - row * p.group;
+      if (row < ns) {
+        const float inv = 1.f / l;
+        bf16 *op = p.out + ((int64_t)(s0 + row) * p.hq + g * p.group + hh) * HD;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = (bf16)(o[dt][i] * inv);
-      *reinterpret_cast<bf16x4 *>(op + 16 * dt + 4 * grp) = w;
+        for (int dt = 0; dt < NDT; ++dt) {
+          bf16x4 w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w[i] = (bf16)(o[qb][dt][i] * inv);
+          *reinterpret_cast<bf16x4 *>(op + 16 * dt + 4 * grp) = w;
+        }
+      }
+    } else {
+      float *w = p.ws + (int64_t)blockIdx.x * (QT * HD + 2 * QT);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        *reinterpret_cast<f32x4 *>(w + qv * HD + 16 * dt + 4 * grp) = o[qb][dt];
+      if (grp == 0) {
+        w[QT * HD + qv] = m_run[qb];
+        w[QT * HD + QT + qv] = l;
+      }
     }
   }
 }
 
-int attn_mfma_rows_per_tile(int dtype, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim) {
+// Merge the key-chunk partials of one (query tile, KV head).
+template <int HD, int QB>
+__global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
+  constexpr int QT = 64 * QB;
+  constexpr int UNIT = QT * HD + 2 * QT;
+  const int g = blockIdx.x % p.hkv;
+  const int tile_u = blockIdx.x / p.hkv;
+  int r, tile = 0, cr = 1;
+  int64_t ubase = 0, tbase = 0;
+  for (r = 0; r < p.n_req; ++r) {
+    const int kr = p.sel_off[r + 1] - p.sel_off[r];
+    const int n = p.tok_off[r + 1] - p.tok_off[r];
+    const int tr = (kr + p.rows_per_tile - 1) / p.rows_per_tile;
+    cr = (int)(((int64_t)n + p.key_chunk - 1) / p.key_chunk);
+    if (tile_u < tbase + tr) { tile = (int)(tile_u - tbase); break; }
+    tbase += tr;
+    ubase += (int64_t)tr * cr;
+  }
+  if (r == p.n_req || cr == 1) return;
+  const int s0 = p.sel_off[r] + tile * p.rows_per_tile;
+  const int ns = min(p.rows_per_tile, p.sel_off[r + 1] - s0);
+  const int lo = p.tok_off[r];
+  const int p_last = p.sel_global[s0 + ns - 1];
+  const int n_active = (p_last - lo) / p.key_chunk + 1;
+  const float *w0 = p.ws + ((ubase + (int64_t)tile * cr) * p.hkv + g) * UNIT;
+  const int64_t ustride = (int64_t)p.hkv * UNIT;
+  for (int task = threadIdx.x; task < QT * HD / 4; task += blockDim.x) {
+    const int qv = task / (HD / 4), d4 = task - qv * (HD / 4);
+    const int row = qv / p.group, hh = qv - row * p.group;
+    if (row >= ns) continue;
+    float mx = kNegFloor;
+    for (int c = 0; c < n_active; ++c) mx = fmaxf(mx, w0[c * ustride + QT * HD + qv]);
+    float l = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < n_active; ++c) {
+      const float *w = w0 + c * ustride;
+      const float sc = exp2f(w[QT * HD + qv] - mx);
+      l += w[QT * HD + QT + qv] * sc;
+      acc += *reinterpret_cast<const f32x4 *>(w + qv * HD + 4 * d4) * sc;
+    }
+    const float inv = 1.f / l;
+    bf16x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = (bf16)(acc[i] * inv);
+    *reinterpret_cast<bf16x4 *>(p.out + ((int64_t)(s0 + row) * p.hq + g * p.group + hh) * HD +
+                                4 * d4) = o;
+  }
+}
+
+int attn_mfma_rows_per_tile(int dtype, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                            int qb) {
   if (dtype != kBF16) return 0;
   if (head_dim != 32 && head_dim != 64 && head_dim != 128) return 0;
   const int group = n_q_heads / n_kv_heads;
-  if (group < 1 || group > 64 || 64 % group != 0) return 0;
-  return 64 / group;
+  const int qt = 64 * qb;
+  if (group < 1 || group > qt || qt % group != 0) return 0;
+  return qt / group;
 }
 
-hipError_t launch_attn_mfma(const AttnArgs &a, int32_t rows_per_tile, int32_t n_tiles,
-                            hipStream_t stream) {
-  if (n_tiles == 0) return hipSuccess;
-  const int group = a.n_q_heads / a.n_kv_heads;
-  const float scale_log2 = a.softmax_scale * 1.4426950408889634f;
-  const dim3 grid((unsigned)((int64_t)n_tiles * a.n_kv_heads)), block(256);
-#define CB_ATTN_ARGS                                                                         \
-  (bf16 *)a.out, (const bf16 *)a.q_c, a.sel_local, a.sel_global, (const bf16 *)a.k_fused, \
-      (const bf16 *)a.v_fused, a.tok_off, a.sel_off, a.n_req, a.n_q_heads, a.n_kv_heads,  \
-      group, rows_per_tile, n_tiles, scale_log2
+size_t attn_unit_bytes(int32_t head_dim, int qb) {
+  const size_t qt = 64 * (size_t)qb;
+  return (qt * head_dim + 2 * qt) * sizeof(float);
+}
+
+template <int QB>
+static hipError_t launch_mfma_qb(const AttnArgs &a, const AttnPlan &plan, hipStream_t stream) {
+  AttnParams p;
+  p.out = (bf16 *)a.out;
+  p.q_c = (const bf16 *)a.q_c;
+  p.sel_local = a.sel_local;
+  p.sel_global = a.sel_global;
+  p.k_fused = (const bf16 *)a.k_fused;
+  p.v_fused = (const bf16 *)a.v_fused;
+  p.tok_off = a.tok_off;
+  p.sel_off = a.sel_off;
+  p.ws = (float *)a.workspace;
+  p.n_req = a.n_req;
+  p.hq = a.n_q_heads;
+  p.hkv = a.n_kv_heads;
+  p.group = a.n_q_heads / a.n_kv_heads;
+  p.rows_per_tile = plan.rows_per_tile;
+  p.key_chunk = plan.key_chunk;
+  p.scale_log2 = a.softmax_scale * 1.4426950408889634f;
+  const dim3 grid((unsigned)(plan.units * a.n_kv_heads)), block(256);
   switch (a.head_dim) {
-    case 32: hipLaunchKernelGGL(attn_mfma_kernel<32>, grid, block, 0, stream, CB_ATTN_ARGS); break;
-    case 64: hipLaunchKernelGGL(attn_mfma_kernel<64>, grid, block, 0, stream, CB_ATTN_ARGS); break;
-    default: hipLaunchKernelGGL(attn_mfma_kernel<128>, grid, block, 0, stream, CB_ATTN_ARGS); break;
+    case 32: hipLaunchKernelGGL((attn_mfma_kernel<32, QB>), grid, block, 0, stream, p); break;
+    case 64: hipLaunchKernelGGL((attn_mfma_kernel<64, QB>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((attn_mfma_kernel<128, QB>), grid, block, 0, stream, p); break;
   }
-#undef CB_ATTN_ARGS
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !plan.split) return e;
+  const dim3 cgrid((unsigned)(plan.tiles * a.n_kv_heads));
+  switch (a.head_dim) {
+    case 32: hipLaunchKernelGGL((attn_combine_kernel<32, QB>), cgrid, block, 0, stream, p); break;
+    case 64: hipLaunchKernelGGL((attn_combine_kernel<64, QB>), cgrid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((attn_combine_kernel<128, QB>), cgrid, block, 0, stream, p); break;
+  }
   return hipGetLastError();
+}
+
+hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &plan, hipStream_t stream) {
+  if (plan.units == 0) return hipSuccess;
+  return plan.qb == 1 ? launch_mfma_qb<1>(a, plan, stream) : launch_mfma_qb<2>(a, plan, stream);
 }
 
 // ---------------------------------------------------------------------------
 // Plain kernel for every other geometry (fp32 storage, head_dim 16, group
-// sizes that do not divide 64): one wave per (selected row, query head),
-// 64 keys per step (one per lane), online softmax, fp32 throughout.
+// sizes that do not divide the MFMA tile): one wave per (selected row, query
+// head), 64 keys per step (one per lane), online softmax, fp32 throughout.
 // ---------------------------------------------------------------------------
 template <typename T>
 __device__ inline float ld(const T *p) { return (float)*p; }

@@ -35,8 +35,7 @@ hipError_t launch_fuse(void *k_fused, void *v_fused, const void *k_new_c,
                        const int32_t *sel_global, int64_t k_total,
                        int32_t row_bytes, hipStream_t stream);
 
-// Partial attention.  `tiles` is the number of query tiles over all requests
-// for the MFMA kernel (computed by the host from the selected counts).
+// Partial attention.
 struct AttnArgs {
   void *out;
   const void *q_c;
@@ -46,6 +45,7 @@ struct AttnArgs {
   const void *v_fused;
   const int32_t *tok_off;
   const int32_t *sel_off;
+  void *workspace;
   int32_t n_req;
   int32_t k_total;
   int32_t n_q_heads;
@@ -54,13 +54,25 @@ struct AttnArgs {
   float softmax_scale;
 };
 
-// Rows of one MFMA query tile (64 query vectors = rows x group heads), or 0
-// if the MFMA kernel does not cover this geometry.
-int attn_mfma_rows_per_tile(int dtype, int32_t n_q_heads, int32_t n_kv_heads,
-                            int32_t head_dim);
+// Host-side decomposition of the MFMA attention launch.
+struct AttnPlan {
+  int qb;              // blocks of 16 query vectors per wave (1 or 2)
+  int rows_per_tile;   // selected rows per query tile
+  int key_chunk;       // keys per unit (multiple of 64); huge = no split
+  bool split;          // some request has more than one chunk
+  int64_t tiles;       // query tiles over all requests
+  int64_t units;       // (tile, chunk) units over all requests
+  size_t ws_bytes;     // workspace the split needs
+};
 
-hipError_t launch_attn_mfma(const AttnArgs &a, int32_t rows_per_tile,
-                            int32_t n_tiles, hipStream_t stream);
+// Selected rows per MFMA query tile (64*qb query vectors), or 0 if the MFMA
+// kernel does not cover this geometry.
+int attn_mfma_rows_per_tile(int dtype, int32_t n_q_heads, int32_t n_kv_heads,
+                            int32_t head_dim, int qb);
+// Workspace bytes of one split unit.
+size_t attn_unit_bytes(int32_t head_dim, int qb);
+
+hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &plan, hipStream_t stream);
 
 hipError_t launch_attn_simple(int dtype, const AttnArgs &a, hipStream_t stream);
 

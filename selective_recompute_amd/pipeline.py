@@ -85,6 +85,9 @@ class BlendRunner:
                 sel_local=torch.empty(k, dtype=torch.int32, device=device),
                 sel_global=torch.empty(k, dtype=torch.int32, device=device),
                 out=torch.empty((k, n_q_heads, head_dim), dtype=dtype, device=device)))
+        # one attention workspace, sized for the largest layer, shared in stream order
+        ws = max(B.attn_workspace_bytes(self.geom, rb) for rb in self.batches)
+        self.workspace = B.workspace_tensor(ws, device)
 
     def candidates(self, layer: int) -> torch.Tensor:
         src = self.filter.cand_source(layer)
@@ -98,7 +101,8 @@ class BlendRunner:
                       delta=x["delta"], cand_idx=self.candidates(layer),
                       rope_theta=self.theta, rope_style=self.style,
                       softmax_scale=self.scale, dev=o["dev"], sel_local=o["sel_local"],
-                      sel_global=o["sel_global"], out=o["out"], stream=stream)
+                      sel_global=o["sel_global"], out=o["out"], workspace=self.workspace,
+                      stream=stream)
         return o
 
     def run(self, layers_inputs: Sequence[dict], stream=None):

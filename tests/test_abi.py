@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
             "cb_blend_layer"} <= declared
     for name in sorted(declared):
         assert hasattr(lib, name), name
-    assert lib.cb_abi_version() == 1
+    assert lib.cb_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -120,11 +120,14 @@ def test_fuse_and_attention_errors(lib):
     assert lib.cb_fuse_scatter(ctypes.byref(g), P, None, P, P, P, P, 4, None) == 1
     assert lib.cb_fuse_scatter(ctypes.byref(_geom(d=80)), P, P, P, P, P, P, 4, None) == 2
     rg, keep = _ragged([0, 10], [0, 10], [0, 3])
-    assert lib.cb_partial_attn(ctypes.byref(g), ctypes.byref(rg), P, P, P, P, P, P, 0.0, None) == 1
+    assert lib.cb_partial_attn(ctypes.byref(g), ctypes.byref(rg), P, P, P, P, P, P, 0.0, None, 0, None) == 1
     assert "softmax_scale" in lib.cb_last_error().decode()
-    assert lib.cb_partial_attn(ctypes.byref(g), ctypes.byref(rg), P, None, P, P, P, P, 0.1, None) == 1
+    assert lib.cb_partial_attn(ctypes.byref(g), ctypes.byref(rg), P, None, P, P, P, P, 0.1, None, 0, None) == 1
+    # a workspace size with no pointer is an error
+    assert lib.cb_partial_attn(ctypes.byref(g), ctypes.byref(rg), P, P, P, P, P, P, 0.1, None, 64, None) == 1
+    assert "workspace" in lib.cb_last_error().decode()
     rg2, keep2 = _ragged([0, 10], [0, 10], [0, 11])
-    assert lib.cb_partial_attn(ctypes.byref(g), ctypes.byref(rg2), P, P, P, P, P, P, 0.1, None) == 1
+    assert lib.cb_partial_attn(ctypes.byref(g), ctypes.byref(rg2), P, P, P, P, P, P, 0.1, None, 0, None) == 1
 
 
 def test_blend_layer_validates_every_stage_first(lib):
@@ -132,10 +135,11 @@ def test_blend_layer_validates_every_stage_first(lib):
     rg, keep = _ragged([0, 10], [0, 10], [0, 3])
     good = dict(geom=_geom(), rg=rg, k=P, v=P2, k_new_c=P, v_new_c=P, q_c=P, delta=P,
                 cand_idx=P, rope_theta=1e4, rope_style=0, softmax_scale=0.1, dev=P,
-                sel_local=P, sel_global=P, out=P)
+                sel_local=P, sel_global=P, out=P, workspace=None, workspace_bytes=0)
     # a bad field of the LAST stage still fails before anything is enqueued
     for field, value, status in [("out", None, 1), ("softmax_scale", -1.0, 1),
                                  ("rope_style", 3, 1), ("cand_idx", None, 1),
+                                 ("workspace_bytes", 1024, 1),
                                  ("geom", B.Geom(32, 8, 128, 9), 2)]:
         args = dict(good)
         args[field] = value
@@ -150,3 +154,20 @@ def test_zero_sized_calls_are_noops(lib):
     assert _rr(lib, g, k_out=None, k_in=None, delta=None, n_tok=0) == 0
     assert lib.cb_fuse_scatter(ctypes.byref(g), None, None, None, None, None, None, 0, None) == 0
     assert lib.cb_last_error() == b""
+
+
+def test_workspace_size_plan(lib):
+    """The split plan is a pure host computation: small tile counts ask for a
+    workspace, large ones or unsupported geometries do not."""
+    def size(g, tok, sel):
+        rg, keep = _ragged(tok, tok, sel)
+        n = ctypes.c_size_t(123)
+        assert lib.cb_partial_attn_workspace_size(ctypes.byref(g), ctypes.byref(rg), ctypes.byref(n)) == 0
+        return n.value
+    unit = (64 * 128 + 2 * 64) * 4
+    # 308 rows / 16 per tile = 20 tiles x 8 heads, 2048 keys in chunks of 256
+    assert size(_geom(), [0, 2048], [0, 308]) == 20 * 8 * 8 * unit
+    assert size(_geom(), [0, 32768], [0, 6554]) == 0            # enough tiles already
+    assert size(_geom(dt=B.CB_DTYPE_F32), [0, 2048], [0, 308]) == 0   # plain kernel
+    assert size(_geom(d=16), [0, 2048], [0, 308]) == 0
+    assert lib.cb_partial_attn_workspace_size(ctypes.byref(_geom()), None, None) == 1

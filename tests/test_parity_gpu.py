@@ -192,10 +192,11 @@ ATTN_CASES = [
 ]
 
 
+@pytest.mark.parametrize("use_ws", [False, True], ids=["direct", "split"])
 @pytest.mark.parametrize("case", ATTN_CASES, ids=[f"a{i}" for i in range(len(ATTN_CASES))])
-def test_partial_attention_parity(case):
+def test_partial_attention_parity(case, use_ws):
     dtype, hq, hkv, d, lens, ks = case
-    say(f"attention {case}")
+    say(f"attention {case} workspace={use_ws}")
     rng = np.random.default_rng(sum(lens) + hq)
     t_count = sum(lens)
     tok_off = PL.offsets(lens)
@@ -218,10 +219,18 @@ def test_partial_attention_parity(case):
     kf = torch.randn(t_count, hkv, d).to(dtype)
     vf = torch.randn(t_count, hkv, d).to(dtype)
     rb = B.RaggedBatch(tok_off, tok_off, sel_off, DEV)
+    g = B.geom(hq, hkv, d, dtype)
+    ws = None
+    if use_ws:
+        nbytes = B.attn_workspace_bytes(g, rb)
+        if nbytes == 0:
+            pytest.skip("this geometry never splits")
+        ws = B.workspace_tensor(nbytes, DEV)
+        ws.fill_(0xFF)                                        # NaN garbage: must be overwritten
     out = torch.full((rb.n_sel, hq, d), float("nan"), dtype=dtype, device=DEV)
     scale = 1.0 / math.sqrt(d)
-    B.partial_attn(B.geom(hq, hkv, d, dtype), rb, out, q.to(DEV), torch.from_numpy(sel_l).to(DEV),
-                   torch.from_numpy(sel_g).to(DEV), kf.to(DEV), vf.to(DEV), scale)
+    B.partial_attn(g, rb, out, q.to(DEV), torch.from_numpy(sel_l).to(DEV),
+                   torch.from_numpy(sel_g).to(DEV), kf.to(DEV), vf.to(DEV), scale, workspace=ws)
     torch.cuda.synchronize()
     ref = O.attention_rows(np64(q), sel_l, sel_g, row_start, np64(kf), np64(vf), hq, hkv, scale)
     got = np64(out)
