@@ -45,6 +45,9 @@ def parse_args():
     ap.add_argument("--schedule", default="pool", choices=["pool", "chain"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="budget of the CPU oracle baseline (0 disables it)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the run, copy this many MiB device to device once (a "
+                         "plain copy of known size that calibrates byte counters)")
     return ap.parse_args()
 
 
@@ -285,6 +288,15 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None}
     del stage_calls, copies, keep
     torch.cuda.empty_cache()
+
+    if a.copy_probe_mib > 0:
+        n = a.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if a.cpu_seconds > 0:

@@ -223,12 +223,16 @@ constexpr int kNoSplit = 1 << 30;
 // `ws_bytes` of workspace and is dropped when `ws_avail` is smaller.
 cb::AttnPlan plan_attn(const cb_geom *g, const cb_ragged *rg, size_t ws_avail) {
   cb::AttnPlan pl{};
-  // One 16-query block per wave: with 32 queries per wave the head_dim-128
-  // kernel needs more than 256 registers and drops to one wave per SIMD,
-  // which measured slower.
-  pl.qb = 1;
+  // Two 16-query blocks per wave (each K/V fragment read from LDS feeds two
+  // MFMAs); one block where the group size does not divide 128.
+  pl.qb = 2;
   pl.rows_per_tile = cb::attn_mfma_rows_per_tile(g->dtype, g->n_q_heads, g->n_kv_heads,
-                                                 g->head_dim, 1);
+                                                 g->head_dim, 2);
+  if (pl.rows_per_tile == 0) {
+    pl.qb = 1;
+    pl.rows_per_tile = cb::attn_mfma_rows_per_tile(g->dtype, g->n_q_heads, g->n_kv_heads,
+                                                   g->head_dim, 1);
+  }
   pl.key_chunk = kNoSplit;
   if (pl.rows_per_tile == 0) return pl;
   const int rows = pl.rows_per_tile;
@@ -240,7 +244,7 @@ cb::AttnPlan plan_attn(const cb_geom *g, const cb_ragged *rg, size_t ws_avail) {
   }
   const int64_t blocks = pl.tiles * g->n_kv_heads;
   if (blocks > 0 && blocks < 1024) {
-    const int64_t want = (2048 + blocks - 1) / blocks;
+    const int64_t want = std::min<int64_t>((2048 + blocks - 1) / blocks, cb::attn_max_chunks());
     int64_t kc = (max_n + want - 1) / want;
     kc = std::max<int64_t>(256, (kc + 63) / 64 * 64);
     if (kc < max_n) pl.key_chunk = (int)kc;

@@ -19,28 +19,34 @@ namespace cb {
 // QT = 64*QB query vectors: rows_per_tile selected rows of one request times
 // the G = Hq/Hkv query heads that read KV head g, so one K/V stream serves
 // all of them.  A workgroup of 4 waves owns a unit; each wave owns 16*QB
-// query vectors.  Keys are streamed through LDS in tiles of 64:
+// query vectors.  Keys stream through LDS in tiles of 64:
 //
+//  * Staging: K and V tiles go global -> LDS with global_load_lds_dwordx4
+//    (no registers), two stages: while tile t is multiplied, tile t+1 is in
+//    flight.  The LDS tiles are row-major with an XOR swizzle of the 16-byte
+//    chunks of each key row (different for K and V) so that the two read
+//    patterns below are free of bank conflicts.
 //  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (keys on the M side, queries
-//    on the N side): a lane's accumulators all belong to one query column,
-//    so the online-softmax statistics stay in the lane (plus its partners
-//    l^16, l^32, l^48) and the probabilities are already laid out as the B
-//    operand of the second product.
-//  * O^T += V^T P^T.  V is stored row-major in LDS; the A operand (8 keys of
-//    one head dimension per lane) is read with gfx950's ds_read_b64_tr_b16:
-//    in each 16-lane group, lane j points at V[key0 + j/4][d0 + 4(j%4)] and
-//    lane i receives V[key0 .. key0+3][d0 + i].
-//  * The next tile's K/V are loaded into registers while the current one is
-//    multiplied, then stored to LDS.
-//  * Each K (A operand) and V^T read from LDS feeds QB MFMAs, one per block
-//    of 16 query vectors.
+//    on the N side): a lane's accumulators all belong to one query column, so
+//    the online-softmax statistics stay in the lane (plus its partners l^16,
+//    l^32, l^48) and the probabilities are already laid out as the B operand
+//    of the second product.  Each K fragment read from LDS feeds QB MFMAs.
+//  * O^T += V^T P^T.  The A operand (8 keys of one head dimension per lane)
+//    comes from gfx950's ds_read_b64_tr_b16: in each 16-lane group, lane j
+//    points at V[key0 + j/4][d0 + 4(j%4)] and lane i receives
+//    V[key0 .. key0+3][d0 + i].
+//  * Softmax in base 2 with the scale folded into one FMA; the running max is
+//    only raised (and O rescaled) when a column's tile max exceeds it by more
+//    than 2^8, so most tiles skip the rescale; tiles that every query of the
+//    unit sees in full skip the causal mask.
 //
 // Long rows with too few tiles to fill the chip are split over key chunks of
 // `key_chunk` keys (a multiple of 64); every chunk writes its unnormalised
 // fp32 partial (O, running max, running sum) to the workspace and
 // attn_combine_kernel merges them.  Unsplit units write the output directly.
 // Block order: blockIdx % Hkv is the KV head, so with Hkv = 8 the round-robin
-// dispatch over the 8 XCDs keeps each head's K/V stream in one XCD's L2.
+// dispatch over the 8 XCDs keeps each head's K/V stream in one XCD's L2; in a
+// request the last (longest) tiles start first.
 // ---------------------------------------------------------------------------
 struct AttnParams {
   bf16 *out;
@@ -58,17 +64,30 @@ struct AttnParams {
 
 constexpr int kKeyTile = 64;
 constexpr float kNegFloor = -1.0e30f;  // finite start of the running max
+constexpr float kRescaleSlack = 8.0f;  // log2 headroom before the max is raised
+constexpr int kMaxChunks = 8;          // key chunks per row (split plan bound)
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void global_cvoid;
 
 __device__ inline bf16x4 lds_read_tr(const bf16 *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p));
 }
 
-// Which (request, tile, chunk) unit `u` is; returns false if u is out of range.
+// Swizzled chunk of key row r: physical 16-byte chunk = logical ^ f(r).
+template <int HD> __device__ constexpr int swz_k(int r) {
+  return (r / (128 / HD)) & (HD / 8 - 1);
+}
+template <int HD> __device__ constexpr int swz_v(int r) {
+  return 2 * ((r / (128 / HD)) & (HD / 16 - 1));
+}
+
+// Unit u -> (request r, tile, chunk); units of a request run from its last
+// tile to its first.  Returns false past the last unit.
 __device__ inline bool locate_unit(const AttnParams &p, int u, int &r, int &tile, int &chunk,
-                                   int &nchunks, int64_t &ubase) {
-  ubase = 0;
+                                   int &nchunks) {
+  int64_t ubase = 0;
   for (r = 0; r < p.n_req; ++r) {
     const int kr = p.sel_off[r + 1] - p.sel_off[r];
     const int n = p.tok_off[r + 1] - p.tok_off[r];
@@ -77,8 +96,8 @@ __device__ inline bool locate_unit(const AttnParams &p, int u, int &r, int &tile
     const int64_t nu = (int64_t)tr * cr;
     if (u < ubase + nu) {
       const int ul = (int)(u - ubase);
-      tile = ul / cr;
-      chunk = ul - tile * cr;
+      tile = tr - 1 - ul / cr;
+      chunk = ul - (ul / cr) * cr;
       nchunks = cr;
       return true;
     }
@@ -88,32 +107,67 @@ __device__ inline bool locate_unit(const AttnParams &p, int u, int &r, int &tile
 }
 
 template <int HD, int QB>
-__global__ __launch_bounds__(256) void attn_mfma_kernel(const AttnParams p) {
-  constexpr int LS = HD + 8;            // LDS row stride (elements) of the K and V tiles
-  constexpr int NST = HD / 32;          // 32-wide contraction steps over head_dim
-  constexpr int NDT = HD / 16;          // 16-row output tiles over head_dim
-  constexpr int QT = 64 * QB;           // query vectors per unit
-  constexpr int CPR = HD / 8;           // 16-byte chunks per key row
-  constexpr int CPT = kKeyTile * CPR / 256;  // chunks per thread per tensor
-  __shared__ __attribute__((aligned(16))) bf16 ks[kKeyTile * LS];
-  __shared__ __attribute__((aligned(16))) bf16 vs[kKeyTile * LS];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_mfma_kernel(const AttnParams p) {
+  constexpr int NST = HD / 32;            // 32-wide contraction steps over head_dim
+  constexpr int NDT = HD / 16;            // 16-row output tiles over head_dim
+  constexpr int QT = 64 * QB;             // query vectors per unit
+  constexpr int CPR = HD / 8;             // 16-byte chunks per key row
+  constexpr int TILE = kKeyTile * HD;     // elements per tensor per stage
+  constexpr int DPW = CPR / 4;            // 1 KiB DMA instructions per wave per tensor
+  __shared__ __attribute__((aligned(1024))) bf16 kst[2][TILE];  // K stages
+  __shared__ __attribute__((aligned(1024))) bf16 vst[2][TILE];  // V stages
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int g = blockIdx.x % p.hkv;
   int r, tile, chunk, nchunks;
-  int64_t ubase;
-  if (!locate_unit(p, (int)(blockIdx.x / p.hkv), r, tile, chunk, nchunks, ubase)) return;
+  if (!locate_unit(p, (int)(blockIdx.x / p.hkv), r, tile, chunk, nchunks)) return;
   const int s0 = p.sel_off[r] + tile * p.rows_per_tile;
   const int ns = min(p.rows_per_tile, p.sel_off[r + 1] - s0);
   const int lo = p.tok_off[r];
+  const int p_first = p.sel_global[s0];
   const int p_last = p.sel_global[s0 + ns - 1];
   const int64_t kb = (int64_t)lo + (int64_t)chunk * p.key_chunk;
   if (kb > p_last) return;  // whole chunk after the tile's last row (uniform)
   const int k_begin = (int)kb;
   const int k_end = (int)min((int64_t)p_last + 1, kb + p.key_chunk);
 
-  // Query columns of this lane: one per block of 16.
+  // DMA slots of this thread: instruction i writes 64 consecutive 16-byte
+  // chunks of the tile; lane -> (row, physical chunk) -> logical chunk.  The
+  // byte offsets from the tile's first key row are loop invariant; only the
+  // last tile, which may run past the tile's last row, clamps its rows.
+  const int64_t rs = (int64_t)p.hkv * HD;
+  int dma_row[DPW];
+  uint32_t dma_ko[DPW], dma_vo[DPW];
+#pragma unroll
+  for (int i = 0; i < DPW; ++i) {
+    const int pos = (wave * DPW + i) * 64 + lane;
+    const int row = pos / CPR, q = pos - row * CPR;
+    dma_row[i] = row;
+    dma_ko[i] = (uint32_t)((row * rs + (q ^ swz_k<HD>(row)) * 8) * 2);
+    dma_vo[i] = (uint32_t)((row * rs + (q ^ swz_v<HD>(row)) * 8) * 2);
+  }
+  const char *kbase = (const char *)(p.k_fused + (int64_t)g * HD);
+  const char *vbase = (const char *)(p.v_fused + (int64_t)g * HD);
+  // One tensor's tile of 64 keys starting at k0 into an LDS stage buffer.
+  auto issue = [&](bf16 *dst, const char *base, const uint32_t *offs, int k0) {
+    const char *tile_base = base + (int64_t)k0 * rs * 2;
+    const bool clamp = k0 + kKeyTile - 1 > p_last;
+#pragma unroll
+    for (int i = 0; i < DPW; ++i) {
+      uint32_t off = offs[i];
+      if (clamp && k0 + dma_row[i] > p_last)  // rows past the last key are masked
+        off -= (uint32_t)((k0 + dma_row[i] - p_last) * rs * 2);
+      __builtin_amdgcn_global_load_lds((global_cvoid *)(tile_base + off),
+                                       (lds_void *)(dst + (wave * DPW + i) * 512), 16, 0, 0);
+    }
+  };
+  issue(kst[0], kbase, dma_ko, k_begin);
+  issue(vst[0], vbase, dma_vo, k_begin);
+
+  // Query columns of this lane: one per block of 16.  Padding columns (past
+  // the tile's last row) see every key; their results are dropped.
   int p_q[QB];
   bf16x8 qreg[QB][NST];
 #pragma unroll
@@ -122,7 +176,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(const AttnParams p) {
     const int row = qv / p.group, hh = qv - row * p.group;
     const bool valid = row < ns;
     const int s = s0 + (valid ? row : 0);
-    p_q[qb] = valid ? p.sel_global[s] : lo;
+    p_q[qb] = valid ? p.sel_global[s] : p_last;
     const bf16 *qp = p.q_c + ((int64_t)p.sel_local[s] * p.hq + g * p.group + hh) * HD + 8 * grp;
 #pragma unroll
     for (int st = 0; st < NST; ++st) qreg[qb][st] = *reinterpret_cast<const bf16x8 *>(qp + 32 * st);
@@ -138,40 +192,38 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(const AttnParams p) {
     for (int dt = 0; dt < NDT; ++dt) o[qb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int64_t rs = (int64_t)p.hkv * HD;
-  const bf16 *kbase = p.k_fused + (int64_t)g * HD;
-  const bf16 *vbase = p.v_fused + (int64_t)g * HD;
-  bf16x8 kpre[CPT], vpre[CPT];
-  auto load_tile = [&](int k0) {
+  // LDS read offsets of this lane (elements within a stage buffer): the K
+  // fragment of contraction step st for key sub-tile t is at koff[st] + t*16*HD;
+  // the V^T fragment of head-dim tile dt is at voff[dt] (+16*HD for the second
+  // 4 keys, +32*HD for the second 32-key half).
+  int koff[NST], voff[NDT];
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + 256 * i, key = c / CPR, c8 = c - key * CPR;
-      if (k0 + key <= p_last) {
-        const int64_t off = (int64_t)(k0 + key) * rs + c8 * 8;
-        kpre[i] = *reinterpret_cast<const bf16x8 *>(kbase + off);
-        vpre[i] = *reinterpret_cast<const bf16x8 *>(vbase + off);
-      } else {
-        kpre[i] = bf16x8{};
-        vpre[i] = bf16x8{};
-      }
-    }
-  };
-  auto store_tile = [&]() {
+  for (int st = 0; st < NST; ++st) koff[st] = col * HD + (((4 * st + grp) ^ swz_k<HD>(col)) << 3);
+  {
+    const int r0 = 4 * grp + (col >> 2);
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + 256 * i, key = c / CPR, c8 = c - key * CPR;
-      *reinterpret_cast<bf16x8 *>(ks + key * LS + c8 * 8) = kpre[i];
-      *reinterpret_cast<bf16x8 *>(vs + key * LS + c8 * 8) = vpre[i];
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int e = 16 * dt + 4 * (col & 3);
+      voff[dt] = r0 * HD + (((e >> 3) ^ swz_v<HD>(r0)) << 3) + (e & 7);
     }
-  };
+  }
 
+  // Two LDS stages per tensor: while tile kt is multiplied, tile kt+1 is in
+  // flight.
   const int n_kt = (k_end - k_begin + kKeyTile - 1) / kKeyTile;
-  load_tile(k_begin);
   for (int kt = 0; kt < n_kt; ++kt) {
+    const int stage = kt & 1;
     const int k0 = k_begin + kt * kKeyTile;
-    store_tile();
+    // tile kt has landed (this wave's DMA: vmcnt 0; the others': barrier) and
+    // every wave is done reading tile kt-1, whose buffers are refilled next
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kt + 1 < n_kt) load_tile(k0 + kKeyTile);
+    if (kt + 1 < n_kt) {
+      issue(kst[stage ^ 1], kbase, dma_ko, k0 + kKeyTile);
+      issue(vst[stage ^ 1], vbase, dma_vo, k0 + kKeyTile);
+    }
+    const bf16 *ks = kst[stage];
+    const bf16 *vs = vst[stage];
 
     // S^T: sacc[qb][t][i] = score(key k0 + 16t + 4grp + i, query column qb).
     f32x4 sacc[QB][4];
@@ -181,45 +233,52 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(const AttnParams p) {
       for (int qb = 0; qb < QB; ++qb) sacc[qb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < NST; ++st) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(ks + (16 * t + col) * LS + 32 * st + 8 * grp);
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(ks + koff[st] + t * 16 * HD);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           sacc[qb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[qb][st], sacc[qb][t], 0, 0, 0);
       }
     }
 
-    // Online softmax in base 2, per query column.
+    const bool need_mask = k0 + kKeyTile - 1 > p_first;
     bf16x8 bp[QB][2];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = -INFINITY;
+      if (need_mask) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (k0 + 16 * t + 4 * grp + i > p_q[qb]) sacc[qb][t][i] = -INFINITY;
+      }
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = k0 + 16 * t + 4 * grp + i;
-          float v = sacc[qb][t][i] * p.scale_log2;
-          if (key > p_q[qb]) v = -INFINITY;
-          sacc[qb][t][i] = v;
-          mx = fmaxf(mx, v);
-        }
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[qb][t][i]);
       mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
       mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float m_new = fmaxf(m_run[qb], mx);
-      const float alpha = exp2f(m_run[qb] - m_new);
+      const float mxs = mx * p.scale_log2;
+      const bool up = mxs > m_run[qb] + kRescaleSlack;
+      if (__any(up)) {
+        const float m_new = up ? mxs : m_run[qb];
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        m_run[qb] = m_new;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[qb][dt] *= alpha;
+      }
+      const float neg_m = -m_run[qb];
       float psum = 0.f;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pv = exp2f(sacc[qb][t][i] - m_new);
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[qb][t][i], p.scale_log2, neg_m));
           psum += pv;
           bp[qb][t >> 1][4 * (t & 1) + i] = (bf16)pv;
         }
-      l_run[qb] = l_run[qb] * alpha + psum;
-      m_run[qb] = m_new;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[qb][dt] *= alpha;
+      l_run[qb] += psum;
     }
 
     // O^T += V^T P^T over two 32-key halves; V^T comes from transpose reads.
@@ -227,16 +286,15 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(const AttnParams p) {
     for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const bf16 *a0 = vs + (32 * kh + 4 * grp + (col >> 2)) * LS + 16 * dt + 4 * (col & 3);
-        const bf16x4 lo4 = lds_read_tr(a0);
-        const bf16x4 hi4 = lds_read_tr(a0 + 16 * LS);
+        const bf16 *vp = vs + voff[dt] + kh * 32 * HD;
+        const bf16x4 lo4 = lds_read_tr(vp);
+        const bf16x4 hi4 = lds_read_tr(vp + 16 * HD);
         const bf16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           o[qb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bp[qb][kh], o[qb][dt], 0, 0, 0);
       }
     }
-    __syncthreads();
   }
 
 #pragma unroll
@@ -271,19 +329,27 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(const AttnParams p) {
   }
 }
 
-// Merge the key-chunk partials of one (query tile, KV head).
+// Merge the key-chunk partials.  One thread per (query vector, 4 head dims):
+// it loads the running max, running sum and partial O of every chunk at once
+// (unrolled over the chunk bound, inactive chunks clamped to chunk 0 and
+// weighted 0), so each thread waits for a single round of loads.
 template <int HD, int QB>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   constexpr int QT = 64 * QB;
   constexpr int UNIT = QT * HD + 2 * QT;
+  constexpr int D4 = HD / 4;              // float4 groups per query vector
+  constexpr int QPB = 256 / D4;           // query vectors per workgroup
+  constexpr int GROUPS = QT / QPB;        // workgroups per (tile, head)
   const int g = blockIdx.x % p.hkv;
-  const int tile_u = blockIdx.x / p.hkv;
-  int r, tile = 0, cr = 1;
+  const int rest = blockIdx.x / p.hkv;
+  const int qgroup = rest % GROUPS;
+  const int tile_u = rest / GROUPS;
+  int r, tile = 0, cr = 1, tr = 0;
   int64_t ubase = 0, tbase = 0;
   for (r = 0; r < p.n_req; ++r) {
     const int kr = p.sel_off[r + 1] - p.sel_off[r];
     const int n = p.tok_off[r + 1] - p.tok_off[r];
-    const int tr = (kr + p.rows_per_tile - 1) / p.rows_per_tile;
+    tr = (kr + p.rows_per_tile - 1) / p.rows_per_tile;
     cr = (int)(((int64_t)n + p.key_chunk - 1) / p.key_chunk);
     if (tile_u < tbase + tr) { tile = (int)(tile_u - tbase); break; }
     tbase += tr;
@@ -292,32 +358,42 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   if (r == p.n_req || cr == 1) return;
   const int s0 = p.sel_off[r] + tile * p.rows_per_tile;
   const int ns = min(p.rows_per_tile, p.sel_off[r + 1] - s0);
+  const int qv = qgroup * QPB + (int)threadIdx.x / D4;
+  const int d4 = (int)threadIdx.x % D4;
+  const int row = qv / p.group, hh = qv - row * p.group;
+  if (row >= ns) return;
   const int lo = p.tok_off[r];
   const int p_last = p.sel_global[s0 + ns - 1];
   const int n_active = (p_last - lo) / p.key_chunk + 1;
-  const float *w0 = p.ws + ((ubase + (int64_t)tile * cr) * p.hkv + g) * UNIT;
+  // unit of (tile, chunk c) is ubase + (tr - 1 - tile) * cr + c
+  const float *w0 = p.ws + ((ubase + (int64_t)(tr - 1 - tile) * cr) * p.hkv + g) * UNIT;
   const int64_t ustride = (int64_t)p.hkv * UNIT;
-  for (int task = threadIdx.x; task < QT * HD / 4; task += blockDim.x) {
-    const int qv = task / (HD / 4), d4 = task - qv * (HD / 4);
-    const int row = qv / p.group, hh = qv - row * p.group;
-    if (row >= ns) continue;
-    float mx = kNegFloor;
-    for (int c = 0; c < n_active; ++c) mx = fmaxf(mx, w0[c * ustride + QT * HD + qv]);
-    float l = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < n_active; ++c) {
-      const float *w = w0 + c * ustride;
-      const float sc = exp2f(w[QT * HD + qv] - mx);
-      l += w[QT * HD + QT + qv] * sc;
-      acc += *reinterpret_cast<const f32x4 *>(w + qv * HD + 4 * d4) * sc;
-    }
-    const float inv = 1.f / l;
-    bf16x4 o;
+  float mc[kMaxChunks], lc[kMaxChunks];
+  f32x4 oc[kMaxChunks];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = (bf16)(acc[i] * inv);
-    *reinterpret_cast<bf16x4 *>(p.out + ((int64_t)(s0 + row) * p.hq + g * p.group + hh) * HD +
-                                4 * d4) = o;
+  for (int c = 0; c < kMaxChunks; ++c) {
+    const float *w = w0 + (c < n_active ? c : 0) * ustride;
+    mc[c] = w[QT * HD + qv];
+    lc[c] = w[QT * HD + QT + qv];
+    oc[c] = *reinterpret_cast<const f32x4 *>(w + qv * HD + 4 * d4);
   }
+  float mx = kNegFloor;
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) mx = fmaxf(mx, c < n_active ? mc[c] : kNegFloor);
+  float l = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    const float wgt = c < n_active ? __builtin_amdgcn_exp2f(mc[c] - mx) : 0.f;
+    l += lc[c] * wgt;
+    acc += oc[c] * wgt;
+  }
+  const float inv = 1.f / l;
+  bf16x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = (bf16)(acc[i] * inv);
+  *reinterpret_cast<bf16x4 *>(p.out + ((int64_t)(s0 + row) * p.hq + g * p.group + hh) * HD +
+                              4 * d4) = o;
 }
 
 int attn_mfma_rows_per_tile(int dtype, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
@@ -334,6 +410,8 @@ size_t attn_unit_bytes(int32_t head_dim, int qb) {
   const size_t qt = 64 * (size_t)qb;
   return (qt * head_dim + 2 * qt) * sizeof(float);
 }
+
+int attn_max_chunks() { return kMaxChunks; }
 
 template <int QB>
 static hipError_t launch_mfma_qb(const AttnArgs &a, const AttnPlan &plan, hipStream_t stream) {
@@ -362,7 +440,8 @@ static hipError_t launch_mfma_qb(const AttnArgs &a, const AttnPlan &plan, hipStr
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !plan.split) return e;
-  const dim3 cgrid((unsigned)(plan.tiles * a.n_kv_heads));
+  const int groups = 64 * QB / (256 / (a.head_dim / 4));
+  const dim3 cgrid((unsigned)(plan.tiles * a.n_kv_heads * groups));
   switch (a.head_dim) {
     case 32: hipLaunchKernelGGL((attn_combine_kernel<32, QB>), cgrid, block, 0, stream, p); break;
     case 64: hipLaunchKernelGGL((attn_combine_kernel<64, QB>), cgrid, block, 0, stream, p); break;

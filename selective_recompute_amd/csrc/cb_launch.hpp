@@ -71,6 +71,8 @@ int attn_mfma_rows_per_tile(int dtype, int32_t n_q_heads, int32_t n_kv_heads,
                             int32_t head_dim, int qb);
 // Workspace bytes of one split unit.
 size_t attn_unit_bytes(int32_t head_dim, int qb);
+// Most key chunks one row may be split into.
+int attn_max_chunks();
 
 hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &plan, hipStream_t stream);
 
