@@ -116,6 +116,13 @@ cb_status check_ragged(const cb_ragged *rg, bool want_tok, bool want_cand, bool 
   return CB_OK;
 }
 
+int32_t max_cand(const cb_ragged *rg) {
+  int32_t mx = 0;
+  for (int32_t r = 0; r < rg->n_req; ++r)
+    mx = std::max(mx, rg->h_cand_off[r + 1] - rg->h_cand_off[r]);
+  return mx;
+}
+
 cb_status hip_status(hipError_t e, const char *what) {
   if (e == hipSuccess) return CB_OK;
   return fail(CB_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -223,16 +230,8 @@ constexpr int kNoSplit = 1 << 30;
 // `ws_bytes` of workspace and is dropped when `ws_avail` is smaller.
 cb::AttnPlan plan_attn(const cb_geom *g, const cb_ragged *rg, size_t ws_avail) {
   cb::AttnPlan pl{};
-  // Two 16-query blocks per wave (each K/V fragment read from LDS feeds two
-  // MFMAs); one block where the group size does not divide 128.
-  pl.qb = 2;
   pl.rows_per_tile = cb::attn_mfma_rows_per_tile(g->dtype, g->n_q_heads, g->n_kv_heads,
-                                                 g->head_dim, 2);
-  if (pl.rows_per_tile == 0) {
-    pl.qb = 1;
-    pl.rows_per_tile = cb::attn_mfma_rows_per_tile(g->dtype, g->n_q_heads, g->n_kv_heads,
-                                                   g->head_dim, 1);
-  }
+                                                 g->head_dim);
   pl.key_chunk = kNoSplit;
   if (pl.rows_per_tile == 0) return pl;
   const int rows = pl.rows_per_tile;
@@ -264,7 +263,7 @@ cb::AttnPlan plan_attn(const cb_geom *g, const cb_ragged *rg, size_t ws_avail) {
   };
   pl.units = count_units(pl.key_chunk, pl.split);
   if (pl.split) {
-    pl.ws_bytes = (size_t)pl.units * g->n_kv_heads * cb::attn_unit_bytes(g->head_dim, pl.qb);
+    pl.ws_bytes = (size_t)pl.units * g->n_kv_heads * cb::attn_unit_bytes(g->head_dim);
     if (pl.ws_bytes > ws_avail) {
       pl.key_chunk = kNoSplit;
       pl.units = count_units(pl.key_chunk, pl.split);
@@ -322,7 +321,7 @@ CB_EXPORT cb_status cb_deviation_topk(const cb_geom *geom, const cb_ragged *rg,
                     "deviation"));
   if (rg->h_sel_off[rg->n_req] == 0) return CB_OK;
   return hip_status(cb::launch_topk(rg->n_req, dev, cand_idx, rg->cand_off, rg->sel_off,
-                                    sel_local, sel_global, (hipStream_t)stream),
+                                    sel_local, sel_global, max_cand(rg), (hipStream_t)stream),
                     "topk");
 }
 
@@ -332,7 +331,7 @@ CB_EXPORT cb_status cb_topk(const cb_ragged *rg, const float *dev, const int32_t
   CB_TRY(validate_topk(rg, dev, cand_idx, sel_local, sel_global));
   if (rg->h_sel_off[rg->n_req] == 0) return CB_OK;
   return hip_status(cb::launch_topk(rg->n_req, dev, cand_idx, rg->cand_off, rg->sel_off,
-                                    sel_local, sel_global, (hipStream_t)stream),
+                                    sel_local, sel_global, max_cand(rg), (hipStream_t)stream),
                     "topk");
 }
 
@@ -392,18 +391,28 @@ CB_EXPORT cb_status cb_blend_layer(const cb_layer_args *a, void *stream) {
                        a->softmax_scale));
   CB_TRY(need_ptr(a->workspace, "workspace", a->workspace_bytes > 0));
   const hipStream_t s = (hipStream_t)stream;
-  if (a->delta && n_tok > 0)
-    CB_TRY(hip_status(cb::launch_rerotate(geom->dtype, a->rope_style, a->k, a->k, a->delta, n_tok,
-                                          1, geom->n_kv_heads, geom->head_dim,
-                                          rope_table(geom->head_dim, a->rope_theta), s),
-                      "rerotate"));
   const int32_t m = rg->h_cand_off[rg->n_req];
-  CB_TRY(hip_status(cb::launch_deviation(geom->dtype, a->v_new_c, a->v, a->cand_idx, a->dev, m,
-                                         (int32_t)row_elems(geom), s),
-                    "deviation"));
+  if (a->delta && n_tok > 0 &&
+      cb::rerotate_deviation_fits(geom->dtype, geom->n_kv_heads, geom->head_dim)) {
+    // independent K and V work in one launch
+    CB_TRY(hip_status(cb::launch_rerotate_deviation(
+                          geom->dtype, a->rope_style, a->k, a->delta, n_tok, geom->n_kv_heads,
+                          geom->head_dim, rope_table(geom->head_dim, a->rope_theta), a->v_new_c,
+                          a->v, a->cand_idx, a->dev, m, s),
+                      "rerotate+deviation"));
+  } else {
+    if (a->delta && n_tok > 0)
+      CB_TRY(hip_status(cb::launch_rerotate(geom->dtype, a->rope_style, a->k, a->k, a->delta,
+                                            n_tok, 1, geom->n_kv_heads, geom->head_dim,
+                                            rope_table(geom->head_dim, a->rope_theta), s),
+                        "rerotate"));
+    CB_TRY(hip_status(cb::launch_deviation(geom->dtype, a->v_new_c, a->v, a->cand_idx, a->dev,
+                                           m, (int32_t)row_elems(geom), s),
+                      "deviation"));
+  }
   if (k_total == 0) return CB_OK;
   CB_TRY(hip_status(cb::launch_topk(rg->n_req, a->dev, a->cand_idx, rg->cand_off, rg->sel_off,
-                                    a->sel_local, a->sel_global, s),
+                                    a->sel_local, a->sel_global, max_cand(rg), s),
                     "topk"));
   CB_TRY(hip_status(cb::launch_fuse(a->k, a->v, a->k_new_c, a->v_new_c, a->sel_local,
                                     a->sel_global, k_total,

@@ -15,26 +15,29 @@ namespace cb {
 // ---------------------------------------------------------------------------
 // MFMA kernel (bf16, head_dim HD in {32, 64, 128}).
 //
-// Work unit = (query tile, KV head g, key chunk).  A query tile holds
-// QT = 64*QB query vectors: rows_per_tile selected rows of one request times
-// the G = Hq/Hkv query heads that read KV head g, so one K/V stream serves
-// all of them.  A workgroup of 4 waves owns a unit; each wave owns 16*QB
-// query vectors.  Keys stream through LDS in tiles of 64:
+// Work unit = (query tile, KV head g, key chunk).  A query tile holds 128
+// query vectors: rows_per_tile selected rows of one request times the
+// G = Hq/Hkv query heads that read KV head g, so one K/V stream serves all of
+// them.  A workgroup of 4 waves owns a unit; each wave owns 32 query vectors.
+// Keys stream through LDS in tiles of 64.  All products use
+// v_mfma_f32_32x32x16_bf16, which on gfx950 sustains about twice the rate of
+// the 16x16x32 form.  Lane l of a 32x32 result holds rows
+// 8(r/4) + 4(l/32) + r%4 (r = 0..15) of column l%32.
 //
 //  * Staging: K and V tiles go global -> LDS with global_load_lds_dwordx4
 //    (no registers), two stages: while tile t is multiplied, tile t+1 is in
 //    flight.  The LDS tiles are row-major with an XOR swizzle of the 16-byte
 //    chunks of each key row (different for K and V) so that the two read
 //    patterns below are free of bank conflicts.
-//  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (keys on the M side, queries
-//    on the N side): a lane's accumulators all belong to one query column, so
-//    the online-softmax statistics stay in the lane (plus its partners l^16,
-//    l^32, l^48) and the probabilities are already laid out as the B operand
-//    of the second product.  Each K fragment read from LDS feeds QB MFMAs.
-//  * O^T += V^T P^T.  The A operand (8 keys of one head dimension per lane)
-//    comes from gfx950's ds_read_b64_tr_b16: in each 16-lane group, lane j
-//    points at V[key0 + j/4][d0 + 4(j%4)] and lane i receives
-//    V[key0 .. key0+3][d0 + i].
+//  * S^T = K Q^T (keys on the M side, queries on the N side) in two 32-key
+//    blocks: a lane's 32 scores all belong to one query column, so the
+//    online-softmax statistics stay in the lane and its partner l^32, and the
+//    probabilities of 16 consecutive keys are 8 consecutive accumulator
+//    registers -- already the B operand of the second product.
+//  * O^T += V^T P^T in 32-dim blocks.  The A operand (8 keys of one head
+//    dimension per lane) comes from gfx950's ds_read_b64_tr_b16: in each
+//    16-lane group, lane j points at V[key0 + j/4][d0 + 4(j%4)] and lane i
+//    receives V[key0 .. key0+3][d0 + i].
 //  * Softmax in base 2 with the scale folded into one FMA; the running max is
 //    only raised (and O rescaled) when a column's tile max exceeds it by more
 //    than 2^8, so most tiles skip the rescale; tiles that every query of the
@@ -63,10 +66,12 @@ struct AttnParams {
 };
 
 constexpr int kKeyTile = 64;
+constexpr int kQT = 128;               // query vectors per unit
 constexpr float kNegFloor = -1.0e30f;  // finite start of the running max
 constexpr float kRescaleSlack = 8.0f;  // log2 headroom before the max is raised
 constexpr int kMaxChunks = 8;          // key chunks per row (split plan bound)
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void global_cvoid;
@@ -75,12 +80,16 @@ __device__ inline bf16x4 lds_read_tr(const bf16 *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p));
 }
 
-// Swizzled chunk of key row r: physical 16-byte chunk = logical ^ f(r).
+// Swizzled 16-byte chunk of key row r: physical chunk = logical ^ f(r).
+// K (b128 reads of 16 consecutive rows at one chunk): rows sharing a 256-byte
+// line get distinct chunks.  V (transpose reads of 4 consecutive rows x 32
+// bytes): the 8 row-segments read per 32 lanes land in distinct 32-byte bank
+// groups.
 template <int HD> __device__ constexpr int swz_k(int r) {
   return (r / (128 / HD)) & (HD / 8 - 1);
 }
 template <int HD> __device__ constexpr int swz_v(int r) {
-  return 2 * ((r / (128 / HD)) & (HD / 16 - 1));
+  return 2 * (128 / HD) * ((r / (128 / HD)) & (4 / (128 / HD) - 1));
 }
 
 // Unit u -> (request r, tile, chunk); units of a request run from its last
@@ -106,12 +115,11 @@ __device__ inline bool locate_unit(const AttnParams &p, int u, int &r, int &tile
   return false;
 }
 
-template <int HD, int QB>
+template <int HD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_mfma_kernel(const AttnParams p) {
-  constexpr int NST = HD / 32;            // 32-wide contraction steps over head_dim
-  constexpr int NDT = HD / 16;            // 16-row output tiles over head_dim
-  constexpr int QT = 64 * QB;             // query vectors per unit
+  constexpr int NKS = HD / 16;            // 16-wide contraction steps of S over head_dim
+  constexpr int NDT = HD / 32;            // 32-dim output blocks
   constexpr int CPR = HD / 8;             // 16-byte chunks per key row
   constexpr int TILE = kKeyTile * HD;     // elements per tensor per stage
   constexpr int DPW = CPR / 4;            // 1 KiB DMA instructions per wave per tensor
@@ -119,7 +127,7 @@ void attn_mfma_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(1024))) bf16 vst[2][TILE];  // V stages
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 15, grp = lane >> 4;
+  const int col = lane & 31, half = lane >> 5;
   const int g = blockIdx.x % p.hkv;
   int r, tile, chunk, nchunks;
   if (!locate_unit(p, (int)(blockIdx.x / p.hkv), r, tile, chunk, nchunks)) return;
@@ -166,50 +174,45 @@ void attn_mfma_kernel(const AttnParams p) {
   issue(kst[0], kbase, dma_ko, k_begin);
   issue(vst[0], vbase, dma_vo, k_begin);
 
-  // Query columns of this lane: one per block of 16.  Padding columns (past
-  // the tile's last row) see every key; their results are dropped.
-  int p_q[QB];
-  bf16x8 qreg[QB][NST];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qv = wave * 16 * QB + qb * 16 + col;
-    const int row = qv / p.group, hh = qv - row * p.group;
-    const bool valid = row < ns;
-    const int s = s0 + (valid ? row : 0);
-    p_q[qb] = valid ? p.sel_global[s] : p_last;
-    const bf16 *qp = p.q_c + ((int64_t)p.sel_local[s] * p.hq + g * p.group + hh) * HD + 8 * grp;
-#pragma unroll
-    for (int st = 0; st < NST; ++st) qreg[qb][st] = *reinterpret_cast<const bf16x8 *>(qp + 32 * st);
-  }
-
-  f32x4 o[QB][NDT];
-  float m_run[QB], l_run[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = kNegFloor;
-    l_run[qb] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[qb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // LDS read offsets of this lane (elements within a stage buffer): the K
-  // fragment of contraction step st for key sub-tile t is at koff[st] + t*16*HD;
-  // the V^T fragment of head-dim tile dt is at voff[dt] (+16*HD for the second
-  // 4 keys, +32*HD for the second 32-key half).
-  int koff[NST], voff[NDT];
-#pragma unroll
-  for (int st = 0; st < NST; ++st) koff[st] = col * HD + (((4 * st + grp) ^ swz_k<HD>(col)) << 3);
+  // This lane's query column.  Padding columns (past the tile's last row)
+  // see every key; their results are dropped.
+  const int qv = wave * 32 + col;
+  const int qrow = qv / p.group, qhh = qv - qrow * p.group;
+  const bool qvalid = qrow < ns;
+  int p_q;
+  bf16x8 qreg[NKS];  // Q^T fragment of step s: dims 16s + 8*half .. +7
   {
-    const int r0 = 4 * grp + (col >> 2);
+    const int s = s0 + (qvalid ? qrow : 0);
+    p_q = qvalid ? p.sel_global[s] : p_last;
+    const bf16 *qp = p.q_c + ((int64_t)p.sel_local[s] * p.hq + g * p.group + qhh) * HD + 8 * half;
+#pragma unroll
+    for (int st = 0; st < NKS; ++st) qreg[st] = *reinterpret_cast<const bf16x8 *>(qp + 16 * st);
+  }
+
+  f32x16 o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
+  float m_run = kNegFloor, l_run = 0.f;
+
+  // LDS read offsets of this lane (elements within a stage buffer).
+  // K fragment of step st for key block sb: koff[st] + sb*32*HD.
+  // V^T fragment of dim block dt, 16-key step c, second 4 keys: voff[dt] +
+  // c*16*HD (+ 8*HD).
+  int koff[NKS], voff[NDT];
+#pragma unroll
+  for (int st = 0; st < NKS; ++st) koff[st] = col * HD + (((2 * st + half) ^ swz_k<HD>(col)) << 3);
+  {
+    const int q4 = (lane & 15) >> 2;
+    const int row = 4 * half + q4;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const int e = 16 * dt + 4 * (col & 3);
-      voff[dt] = r0 * HD + (((e >> 3) ^ swz_v<HD>(r0)) << 3) + (e & 7);
+      const int e = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      voff[dt] = row * HD + (((e >> 3) ^ swz_v<HD>(q4)) << 3) + (e & 7);
     }
   }
 
-  // Two LDS stages per tensor: while tile kt is multiplied, tile kt+1 is in
-  // flight.
   const int n_kt = (k_end - k_begin + kKeyTile - 1) / kKeyTile;
   for (int kt = 0; kt < n_kt; ++kt) {
     const int stage = kt & 1;
@@ -225,106 +228,97 @@ void attn_mfma_kernel(const AttnParams p) {
     const bf16 *ks = kst[stage];
     const bf16 *vs = vst[stage];
 
-    // S^T: sacc[qb][t][i] = score(key k0 + 16t + 4grp + i, query column qb).
-    f32x4 sacc[QB][4];
+    // S^T: sacc[sb][r] = score(key k0 + 32sb + 8(r/4) + 4*half + r%4, column).
+    f32x16 sacc[2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sacc[qb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int e = 0; e < 16; ++e) sacc[sb][e] = 0.f;
 #pragma unroll
-      for (int st = 0; st < NST; ++st) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(ks + koff[st] + t * 16 * HD);
+    for (int st = 0; st < NKS; ++st) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          sacc[qb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[qb][st], sacc[qb][t], 0, 0, 0);
+      for (int sb = 0; sb < 2; ++sb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(ks + koff[st] + sb * 32 * HD);
+        sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[st], sacc[sb], 0, 0, 0);
       }
     }
 
-    const bool need_mask = k0 + kKeyTile - 1 > p_first;
-    bf16x8 bp[QB][2];
+    if (k0 + kKeyTile - 1 > p_first) {  // causal mask (tiles past the first row)
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
-      if (need_mask) {
+      for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (k0 + 16 * t + 4 * grp + i > p_q[qb]) sacc[qb][t][i] = -INFINITY;
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[qb][t][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float mxs = mx * p.scale_log2;
-      const bool up = mxs > m_run[qb] + kRescaleSlack;
-      if (__any(up)) {
-        const float m_new = up ? mxs : m_run[qb];
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-        m_run[qb] = m_new;
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[qb][dt] *= alpha;
-      }
-      const float neg_m = -m_run[qb];
-      float psum = 0.f;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[qb][t][i], p.scale_log2, neg_m));
-          psum += pv;
-          bp[qb][t >> 1][4 * (t & 1) + i] = (bf16)pv;
-        }
-      l_run[qb] += psum;
+        for (int e = 0; e < 16; ++e)
+          if (k0 + 32 * sb + 8 * (e >> 2) + 4 * half + (e & 3) > p_q) sacc[sb][e] = -INFINITY;
     }
-
-    // O^T += V^T P^T over two 32-key halves; V^T comes from transpose reads.
+    float mx = -INFINITY;
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[sb][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float mxs = mx * p.scale_log2;
+    const bool up = mxs > m_run + kRescaleSlack;
+    if (__any(up)) {
+      const float m_new = up ? mxs : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+    }
+    const float neg_m = -m_run;
+    float psum = 0.f;
+    bf16x8 bp[4];  // probabilities of keys 16c .. 16c+15 of the tile
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[sb][e], p.scale_log2, neg_m));
+        psum += pv;
+        bp[2 * sb + (e >> 3)][e & 7] = (bf16)pv;
+      }
+    l_run += psum;
+
+    // O^T += V^T P^T: per 16-key step c, one transposed V fragment per dim block.
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const bf16 *vp = vs + voff[dt] + kh * 32 * HD;
+        const bf16 *vp = vs + voff[dt] + c * 16 * HD;
         const bf16x4 lo4 = lds_read_tr(vp);
-        const bf16x4 hi4 = lds_read_tr(vp + 16 * HD);
+        const bf16x4 hi4 = lds_read_tr(vp + 8 * HD);
         const bf16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          o[qb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bp[qb][kh], o[qb][dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bp[c], o[dt], 0, 0, 0);
       }
     }
   }
 
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    float l = l_run[qb];
-    l += __shfl_xor(l, 16, kWave);
-    l += __shfl_xor(l, 32, kWave);
-    const int qv = wave * 16 * QB + qb * 16 + col;
-    if (nchunks == 1) {
-      const int row = qv / p.group, hh = qv - row * p.group;
-      if (row < ns) {
-        const float inv = 1.f / l;
-        bf16 *op = p.out + ((int64_t)(s0 + row) * p.hq + g * p.group + hh) * HD;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          bf16x4 w;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) w[i] = (bf16)(o[qb][dt][i] * inv);
-          *reinterpret_cast<bf16x4 *>(op + 16 * dt + 4 * grp) = w;
-        }
-      }
-    } else {
-      float *w = p.ws + (int64_t)blockIdx.x * (QT * HD + 2 * QT);
+  float l = l_run + __shfl_xor(l_run, 32, kWave);
+  if (nchunks == 1) {
+    if (qvalid) {
+      const float inv = 1.f / l;
+      bf16 *op = p.out + ((int64_t)(s0 + qrow) * p.hq + g * p.group + qhh) * HD + 4 * half;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
-        *reinterpret_cast<f32x4 *>(w + qv * HD + 16 * dt + 4 * grp) = o[qb][dt];
-      if (grp == 0) {
-        w[QT * HD + qv] = m_run[qb];
-        w[QT * HD + QT + qv] = l;
-      }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          bf16x4 w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w[i] = (bf16)(o[dt][4 * q + i] * inv);
+          *reinterpret_cast<bf16x4 *>(op + 32 * dt + 8 * q) = w;
+        }
+    }
+  } else {
+    float *w = p.ws + (int64_t)blockIdx.x * (kQT * HD + 2 * kQT);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4 *>(w + qv * HD + 32 * dt + 8 * q + 4 * half) =
+            f32x4{o[dt][4 * q], o[dt][4 * q + 1], o[dt][4 * q + 2], o[dt][4 * q + 3]};
+    if (half == 0) {
+      w[kQT * HD + qv] = m_run;
+      w[kQT * HD + kQT + qv] = l;
     }
   }
 }
@@ -333,9 +327,9 @@ void attn_mfma_kernel(const AttnParams p) {
 // it loads the running max, running sum and partial O of every chunk at once
 // (unrolled over the chunk bound, inactive chunks clamped to chunk 0 and
 // weighted 0), so each thread waits for a single round of loads.
-template <int HD, int QB>
+template <int HD>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
-  constexpr int QT = 64 * QB;
+  constexpr int QT = kQT;
   constexpr int UNIT = QT * HD + 2 * QT;
   constexpr int D4 = HD / 4;              // float4 groups per query vector
   constexpr int QPB = 256 / D4;           // query vectors per workgroup
@@ -396,25 +390,22 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
                               4 * d4) = o;
 }
 
-int attn_mfma_rows_per_tile(int dtype, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
-                            int qb) {
+int attn_mfma_rows_per_tile(int dtype, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim) {
   if (dtype != kBF16) return 0;
   if (head_dim != 32 && head_dim != 64 && head_dim != 128) return 0;
   const int group = n_q_heads / n_kv_heads;
-  const int qt = 64 * qb;
-  if (group < 1 || group > qt || qt % group != 0) return 0;
-  return qt / group;
+  if (group < 1 || group > kQT || kQT % group != 0) return 0;
+  return kQT / group;
 }
 
-size_t attn_unit_bytes(int32_t head_dim, int qb) {
-  const size_t qt = 64 * (size_t)qb;
-  return (qt * head_dim + 2 * qt) * sizeof(float);
+size_t attn_unit_bytes(int32_t head_dim) {
+  return ((size_t)kQT * head_dim + 2 * kQT) * sizeof(float);
 }
 
 int attn_max_chunks() { return kMaxChunks; }
 
-template <int QB>
-static hipError_t launch_mfma_qb(const AttnArgs &a, const AttnPlan &plan, hipStream_t stream) {
+hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &plan, hipStream_t stream) {
+  if (plan.units == 0) return hipSuccess;
   AttnParams p;
   p.out = (bf16 *)a.out;
   p.q_c = (const bf16 *)a.q_c;
@@ -434,25 +425,20 @@ static hipError_t launch_mfma_qb(const AttnArgs &a, const AttnPlan &plan, hipStr
   p.scale_log2 = a.softmax_scale * 1.4426950408889634f;
   const dim3 grid((unsigned)(plan.units * a.n_kv_heads)), block(256);
   switch (a.head_dim) {
-    case 32: hipLaunchKernelGGL((attn_mfma_kernel<32, QB>), grid, block, 0, stream, p); break;
-    case 64: hipLaunchKernelGGL((attn_mfma_kernel<64, QB>), grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL((attn_mfma_kernel<128, QB>), grid, block, 0, stream, p); break;
+    case 32: hipLaunchKernelGGL(attn_mfma_kernel<32>, grid, block, 0, stream, p); break;
+    case 64: hipLaunchKernelGGL(attn_mfma_kernel<64>, grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL(attn_mfma_kernel<128>, grid, block, 0, stream, p); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !plan.split) return e;
-  const int groups = 64 * QB / (256 / (a.head_dim / 4));
+  const int groups = kQT / (256 / (a.head_dim / 4));
   const dim3 cgrid((unsigned)(plan.tiles * a.n_kv_heads * groups));
   switch (a.head_dim) {
-    case 32: hipLaunchKernelGGL((attn_combine_kernel<32, QB>), cgrid, block, 0, stream, p); break;
-    case 64: hipLaunchKernelGGL((attn_combine_kernel<64, QB>), cgrid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL((attn_combine_kernel<128, QB>), cgrid, block, 0, stream, p); break;
+    case 32: hipLaunchKernelGGL(attn_combine_kernel<32>, cgrid, block, 0, stream, p); break;
+    case 64: hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, block, 0, stream, p); break;
   }
   return hipGetLastError();
-}
-
-hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &plan, hipStream_t stream) {
-  if (plan.units == 0) return hipSuccess;
-  return plan.qb == 1 ? launch_mfma_qb<1>(a, plan, stream) : launch_mfma_qb<2>(a, plan, stream);
 }
 
 // ---------------------------------------------------------------------------

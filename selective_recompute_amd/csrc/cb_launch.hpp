@@ -21,13 +21,23 @@ hipError_t launch_rerotate(int dtype, int style, void *k_out, const void *k_in,
                            int32_t n_kv_heads, int32_t head_dim,
                            const RopeTable &tab, hipStream_t stream);
 
+// Re-rotation (in place, one layer) and deviation fused in one launch; only
+// for geometries where a re-rotation row fits a 256-thread workgroup.
+bool rerotate_deviation_fits(int dtype, int32_t n_kv_heads, int32_t head_dim);
+hipError_t launch_rerotate_deviation(int dtype, int style, void *k, const int32_t *delta,
+                                     int64_t n_tok, int32_t n_kv_heads, int32_t head_dim,
+                                     const RopeTable &tab, const void *v_new_c,
+                                     const void *v_old, const int32_t *cand_idx, float *dev,
+                                     int64_t m, hipStream_t stream);
+
 hipError_t launch_deviation(int dtype, const void *v_new_c, const void *v_old,
                             const int32_t *cand_idx, float *dev, int64_t m,
                             int32_t row_elems, hipStream_t stream);
 
+// max_m: the largest candidate count of any request (host mirror).
 hipError_t launch_topk(int32_t n_req, const float *dev, const int32_t *cand_idx,
                        const int32_t *cand_off, const int32_t *sel_off,
-                       int32_t *sel_local, int32_t *sel_global,
+                       int32_t *sel_local, int32_t *sel_global, int32_t max_m,
                        hipStream_t stream);
 
 hipError_t launch_fuse(void *k_fused, void *v_fused, const void *k_new_c,
@@ -56,8 +66,7 @@ struct AttnArgs {
 
 // Host-side decomposition of the MFMA attention launch.
 struct AttnPlan {
-  int qb;              // blocks of 16 query vectors per wave (1 or 2)
-  int rows_per_tile;   // selected rows per query tile
+  int rows_per_tile;   // selected rows per query tile (128 query vectors)
   int key_chunk;       // keys per unit (multiple of 64); huge = no split
   bool split;          // some request has more than one chunk
   int64_t tiles;       // query tiles over all requests
@@ -65,12 +74,12 @@ struct AttnPlan {
   size_t ws_bytes;     // workspace the split needs
 };
 
-// Selected rows per MFMA query tile (64*qb query vectors), or 0 if the MFMA
+// Selected rows per MFMA query tile (128 query vectors), or 0 if the MFMA
 // kernel does not cover this geometry.
 int attn_mfma_rows_per_tile(int dtype, int32_t n_q_heads, int32_t n_kv_heads,
-                            int32_t head_dim, int qb);
+                            int32_t head_dim);
 // Workspace bytes of one split unit.
-size_t attn_unit_bytes(int32_t head_dim, int qb);
+size_t attn_unit_bytes(int32_t head_dim);
 // Most key chunks one row may be split into.
 int attn_max_chunks();
 

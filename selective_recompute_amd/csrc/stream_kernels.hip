@@ -19,23 +19,28 @@ namespace cb {
 // bf16, 4 for fp32 so that each half is one 16-byte access).  Its pairs are
 // fixed for the whole kernel, so the cos/sin of its VP angles are computed
 // only when delta changes between the tokens it visits (a token's delta is
-// the start of its chunk, so that happens once per chunk) and are reused
-// across all layers.  Angles are reduced in double precision to a fraction
-// of a turn before the fp32 sincos, so |delta| up to 2^31 keeps ~1e-7 rad.
+// the start of its chunk) and are reused across all layers.  The angle is
+// reduced in double precision to a fraction of a turn in [-1/2, 1/2]; the
+// gfx950 v_sin_f32 / v_cos_f32 instructions take their argument in turns.
 // ---------------------------------------------------------------------------
+struct RotGeom {
+  int64_t n_tok;
+  int32_t n_layers, head_dim, units_per_head, units_per_row, tok_per_iter, tok_per_block;
+};
+
 template <typename T, int STYLE>
-__global__ __launch_bounds__(1024) void rerotate_kernel(
-    T *__restrict__ k_out, const T *__restrict__ k_in,
-    const int32_t *__restrict__ delta, int64_t n_tok, int32_t n_layers,
-    int32_t head_dim, int32_t units_per_head, int32_t units_per_row,
-    int32_t tok_per_iter, int32_t tok_per_block, RopeTable tab) {
+__device__ inline void rerotate_block(T *__restrict__ k_out, const T *__restrict__ k_in,
+                                      const int32_t *__restrict__ delta, const RotGeom &gm,
+                                      const RopeTable &tab, int block) {
   constexpr int VP = Vec16<T>::N;  // pairs per unit
   const int tid = threadIdx.x;
-  const int unit = tid % units_per_row;
-  const int slot = tid / units_per_row;
-  const int head = unit / units_per_head;
-  const int j0 = (unit % units_per_head) * VP;
-  const int64_t row_elems = (int64_t)(units_per_row / units_per_head) * head_dim;
+  if (tid >= gm.units_per_row * gm.tok_per_iter) return;
+  const int unit = tid % gm.units_per_row;
+  const int slot = tid / gm.units_per_row;
+  const int head = unit / gm.units_per_head;
+  const int j0 = (unit % gm.units_per_head) * VP;
+  const int hd = gm.head_dim;
+  const int64_t row_elems = (int64_t)(gm.units_per_row / gm.units_per_head) * hd;
   const bool in_place = (k_out == k_in);
 
   double rev[VP];
@@ -44,9 +49,9 @@ __global__ __launch_bounds__(1024) void rerotate_kernel(
   float cs[VP], sn[VP];
   int cur = INT_MIN;
 
-  const int64_t t_begin = (int64_t)blockIdx.x * tok_per_block;
-  const int64_t t_end = t_begin + tok_per_block < n_tok ? t_begin + tok_per_block : n_tok;
-  for (int64_t t = t_begin + slot; t < t_end; t += tok_per_iter) {
+  const int64_t t_begin = (int64_t)block * gm.tok_per_block;
+  const int64_t t_end = t_begin + gm.tok_per_block < gm.n_tok ? t_begin + gm.tok_per_block : gm.n_tok;
+  for (int64_t t = t_begin + slot; t < t_end; t += gm.tok_per_iter) {
     const int d = delta[t];
     if (d == 0 && in_place) continue;  // R_0 = I
     if (d != cur && d != 0) {
@@ -54,19 +59,19 @@ __global__ __launch_bounds__(1024) void rerotate_kernel(
 #pragma unroll
       for (int i = 0; i < VP; ++i) {
         const double turns = (double)d * rev[i];
-        const double frac = turns - rint(turns);            // in [-1/2, 1/2]
-        const float ang = (float)(frac * 6.283185307179586476925);
-        sincosf(ang, &sn[i], &cs[i]);
+        const float frac = (float)(turns - rint(turns));  // in [-1/2, 1/2]
+        sn[i] = __builtin_amdgcn_sinf(frac);
+        cs[i] = __builtin_amdgcn_cosf(frac);
       }
     }
-    for (int l = 0; l < n_layers; ++l) {
-      const int64_t off = ((int64_t)l * n_tok + t) * row_elems + (int64_t)head * head_dim;
+    for (int l = 0; l < gm.n_layers; ++l) {
+      const int64_t off = ((int64_t)l * gm.n_tok + t) * row_elems + (int64_t)head * hd;
       const T *src = k_in + off;
       T *dst = k_out + off;
       float a[VP], b[VP];
       if (STYLE == 0) {  // pairs (j, j + D/2)
         Vec16<T>::load(src + j0, a);
-        Vec16<T>::load(src + head_dim / 2 + j0, b);
+        Vec16<T>::load(src + hd / 2 + j0, b);
       } else {           // pairs (2j, 2j + 1)
         float x0[VP], x1[VP];
         Vec16<T>::load(src + 2 * j0, x0);
@@ -87,7 +92,7 @@ __global__ __launch_bounds__(1024) void rerotate_kernel(
       }
       if (STYLE == 0) {
         Vec16<T>::store(dst + j0, a);
-        Vec16<T>::store(dst + head_dim / 2 + j0, b);
+        Vec16<T>::store(dst + hd / 2 + j0, b);
       } else {
         float x0[VP], x1[VP];
 #pragma unroll
@@ -102,26 +107,45 @@ __global__ __launch_bounds__(1024) void rerotate_kernel(
   }
 }
 
+template <typename T>
+static RotGeom rot_geom(int64_t n_tok, int32_t n_layers, int32_t n_kv_heads, int32_t head_dim,
+                        int64_t &blocks) {
+  constexpr int VP = Vec16<T>::N;
+  RotGeom gm;
+  gm.n_tok = n_tok;
+  gm.n_layers = n_layers;
+  gm.head_dim = head_dim;
+  gm.units_per_head = (head_dim / 2) / VP;
+  gm.units_per_row = gm.units_per_head * n_kv_heads;
+  gm.tok_per_iter = gm.units_per_row >= 256 ? 1 : 256 / gm.units_per_row;
+  // Enough blocks to fill the chip; each block then walks a short contiguous
+  // token range so the cached trig is reused within a chunk.
+  int64_t iters = (n_tok + (int64_t)gm.tok_per_iter * 2048 - 1) / ((int64_t)gm.tok_per_iter * 2048);
+  if (iters < 1) iters = 1;
+  if (iters > 16) iters = 16;
+  gm.tok_per_block = (int)(gm.tok_per_iter * iters);
+  blocks = (n_tok + gm.tok_per_block - 1) / gm.tok_per_block;
+  return gm;
+}
+
+template <typename T, int STYLE>
+__global__ __launch_bounds__(1024) void rerotate_kernel(T *__restrict__ k_out,
+                                                        const T *__restrict__ k_in,
+                                                        const int32_t *__restrict__ delta,
+                                                        RotGeom gm, RopeTable tab) {
+  rerotate_block<T, STYLE>(k_out, k_in, delta, gm, tab, blockIdx.x);
+}
+
 template <typename T, int STYLE>
 static hipError_t rerotate_typed(void *k_out, const void *k_in, const int32_t *delta,
                                  int64_t n_tok, int32_t n_layers, int32_t n_kv_heads,
                                  int32_t head_dim, const RopeTable &tab, hipStream_t stream) {
-  constexpr int VP = Vec16<T>::N;
-  const int units_per_head = (head_dim / 2) / VP;
-  const int units_per_row = units_per_head * n_kv_heads;
-  const int tok_per_iter = units_per_row >= 256 ? 1 : 256 / units_per_row;
-  const int threads = units_per_row * tok_per_iter;
-  // Enough blocks to fill the chip; each block then walks a short contiguous
-  // token range so the cached trig is reused within a chunk.
-  int64_t iters = (n_tok + (int64_t)tok_per_iter * 2048 - 1) / ((int64_t)tok_per_iter * 2048);
-  if (iters < 1) iters = 1;
-  if (iters > 16) iters = 16;
-  const int tok_per_block = (int)(tok_per_iter * iters);
-  const int64_t blocks = (n_tok + tok_per_block - 1) / tok_per_block;
+  int64_t blocks;
+  const RotGeom gm = rot_geom<T>(n_tok, n_layers, n_kv_heads, head_dim, blocks);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((rerotate_kernel<T, STYLE>), dim3((unsigned)blocks), dim3(threads), 0, stream,
-                     (T *)k_out, (const T *)k_in, delta, n_tok, n_layers, head_dim,
-                     units_per_head, units_per_row, tok_per_iter, tok_per_block, tab);
+  hipLaunchKernelGGL((rerotate_kernel<T, STYLE>), dim3((unsigned)blocks),
+                     dim3(gm.units_per_row * gm.tok_per_iter), 0, stream, (T *)k_out,
+                     (const T *)k_in, delta, gm, tab);
   return hipGetLastError();
 }
 
@@ -142,14 +166,14 @@ hipError_t launch_rerotate(int dtype, int style, void *k_out, const void *k_in,
 // fp32 fused multiply-add accumulation, butterfly reduction across the wave.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void deviation_kernel(
-    const T *__restrict__ v_new_c, const T *__restrict__ v_old,
-    const int32_t *__restrict__ cand_idx, float *__restrict__ dev, int64_t m,
-    int32_t row_elems) {
+__device__ inline void deviation_block(const T *__restrict__ v_new_c, const T *__restrict__ v_old,
+                                       const int32_t *__restrict__ cand_idx,
+                                       float *__restrict__ dev, int64_t m, int32_t row_elems,
+                                       int64_t block, int64_t n_blocks) {
   constexpr int V = Vec16<T>::N;
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
-  const int64_t n_waves = ((int64_t)gridDim.x * blockDim.x) / kWave;
+  const int64_t wave = (block * blockDim.x + threadIdx.x) / kWave;
+  const int64_t n_waves = (n_blocks * blockDim.x) / kWave;
   const int nvec = row_elems / V;
   for (int64_t j = wave; j < m; j += n_waves) {
     const T *a = v_new_c + j * row_elems;
@@ -170,12 +194,24 @@ __global__ __launch_bounds__(256) void deviation_kernel(
   }
 }
 
+template <typename T>
+__global__ __launch_bounds__(256) void deviation_kernel(
+    const T *__restrict__ v_new_c, const T *__restrict__ v_old,
+    const int32_t *__restrict__ cand_idx, float *__restrict__ dev, int64_t m,
+    int32_t row_elems) {
+  deviation_block<T>(v_new_c, v_old, cand_idx, dev, m, row_elems, blockIdx.x, gridDim.x);
+}
+
+static int64_t deviation_blocks(int64_t m) {
+  int64_t blocks = (m + 3) / 4;  // 4 waves per block, one row per wave
+  return blocks > 8192 ? 8192 : blocks;
+}
+
 hipError_t launch_deviation(int dtype, const void *v_new_c, const void *v_old,
                             const int32_t *cand_idx, float *dev, int64_t m,
                             int32_t row_elems, hipStream_t stream) {
   if (m == 0) return hipSuccess;
-  int64_t blocks = (m + 3) / 4;  // 4 waves per block, one row per wave
-  if (blocks > 8192) blocks = 8192;
+  const int64_t blocks = deviation_blocks(m);
   if (dtype == kBF16)
     hipLaunchKernelGGL(deviation_kernel<bf16>, dim3((unsigned)blocks), dim3(256), 0, stream,
                        (const bf16 *)v_new_c, (const bf16 *)v_old, cand_idx, dev, m, row_elems);
@@ -186,13 +222,70 @@ hipError_t launch_deviation(int dtype, const void *v_new_c, const void *v_old,
 }
 
 // ---------------------------------------------------------------------------
+// Re-rotation of K and deviation of V in one launch: the two are independent
+// (they touch different tensors), and at small sizes neither fills the chip
+// alone.  Blocks [0, rot_blocks) re-rotate, the rest score candidates.
+// ---------------------------------------------------------------------------
+template <typename T, int STYLE>
+__global__ __launch_bounds__(256) void rerotate_deviation_kernel(
+    T *__restrict__ k, const int32_t *__restrict__ delta, RotGeom gm, RopeTable tab,
+    int64_t rot_blocks, const T *__restrict__ v_new_c, const T *__restrict__ v_old,
+    const int32_t *__restrict__ cand_idx, float *__restrict__ dev, int64_t m, int32_t row_elems) {
+  if ((int64_t)blockIdx.x < rot_blocks)
+    rerotate_block<T, STYLE>(k, k, delta, gm, tab, blockIdx.x);
+  else
+    deviation_block<T>(v_new_c, v_old, cand_idx, dev, m, row_elems, blockIdx.x - rot_blocks,
+                       gridDim.x - rot_blocks);
+}
+
+template <typename T, int STYLE>
+static hipError_t rerotate_deviation_typed(void *k, const int32_t *delta, int64_t n_tok,
+                                           int32_t n_kv_heads, int32_t head_dim,
+                                           const RopeTable &tab, const void *v_new_c,
+                                           const void *v_old, const int32_t *cand_idx,
+                                           float *dev, int64_t m, hipStream_t stream) {
+  int64_t rot_blocks;
+  const RotGeom gm = rot_geom<T>(n_tok, 1, n_kv_heads, head_dim, rot_blocks);
+  const int64_t dev_blocks = m > 0 ? deviation_blocks(m) : 0;
+  if (rot_blocks + dev_blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((rerotate_deviation_kernel<T, STYLE>), dim3((unsigned)(rot_blocks + dev_blocks)),
+                     dim3(256), 0, stream, (T *)k, delta, gm, tab, rot_blocks,
+                     (const T *)v_new_c, (const T *)v_old, cand_idx, dev, m,
+                     (int32_t)(n_kv_heads * head_dim));
+  return hipGetLastError();
+}
+
+bool rerotate_deviation_fits(int dtype, int32_t n_kv_heads, int32_t head_dim) {
+  const int vp = dtype == kBF16 ? 8 : 4;
+  return (head_dim / 2) / vp * n_kv_heads <= 256;  // one re-rotation row per 256 threads
+}
+
+hipError_t launch_rerotate_deviation(int dtype, int style, void *k, const int32_t *delta,
+                                     int64_t n_tok, int32_t n_kv_heads, int32_t head_dim,
+                                     const RopeTable &tab, const void *v_new_c,
+                                     const void *v_old, const int32_t *cand_idx, float *dev,
+                                     int64_t m, hipStream_t stream) {
+#define CB_RD(T, S) \
+  rerotate_deviation_typed<T, S>(k, delta, n_tok, n_kv_heads, head_dim, tab, v_new_c, v_old, cand_idx, dev, m, stream)
+  if (dtype == kBF16) return style == 0 ? CB_RD(bf16, 0) : CB_RD(bf16, 1);
+  return style == 0 ? CB_RD(float, 0) : CB_RD(float, 1);
+#undef CB_RD
+}
+
+// ---------------------------------------------------------------------------
 // Top-k, [Derivations, "近似解"] (greedy TopK of the deviation) with ties to
-// the lower index and NaN above +inf.  One 1024-thread workgroup per request:
+// the lower index and NaN above +inf.  One 1024-thread workgroup per request;
+// thread t owns the contiguous candidate segment [t*seg, (t+1)*seg), held in
+// registers when seg <= KPT (KPT = 0: re-read from memory every pass).
 //   1. MSB-first radix select over the order-preserving uint32 key of each
-//      fp32 score (4 passes of 8 bits, LDS histogram) finds the exact key tau
-//      of the k-th largest score and how many keys equal to tau to keep;
-//   2. an ordered compaction emits, in candidate order (= ascending packed
-//      row), every key > tau and the first `keep_eq` keys == tau.
+//      fp32 score, 8 bits per pass with an LDS histogram.  Histogram updates
+//      are aggregated per wave (one atomic per distinct bin and wave), since
+//      most scores share their leading bits.  The select stops at the first
+//      pass whose boundary bin holds exactly the keys still missing: then the
+//      whole bin is selected.
+//   2. An ordered compaction emits, in candidate order (= ascending packed
+//      row), every key above the boundary bin and the first `keep_eq` keys
+//      inside it (ties to the lower index).
 // ---------------------------------------------------------------------------
 __device__ inline uint32_t order_key(float x) {
   uint32_t u = __float_as_uint(x);
@@ -217,12 +310,25 @@ __device__ inline void block_excl_scan2(uint32_t a, uint32_t b, uint32_t &a_excl
   b_excl = b_before + bi - b;
 }
 
+// hist[bin] += 1 for every lane with bin >= 0, one atomic per distinct bin.
+__device__ inline void wave_hist_add(uint32_t *hist, int bin) {
+  uint64_t pending = __ballot(bin >= 0);
+  while (pending) {
+    const int leader = __builtin_ctzll(pending);
+    const int lb = __builtin_amdgcn_readlane(bin, leader);
+    const uint64_t same = __ballot(bin == lb);
+    if ((int)(threadIdx.x & (kWave - 1)) == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(same));
+    pending &= ~same;
+  }
+}
+
+template <int KPT>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     const float *__restrict__ dev, const int32_t *__restrict__ cand_idx,
     const int32_t *__restrict__ cand_off, const int32_t *__restrict__ sel_off,
     int32_t *__restrict__ sel_local, int32_t *__restrict__ sel_global) {
   __shared__ uint32_t hist[256];
-  __shared__ uint32_t sh_digit, sh_above;
+  __shared__ uint32_t sh_digit, sh_above, sh_count;
   __shared__ uint32_t wave_tot[2][kTopkWaves];
 
   const int r = blockIdx.x;
@@ -239,15 +345,34 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     }
     return;
   }
+  const int seg = (m + kTopkThreads - 1) / kTopkThreads;
+  const int jb = tid * seg < m ? tid * seg : m;
+  const int n_my = (jb + seg < m ? jb + seg : m) - jb;
+  uint32_t keys[KPT > 0 ? KPT : 1];
+  if (KPT > 0) {
+#pragma unroll
+    for (int i = 0; i < (KPT > 0 ? KPT : 1); ++i)
+      keys[i] = i < n_my ? order_key(dev[c0 + jb + i]) : 0u;
+  }
+  auto key_at = [&](int i) -> uint32_t {
+    if (KPT > 0) return keys[i];
+    return order_key(dev[c0 + jb + i]);
+  };
+  const int iters = KPT > 0 ? KPT : seg;  // uniform over the workgroup
 
   uint32_t prefix = 0, mask = 0, krem = (uint32_t)k;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0;
+    if (tid < 256) hist[tid] = 0;
     __syncthreads();
-    for (int j = tid; j < m; j += kTopkThreads) {
-      const uint32_t key = order_key(dev[c0 + j]);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+#pragma unroll
+    for (int i = 0; i < iters; ++i) {
+      int bin = -1;
+      if (i < n_my) {
+        const uint32_t key = key_at(i);
+        if ((key & mask) == prefix) bin = (int)((key >> shift) & 255u);
+      }
+      wave_hist_add(hist, bin);
     }
     __syncthreads();
     if (tid < kWave) {
@@ -264,7 +389,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
       uint32_t above = suf - tot;
       if (above < krem && suf >= krem) {
         for (int q = 3; q >= 0; --q) {
-          if (above + h[q] >= krem) { sh_digit = 4 * tid + q; sh_above = above; break; }
+          if (above + h[q] >= krem) { sh_digit = 4 * tid + q; sh_above = above; sh_count = h[q]; break; }
           above += h[q];
         }
       }
@@ -273,43 +398,55 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     prefix |= sh_digit << shift;
     mask |= 255u << shift;
     krem -= sh_above;
-    __syncthreads();
+    const uint32_t cnt = sh_count;
+    __syncthreads();  // every thread has read sh_* before the next pass
+    if (cnt == krem) break;  // the whole boundary bin is selected
   }
-  const uint32_t tau = prefix;   // key of the k-th largest score
-  const uint32_t keep_eq = krem; // how many keys equal to tau are selected
+  const uint32_t keep_eq = krem;  // keys of the boundary bin to keep, lowest index first
 
-  // Ordered compaction over contiguous per-thread segments.
-  const int seg = (m + kTopkThreads - 1) / kTopkThreads;
-  const int jb = tid * seg < m ? tid * seg : m;
-  const int je = jb + seg < m ? jb + seg : m;
   uint32_t n_gt = 0, n_eq = 0;
-  for (int j = jb; j < je; ++j) {
-    const uint32_t key = order_key(dev[c0 + j]);
-    n_gt += key > tau;
-    n_eq += key == tau;
+#pragma unroll
+  for (int i = 0; i < iters; ++i) {
+    if (i < n_my) {
+      const uint32_t km = key_at(i) & mask;
+      n_gt += km > prefix;
+      n_eq += km == prefix;
+    }
   }
   uint32_t gt_before, eq_before;
   block_excl_scan2(n_gt, n_eq, gt_before, eq_before, wave_tot);
-  for (int j = jb; j < je; ++j) {
-    const uint32_t key = order_key(dev[c0 + j]);
-    const bool gt = key > tau, eq = key == tau;
-    const bool take = gt || (eq && eq_before < keep_eq);
-    if (take) {
-      const uint32_t pos = gt_before + (eq_before < keep_eq ? eq_before : keep_eq);
-      sel_local[s0 + pos] = c0 + j;
-      sel_global[s0 + pos] = cand_idx[c0 + j];
+#pragma unroll
+  for (int i = 0; i < iters; ++i) {
+    if (i < n_my) {
+      const uint32_t km = key_at(i) & mask;
+      const bool gt = km > prefix, eq = km == prefix;
+      if (gt || (eq && eq_before < keep_eq)) {
+        const uint32_t pos = gt_before + (eq_before < keep_eq ? eq_before : keep_eq);
+        sel_local[s0 + pos] = c0 + jb + i;
+        sel_global[s0 + pos] = cand_idx[c0 + jb + i];
+      }
+      gt_before += gt;
+      eq_before += eq;
     }
-    gt_before += gt;
-    eq_before += eq;
   }
 }
 
 hipError_t launch_topk(int32_t n_req, const float *dev, const int32_t *cand_idx,
                        const int32_t *cand_off, const int32_t *sel_off, int32_t *sel_local,
-                       int32_t *sel_global, hipStream_t stream) {
+                       int32_t *sel_global, int32_t max_m, hipStream_t stream) {
   if (n_req == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3(n_req), dim3(kTopkThreads), 0, stream, dev, cand_idx,
-                     cand_off, sel_off, sel_local, sel_global);
+  const int seg = (max_m + kTopkThreads - 1) / kTopkThreads;
+#define CB_TOPK(K)                                                                            \
+  hipLaunchKernelGGL(topk_kernel<K>, dim3(n_req), dim3(kTopkThreads), 0, stream, dev, cand_idx, \
+                     cand_off, sel_off, sel_local, sel_global)
+  if (seg <= 1) CB_TOPK(1);
+  else if (seg <= 2) CB_TOPK(2);
+  else if (seg <= 4) CB_TOPK(4);
+  else if (seg <= 8) CB_TOPK(8);
+  else if (seg <= 16) CB_TOPK(16);
+  else if (seg <= 32) CB_TOPK(32);
+  else CB_TOPK(0);
+#undef CB_TOPK
   return hipGetLastError();
 }
 

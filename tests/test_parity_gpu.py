@@ -332,3 +332,22 @@ def test_blend_is_deterministic():
                      o["out"].cpu()))
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("m,k", [(30000, 4567), (40000, 9999), (40000, 1), (1024, 1023)])
+def test_topk_register_and_memory_paths(m, k):
+    """Up to 32 keys per thread stay in registers; larger requests re-read
+    their scores every radix pass.  Both paths, with many exact ties."""
+    say(f"topk m={m} k={k}")
+    rng = np.random.default_rng(m + k)
+    dev = rng.integers(0, 50, size=m).astype(np.float32) * np.float32(0.125)
+    cand = np.sort(rng.choice(4 * m, size=m, replace=False)).astype(np.int32)
+    off = PL.offsets([m])
+    rb = B.RaggedBatch(off, off, PL.offsets([k]), DEV)
+    sl = torch.empty(k, dtype=torch.int32, device=DEV)
+    sg = torch.empty(k, dtype=torch.int32, device=DEV)
+    B.topk(rb, torch.from_numpy(dev).to(DEV), torch.from_numpy(cand).to(DEV), sl, sg)
+    torch.cuda.synchronize()
+    loc, glob = O.topk_select(dev.astype(np.float64), cand, k)
+    assert np.array_equal(npi(sg), glob)
+    assert np.array_equal(npi(sl), loc)
