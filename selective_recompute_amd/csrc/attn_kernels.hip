@@ -72,6 +72,7 @@ constexpr float kRescaleSlack = 8.0f;  // log2 headroom before the max is raised
 constexpr int kMaxChunks = 8;          // key chunks per row (split plan bound)
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void global_cvoid;
@@ -81,15 +82,21 @@ __device__ inline bf16x4 lds_read_tr(const bf16 *p) {
 }
 
 // Swizzled 16-byte chunk of key row r: physical chunk = logical ^ f(r).
-// K (b128 reads of 16 consecutive rows at one chunk): rows sharing a 256-byte
-// line get distinct chunks.  V (transpose reads of 4 consecutive rows x 32
-// bytes): the 8 row-segments read per 32 lanes land in distinct 32-byte bank
-// groups.
+// Chosen so that both read patterns below hit every bank once whether LDS
+// serves 128 B per cycle (b128 reads in groups of 8 lanes, b64 in groups of
+// 16) or 256 B (groups of 16 and 32).
+//  K: b128 reads of 32 consecutive rows (lane l: row l%32) at one logical chunk.
+//  V: transpose reads; lane l reads 8 bytes of row 4(l/32) + (l%16)/4 at
+//     logical chunk 4*dt + 2*((l/16)%2) + (l%4)/2.
 template <int HD> __device__ constexpr int swz_k(int r) {
-  return (r / (128 / HD)) & (HD / 8 - 1);
+  if constexpr (HD == 128) return r & 15;
+  else if constexpr (HD == 64) return ((r >> 1) & 7) ^ (4 * (r & 1));
+  else return ((r >> 2) & 3) ^ (2 * ((r >> 1) & 1));
 }
 template <int HD> __device__ constexpr int swz_v(int r) {
-  return 2 * (128 / HD) * ((r / (128 / HD)) & (4 / (128 / HD) - 1));
+  if constexpr (HD == 128) return 10 * (r & 1) + 4 * ((r >> 1) & 1);
+  else if constexpr (HD == 64) return 2 * (r & 3);
+  else return 2 * ((r >> 1) & 1);
 }
 
 // Unit u -> (request r, tile, chunk); units of a request run from its last
@@ -209,7 +216,7 @@ void attn_mfma_kernel(const AttnParams p) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       const int e = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-      voff[dt] = row * HD + (((e >> 3) ^ swz_v<HD>(q4)) << 3) + (e & 7);
+      voff[dt] = row * HD + (((e >> 3) ^ swz_v<HD>(row)) << 3) + (e & 7);
     }
   }
 
@@ -267,17 +274,26 @@ void attn_mfma_kernel(const AttnParams p) {
       for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
     }
     const float neg_m = -m_run;
-    float psum = 0.f;
     bf16x8 bp[4];  // probabilities of keys 16c .. 16c+15 of the tile
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[sb][e], p.scale_log2, neg_m));
-        psum += pv;
-        bp[2 * sb + (e >> 3)][e & 7] = (bf16)pv;
-      }
-    l_run += psum;
+      for (int e = 0; e < 16; ++e)
+        bp[2 * sb + (e >> 3)][e & 7] =
+            (bf16)__builtin_amdgcn_exp2f(fmaf(sacc[sb][e], p.scale_log2, neg_m));
+    // The running sum adds the probabilities as they enter the PV product
+    // (bf16), two per v_dot2c_f32_bf16, in two independent chains.
+    {
+      const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
+      float ps[2] = {0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          ps[i & 1] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{bp[c][2 * i], bp[c][2 * i + 1]},
+                                                      one2, ps[i & 1], false);
+      l_run += ps[0] + ps[1];
+    }
 
     // O^T += V^T P^T: per 16-key step c, one transposed V fragment per dim block.
 #pragma unroll
