@@ -34,6 +34,36 @@ BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3       # fp32 vector
 DEFAULT_STEPS = {"c0": (200, 20), "c1": (200, 20), "c2": (20, 3), "c3": (4, 1), "c4": (2, 1)}
 STAGES = ("rerotate", "deviation_topk", "fuse_scatter", "partial_attn")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def source_fingerprint():
+    """sha256 over the library's sources: a recorded byte count is only valid
+    for the kernels it was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    for d in (os.path.join(ROOT, "selective_recompute_amd", "csrc"), os.path.join(ROOT, "include")):
+        for name in sorted(os.listdir(d)):
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(stage, workload):
+    """HBM bytes per launch of `stage` from the rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary under profiles/, or None when there is none for this workload or
+    the sources changed since it was taken."""
+    path = os.path.join(PROFILES, f"traffic_{stage}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+    if rec.get("source_sha256") != source_fingerprint():
+        return None
+    return float(rec["hbm_bytes_per_launch"])
 
 
 def parse_args():
@@ -45,6 +75,8 @@ def parse_args():
     ap.add_argument("--schedule", default="pool", choices=["pool", "chain"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="budget of the CPU oracle baseline (0 disables it)")
+    ap.add_argument("--print-source-sha", action="store_true",
+                    help="print the sources' fingerprint and exit")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the run, copy this many MiB device to device once (a "
                          "plain copy of known size that calibrates byte counters)")
@@ -132,6 +164,9 @@ def cpu_baseline(wl, seconds):
 
 def main():
     a = parse_args()
+    if a.print_source_sha:
+        print(source_fingerprint())
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported by this "
               "single-GPU build (no multi-GPU path exists).", file=sys.stderr)
@@ -281,11 +316,13 @@ def main():
         achieved = kernels[dominant]["tflops"]
         roof = {"kernel": "partial_attn", "bound": "mfma" if bf16 else "alu",
                 "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 5), "traffic": None}
+                "frac": round(achieved / peak, 5),
+                "traffic": recorded_traffic(dominant, wl.name)}
     else:
         achieved = kernels[dominant]["gbs"]
         roof = {"kernel": dominant, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None}
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
+                "traffic": recorded_traffic(dominant, wl.name)}
     del stage_calls, copies, keep
     torch.cuda.empty_cache()
 
