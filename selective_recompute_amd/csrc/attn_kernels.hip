@@ -66,7 +66,9 @@ struct AttnParams {
 };
 
 constexpr int kKeyTile = 64;
-constexpr int kQT = 128;               // query vectors per unit
+constexpr int kWaves = 8;              // waves per workgroup, two per SIMD
+constexpr int kQT = 32 * kWaves;       // query vectors per unit
+constexpr int kStages = 4;             // K/V tiles resident in LDS
 constexpr float kNegFloor = -1.0e30f;  // finite start of the running max
 constexpr float kRescaleSlack = 8.0f;  // log2 headroom before the max is raised
 constexpr int kMaxChunks = 8;          // key chunks per row (split plan bound)
@@ -122,16 +124,55 @@ __device__ inline bool locate_unit(const AttnParams &p, int u, int &r, int &tile
   return false;
 }
 
+// Wave-count encodings of s_waitcnt (gfx9): vmcnt(n) with the LGKM and EXP
+// counters left free, and lgkmcnt(0) with the VM counter left free.
+__device__ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
+
+// 16 bytes per lane from global memory straight into LDS: lane l writes
+// lds_byte + 16 l (gfx950 global_load_lds_dwordx4, LDS base in M0).  Written
+// as inline assembly so the compiler, which cannot tell the LDS stages apart,
+// does not wait for every copy in flight before each LDS read; the kernel
+// waits for its copies itself (waitcnt on the VM counter, then a barrier).
+// Nothing else in the kernel uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ inline void dma16(const char *base, uint32_t off, uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2"
+               :: "v"(off), "s"(__builtin_amdgcn_readfirstlane(lds_byte)), "s"(base)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ inline uint32_t lds_addr(const bf16 *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) bf16 *)p;
+}
+
+// Workgroup barrier between two tiles: LDS reads of this wave are complete,
+// and neither the compiler nor the scheduler moves work across it.  Global
+// loads into LDS stay in flight (their completion is waited for explicitly).
+__device__ inline void phase_barrier() {
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int HD>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_mfma_kernel(const AttnParams p) {
   constexpr int NKS = HD / 16;            // 16-wide contraction steps of S over head_dim
   constexpr int NDT = HD / 32;            // 32-dim output blocks
   constexpr int CPR = HD / 8;             // 16-byte chunks per key row
   constexpr int TILE = kKeyTile * HD;     // elements per tensor per stage
-  constexpr int DPW = CPR / 4;            // 1 KiB DMA instructions per wave per tensor
-  __shared__ __attribute__((aligned(1024))) bf16 kst[2][TILE];  // K stages
-  __shared__ __attribute__((aligned(1024))) bf16 vst[2][TILE];  // V stages
+  constexpr int NI = TILE / 512;          // 1 KiB DMA instructions per tensor per tile
+  constexpr int DMA_WAVES = NI < kWaves ? NI : kWaves;
+  constexpr int IPW = NI / DMA_WAVES;     // per issuing wave and tensor
+  constexpr int PER_TILE = 2 * IPW;       // vector-memory ops per tile and issuing wave
+  __shared__ __attribute__((aligned(1024))) bf16 kst[kStages][TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 vst[kStages][TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
@@ -147,17 +188,18 @@ void attn_mfma_kernel(const AttnParams p) {
   if (kb > p_last) return;  // whole chunk after the tile's last row (uniform)
   const int k_begin = (int)kb;
   const int k_end = (int)min((int64_t)p_last + 1, kb + p.key_chunk);
+  const int n_kt = (k_end - k_begin + kKeyTile - 1) / kKeyTile;
 
-  // DMA slots of this thread: instruction i writes 64 consecutive 16-byte
-  // chunks of the tile; lane -> (row, physical chunk) -> logical chunk.  The
-  // byte offsets from the tile's first key row are loop invariant; only the
-  // last tile, which may run past the tile's last row, clamps its rows.
+  // DMA slots of this wave: instruction i writes 64 consecutive 16-byte chunks
+  // of the tile; lane -> (row, physical chunk) -> logical chunk.  Rows past
+  // the tile's last key are clamped onto it (their scores are masked).
   const int64_t rs = (int64_t)p.hkv * HD;
-  int dma_row[DPW];
-  uint32_t dma_ko[DPW], dma_vo[DPW];
+  const bool dma_wave = wave < DMA_WAVES;
+  int dma_row[IPW];
+  uint32_t dma_ko[IPW], dma_vo[IPW];
 #pragma unroll
-  for (int i = 0; i < DPW; ++i) {
-    const int pos = (wave * DPW + i) * 64 + lane;
+  for (int i = 0; i < IPW; ++i) {
+    const int pos = ((dma_wave ? wave : 0) * IPW + i) * 64 + lane;
     const int row = pos / CPR, q = pos - row * CPR;
     dma_row[i] = row;
     dma_ko[i] = (uint32_t)((row * rs + (q ^ swz_k<HD>(row)) * 8) * 2);
@@ -165,21 +207,21 @@ void attn_mfma_kernel(const AttnParams p) {
   }
   const char *kbase = (const char *)(p.k_fused + (int64_t)g * HD);
   const char *vbase = (const char *)(p.v_fused + (int64_t)g * HD);
-  // One tensor's tile of 64 keys starting at k0 into an LDS stage buffer.
-  auto issue = [&](bf16 *dst, const char *base, const uint32_t *offs, int k0) {
-    const char *tile_base = base + (int64_t)k0 * rs * 2;
+  auto issue_tile = [&](int t) {
+    if (!dma_wave) return;
+    const int k0 = k_begin + t * kKeyTile;
+    const int64_t tb = (int64_t)k0 * rs * 2;
     const bool clamp = k0 + kKeyTile - 1 > p_last;
+    const uint32_t kd = lds_addr(kst[t % kStages]) + wave * IPW * 1024;
+    const uint32_t vd = lds_addr(vst[t % kStages]) + wave * IPW * 1024;
 #pragma unroll
-    for (int i = 0; i < DPW; ++i) {
-      uint32_t off = offs[i];
-      if (clamp && k0 + dma_row[i] > p_last)  // rows past the last key are masked
-        off -= (uint32_t)((k0 + dma_row[i] - p_last) * rs * 2);
-      __builtin_amdgcn_global_load_lds((global_cvoid *)(tile_base + off),
-                                       (lds_void *)(dst + (wave * DPW + i) * 512), 16, 0, 0);
+    for (int i = 0; i < IPW; ++i) {
+      uint32_t back = 0;
+      if (clamp && k0 + dma_row[i] > p_last) back = (uint32_t)((k0 + dma_row[i] - p_last) * rs * 2);
+      dma16(kbase + tb, dma_ko[i] - back, kd + i * 1024);
+      dma16(vbase + tb, dma_vo[i] - back, vd + i * 1024);
     }
   };
-  issue(kst[0], kbase, dma_ko, k_begin);
-  issue(vst[0], vbase, dma_vo, k_begin);
 
   // This lane's query column.  Padding columns (past the tile's last row)
   // see every key; their results are dropped.
@@ -195,6 +237,7 @@ void attn_mfma_kernel(const AttnParams p) {
 #pragma unroll
     for (int st = 0; st < NKS; ++st) qreg[st] = *reinterpret_cast<const bf16x8 *>(qp + 16 * st);
   }
+  for (int t = 0; t < kStages - 1 && t < n_kt; ++t) issue_tile(t);
 
   f32x16 o[NDT];
 #pragma unroll
@@ -220,20 +263,28 @@ void attn_mfma_kernel(const AttnParams p) {
     }
   }
 
-  const int n_kt = (k_end - k_begin + kKeyTile - 1) / kKeyTile;
+  // Q and the first tiles resident.  Waiting for everything here (instead of
+  // tile 0 only) also tells the compiler that no load of its own is pending
+  // inside the loop, so it adds no waits there.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
+
   for (int kt = 0; kt < n_kt; ++kt) {
-    const int stage = kt & 1;
     const int k0 = k_begin + kt * kKeyTile;
-    // tile kt has landed (this wave's DMA: vmcnt 0; the others': barrier) and
-    // every wave is done reading tile kt-1, whose buffers are refilled next
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (kt + 1 < n_kt) {
-      issue(kst[stage ^ 1], kbase, dma_ko, k0 + kKeyTile);
-      issue(vst[stage ^ 1], vbase, dma_vo, k0 + kKeyTile);
+    // Tile kt has landed for this wave's share; the tiles issued after it
+    // (up to kStages - 2 of them) may stay in flight.  The barrier then makes
+    // every wave's share visible and tells that all waves are done with tile
+    // kt - 1, whose stage is refilled with tile kt + kStages - 1.
+    if (kt > 0) {
+      const int ahead = min(kt + kStages - 2, n_kt - 1) - kt;
+      if (ahead >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * PER_TILE));
+      else if (ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(PER_TILE));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
-    const bf16 *ks = kst[stage];
-    const bf16 *vs = vst[stage];
+    phase_barrier();
+    if (kt + kStages - 1 < n_kt) issue_tile(kt + kStages - 1);
+    const bf16 *ks = kst[kt % kStages];
+    const bf16 *vs = vst[kt % kStages];
 
     // S^T: sacc[sb][r] = score(key k0 + 32sb + 8(r/4) + 4*half + r%4, column).
     f32x16 sacc[2];
@@ -283,17 +334,14 @@ void attn_mfma_kernel(const AttnParams p) {
             (bf16)__builtin_amdgcn_exp2f(fmaf(sacc[sb][e], p.scale_log2, neg_m));
     // The running sum adds the probabilities as they enter the PV product
     // (bf16), two per v_dot2c_f32_bf16, in two independent chains.
-    {
-      const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
-      float ps[2] = {0.f, 0.f};
+    float ps[2] = {0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          ps[i & 1] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{bp[c][2 * i], bp[c][2 * i + 1]},
-                                                      one2, ps[i & 1], false);
-      l_run += ps[0] + ps[1];
-    }
+      for (int i = 0; i < 4; ++i)
+        ps[i & 1] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{bp[c][2 * i], bp[c][2 * i + 1]},
+                                                    one2, ps[i & 1], false);
+    l_run += ps[0] + ps[1];
 
     // O^T += V^T P^T: per 16-key step c, one transposed V fragment per dim block.
 #pragma unroll
@@ -439,7 +487,7 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &plan, hipStream_t
   p.rows_per_tile = plan.rows_per_tile;
   p.key_chunk = plan.key_chunk;
   p.scale_log2 = a.softmax_scale * 1.4426950408889634f;
-  const dim3 grid((unsigned)(plan.units * a.n_kv_heads)), block(256);
+  const dim3 grid((unsigned)(plan.units * a.n_kv_heads)), block(64 * kWaves);
   switch (a.head_dim) {
     case 32: hipLaunchKernelGGL(attn_mfma_kernel<32>, grid, block, 0, stream, p); break;
     case 64: hipLaunchKernelGGL(attn_mfma_kernel<64>, grid, block, 0, stream, p); break;
@@ -448,11 +496,11 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &plan, hipStream_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !plan.split) return e;
   const int groups = kQT / (256 / (a.head_dim / 4));
-  const dim3 cgrid((unsigned)(plan.tiles * a.n_kv_heads * groups));
+  const dim3 cgrid((unsigned)(plan.tiles * a.n_kv_heads * groups)), cblock(256);
   switch (a.head_dim) {
-    case 32: hipLaunchKernelGGL(attn_combine_kernel<32>, cgrid, block, 0, stream, p); break;
-    case 64: hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, block, 0, stream, p); break;
+    case 32: hipLaunchKernelGGL(attn_combine_kernel<32>, cgrid, cblock, 0, stream, p); break;
+    case 64: hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, cblock, 0, stream, p); break;
+    default: hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, cblock, 0, stream, p); break;
   }
   return hipGetLastError();
 }

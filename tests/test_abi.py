@@ -164,11 +164,11 @@ def test_workspace_size_plan(lib):
         n = ctypes.c_size_t(123)
         assert lib.cb_partial_attn_workspace_size(ctypes.byref(g), ctypes.byref(rg), ctypes.byref(n)) == 0
         return n.value
-    unit = (128 * 128 + 2 * 128) * 4
-    # 128 query vectors per tile: 308 rows / 32 = 10 tiles x 8 heads, 2048 keys
+    unit = (256 * 128 + 2 * 256) * 4
+    # 256 query vectors per tile: 308 rows / 64 = 5 tiles x 8 heads, 2048 keys
     # in chunks of 256
-    assert size(_geom(), [0, 2048], [0, 308]) == 10 * 8 * 8 * unit
-    assert size(_geom(), [0, 32768], [0, 6554]) == 0            # enough tiles already
+    assert size(_geom(), [0, 2048], [0, 308]) == 5 * 8 * 8 * unit
+    assert size(_geom(), [0, 65536], [0, 16384]) == 0           # enough tiles already
     assert size(_geom(dt=B.CB_DTYPE_F32), [0, 2048], [0, 308]) == 0   # plain kernel
     assert size(_geom(d=16), [0, 2048], [0, 308]) == 0
     assert lib.cb_partial_attn_workspace_size(ctypes.byref(_geom()), None, None) == 1
