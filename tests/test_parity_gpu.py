@@ -189,6 +189,11 @@ ATTN_CASES = [
     (torch.float32, 4, 2, 16, [64, 64], [10, 10]),
     (torch.float32, 32, 8, 128, [1000], [50]),
     (torch.bfloat16, 128, 2, 128, [300, 0, 200], [40, 0, 9]),  # group 64, empty request
+    # 64 requests (longest-first schedule) and 70 (natural order in batches of 64)
+    (torch.bfloat16, 8, 2, 64, [(i * 37) % 41 + 1 for i in range(64)],
+     [((i * 37) % 41 + 1 + 2) // 3 for i in range(64)]),
+    (torch.bfloat16, 8, 2, 128, [(i * 53) % 97 + 1 for i in range(70)],
+     [((i * 53) % 97 + 1 + 3) // 4 for i in range(70)]),
 ]
 
 
