@@ -12,8 +12,11 @@ Metric: blended context tokens per second per layer = tokens * layers / time.
 
 Printed: one JSON line with the metric, a roofline entry for the dominant
 kernel (algorithmic work per launch / its average launch time, measured with
-HIP events on the launch stream), per-kernel figures and the CPU oracle timed
-on the host as a reported baseline.
+HIP events on the launch stream, against the published peak and against the
+peak measured by the in-tree probe `cb_peaks`), the whole-step roofline
+fraction (streaming bytes at 8 TB/s plus attention flops at the MFMA peak,
+over the step time), per-kernel figures and the CPU oracle timed on the host
+as a reported baseline.
 """
 from __future__ import annotations
 
@@ -38,15 +41,34 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 def source_fingerprint():
-    """sha256 over the library's sources: a recorded byte count is only valid
-    for the kernels it was measured on."""
+    """sha256 over the library's sources (its compiled files, their headers and
+    the public header): a recorded byte count is only valid for the kernels it
+    was measured on."""
     import hashlib
+    from selective_recompute_amd import build as BLD
+    csrc = os.path.join(ROOT, "selective_recompute_amd", "csrc")
+    files = [os.path.join(csrc, n) for n in BLD.SOURCES]
+    files += sorted(os.path.join(csrc, n) for n in os.listdir(csrc) if n.endswith(".hpp"))
+    files += sorted(os.path.join(ROOT, "include", n) for n in os.listdir(os.path.join(ROOT, "include")))
     h = hashlib.sha256()
-    for d in (os.path.join(ROOT, "selective_recompute_amd", "csrc"), os.path.join(ROOT, "include")):
-        for name in sorted(os.listdir(d)):
-            with open(os.path.join(d, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for path in files:
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
     return h.hexdigest()
+
+
+def attainable_peaks():
+    """Run the in-tree probe (built next to the library) in a child process
+    before this process touches the GPU; None if it is not built."""
+    import subprocess
+    from selective_recompute_amd import build as BLD
+    if not os.path.exists(BLD.PEAKS):
+        return None
+    res = subprocess.run([BLD.PEAKS], capture_output=True, text=True, timeout=120)
+    if res.returncode != 0:
+        log(f"[bench] peak probe failed: {res.stderr.strip()}")
+        return None
+    return json.loads(res.stdout.strip().splitlines()[-1])
 
 
 def recorded_traffic(stage, workload):
@@ -75,6 +97,9 @@ def parse_args():
     ap.add_argument("--schedule", default="pool", choices=["pool", "chain"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="budget of the CPU oracle baseline (0 disables it)")
+    ap.add_argument("--attainable", type=int, default=1,
+                    help="1: measure attainable MFMA / HBM peaks first and report "
+                         "fractions against them too")
     ap.add_argument("--print-source-sha", action="store_true",
                     help="print the sources' fingerprint and exit")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -171,6 +196,7 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported by this "
               "single-GPU build (no multi-GPU path exists).", file=sys.stderr)
         sys.exit(2)
+    peaks = attainable_peaks() if a.attainable else None
     import numpy as np
     import torch
 
@@ -323,6 +349,11 @@ def main():
         roof = {"kernel": dominant, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
                 "traffic": recorded_traffic(dominant, wl.name)}
+    if peaks:
+        att = peaks["mfma_bf16_32x32x16_tflops"] if roof["unit"] == "TFLOP/s" else peaks["copy_gbs"]
+        if roof["bound"] in ("mfma", "hbm"):
+            roof["attainable_peak"] = att
+            roof["frac_attainable"] = round(roof["achieved"] / att, 5)
     del stage_calls, copies, keep
     torch.cuda.empty_cache()
 
@@ -341,6 +372,13 @@ def main():
         cpu = cpu_baseline(wl, a.cpu_seconds)
 
     value = wl.n_tokens * L / (ms_per_step * 1e-3)
+    # whole-step roofline: streaming bytes at the HBM peak plus attention flops
+    # at the MFMA (bf16) or vector (fp32) peak, over the measured step time
+    flop_peak = (BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS) * 1e12
+    t_star = sum((w["rerotate"] + w["deviation_topk"] + w["fuse_scatter"]) / (HBM_PEAK_GBS * 1e9)
+                 + w["partial_attn"] / flop_peak for w in work)
+    step_roofline = {"t_star_ms": round(t_star * 1e3, 6),
+                     "frac": round(t_star / (ms_per_step * 1e-3), 5)}
     ratio = {"c0": "r=15%", "c1": "r=15%"}.get(wl.name, f"r1={wl.r1_pct}% -> r2={wl.r2_pct}%")
     line = {
         "metric": "blended context tokens/s per layer (1 GPU) + % HBM / MFMA roofline",
@@ -352,6 +390,8 @@ def main():
                    "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "selection": ratio,
                    "hkvd_pct": wl.hkvd_pct, "schedule": a.schedule},
         "roofline": roof,
+        "step_roofline": step_roofline,
+        "attainable": peaks,
         "cpu_baseline": cpu,
         "kernels": kernels,
         "wall_ms_per_step": round(wall_ms_per_step, 5),

@@ -15,6 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcacheblend.so")
+PEAKS = os.path.join(PKG, "cb_peaks")    # attainable-peak probe run by bench.py
 
 SOURCES = ["api.cpp", "stream_kernels.hip", "attn_kernels.hip"]
 ARCH = "gfx950"
@@ -57,8 +58,13 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB)
+    cmd = [_hipcc(), *_flags(), "-x", "hip", os.path.join(CSRC, "peaks.hip"), "-o", PEAKS + ".tmp"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on peaks.hip:\n{res.stdout}\n{res.stderr}")
+    os.replace(PEAKS + ".tmp", PEAKS)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PEAKS}")
     return LIB
 
 
