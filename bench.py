@@ -100,6 +100,9 @@ def parse_args():
     ap.add_argument("--attainable", type=int, default=1,
                     help="1: measure attainable MFMA / HBM peaks first and report "
                          "fractions against them too")
+    ap.add_argument("--prefill", action="store_true",
+                    help="instead of the blend step: dense causal attention of every "
+                         "row (layer-1 full prefill) at the workload's shape")
     ap.add_argument("--print-source-sha", action="store_true",
                     help="print the sources' fingerprint and exit")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -187,6 +190,66 @@ def cpu_baseline(wl, seconds):
             "kind": "oracle", "sample": sample}
 
 
+def prefill_main(a, peaks):
+    """Layer-1 full prefill: every row of every request attends causally over
+    its request, through the same cb_partial_attn entry point (all rows
+    selected).  Prints one JSON line in TFLOP/s."""
+    import numpy as np
+    import torch
+
+    from selective_recompute_amd import binding as B
+    from selective_recompute_amd import pipeline as PL
+    from selective_recompute_amd import workloads as W
+
+    wl = W.make_workload(a.workload)
+    if wl.dtype != "bf16":
+        raise SystemExit("--prefill measures the bf16 MFMA path")
+    steps = a.steps if a.steps is not None else 5
+    warmup = a.warmup if a.warmup is not None else 1
+    lens = wl.request_lengths
+    t_count = int(sum(lens))
+    tok_off = PL.offsets(lens)
+    gen = torch.Generator(device="cuda").manual_seed(0xCB10 + t_count)
+    mk = lambda h: torch.randn(t_count, h, wl.head_dim, generator=gen, device="cuda").to(torch.bfloat16)
+    q, k, v = mk(wl.n_q_heads), mk(wl.n_kv_heads), mk(wl.n_kv_heads)
+    idx = torch.arange(t_count, dtype=torch.int32, device="cuda")
+    rb = B.RaggedBatch(tok_off, tok_off, tok_off, "cuda")
+    g = B.geom(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, torch.bfloat16)
+    ws = B.workspace_tensor(B.attn_workspace_bytes(g, rb), "cuda")
+    out = torch.empty_like(q)
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    stream = torch.cuda.Stream()
+    run = lambda: B.partial_attn(g, rb, out, q, idx, idx, k, v, scale, workspace=ws, stream=stream)
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 4.0 * wl.head_dim * wl.n_q_heads * sum(n * (n + 1) / 2 for n in lens)
+    tf = flops / (ms * 1e-3) / 1e12
+    roof = {"kernel": "partial_attn (all rows)", "bound": "mfma", "achieved": round(tf, 3),
+            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 5),
+            "traffic": None}
+    if peaks:
+        roof["attainable_peak"] = peaks["mfma_bf16_32x32x16_tflops"]
+        roof["frac_attainable"] = round(tf / peaks["mfma_bf16_32x32x16_tflops"], 5)
+    print(json.dumps({
+        "metric": "dense causal attention TFLOP/s (layer-1 full prefill)", "value": round(tf, 3),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{wl.name} shape, every row selected", "tokens": t_count,
+                   "requests": len(lens), "q_heads": wl.n_q_heads, "kv_heads": wl.n_kv_heads,
+                   "head_dim": wl.head_dim, "gflop_per_launch": round(flops / 1e9, 3)},
+        "roofline": roof, "attainable": peaks}), flush=True)
+
+
 def main():
     a = parse_args()
     if a.print_source_sha:
@@ -197,6 +260,8 @@ def main():
               "single-GPU build (no multi-GPU path exists).", file=sys.stderr)
         sys.exit(2)
     peaks = attainable_peaks() if a.attainable else None
+    if a.prefill:
+        return prefill_main(a, peaks)
     import numpy as np
     import torch
 

@@ -244,6 +244,39 @@ def test_partial_attention_parity(case, use_ws):
     assert err.max() <= ATTN_ABS, f"max err {err.max()}"
 
 
+DENSE = [(32, 8, 128, [2048], 64), (64, 8, 128, [700, 1300], 48), (8, 8, 64, [333], None)]
+
+
+@pytest.mark.parametrize("hq,hkv,d,lens,n_rows", DENSE, ids=[f"d{i}" for i in range(len(DENSE))])
+def test_dense_prefill_attention(hq, hkv, d, lens, n_rows):
+    """Layer-1 full prefill: every row of every request is selected, so the
+    kernel runs dense causal attention (query tiles of consecutive positions)."""
+    say(f"dense prefill {hq} {hkv} {d} {lens}")
+    gen = torch.Generator().manual_seed(sum(lens) + hq)
+    t_count = sum(lens)
+    tok_off = PL.offsets(lens)
+    q = torch.randn(t_count, hq, d, generator=gen).to(torch.bfloat16)
+    kf = torch.randn(t_count, hkv, d, generator=gen).to(torch.bfloat16)
+    vf = torch.randn(t_count, hkv, d, generator=gen).to(torch.bfloat16)
+    idx = np.arange(t_count, dtype=np.int32)
+    rb = B.RaggedBatch(tok_off, tok_off, tok_off, DEV)
+    g = B.geom(hq, hkv, d, torch.bfloat16)
+    out = torch.full((t_count, hq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    scale = 1.0 / math.sqrt(d)
+    ws = B.workspace_tensor(B.attn_workspace_bytes(g, rb), DEV)
+    B.partial_attn(g, rb, out, q.to(DEV), torch.from_numpy(idx).to(DEV), torch.from_numpy(idx).to(DEV),
+                   kf.to(DEV), vf.to(DEV), scale, workspace=ws)
+    torch.cuda.synchronize()
+    row_start = np.repeat(tok_off[:-1], lens)
+    rows = idx if n_rows is None else np.unique(np.concatenate(
+        [tok_off[:-1], tok_off[1:] - 1, np.random.default_rng(0).choice(t_count, n_rows, replace=False)]))
+    ref = O.attention_rows(np64(q)[rows], np.arange(len(rows)), idx[rows], row_start[rows],
+                           np64(kf), np64(vf), hq, hkv, scale)
+    got = np64(out)[rows]
+    assert np.isfinite(np64(out)).all()
+    assert np.abs(got - ref).max() <= ATTN_ABS
+
+
 # ------------------------------------------------------------- end to end ----
 def _oracle_layer(wl, x, cand, counts, attend_rows=None):
     """Oracle for one layer on the exact stored inputs; attention only for the
@@ -270,18 +303,19 @@ def _oracle_layer(wl, x, cand, counts, attend_rows=None):
                 v_fused=v_fused, out=out, rows=rows)
 
 
-E2E = [("c0", [0], None), ("c1", [0], None), ("c2", [0, 1, 2], 96),
-       ("c3", [0, 1], 24), ("c4", [0, 1], 24)]
+E2E = [("c0", [0], None, "pool"), ("c1", [0], None, "pool"), ("c2", [0, 1, 2], 96, "pool"),
+       ("c2", [0, 1, 2, 3], 96, "chain"), ("c3", [0, 1], 24, "pool"), ("c4", [0, 1], 24, "pool")]
 
 
-@pytest.mark.parametrize("name,layers,n_rows", E2E, ids=[e[0] for e in E2E])
-def test_blend_layers_end_to_end(name, layers, n_rows):
+@pytest.mark.parametrize("name,layers,n_rows,schedule", E2E,
+                         ids=[f"{e[0]}-{e[3]}" for e in E2E])
+def test_blend_layers_end_to_end(name, layers, n_rows, schedule):
     wl = W.make_workload(name)
-    sets = W.PlantedSets(wl)
+    sets = W.PlantedSets(wl, schedule)
     gen_dev = "cpu" if wl.n_tokens <= 8192 else DEV
     runner = PL.BlendRunner(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.torch_dtype,
                             wl.request_lengths, wl.r1_pct, wl.r2_pct, max(layers) + 1,
-                            wl.rope_theta)
+                            wl.rope_theta, schedule=schedule)
     for layer in layers:
         say(f"blend {name} layer {layer}")
         x = W.layer_inputs(wl, sets, layer, device=gen_dev)
@@ -292,7 +326,7 @@ def test_blend_layers_end_to_end(name, layers, n_rows):
         x_cpu["v_new_c"], x_cpu["k_new_c"] = x["v_new_c"].cpu(), x["k_new_c"].cpu()
         x_cpu["q_c"] = x["q_c"].cpu()
         if layer > 0:
-            # the device keeps layer 1's selection as this layer's candidates
+            # the device keeps the source layer's selection as this layer's candidates
             assert np.array_equal(npi(runner.candidates(layer)), npi(x["cand_idx"]))
         o = runner.run_layer(layer, xg)
         torch.cuda.synchronize()
