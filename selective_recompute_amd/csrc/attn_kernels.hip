@@ -373,12 +373,15 @@ void attn_mfma_kernel(const AttnParams p) {
         }
     }
   } else {
+    // Partial in fragment order: store (dt, q) of wave w writes 64 lanes x 16
+    // contiguous bytes at float4 index ((w*NDT + dt)*4 + q)*64 + lane; then
+    // the running max and sum of the 256 query vectors.
     float *w = p.ws + (int64_t)blockIdx.x * (kQT * HD + 2 * kQT);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<f32x4 *>(w + qv * HD + 32 * dt + 8 * q + 4 * half) =
+        *reinterpret_cast<f32x4 *>(w + 4 * ((((wave * NDT + dt) * 4 + q) << 6) + lane)) =
             f32x4{o[dt][4 * q], o[dt][4 * q + 1], o[dt][4 * q + 2], o[dt][4 * q + 3]};
     if (half == 0) {
       w[kQT * HD + qv] = m_run;
@@ -387,7 +390,8 @@ void attn_mfma_kernel(const AttnParams p) {
   }
 }
 
-// Merge the key-chunk partials.  One thread per (query vector, 4 head dims):
+// Merge the key-chunk partials.  One thread per float4 of a partial, in the
+// partial's fragment order (consecutive threads read consecutive 16 bytes):
 // it loads the running max, running sum and partial O of every chunk at once
 // (unrolled over the chunk bound, inactive chunks clamped to chunk 0 and
 // weighted 0), so each thread waits for a single round of loads.
@@ -395,9 +399,7 @@ template <int HD>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   constexpr int QT = kQT;
   constexpr int UNIT = QT * HD + 2 * QT;
-  constexpr int D4 = HD / 4;              // float4 groups per query vector
-  constexpr int QPB = 256 / D4;           // query vectors per workgroup
-  constexpr int GROUPS = QT / QPB;        // workgroups per (tile, head)
+  constexpr int GROUPS = QT * HD / 4 / 256;  // workgroups per (tile, head)
   const int g = blockIdx.x % p.hkv;
   const int rest = blockIdx.x / p.hkv;
   const int qgroup = rest % GROUPS;
@@ -416,8 +418,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   if (r == p.n_req || cr == 1) return;
   const int s0 = p.sel_off[r] + tile * p.rows_per_tile;
   const int ns = min(p.rows_per_tile, p.sel_off[r + 1] - s0);
-  const int qv = qgroup * QPB + (int)threadIdx.x / D4;
-  const int d4 = (int)threadIdx.x % D4;
+  // float4 index f = ((wave*NDT + dt)*4 + q)*64 + lane of the partial holds
+  // dims 32dt + 8q + 4(lane/32) .. +3 of query vector 32*wave + lane%32
+  constexpr int NDT = HD / 32;
+  const int f = qgroup * 256 + (int)threadIdx.x;
+  const int lane = f & 63, q = (f >> 6) & 3, dt = (f >> 8) % NDT, wv = (f >> 8) / NDT;
+  const int qv = wv * 32 + (lane & 31);
+  const int d0 = 32 * dt + 8 * q + 4 * (lane >> 5);
   const int row = qv / p.group, hh = qv - row * p.group;
   if (row >= ns) return;
   const int lo = p.tok_off[r];
@@ -433,7 +440,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
     const float *w = w0 + (c < n_active ? c : 0) * ustride;
     mc[c] = w[QT * HD + qv];
     lc[c] = w[QT * HD + QT + qv];
-    oc[c] = *reinterpret_cast<const f32x4 *>(w + qv * HD + 4 * d4);
+    oc[c] = *reinterpret_cast<const f32x4 *>(w + 4 * f);
   }
   float mx = kNegFloor;
 #pragma unroll
@@ -451,7 +458,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = (bf16)(acc[i] * inv);
   *reinterpret_cast<bf16x4 *>(p.out + ((int64_t)(s0 + row) * p.hq + g * p.group + hh) * HD +
-                              4 * d4) = o;
+                              d0) = o;
 }
 
 int attn_mfma_rows_per_tile(int dtype, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim) {
