@@ -359,18 +359,35 @@ void attn_mfma_kernel(const AttnParams p) {
 
   float l = l_run + __shfl_xor(l_run, 32, kWave);
   if (nchunks == 1) {
-    if (qvalid) {
-      const float inv = 1.f / l;
-      bf16 *op = p.out + ((int64_t)(s0 + qrow) * p.hq + g * p.group + qhh) * HD + 4 * half;
+    // Output through LDS (the K stage buffers are free once every wave is
+    // past its last tile): each wave writes its normalised bf16 rows (16-byte
+    // chunk index XOR-swizzled by the query vector against bank conflicts),
+    // then the workgroup stores 16-byte chunks in output order -- the G query
+    // heads of one selected row are adjacent in `out`, so a wave writes whole
+    // 1 KiB runs instead of 8 bytes per lane 256 bytes apart.
+    constexpr int CPQ = HD / 8;  // 16-byte chunks per query vector
+    bf16 *stage = &kst[0][0];
+    static_assert(kStages * TILE >= kQT * HD, "output staging does not fit");
+    phase_barrier();
+    const float inv = 1.f / l;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          bf16x4 w;
+      for (int q = 0; q < 4; ++q) {
+        bf16x4 w;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) w[i] = (bf16)(o[dt][4 * q + i] * inv);
-          *reinterpret_cast<bf16x4 *>(op + 32 * dt + 8 * q) = w;
-        }
+        for (int i = 0; i < 4; ++i) w[i] = (bf16)(o[dt][4 * q + i] * inv);
+        const int chunk = (4 * dt + q) ^ (qv & (CPQ - 1));
+        *reinterpret_cast<bf16x4 *>(stage + qv * HD + 8 * chunk + 4 * half) = w;
+      }
+    phase_barrier();
+    for (int c = tid; c < kQT * CPQ; c += 64 * kWaves) {
+      const int v = c / CPQ, part = c - v * CPQ;
+      const int vrow = v / p.group, vh = v - vrow * p.group;
+      if (vrow < ns)
+        *reinterpret_cast<uint4 *>(p.out + ((int64_t)(s0 + vrow) * p.hq + g * p.group + vh) * HD +
+                                   8 * part) =
+            *reinterpret_cast<const uint4 *>(stage + v * HD + 8 * (part ^ (v & (CPQ - 1))));
     }
   } else {
     // Partial in fragment order: store (dt, q) of wave w writes 64 lanes x 16

@@ -349,10 +349,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   const int jb = tid * seg < m ? tid * seg : m;
   const int n_my = (jb + seg < m ? jb + seg : m) - jb;
   uint32_t keys[KPT > 0 ? KPT : 1];
+  int32_t cands[KPT > 0 ? KPT : 1];  // loaded with the scores: no load left at the end
   if (KPT > 0) {
 #pragma unroll
-    for (int i = 0; i < (KPT > 0 ? KPT : 1); ++i)
+    for (int i = 0; i < (KPT > 0 ? KPT : 1); ++i) {
       keys[i] = i < n_my ? order_key(dev[c0 + jb + i]) : 0u;
+      cands[i] = i < n_my ? cand_idx[c0 + jb + i] : 0;
+    }
   }
   auto key_at = [&](int i) -> uint32_t {
     if (KPT > 0) return keys[i];
@@ -423,7 +426,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
       if (gt || (eq && eq_before < keep_eq)) {
         const uint32_t pos = gt_before + (eq_before < keep_eq ? eq_before : keep_eq);
         sel_local[s0 + pos] = c0 + jb + i;
-        sel_global[s0 + pos] = cand_idx[c0 + jb + i];
+        sel_global[s0 + pos] = KPT > 0 ? cands[i] : cand_idx[c0 + jb + i];
       }
       gt_before += gt;
       eq_before += eq;
