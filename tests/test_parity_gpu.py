@@ -373,7 +373,8 @@ def test_blend_is_deterministic():
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("m,k", [(30000, 4567), (40000, 9999), (40000, 1), (1024, 1023)])
+@pytest.mark.parametrize("m,k", [(30000, 4567), (40000, 9999), (40000, 1), (1024, 1023),
+                                 (4096, 700), (4097, 700), (2048, 308)])
 def test_topk_register_and_memory_paths(m, k):
     """Up to 32 keys per thread stay in registers; larger requests re-read
     their scores every radix pass.  Both paths, with many exact ties."""
