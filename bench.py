@@ -100,6 +100,9 @@ def parse_args():
     ap.add_argument("--attainable", type=int, default=1,
                     help="1: measure attainable MFMA / HBM peaks first and report "
                          "fractions against them too")
+    ap.add_argument("--graph", type=int, default=0,
+                    help="1: capture the timed steps' launches in one HIP graph and "
+                         "time its replay (same kernels, no host launch cost)")
     ap.add_argument("--prefill", action="store_true",
                     help="instead of the blend step: dense causal attention of every "
                          "row (layer-1 full prefill) at the workload's shape")
@@ -308,20 +311,34 @@ def main():
                                        sel_local=o["sel_local"], sel_global=o["sel_global"],
                                        out=o["out"], workspace=runner.workspace))
         prepared.append(row)
+    graph = None
     with torch.cuda.stream(stream):
         for c in range(warmup):
             for p in prepared[c]:
                 p.launch(h)
         torch.cuda.synchronize()
+        if a.graph:
+            # capture records the launches without running them: the timed
+            # copies are still pristine when the graph is replayed
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                for c in range(warmup, warmup + steps):
+                    for p in prepared[c]:
+                        p.launch(h)
+            torch.cuda.synchronize()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         ev0.record(stream)
-        for c in range(warmup, warmup + steps):
-            for p in prepared[c]:
-                p.launch(h)
+        if graph is not None:
+            graph.replay()
+        else:
+            for c in range(warmup, warmup + steps):
+                for p in prepared[c]:
+                    p.launch(h)
         ev1.record(stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+    del graph
     ms_per_step = ev0.elapsed_time(ev1) / steps
     wall_ms_per_step = (t1 - t0) * 1e3 / steps
     log(f"[bench] timed {steps} steps: {ms_per_step:.4f} ms/step (wall {wall_ms_per_step:.4f})")
@@ -453,7 +470,8 @@ def main():
         "config": {"workload": f"{wl.name}: {wl.description}", "tokens": wl.n_tokens,
                    "layers": L, "requests": wl.n_requests, "q_heads": wl.n_q_heads,
                    "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "selection": ratio,
-                   "hkvd_pct": wl.hkvd_pct, "schedule": a.schedule},
+                   "hkvd_pct": wl.hkvd_pct, "schedule": a.schedule,
+                   "launch": "hip graph replay" if a.graph else "stream launches"},
         "roofline": roof,
         "step_roofline": step_roofline,
         "attainable": peaks,
