@@ -411,3 +411,52 @@ def test_blend_layer_ragged_requests_are_independent():
                            sel_counts=[2], **args)
     assert list(both["sel_global"][3:] - 10) == list(second["sel_global"])
     assert np.max(np.abs(both["out"][3:] - second["out"])) < 1e-12
+
+
+# ------------------------------------------------- the selection objective --
+def test_deviation_selection_beats_random_on_the_fusion_objective():
+    """[Derivations, "近似解"]: choosing the tokens with the largest V deviation
+    makes the fused cache's attention close to the full recompute's.  Built
+    here on data whose cached keys are the new keys at old positions (so
+    re-rotation restores them up to small noise) and whose values deviate
+    strongly on 15% of the tokens: the deviation top-k must give a smaller
+    attention error than every one of 20 random selections of the same size,
+    and re-rotation must beat leaving the cached keys unrotated."""
+    rng = np.random.default_rng(7)
+    theta, hq, hkv, d = 10000.0, 4, 2, 16
+    chunk, n_chunks = 64, 3
+    t = chunk * n_chunks
+    p_old = np.tile(np.arange(chunk), n_chunks)
+    p_new = np.arange(t)
+    k_base = rng.standard_normal((t, hkv, d))
+    v_old = rng.standard_normal((t, hkv, d))
+    k_old = O.rotate(k_base, p_old, theta)
+    k_new = O.rotate(k_base + 0.01 * rng.standard_normal((t, hkv, d)), p_new, theta)
+    hot = rng.choice(t, int(0.15 * t), replace=False)
+    sigma = np.full(t, 0.01)
+    sigma[hot] = 1.0
+    v_new = v_old + sigma[:, None, None] * rng.standard_normal((t, hkv, d))
+    q = O.rotate(rng.standard_normal((t, hq, d)), p_new, theta)
+    everyone = np.arange(t)
+    start = np.zeros(t, dtype=np.int64)
+    scale = 1.0 / math.sqrt(d)
+
+    def attend(k_f, v_f):
+        return O.attention_rows(q, everyone, everyone, start, k_f, v_f, hq, hkv, scale)
+
+    full = attend(k_new, v_new)
+    k_rot = O.rerotate(k_old, p_new - p_old, theta)
+    k = len(hot)
+
+    def err(sel, keys=k_rot):
+        sel = np.sort(sel)
+        k_f, v_f = O.fuse(keys, v_old, k_new, v_new, sel, sel)
+        return np.linalg.norm(attend(k_f, v_f) - full)
+
+    dev = O.deviation(v_new, v_old, everyone)
+    sel_local, sel_global = O.topk_select(dev, everyone, k)
+    assert set(sel_global) == set(hot)
+    e_top = err(sel_global)
+    e_rand = [err(rng.choice(t, k, replace=False)) for _ in range(20)]
+    assert e_top < 0.5 * min(e_rand), (e_top, min(e_rand))
+    assert e_top < 0.5 * err(sel_global, keys=k_old)       # re-rotation matters
