@@ -35,7 +35,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3       # fp32 vector
-DEFAULT_STEPS = {"c0": (200, 20), "c1": (200, 20), "c2": (20, 3), "c3": (4, 1), "c4": (2, 1)}
+DEFAULT_STEPS = {"tiny": (200, 20), "mistral7b-layer": (200, 20), "7b-32layer-6k": (20, 3),
+                 "7b-32layer-32k": (4, 1), "70b-80layer-8req": (2, 1)}
 STAGES = ("rerotate", "deviation_topk", "fuse_scatter", "partial_attn")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -93,7 +94,7 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="c1", choices=["c0", "c1", "c2", "c3", "c4"])
+    ap.add_argument("--workload", default="mistral7b-layer", choices=list(DEFAULT_STEPS))
     ap.add_argument("--schedule", default="pool", choices=["pool", "chain"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="budget of the CPU oracle baseline (0 disables it)")
@@ -461,7 +462,8 @@ def main():
                  + w["partial_attn"] / flop_peak for w in work)
     step_roofline = {"t_star_ms": round(t_star * 1e3, 6),
                      "frac": round(t_star / (ms_per_step * 1e-3), 5)}
-    ratio = {"c0": "r=15%", "c1": "r=15%"}.get(wl.name, f"r1={wl.r1_pct}% -> r2={wl.r2_pct}%")
+    ratio = (f"r={wl.r1_pct}%" if wl.n_layers == 1
+             else f"r1={wl.r1_pct}% -> r2={wl.r2_pct}%")
     line = {
         "metric": "blended context tokens/s per layer (1 GPU) + % HBM / MFMA roofline",
         "value": round(value, 1), "unit": "tokens/s/layer", "n_gpus": 1, "steps": steps,

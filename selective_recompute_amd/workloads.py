@@ -119,27 +119,27 @@ def _draw_batched_chunks(seed: int, n_req=8, min_chunks=2, max_chunks=16,
 
 
 def make_workload(name: str) -> Workload:
-    """The five synthetic workloads, by name ("c0" ... "c4")."""
-    if name == "c0":
-        return Workload("c0", 1, ((64, 64),), 4, 2, 16, 10000.0, "f32", 15, 15, 15, 80, 0xCB00,
+    """The five synthetic workloads, by name (see WORKLOADS)."""
+    if name == "tiny":
+        return Workload("tiny", 1, ((64, 64),), 4, 2, 16, 10000.0, "f32", 15, 15, 15, 80, 0xCB00,
                         "tiny blend: 1 layer, 2x64 tokens, 4 Q / 2 KV heads, head_dim 16, fp32")
-    if name == "c1":
-        return Workload("c1", 1, ((512,) * 4,), 32, 8, 128, 10000.0, "bf16", 15, 15, 15, 80, 0xCB01,
+    if name == "mistral7b-layer":
+        return Workload("mistral7b-layer", 1, ((512,) * 4,), 32, 8, 128, 10000.0, "bf16", 15, 15, 15, 80, 0xCB01,
                         "Mistral-7B-shaped layer: 4x512 tokens, 32 Q / 8 KV heads, head_dim 128, bf16")
-    if name == "c2":
-        return Workload("c2", 32, ((1024,) * 6,), 32, 8, 128, 10000.0, "bf16", 15, 30, 15, 80, 0xCB02,
+    if name == "7b-32layer-6k":
+        return Workload("7b-32layer-6k", 32, ((1024,) * 6,), 32, 8, 128, 10000.0, "bf16", 15, 30, 15, 80, 0xCB02,
                         "32-layer gradual filter at 7B shape: 6x1024 tokens, r1 30% -> r2 15%")
-    if name == "c3":
-        return Workload("c3", 32, ((2048,) * 16,), 32, 8, 128, 10000.0, "bf16", 10, 20, 10, 80, 0xCB03,
+    if name == "7b-32layer-32k":
+        return Workload("7b-32layer-32k", 32, ((2048,) * 16,), 32, 8, 128, 10000.0, "bf16", 10, 20, 10, 80, 0xCB03,
                         "long-context blend: 16x2048 tokens, 32 layers, r1 20% -> r2 10%")
-    if name == "c4":
+    if name == "70b-80layer-8req":
         chunks = _draw_batched_chunks(0xCB04)
-        return Workload("c4", 80, chunks, 64, 8, 128, 10000.0, "bf16", 15, 25, 15, 80, 0xCB04,
+        return Workload("70b-80layer-8req", 80, chunks, 64, 8, 128, 10000.0, "bf16", 15, 25, 15, 80, 0xCB04,
                         "batched 70B-layer blend: 8 ragged requests of 2-16 chunks, ~64k tokens, 80 layers")
     raise KeyError(name)
 
 
-WORKLOADS = ("c0", "c1", "c2", "c3", "c4")
+WORKLOADS = ("tiny", "mistral7b-layer", "7b-32layer-6k", "7b-32layer-32k", "70b-80layer-8req")
 
 
 @dataclass

@@ -18,7 +18,7 @@ def say(msg):
     print(f"[graph-test] {msg}", flush=True)
 
 
-@pytest.mark.parametrize("name", ["c1", "c0"])
+@pytest.mark.parametrize("name", ["mistral7b-layer", "tiny"])
 def test_blend_layer_graph_replays_match_eager(name):
     say(f"graph replay {name}")
     wl = W.make_workload(name)

@@ -103,7 +103,7 @@ def _gpu_devtopk(wl, x, k_counts):
     return dev.cpu().numpy().astype(np.float64), npi(sl), npi(sg)
 
 
-@pytest.mark.parametrize("name,layer", [("c0", 0), ("c1", 0), ("c2", 0), ("c2", 1), ("c2", 4)])
+@pytest.mark.parametrize("name,layer", [("tiny", 0), ("mistral7b-layer", 0), ("7b-32layer-6k", 0), ("7b-32layer-6k", 1), ("7b-32layer-6k", 4)])
 def test_deviation_topk_parity(name, layer):
     say(f"deviation_topk {name} layer {layer}")
     wl = W.make_workload(name)
@@ -303,8 +303,8 @@ def _oracle_layer(wl, x, cand, counts, attend_rows=None):
                 v_fused=v_fused, out=out, rows=rows)
 
 
-E2E = [("c0", [0], None, "pool"), ("c1", [0], None, "pool"), ("c2", [0, 1, 2], 96, "pool"),
-       ("c2", [0, 1, 2, 3], 96, "chain"), ("c3", [0, 1], 24, "pool"), ("c4", [0, 1], 24, "pool")]
+E2E = [("tiny", [0], None, "pool"), ("mistral7b-layer", [0], None, "pool"), ("7b-32layer-6k", [0, 1, 2], 96, "pool"),
+       ("7b-32layer-6k", [0, 1, 2, 3], 96, "chain"), ("7b-32layer-32k", [0, 1], 24, "pool"), ("70b-80layer-8req", [0, 1], 24, "pool")]
 
 
 @pytest.mark.parametrize("name,layers,n_rows,schedule", E2E,
@@ -356,8 +356,8 @@ def test_blend_layers_end_to_end(name, layers, n_rows, schedule):
 
 
 def test_blend_is_deterministic():
-    say("determinism c1")
-    wl = W.make_workload("c1")
+    say("determinism mistral7b-layer")
+    wl = W.make_workload("mistral7b-layer")
     sets = W.PlantedSets(wl)
     outs = []
     for _ in range(2):

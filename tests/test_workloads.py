@@ -16,29 +16,29 @@ def _np64(t):
 
 
 def test_presets_shapes():
-    c0, c1 = W.make_workload("c0"), W.make_workload("c1")
-    assert c0.n_tokens == 128 and c0.head_dim == 16 and c0.dtype == "f32"
-    assert c1.n_tokens == 2048 and (c1.n_q_heads, c1.n_kv_heads) == (32, 8)
-    c2, c3, c4 = (W.make_workload(n) for n in ("c2", "c3", "c4"))
-    assert (c2.n_tokens, c2.n_layers) == (6144, 32)
-    assert (c3.n_tokens, c3.n_layers) == (32768, 32)
-    assert c4.n_requests == 8 and c4.n_layers == 80 and 57344 <= c4.n_tokens <= 73728
-    for chunk_lens in c4.chunks:
+    tiny, layer7b = W.make_workload("tiny"), W.make_workload("mistral7b-layer")
+    assert tiny.n_tokens == 128 and tiny.head_dim == 16 and tiny.dtype == "f32"
+    assert layer7b.n_tokens == 2048 and (layer7b.n_q_heads, layer7b.n_kv_heads) == (32, 8)
+    gf6k, ctx32k, b70 = (W.make_workload(n) for n in ("7b-32layer-6k", "7b-32layer-32k", "70b-80layer-8req"))
+    assert (gf6k.n_tokens, gf6k.n_layers) == (6144, 32)
+    assert (ctx32k.n_tokens, ctx32k.n_layers) == (32768, 32)
+    assert b70.n_requests == 8 and b70.n_layers == 80 and 57344 <= b70.n_tokens <= 73728
+    for chunk_lens in b70.chunks:
         assert 2 <= len(chunk_lens) <= 16
         assert all(256 <= n <= 4096 for n in chunk_lens)
     # deterministic draw
-    assert W.make_workload("c4").chunks == c4.chunks
+    assert W.make_workload("70b-80layer-8req").chunks == b70.chunks
 
 
 def test_delta_is_chunk_start():
-    wl = W.make_workload("c0")
+    wl = W.make_workload("tiny")
     d = wl.delta()
     assert list(d[:64]) == [0] * 64 and list(d[64:]) == [64] * 64
     assert np.array_equal(wl.positions() - d, np.tile(np.arange(64), 2))   # chunk-local p_old
 
 
 def test_generation_is_deterministic():
-    wl = W.make_workload("c0")
+    wl = W.make_workload("tiny")
     a = W.layer_inputs(wl, W.PlantedSets(wl), 0)
     b = W.layer_inputs(wl, W.PlantedSets(wl), 0)
     for key in ("k_old", "v_old", "k_new_c", "v_new_c", "q_c", "cand_idx"):
@@ -47,7 +47,7 @@ def test_generation_is_deterministic():
     assert not torch.equal(a["k_old"], c["k_old"])
 
 
-@pytest.mark.parametrize("name,layers", [("c0", [0]), ("c1", [0]), ("c2", [0, 1, 2, 5])])
+@pytest.mark.parametrize("name,layers", [("tiny", [0]), ("mistral7b-layer", [0]), ("7b-32layer-6k", [0, 1, 2, 5])])
 @pytest.mark.parametrize("schedule", ["pool", "chain"])
 def test_planted_selection_has_gap(name, layers, schedule):
     wl = W.make_workload(name)
@@ -70,7 +70,7 @@ def test_planted_selection_has_gap(name, layers, schedule):
 
 
 def test_persistence_and_pool():
-    wl = W.make_workload("c2")
+    wl = W.make_workload("7b-32layer-6k")
     sets = W.PlantedSets(wl)
     l0, l1, l2 = sets.layer(0), sets.layer(1), sets.layer(2)
     assert l0.hot.sum() == 922 and len(l0.planted) == 1844
