@@ -48,8 +48,11 @@ namespace cb {
 // fp32 partial (O, running max, running sum) to the workspace and
 // attn_combine_kernel merges them.  Unsplit units write the output directly.
 // Block order: blockIdx % Hkv is the KV head, so with Hkv = 8 the round-robin
-// dispatch over the 8 XCDs keeps each head's K/V stream in one XCD's L2; in a
-// request the last (longest) tiles start first.
+// dispatch over the 8 XCDs keeps each head's K/V stream in one XCD's L2.  In
+// a request, units go chunk by chunk and, within a chunk, from the last
+// (longest) tile to the first: the later chunks of early tiles, which lie
+// past their tile's last row and exit at once, come last and do not hold a
+// CU while a working unit waits for one.
 // ---------------------------------------------------------------------------
 struct AttnParams {
   bf16 *out;
@@ -101,8 +104,8 @@ template <int HD> __device__ constexpr int swz_v(int r) {
   else return 2 * ((r >> 1) & 1);
 }
 
-// Unit u -> (request r, tile, chunk); units of a request run from its last
-// tile to its first.  Returns false past the last unit.
+// Unit u -> (request r, tile, chunk): within a request, chunk-major, tiles
+// from last to first.  Returns false past the last unit.
 __device__ inline bool locate_unit(const AttnParams &p, int u, int &r, int &tile, int &chunk,
                                    int &nchunks) {
   int64_t ubase = 0;
@@ -114,8 +117,8 @@ __device__ inline bool locate_unit(const AttnParams &p, int u, int &r, int &tile
     const int64_t nu = (int64_t)tr * cr;
     if (u < ubase + nu) {
       const int ul = (int)(u - ubase);
-      tile = tr - 1 - ul / cr;
-      chunk = ul - (ul / cr) * cr;
+      chunk = ul / tr;
+      tile = tr - 1 - (ul - chunk * tr);
       nchunks = cr;
       return true;
     }
@@ -447,9 +450,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   const int lo = p.tok_off[r];
   const int p_last = p.sel_global[s0 + ns - 1];
   const int n_active = (p_last - lo) / p.key_chunk + 1;
-  // unit of (tile, chunk c) is ubase + (tr - 1 - tile) * cr + c
-  const float *w0 = p.ws + ((ubase + (int64_t)(tr - 1 - tile) * cr) * p.hkv + g) * UNIT;
-  const int64_t ustride = (int64_t)p.hkv * UNIT;
+  // unit of (tile, chunk c) is ubase + c * tr + (tr - 1 - tile)
+  const float *w0 = p.ws + ((ubase + (int64_t)(tr - 1 - tile)) * p.hkv + g) * UNIT;
+  const int64_t ustride = (int64_t)tr * p.hkv * UNIT;
   float mc[kMaxChunks], lc[kMaxChunks];
   f32x4 oc[kMaxChunks];
 #pragma unroll
