@@ -96,6 +96,9 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="mistral7b-layer", choices=list(DEFAULT_STEPS))
     ap.add_argument("--schedule", default="pool", choices=["pool", "chain"])
+    ap.add_argument("--dev-source", default="v", choices=["v", "k", "kv"],
+                    help="what the token deviation measures: V (default), K at the new "
+                         "position, or the K and V rows as one vector")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="budget of the CPU oracle baseline (0 disables it)")
     ap.add_argument("--attainable", type=int, default=1,
@@ -119,9 +122,10 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def algorithmic_work(wl, runner, planted_per_layer):
+def algorithmic_work(wl, runner, selected_per_layer, dev_tensors=1):
     """Per-layer algorithmic bytes / flops of each stage (what the method must
-    move or compute), from the selection actually made."""
+    move or compute), from the selection actually made.  dev_tensors: 2 when
+    the deviation reads both K and V."""
     import numpy as np
     elem = 2 if wl.dtype == "bf16" else 4
     row = wl.n_kv_heads * wl.head_dim * elem
@@ -131,21 +135,21 @@ def algorithmic_work(wl, runner, planted_per_layer):
     work = []
     for layer in range(wl.n_layers):
         m = runner.batches[layer].n_cand
-        sel = planted_per_layer[layer]
+        sel = selected_per_layer[layer]
         k = len(sel)
         req = np.searchsorted(tok_off, sel, side="right") - 1
         pos = sel - tok_off[req]
         flops = 4.0 * wl.head_dim * wl.n_q_heads * float(np.sum(pos + 1))
         work.append({
             "rerotate": 2.0 * row * nz + 4.0 * t_count,
-            "deviation_topk": 2.0 * row * m + 8.0 * m,
+            "deviation_topk": 2.0 * dev_tensors * row * m + 8.0 * m,
             "fuse_scatter": 4.0 * row * k + 8.0 * k,
             "partial_attn": flops,
         })
     return work
 
 
-def cpu_baseline(wl, seconds):
+def cpu_baseline(wl, seconds, dev_source="v"):
     """The CPU oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np
     import torch
@@ -170,7 +174,7 @@ def cpu_baseline(wl, seconds):
     t_start = time.perf_counter()
     while True:
         t0 = time.perf_counter()
-        res = O.blend_layer(**args, attend=(frac == 1))
+        res = O.blend_layer(**args, attend=(frac == 1), dev_source=dev_source)
         t1 = time.perf_counter()
         t_layer = t1 - t0
         if frac > 1:
@@ -284,7 +288,7 @@ def main():
     sets = W.PlantedSets(wl, a.schedule)
     runner = PL.BlendRunner(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.torch_dtype,
                             wl.request_lengths, wl.r1_pct, wl.r2_pct, L, wl.rope_theta,
-                            schedule=a.schedule, device="cuda")
+                            schedule=a.schedule, dev_source=a.dev_source, device="cuda")
     stream = torch.cuda.Stream()
     h = stream.cuda_stream
 
@@ -310,7 +314,8 @@ def main():
                                        rope_theta=wl.rope_theta, rope_style=B.ROPE_HALF,
                                        softmax_scale=runner.scale, dev=o["dev"],
                                        sel_local=o["sel_local"], sel_global=o["sel_global"],
-                                       out=o["out"], workspace=runner.workspace))
+                                       out=o["out"], workspace=runner.workspace,
+                                       dev_source=runner.dev_source))
         prepared.append(row)
     graph = None
     with torch.cuda.stream(stream):
@@ -343,11 +348,14 @@ def main():
     ms_per_step = ev0.elapsed_time(ev1) / steps
     wall_ms_per_step = (t1 - t0) * 1e3 / steps
     log(f"[bench] timed {steps} steps: {ms_per_step:.4f} ms/step (wall {wall_ms_per_step:.4f})")
-    planted = [sets.layer(l).planted for l in range(L)]
-    for l in range(L):
-        got = runner.outs[l]["sel_global"].cpu().numpy()
-        if not np.array_equal(got, planted[l]):
-            raise RuntimeError(f"layer {l}: selection differs from the planted set")
+    # The inputs plant the deviation tiers in V: a V score must select the
+    # planted rows.  K-based scores select other rows; the attention work is
+    # then counted on the last step's selection.
+    selected = [runner.outs[l]["sel_global"].cpu().numpy() for l in range(L)]
+    if a.dev_source == "v":
+        for l in range(L):
+            if not np.array_equal(selected[l], sets.layer(l).planted):
+                raise RuntimeError(f"layer {l}: selection differs from the planted set")
     del prepared, copies
     torch.cuda.empty_cache()
 
@@ -375,9 +383,10 @@ def main():
                 (lib.cb_rerotate, (gref, k_ptr, k_ptr, x["delta"].data_ptr(), wl.n_tokens, 1,
                                    wl.rope_theta, B.ROPE_HALF, h)))
             stage_calls["deviation_topk"][l].append(
-                (lib.cb_deviation_topk, (gref, ctypes.byref(rgs[l]), x["v_new_c"].data_ptr(),
-                                         v_ptr, cand.data_ptr(), dev_t.data_ptr(), sl.data_ptr(),
-                                         sg.data_ptr(), h)))
+                (lib.cb_kv_deviation_topk, (gref, ctypes.byref(rgs[l]), runner.dev_source,
+                                            x["k_new_c"].data_ptr(), k_ptr,
+                                            x["v_new_c"].data_ptr(), v_ptr, cand.data_ptr(),
+                                            dev_t.data_ptr(), sl.data_ptr(), sg.data_ptr(), h)))
             stage_calls["fuse_scatter"][l].append(
                 (lib.cb_fuse_scatter, (gref, k_ptr, v_ptr, x["k_new_c"].data_ptr(),
                                        x["v_new_c"].data_ptr(), sl.data_ptr(), sg.data_ptr(),
@@ -404,7 +413,7 @@ def main():
     stage_ms = {s: sum(events[(l, s)][0].elapsed_time(events[(l, s)][1]) for l in range(L))
                 for s in STAGES}
     launches = steps * L
-    work = algorithmic_work(wl, runner, planted)
+    work = algorithmic_work(wl, runner, selected, 2 if a.dev_source == "kv" else 1)
     # every layer of every step was launched once
     stage_work = {s: steps * sum(w[s] for w in work) for s in STAGES}
     kernels = {}
@@ -452,7 +461,7 @@ def main():
     cpu = None
     if a.cpu_seconds > 0:
         log("[bench] timing the CPU oracle")
-        cpu = cpu_baseline(wl, a.cpu_seconds)
+        cpu = cpu_baseline(wl, a.cpu_seconds, a.dev_source)
 
     value = wl.n_tokens * L / (ms_per_step * 1e-3)
     # whole-step roofline: streaming bytes at the HBM peak plus attention flops
@@ -473,6 +482,7 @@ def main():
                    "layers": L, "requests": wl.n_requests, "q_heads": wl.n_q_heads,
                    "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "selection": ratio,
                    "hkvd_pct": wl.hkvd_pct, "schedule": a.schedule,
+                   "dev_source": a.dev_source,
                    "launch": "hip graph replay" if a.graph else "stream launches"},
         "roofline": roof,
         "step_roofline": step_roofline,

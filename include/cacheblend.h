@@ -62,6 +62,16 @@ typedef enum cb_rope_style {
   CB_ROPE_INTERLEAVED = 1  /* pairs (2j, 2j + 1) */
 } cb_rope_style;
 
+/* What the deviation of a candidate token measures.  V alone is the score of
+ * [Derivations, "近似解"]; [KV-blog, "核心发现： KV 偏差"] speaks of the
+ * distance between the token's whole KV vectors (cached vs recomputed).  Keys
+ * are compared at the new position: the cached key after re-rotation. */
+typedef enum cb_dev_source {
+  CB_DEV_V = 0,  /* ||V_new - V_old||^2 */
+  CB_DEV_K = 1,  /* ||K_new - K_cached||^2 */
+  CB_DEV_KV = 2  /* the K and V rows read as one vector: the sum of both */
+} cb_dev_source;
+
 /* Head geometry.  n_q_heads % n_kv_heads == 0; query head h reads KV head
  * h / (n_q_heads / n_kv_heads).  head_dim in {16, 32, 64, 128}. */
 typedef struct cb_geom {
@@ -128,6 +138,24 @@ cb_status cb_deviation_topk(const cb_geom *geom, const cb_ragged *rg,
                             const int32_t *cand_idx, float *dev,
                             int32_t *sel_local, int32_t *sel_global,
                             void *stream);
+
+/*
+ * cb_kv_deviation_topk -- cb_deviation_topk with the deviation taken on the
+ * part of the token's KV that `source` (cb_dev_source) names; same selection
+ * and output rules.
+ *
+ *   k_new_c  : [M][n_kv_heads][head_dim]  recomputed K of the candidates
+ *   k_cached : [T][n_kv_heads][head_dim]  cached K, already re-rotated to the
+ *              new positions (cb_rerotate)
+ *   v_new_c, v_old, cand_idx, dev, sel_local, sel_global : as cb_deviation_topk.
+ * The K pointers may be NULL for CB_DEV_V, the V pointers for CB_DEV_K.  An
+ * unknown source returns CB_ERR_INVALID_ARG.
+ */
+cb_status cb_kv_deviation_topk(const cb_geom *geom, const cb_ragged *rg, int32_t source,
+                               const void *k_new_c, const void *k_cached,
+                               const void *v_new_c, const void *v_old,
+                               const int32_t *cand_idx, float *dev,
+                               int32_t *sel_local, int32_t *sel_global, void *stream);
 
 /*
  * cb_topk -- the selection half of cb_deviation_topk on given fp32 scores:
@@ -204,11 +232,13 @@ typedef struct cb_layer_args {
   void *out;            /* [K][Hq][D] out */
   void *workspace;      /* optional attention workspace (see cb_partial_attn) */
   size_t workspace_bytes;
+  int32_t dev_source;   /* cb_dev_source; CB_DEV_V is the score of [Derivations] */
 } cb_layer_args;
 
 /*
  * cb_blend_layer -- one layer: cb_rerotate (in place, when delta != NULL) ->
- * cb_deviation_topk -> cb_fuse_scatter -> cb_partial_attn, all on `stream`.
+ * cb_kv_deviation_topk (keys scored after their re-rotation) ->
+ * cb_fuse_scatter -> cb_partial_attn, all on `stream`.
  * [KV-blog, "渐进式过滤机制"]: the caller runs it per layer, passing all
  * tokens as candidates at layer 1 and the surviving rows afterwards.
  */
@@ -221,7 +251,7 @@ const char *cb_last_error(void);
 /* ABI revision of this header (bumped on any incompatible change). */
 int32_t cb_abi_version(void);
 
-#define CB_ABI_VERSION 2
+#define CB_ABI_VERSION 3
 
 #ifdef __cplusplus
 }

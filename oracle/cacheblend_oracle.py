@@ -29,7 +29,9 @@ is used):
   ("interleaved" style).
 * The deviation is the squared L2 norm of the V difference over every KV head
   and every head dimension of a token ([Derivations, "近似解"]); the blog's
-  absolute-difference form ranks tokens the same way.
+  absolute-difference form ranks tokens the same way.  The blog's deviation of
+  a token's whole KV vector is also offered: on K alone, or on K and V read
+  as one vector; cached keys enter it after re-rotation (at the new position).
 * Ties in the top-k go to the lower global token index; NaN ranks above +inf.
 * Attention is causal inside a request, uses scale ``1/sqrt(D)``, and maps
   query head h to KV head ``h // (Hq // Hkv)``.
@@ -113,6 +115,56 @@ def deviation(v_new_c: np.ndarray, v_old: np.ndarray, cand_idx) -> np.ndarray:
     m = cand_idx.shape[0]
     diff = np.asarray(v_new_c, np.float64).reshape(m, -1) - \
         np.asarray(v_old, np.float64)[cand_idx].reshape(m, -1)
+    return np.sum(diff * diff, axis=1)
+
+
+# --------------------------------------------------------------------------
+# Which part of the token's KV the deviation looks at.  [KV-blog, "核心发现：
+# KV 偏差"] measures the distance between a token's whole KV vector as cached
+# (its chunk encoded alone) and as it would be with the full prefix;
+# [Derivations, "近似解"] scores V alone.  Reading taken for K: the cached key
+# is compared after re-rotation, i.e. both keys at the new position; the
+# cached key at its old position would differ by the rotation alone.
+# --------------------------------------------------------------------------
+DEV_SOURCES = ("v", "k", "kv")
+
+
+def store_as(x, dtype: str) -> np.ndarray:
+    """x as a tensor of storage type ``dtype`` keeps it ("f32" or "bf16"):
+    rounded to the nearest representable value, ties to even, as float64.
+    bf16 keeps 8 significant bits (normal range; the keys here are far from
+    its limits): x = m * 2**e with 1/2 <= |m| < 1 becomes rint(m * 2**8) * 2**(e-8)."""
+    x = np.asarray(x, np.float64)
+    if dtype == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    if dtype == "bf16":
+        m, e = np.frexp(x)
+        return np.ldexp(np.rint(m * 256.0), e - 8)
+    raise ValueError(dtype)
+
+
+def kv_deviation(source: str, *, k_new_c=None, k_cached=None, v_new_c=None, v_old=None,
+                 cand_idx=None) -> np.ndarray:
+    """Squared distance between the recomputed and the cached rows of each candidate.
+
+    source "v":  the V rows (the [Derivations] score, same as ``deviation``)
+    source "k":  the K rows; k_cached holds the cached keys at the new positions
+    source "kv": the token's K row and V row read as one vector (their concatenation)
+    """
+    if source == "v":
+        new_rows, cached_rows = [v_new_c], [v_old]
+    elif source == "k":
+        new_rows, cached_rows = [k_new_c], [k_cached]
+    elif source == "kv":
+        new_rows, cached_rows = [k_new_c, v_new_c], [k_cached, v_old]
+    else:
+        raise ValueError(source)
+    cand_idx = np.asarray(cand_idx, dtype=np.int64)
+    m = cand_idx.shape[0]
+    new_vec = np.concatenate([np.asarray(a, np.float64).reshape(m, -1) for a in new_rows], axis=1)
+    old_vec = np.concatenate([np.asarray(a, np.float64)[cand_idx].reshape(m, -1)
+                              for a in cached_rows], axis=1)
+    diff = new_vec - old_vec
     return np.sum(diff * diff, axis=1)
 
 
@@ -229,19 +281,28 @@ def candidates_for_layer(layer: int, n_tokens: int, first_sel, prev_sel, schedul
 # --------------------------------------------------------------------------
 def blend_layer(*, k_old, v_old, delta, k_new_c, v_new_c, q_c, cand_idx,
                 tok_off, cand_off, sel_counts, n_q_heads, n_kv_heads, theta,
-                style=ROPE_HALF, scale=None, attend=True):
+                style=ROPE_HALF, scale=None, attend=True, dev_source="v", cache_dtype=None):
     """Run re-rotate, deviation, top-k, fuse and partial attention for one layer.
 
     Arrays are float64 (values exactly as stored) except the int index arrays.
     tok_off[B+1] / cand_off[B+1] split tokens and candidates by request;
     sel_counts[B] is each request's k.  cand_idx holds packed (global) rows.
+    delta None means the cached keys already sit at their new positions.
+    dev_source picks what the deviation measures (see ``kv_deviation``); a key
+    deviation reads the re-rotated keys as the cache stores them (cache_dtype
+    "f32" / "bf16", rounded to nearest even; None keeps float64).
     Returns a dict with k_rot, dev, sel_local, sel_global, k_fused, v_fused, out.
     """
     head_dim = np.asarray(k_old).shape[2]
     if scale is None:
         scale = 1.0 / np.sqrt(head_dim)
-    k_rot = rerotate(k_old, delta, theta, style)
-    dev = deviation(v_new_c, v_old, cand_idx)
+    k_rot = np.asarray(k_old, np.float64) if delta is None else rerotate(k_old, delta, theta, style)
+    if dev_source == "v":
+        dev = deviation(v_new_c, v_old, cand_idx)
+    else:
+        k_cached = k_rot if cache_dtype is None else store_as(k_rot, cache_dtype)
+        dev = kv_deviation(dev_source, k_new_c=k_new_c, k_cached=k_cached, v_new_c=v_new_c,
+                           v_old=v_old, cand_idx=cand_idx)
     sel_local, sel_global, row_start = [], [], []
     cand_idx = np.asarray(cand_idx, dtype=np.int64)
     for r in range(len(tok_off) - 1):

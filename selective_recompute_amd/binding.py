@@ -20,6 +20,8 @@ LIB_PATH = os.environ.get("CB_LIBRARY") or os.path.join(
 CB_OK, CB_ERR_INVALID_ARG, CB_ERR_UNSUPPORTED, CB_ERR_HIP = 0, 1, 2, 3
 CB_DTYPE_F32, CB_DTYPE_BF16 = 0, 1
 ROPE_HALF, ROPE_INTERLEAVED = 0, 1
+CB_DEV_V, CB_DEV_K, CB_DEV_KV = 0, 1, 2
+DEV_SOURCES = {"v": CB_DEV_V, "k": CB_DEV_K, "kv": CB_DEV_KV}
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 
@@ -45,7 +47,8 @@ class LayerArgs(ctypes.Structure):
                 ("rope_style", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
                 ("dev", ctypes.c_void_p), ("sel_local", ctypes.c_void_p),
                 ("sel_global", ctypes.c_void_p), ("out", ctypes.c_void_p),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("dev_source", ctypes.c_int32)]
 
 
 class CbError(RuntimeError):
@@ -63,6 +66,10 @@ _SIGNATURES = {
     "cb_deviation_topk": [ctypes.POINTER(Geom), ctypes.POINTER(Ragged), ctypes.c_void_p,
                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                           ctypes.c_void_p, ctypes.c_void_p],
+    "cb_kv_deviation_topk": [ctypes.POINTER(Geom), ctypes.POINTER(Ragged), ctypes.c_int32,
+                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                             ctypes.c_void_p],
     "cb_topk": [ctypes.POINTER(Ragged), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                 ctypes.c_void_p, ctypes.c_void_p],
     "cb_fuse_scatter": [ctypes.POINTER(Geom), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -184,6 +191,16 @@ def deviation_topk(g: Geom, rb: RaggedBatch, v_new_c, v_old, cand_idx, dev, sel_
                                   _stream(stream)))
 
 
+def kv_deviation_topk(g: Geom, rb: RaggedBatch, source: int, k_new_c, k_cached, v_new_c, v_old,
+                      cand_idx, dev, sel_local, sel_global, stream=None):
+    rg = rb.struct()
+    check(lib().cb_kv_deviation_topk(ctypes.byref(g), ctypes.byref(rg), source, _dev(k_new_c),
+                                     _dev(k_cached), _dev(v_new_c), _dev(v_old),
+                                     _dev(cand_idx, torch.int32), _dev(dev, torch.float32),
+                                     _dev(sel_local, torch.int32), _dev(sel_global, torch.int32),
+                                     _stream(stream)))
+
+
 def topk(rb: RaggedBatch, dev, cand_idx, sel_local, sel_global, stream=None):
     rg = rb.struct()
     check(lib().cb_topk(ctypes.byref(rg), _dev(dev, torch.float32), _dev(cand_idx, torch.int32),
@@ -229,12 +246,13 @@ def partial_attn(g: Geom, rb: RaggedBatch, out, q_c, sel_local, sel_global, k_fu
 
 def blend_layer(g: Geom, rb: RaggedBatch, *, k, v, k_new_c, v_new_c, q_c, delta, cand_idx,
                 rope_theta: float, rope_style: int, softmax_scale: float, dev, sel_local,
-                sel_global, out, workspace: Optional[torch.Tensor] = None, stream=None):
+                sel_global, out, workspace: Optional[torch.Tensor] = None,
+                dev_source: int = CB_DEV_V, stream=None):
     args = LayerArgs(g, rb.struct(), _dev(k), _dev(v), _dev(k_new_c), _dev(v_new_c), _dev(q_c),
                      _dev(delta, torch.int32), _dev(cand_idx, torch.int32), rope_theta,
                      rope_style, softmax_scale, _dev(dev, torch.float32),
                      _dev(sel_local, torch.int32), _dev(sel_global, torch.int32), _dev(out),
-                     *_ws(workspace))
+                     *_ws(workspace), dev_source)
     check(lib().cb_blend_layer(ctypes.byref(args), _stream(stream)))
 
 
@@ -244,14 +262,14 @@ class PreparedLayer:
 
     def __init__(self, g: Geom, rb: RaggedBatch, *, k, v, k_new_c, v_new_c, q_c, delta,
                  cand_idx, rope_theta, rope_style, softmax_scale, dev, sel_local, sel_global,
-                 out, workspace: Optional[torch.Tensor] = None):
+                 out, workspace: Optional[torch.Tensor] = None, dev_source: int = CB_DEV_V):
         self._keep = (rb, k, v, k_new_c, v_new_c, q_c, delta, cand_idx, dev, sel_local,
                       sel_global, out, workspace)
         self.args = LayerArgs(g, rb.struct(), _dev(k), _dev(v), _dev(k_new_c), _dev(v_new_c),
                               _dev(q_c), _dev(delta, torch.int32), _dev(cand_idx, torch.int32),
                               rope_theta, rope_style, softmax_scale, _dev(dev, torch.float32),
                               _dev(sel_local, torch.int32), _dev(sel_global, torch.int32),
-                              _dev(out), *_ws(workspace))
+                              _dev(out), *_ws(workspace), dev_source)
         self.ref = ctypes.byref(self.args)
 
     def launch(self, stream_handle: int):

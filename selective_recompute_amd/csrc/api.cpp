@@ -161,19 +161,40 @@ cb::RopeTable rope_table(int head_dim, double theta) {
   return t;
 }
 
-cb_status validate_devtopk(const cb_geom *geom, const cb_ragged *rg, const void *v_new_c,
+cb_status validate_devtopk(const cb_geom *geom, const cb_ragged *rg, int32_t source,
+                           const void *k_new_c, const void *k_cached, const void *v_new_c,
                            const void *v_old, const int32_t *cand_idx, const float *dev,
                            const int32_t *sel_local, const int32_t *sel_global) {
   CB_TRY(check_geom(geom));
   CB_TRY(check_ragged(rg, true, true, true));
+  if (source != CB_DEV_V && source != CB_DEV_K && source != CB_DEV_KV)
+    return fail(CB_ERR_INVALID_ARG, "deviation source %d unknown", source);
   const int32_t m = rg->h_cand_off[rg->n_req], k = rg->h_sel_off[rg->n_req];
-  CB_TRY(need_ptr(v_new_c, "v_new_c", m > 0));
-  CB_TRY(need_ptr(v_old, "v_old", m > 0));
+  const bool uses_k = source != CB_DEV_V, uses_v = source != CB_DEV_K;
+  CB_TRY(need_ptr(k_new_c, "k_new_c", m > 0 && uses_k));
+  CB_TRY(need_ptr(k_cached, "k_cached", m > 0 && uses_k));
+  CB_TRY(need_ptr(v_new_c, "v_new_c", m > 0 && uses_v));
+  CB_TRY(need_ptr(v_old, "v_old", m > 0 && uses_v));
   CB_TRY(need_idx(cand_idx, "cand_idx", m > 0));
   CB_TRY(need_idx(dev, "dev", m > 0));
   CB_TRY(need_idx(sel_local, "sel_local", k > 0));
   CB_TRY(need_idx(sel_global, "sel_global", k > 0));
   return CB_OK;
+}
+
+// The deviation launch of a validated source: one tensor pair, or K then V.
+hipError_t launch_dev_source(const cb_geom *geom, int32_t source, const void *k_new_c,
+                             const void *k_cached, const void *v_new_c, const void *v_old,
+                             const int32_t *cand_idx, float *dev, int64_t m, hipStream_t s) {
+  const int32_t re = (int32_t)row_elems(geom);
+  if (source == CB_DEV_V)
+    return cb::launch_deviation(geom->dtype, v_new_c, v_old, nullptr, nullptr, cand_idx, dev, m,
+                                re, s);
+  if (source == CB_DEV_K)
+    return cb::launch_deviation(geom->dtype, k_new_c, k_cached, nullptr, nullptr, cand_idx, dev,
+                                m, re, s);
+  return cb::launch_deviation(geom->dtype, k_new_c, k_cached, v_new_c, v_old, cand_idx, dev, m,
+                              re, s);
 }
 
 cb_status validate_topk(const cb_ragged *rg, const float *dev, const int32_t *cand_idx,
@@ -309,20 +330,30 @@ CB_EXPORT cb_status cb_rerotate(const cb_geom *geom, void *k_out, const void *k_
                     "rerotate");
 }
 
-CB_EXPORT cb_status cb_deviation_topk(const cb_geom *geom, const cb_ragged *rg,
-                                      const void *v_new_c, const void *v_old,
-                                      const int32_t *cand_idx, float *dev, int32_t *sel_local,
-                                      int32_t *sel_global, void *stream) {
+CB_EXPORT cb_status cb_kv_deviation_topk(const cb_geom *geom, const cb_ragged *rg,
+                                         int32_t source, const void *k_new_c,
+                                         const void *k_cached, const void *v_new_c,
+                                         const void *v_old, const int32_t *cand_idx, float *dev,
+                                         int32_t *sel_local, int32_t *sel_global, void *stream) {
   g_last_error.clear();
-  CB_TRY(validate_devtopk(geom, rg, v_new_c, v_old, cand_idx, dev, sel_local, sel_global));
+  CB_TRY(validate_devtopk(geom, rg, source, k_new_c, k_cached, v_new_c, v_old, cand_idx, dev,
+                          sel_local, sel_global));
   const int32_t m = rg->h_cand_off[rg->n_req];
-  CB_TRY(hip_status(cb::launch_deviation(geom->dtype, v_new_c, v_old, cand_idx, dev, m,
-                                         (int32_t)row_elems(geom), (hipStream_t)stream),
+  CB_TRY(hip_status(launch_dev_source(geom, source, k_new_c, k_cached, v_new_c, v_old, cand_idx,
+                                      dev, m, (hipStream_t)stream),
                     "deviation"));
   if (rg->h_sel_off[rg->n_req] == 0) return CB_OK;
   return hip_status(cb::launch_topk(rg->n_req, dev, cand_idx, rg->cand_off, rg->sel_off,
                                     sel_local, sel_global, max_cand(rg), (hipStream_t)stream),
                     "topk");
+}
+
+CB_EXPORT cb_status cb_deviation_topk(const cb_geom *geom, const cb_ragged *rg,
+                                      const void *v_new_c, const void *v_old,
+                                      const int32_t *cand_idx, float *dev, int32_t *sel_local,
+                                      int32_t *sel_global, void *stream) {
+  return cb_kv_deviation_topk(geom, rg, CB_DEV_V, nullptr, nullptr, v_new_c, v_old, cand_idx,
+                              dev, sel_local, sel_global, stream);
 }
 
 CB_EXPORT cb_status cb_topk(const cb_ragged *rg, const float *dev, const int32_t *cand_idx,
@@ -382,8 +413,8 @@ CB_EXPORT cb_status cb_blend_layer(const cb_layer_args *a, void *stream) {
   const int64_t n_tok = rg->h_tok_off[rg->n_req];
   if (a->delta)
     CB_TRY(validate_rerotate(geom, a->k, a->k, a->delta, n_tok, 1, a->rope_theta, a->rope_style));
-  CB_TRY(validate_devtopk(geom, rg, a->v_new_c, a->v, a->cand_idx, a->dev, a->sel_local,
-                          a->sel_global));
+  CB_TRY(validate_devtopk(geom, rg, a->dev_source, a->k_new_c, a->k, a->v_new_c, a->v,
+                          a->cand_idx, a->dev, a->sel_local, a->sel_global));
   const int32_t k_total = rg->h_sel_off[rg->n_req];
   CB_TRY(validate_fuse(geom, a->k, a->v, a->k_new_c, a->v_new_c, a->sel_local, a->sel_global,
                        k_total));
@@ -392,9 +423,10 @@ CB_EXPORT cb_status cb_blend_layer(const cb_layer_args *a, void *stream) {
   CB_TRY(need_ptr(a->workspace, "workspace", a->workspace_bytes > 0));
   const hipStream_t s = (hipStream_t)stream;
   const int32_t m = rg->h_cand_off[rg->n_req];
-  if (a->delta && n_tok > 0 &&
+  if (a->dev_source == CB_DEV_V && a->delta && n_tok > 0 &&
       cb::rerotate_deviation_fits(geom->dtype, geom->n_kv_heads, geom->head_dim)) {
-    // independent K and V work in one launch
+    // independent K and V work in one launch (a key deviation instead reads
+    // the re-rotated keys, so it follows the re-rotation)
     CB_TRY(hip_status(cb::launch_rerotate_deviation(
                           geom->dtype, a->rope_style, a->k, a->delta, n_tok, geom->n_kv_heads,
                           geom->head_dim, rope_table(geom->head_dim, a->rope_theta), a->v_new_c,
@@ -406,8 +438,8 @@ CB_EXPORT cb_status cb_blend_layer(const cb_layer_args *a, void *stream) {
                                             n_tok, 1, geom->n_kv_heads, geom->head_dim,
                                             rope_table(geom->head_dim, a->rope_theta), s),
                         "rerotate"));
-    CB_TRY(hip_status(cb::launch_deviation(geom->dtype, a->v_new_c, a->v, a->cand_idx, a->dev,
-                                           m, (int32_t)row_elems(geom), s),
+    CB_TRY(hip_status(launch_dev_source(geom, a->dev_source, a->k_new_c, a->k, a->v_new_c, a->v,
+                                        a->cand_idx, a->dev, m, s),
                       "deviation"));
   }
   if (k_total == 0) return CB_OK;

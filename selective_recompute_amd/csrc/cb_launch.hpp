@@ -30,8 +30,11 @@ hipError_t launch_rerotate_deviation(int dtype, int style, void *k, const int32_
                                      const void *v_old, const int32_t *cand_idx, float *dev,
                                      int64_t m, hipStream_t stream);
 
-hipError_t launch_deviation(int dtype, const void *v_new_c, const void *v_old,
-                            const int32_t *cand_idx, float *dev, int64_t m,
+// dev[j] = squared distance of row j of new0 and row cand_idx[j] of old0,
+// plus the same for new1 / old1 when new1 is not NULL (the K and V rows of a
+// token read as one vector).
+hipError_t launch_deviation(int dtype, const void *new0, const void *old0, const void *new1,
+                            const void *old1, const int32_t *cand_idx, float *dev, int64_t m,
                             int32_t row_elems, hipStream_t stream);
 
 // max_m: the largest candidate count of any request (host mirror).

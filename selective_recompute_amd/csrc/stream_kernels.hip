@@ -162,44 +162,55 @@ hipError_t launch_rerotate(int dtype, int style, void *k_out, const void *k_in,
 
 // ---------------------------------------------------------------------------
 // Deviation, [Derivations, "近似解"]: dev[j] = ||V_new_c[j] - V_old[cand[j]]||^2
-// over all KV heads and dims.  One wave per candidate row, 16-byte loads,
-// fp32 fused multiply-add accumulation, butterfly reduction across the wave.
+// over all KV heads and dims.  [KV-blog, "核心发现： KV 偏差"] measures the
+// token's whole KV vector: with NT = 2 the wave adds the squared distance of a
+// second pair of tensors (K, the cached keys already at the new position) to
+// the same sum.  One wave per candidate row, 16-byte loads, fp32 fused
+// multiply-add accumulation, butterfly reduction across the wave.
 // ---------------------------------------------------------------------------
 template <typename T>
-__device__ inline void deviation_block(const T *__restrict__ v_new_c, const T *__restrict__ v_old,
+__device__ inline float sq_dist_share(const T *__restrict__ a, const T *__restrict__ b, int lane,
+                                      int nvec, float acc) {
+  constexpr int V = Vec16<T>::N;
+  for (int v = lane; v < nvec; v += kWave) {
+    float x[V], y[V];
+    Vec16<T>::load(a + v * V, x);
+    Vec16<T>::load(b + v * V, y);
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const float df = x[i] - y[i];
+      acc = fmaf(df, df, acc);
+    }
+  }
+  return acc;
+}
+
+template <typename T, int NT>
+__device__ inline void deviation_block(const T *__restrict__ new0, const T *__restrict__ old0,
+                                       const T *__restrict__ new1, const T *__restrict__ old1,
                                        const int32_t *__restrict__ cand_idx,
                                        float *__restrict__ dev, int64_t m, int32_t row_elems,
                                        int64_t block, int64_t n_blocks) {
-  constexpr int V = Vec16<T>::N;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = (block * blockDim.x + threadIdx.x) / kWave;
   const int64_t n_waves = (n_blocks * blockDim.x) / kWave;
-  const int nvec = row_elems / V;
+  const int nvec = row_elems / Vec16<T>::N;
   for (int64_t j = wave; j < m; j += n_waves) {
-    const T *a = v_new_c + j * row_elems;
-    const T *b = v_old + (int64_t)cand_idx[j] * row_elems;
-    float acc = 0.f;
-    for (int v = lane; v < nvec; v += kWave) {
-      float x[V], y[V];
-      Vec16<T>::load(a + v * V, x);
-      Vec16<T>::load(b + v * V, y);
-#pragma unroll
-      for (int i = 0; i < V; ++i) {
-        const float df = x[i] - y[i];
-        acc = fmaf(df, df, acc);
-      }
-    }
+    const int64_t c = cand_idx[j];
+    float acc = sq_dist_share(new0 + j * row_elems, old0 + c * row_elems, lane, nvec, 0.f);
+    if (NT == 2) acc = sq_dist_share(new1 + j * row_elems, old1 + c * row_elems, lane, nvec, acc);
     acc = wave_sum(acc);
     if (lane == 0) dev[j] = acc;
   }
 }
 
-template <typename T>
+template <typename T, int NT>
 __global__ __launch_bounds__(256) void deviation_kernel(
-    const T *__restrict__ v_new_c, const T *__restrict__ v_old,
-    const int32_t *__restrict__ cand_idx, float *__restrict__ dev, int64_t m,
-    int32_t row_elems) {
-  deviation_block<T>(v_new_c, v_old, cand_idx, dev, m, row_elems, blockIdx.x, gridDim.x);
+    const T *__restrict__ new0, const T *__restrict__ old0, const T *__restrict__ new1,
+    const T *__restrict__ old1, const int32_t *__restrict__ cand_idx, float *__restrict__ dev,
+    int64_t m, int32_t row_elems) {
+  deviation_block<T, NT>(new0, old0, new1, old1, cand_idx, dev, m, row_elems, blockIdx.x,
+                         gridDim.x);
 }
 
 static int64_t deviation_blocks(int64_t m) {
@@ -207,17 +218,29 @@ static int64_t deviation_blocks(int64_t m) {
   return blocks > 8192 ? 8192 : blocks;
 }
 
-hipError_t launch_deviation(int dtype, const void *v_new_c, const void *v_old,
-                            const int32_t *cand_idx, float *dev, int64_t m,
+template <typename T>
+static void deviation_typed(const void *new0, const void *old0, const void *new1,
+                            const void *old1, const int32_t *cand_idx, float *dev, int64_t m,
+                            int32_t row_elems, hipStream_t stream) {
+  const dim3 grid((unsigned)deviation_blocks(m)), block(256);
+  if (new1)
+    hipLaunchKernelGGL((deviation_kernel<T, 2>), grid, block, 0, stream, (const T *)new0,
+                       (const T *)old0, (const T *)new1, (const T *)old1, cand_idx, dev, m,
+                       row_elems);
+  else
+    hipLaunchKernelGGL((deviation_kernel<T, 1>), grid, block, 0, stream, (const T *)new0,
+                       (const T *)old0, (const T *)nullptr, (const T *)nullptr, cand_idx, dev, m,
+                       row_elems);
+}
+
+hipError_t launch_deviation(int dtype, const void *new0, const void *old0, const void *new1,
+                            const void *old1, const int32_t *cand_idx, float *dev, int64_t m,
                             int32_t row_elems, hipStream_t stream) {
   if (m == 0) return hipSuccess;
-  const int64_t blocks = deviation_blocks(m);
   if (dtype == kBF16)
-    hipLaunchKernelGGL(deviation_kernel<bf16>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const bf16 *)v_new_c, (const bf16 *)v_old, cand_idx, dev, m, row_elems);
+    deviation_typed<bf16>(new0, old0, new1, old1, cand_idx, dev, m, row_elems, stream);
   else
-    hipLaunchKernelGGL(deviation_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const float *)v_new_c, (const float *)v_old, cand_idx, dev, m, row_elems);
+    deviation_typed<float>(new0, old0, new1, old1, cand_idx, dev, m, row_elems, stream);
   return hipGetLastError();
 }
 
@@ -234,8 +257,8 @@ __global__ __launch_bounds__(256) void rerotate_deviation_kernel(
   if ((int64_t)blockIdx.x < rot_blocks)
     rerotate_block<T, STYLE>(k, k, delta, gm, tab, blockIdx.x);
   else
-    deviation_block<T>(v_new_c, v_old, cand_idx, dev, m, row_elems, blockIdx.x - rot_blocks,
-                       gridDim.x - rot_blocks);
+    deviation_block<T, 1>(v_new_c, v_old, nullptr, nullptr, cand_idx, dev, m, row_elems,
+                          blockIdx.x - rot_blocks, gridDim.x - rot_blocks);
 }
 
 template <typename T, int STYLE>

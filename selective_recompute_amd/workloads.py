@@ -45,7 +45,7 @@ SIGMA_HOT = 1.0
 SIGMA_WARM = 0.1
 SIGMA_COLD = 0.01
 
-_TID = {"k_old": 1, "v_old": 2, "k_new": 3, "v_noise": 4, "q": 5}
+_TID = {"k_old": 1, "v_old": 2, "k_new": 3, "v_noise": 4, "q": 5, "k_noise": 6}
 
 
 @dataclass(frozen=True)
@@ -225,10 +225,17 @@ def _randn(shape, seed: int, device) -> torch.Tensor:
     return torch.randn(shape, generator=g, device=device, dtype=torch.float32)
 
 
-def layer_inputs(wl: Workload, sets: PlantedSets, layer: int, device="cpu", draw: int = 0) -> dict:
+def layer_inputs(wl: Workload, sets: PlantedSets, layer: int, device="cpu", draw: int = 0,
+                 k_new: str = "independent") -> dict:
     """Tensors of one layer on ``device``: cached K/V, recomputed candidate rows,
     their queries and the index arrays.  ``draw`` selects an independent copy
-    with the same planted structure."""
+    with the same planted structure.
+
+    k_new "independent": K_new_c ~ N(0,1).  k_new "tied": K_new_c[j] =
+    K_old[C[j]] + sigma * N(0,1) with the same tiers as V, i.e. the recomputed
+    key sits next to the cached one: meant for caches whose keys already are
+    at their new positions (no re-rotation), where a key-based deviation then
+    has the same planted gap as the V one."""
     s = sets.layer(layer)
     t_count, m = wl.n_tokens, len(s.cand_idx)
     hkv, hq, d = wl.n_kv_heads, wl.n_q_heads, wl.head_dim
@@ -243,7 +250,14 @@ def layer_inputs(wl: Workload, sets: PlantedSets, layer: int, device="cpu", draw
     noise = _randn((m, hkv, d), _seed(wl, layer, "v_noise", draw), device)
     v_new_c = (v_old.index_select(0, cand_t).float() + sig_c * noise).to(dt)
     del noise
-    k_new_c = _randn((m, hkv, d), _seed(wl, layer, "k_new", draw), device).to(dt)
+    if k_new == "independent":
+        k_new_c = _randn((m, hkv, d), _seed(wl, layer, "k_new", draw), device).to(dt)
+    elif k_new == "tied":
+        noise = _randn((m, hkv, d), _seed(wl, layer, "k_noise", draw), device)
+        k_new_c = (k_old.index_select(0, cand_t).float() + sig_c * noise).to(dt)
+        del noise
+    else:
+        raise ValueError(k_new)
     q_c = _randn((m, hq, d), _seed(wl, layer, "q", draw), device).to(dt)
     i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
     return dict(

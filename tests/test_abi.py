@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
             "cb_blend_layer"} <= declared
     for name in sorted(declared):
         assert hasattr(lib, name), name
-    assert lib.cb_abi_version() == 2
+    assert lib.cb_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -114,6 +114,27 @@ def test_deviation_topk_pointer_errors(lib):
     assert st == 1 and "dev" in lib.cb_last_error().decode()
 
 
+def test_kv_deviation_source_errors(lib):
+    """The source decides which tensors are needed; an unknown source is an
+    argument error; V alone (source 0) needs no K pointer and K alone none of V."""
+    rg, keep = _ragged([0, 10], [0, 10], [0, 3])
+    g = _geom()
+
+    def call(source, k_new=P, k_cached=P, v_new=P, v_old=P, dev=P):
+        return lib.cb_kv_deviation_topk(ctypes.byref(g), ctypes.byref(rg), source, k_new,
+                                        k_cached, v_new, v_old, P, dev, P, P, None)
+    assert call(3) == 1 and "source" in lib.cb_last_error().decode()
+    assert call(-1) == 1
+    assert call(B.CB_DEV_K, k_cached=None) == 1 and "k_cached" in lib.cb_last_error().decode()
+    assert call(B.CB_DEV_KV, k_new=MISALIGNED) == 1 and "aligned" in lib.cb_last_error().decode()
+    assert call(B.CB_DEV_KV, v_old=None) == 1 and "v_old" in lib.cb_last_error().decode()
+    assert call(B.CB_DEV_K, dev=None) == 1 and "dev" in lib.cb_last_error().decode()
+    # no candidates: nothing to read, nothing launched
+    rg0, keep0 = _ragged([0, 10], [0, 0], [0, 0])
+    assert lib.cb_kv_deviation_topk(ctypes.byref(g), ctypes.byref(rg0), B.CB_DEV_KV, None, None,
+                                    None, None, None, None, None, None, None) == 0
+
+
 def test_fuse_and_attention_errors(lib):
     g = _geom()
     assert lib.cb_fuse_scatter(ctypes.byref(g), P, P, P, P, P, P, -1, None) == 1
@@ -139,7 +160,7 @@ def test_blend_layer_validates_every_stage_first(lib):
     # a bad field of the LAST stage still fails before anything is enqueued
     for field, value, status in [("out", None, 1), ("softmax_scale", -1.0, 1),
                                  ("rope_style", 3, 1), ("cand_idx", None, 1),
-                                 ("workspace_bytes", 1024, 1),
+                                 ("workspace_bytes", 1024, 1), ("dev_source", 7, 1),
                                  ("geom", B.Geom(32, 8, 128, 9), 2)]:
         args = dict(good)
         args[field] = value

@@ -156,6 +156,85 @@ def test_deviation_special_cases():
     assert np.allclose(d1, np.linalg.norm(eps.reshape(4, -1), axis=1) ** 2, rtol=1e-12)
 
 
+@pytest.mark.parametrize("style", STYLES)
+def test_key_deviation_compares_at_the_new_position(style):
+    # [KV-blog, "核心发现： KV 偏差"]: the deviation of a token's KV compares
+    # the cached vector with the recomputed one.  Keys are compared after
+    # re-rotation: a key whose content did not change scores exactly zero up
+    # to rounding, although it differs from the cached key at its old position.
+    theta, hkv, head_dim = 10000.0, 2, 32
+    chunk_lens = [16, 16, 32]
+    t = sum(chunk_lens)
+    p_old = np.concatenate([np.arange(n) for n in chunk_lens])
+    p_new = np.arange(t)
+    k_base, v_old = _randn(t, hkv, head_dim), _randn(t, hkv, head_dim)
+    k_old = O.rotate(k_base, p_old, theta, style)
+    k_new = O.rotate(k_base, p_new, theta, style)
+    cand = np.arange(t)
+    out = O.blend_layer(k_old=k_old, v_old=v_old, delta=p_new - p_old, k_new_c=k_new,
+                        v_new_c=v_old.copy(), q_c=_randn(t, hkv, head_dim), cand_idx=cand,
+                        tok_off=[0, t], cand_off=[0, t], sel_counts=[4], n_q_heads=hkv,
+                        n_kv_heads=hkv, theta=theta, style=style, attend=False, dev_source="k")
+    assert np.max(out["dev"]) < 1e-20
+    unrotated = O.kv_deviation("k", k_new_c=k_new, k_cached=k_old, cand_idx=cand)
+    assert np.all(unrotated[16:] > 1e-3) and np.max(unrotated[:16]) < 1e-20   # chunk 0: delta 0
+    # Comparing at the new position equals comparing at the old one (rotations
+    # keep distances): ||K_new - R_d K_old||^2 = ||R_{-d} K_new - K_old||^2.
+    k_other = _randn(t, hkv, head_dim)
+    d = p_new - p_old
+    at_new = O.kv_deviation("k", k_new_c=k_other, k_cached=O.rerotate(k_old, d, theta, style),
+                            cand_idx=cand)
+    at_old = O.kv_deviation("k", k_new_c=O.rotate(k_other, -d, theta, style), k_cached=k_old,
+                            cand_idx=cand)
+    assert np.allclose(at_new, at_old, rtol=1e-12)
+
+
+def test_kv_deviation_reads_the_kv_row_as_one_vector():
+    k_cached, v_old = _randn(12, 3, 8), _randn(12, 3, 8)
+    cand = np.array([11, 0, 6, 3, 8])
+    k_new, v_new = k_cached[cand].copy(), v_old[cand].copy()
+    # one changed K element and one changed V element, in different candidates
+    k_new[1, 2, 5] += 1.5
+    v_new[3, 0, 0] -= 0.25
+    args = dict(k_new_c=k_new, k_cached=k_cached, v_new_c=v_new, v_old=v_old, cand_idx=cand)
+    dk, dv, dkv = (O.kv_deviation(s, **args) for s in ("k", "v", "kv"))
+    assert dv[3] == pytest.approx(0.0625, rel=1e-12) and np.all(np.delete(dv, 3) == 0.0)
+    assert dk[1] == pytest.approx(2.25, rel=1e-12) and np.all(np.delete(dk, 1) == 0.0)
+    assert np.array_equal(dkv, dk + dv)
+    # random rows: "kv" is the squared norm of the concatenated difference,
+    # "v" is the V-only score used elsewhere
+    k_new, v_new = _randn(5, 3, 8), _randn(5, 3, 8)
+    args.update(k_new_c=k_new, v_new_c=v_new)
+    joint = np.concatenate([(k_new - k_cached[cand]).reshape(5, -1),
+                            (v_new - v_old[cand]).reshape(5, -1)], axis=1)
+    assert np.allclose(O.kv_deviation("kv", **args), np.linalg.norm(joint, axis=1) ** 2, rtol=1e-12)
+    assert np.array_equal(O.kv_deviation("v", **args), O.deviation(v_new, v_old, cand))
+    with pytest.raises(ValueError):
+        O.kv_deviation("q", **args)
+
+
+def test_store_as_rounds_to_nearest_even():
+    import torch
+    # hand cases around 1: bf16 steps by 2^-7 there
+    one = 1.0
+    cases = {one + 2 ** -8: one,                      # tie, 1.0 is even
+             one + 3 * 2 ** -8: one + 2 ** -6,        # tie, 1 + 2^-6 is even
+             one + 2 ** -8 + 2 ** -20: one + 2 ** -7,  # just above the tie
+             -(one + 2 ** -8 - 2 ** -30): -one,        # just below the tie
+             0.0: 0.0, 3.0: 3.0, -0.15625: -0.15625}
+    for x, want in cases.items():
+        assert O.store_as(np.array([x]), "bf16")[0] == want, x
+    # float32 inputs: torch's fp32 -> bf16 conversion rounds to nearest even
+    rng = np.random.default_rng(3)
+    x32 = (rng.standard_normal(20000) * np.exp(rng.uniform(-8, 8, 20000))).astype(np.float32)
+    bits = x32.view(np.uint32) & np.uint32(0xFFFF0000)
+    ties = (bits | np.uint32(0x8000)).view(np.float32)[:2000]        # exact halfway values
+    x32 = np.concatenate([x32, ties])
+    ref = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.store_as(x32.astype(np.float64), "bf16"), ref)
+    assert np.array_equal(O.store_as(x32.astype(np.float64), "f32"), x32.astype(np.float64))
+
+
 # ------------------------------------------------------------------- top-k --
 def _brute_force_topk(dev, cand, k):
     best, best_tuple = None, None

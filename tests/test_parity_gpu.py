@@ -121,6 +121,121 @@ def test_deviation_topk_parity(name, layer):
         assert np.array_equal(sl[sel_off[r]:sel_off[r + 1]], loc + off[r])
 
 
+# ------------------------------------------------ deviation on K, or K and V --
+def _gen_device(wl):
+    return "cpu" if wl.n_tokens <= 8192 else DEV
+
+
+@pytest.mark.parametrize("source", ["k", "kv"])
+@pytest.mark.parametrize("name,layer", [("tiny", 0), ("mistral7b-layer", 0), ("7b-32layer-6k", 1),
+                                        ("70b-80layer-8req", 1)])
+def test_kv_deviation_topk_parity(source, name, layer):
+    """cb_kv_deviation_topk on tied keys with the cache at the new positions:
+    deviations to 1e-4 relative, index sets bit-exact (the tiers give the
+    same gap as for V)."""
+    say(f"kv_deviation_topk {source} {name} layer {layer}")
+    wl = W.make_workload(name)
+    x = W.layer_inputs(wl, W.PlantedSets(wl), layer, device=_gen_device(wl), k_new="tied")
+    counts = PL.GradualFilter(wl.request_lengths, wl.r1_pct, wl.r2_pct).counts(layer)
+    g = B.geom(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.torch_dtype)
+    rb = B.RaggedBatch(x["h_tok_off"], x["h_cand_off"], PL.offsets(counts), DEV)
+    dev = torch.empty(rb.n_cand, dtype=torch.float32, device=DEV)
+    sl = torch.empty(rb.n_sel, dtype=torch.int32, device=DEV)
+    sg = torch.empty(rb.n_sel, dtype=torch.int32, device=DEV)
+    B.kv_deviation_topk(g, rb, B.DEV_SOURCES[source], x["k_new_c"].to(DEV), x["k_old"].to(DEV),
+                        x["v_new_c"].to(DEV), x["v_old"].to(DEV), x["cand_idx"].to(DEV), dev, sl, sg)
+    torch.cuda.synchronize()
+    cand = npi(x["cand_idx"])
+    ref_dev = O.kv_deviation(source, k_new_c=np64(x["k_new_c"]), k_cached=np64(x["k_old"]),
+                             v_new_c=np64(x["v_new_c"]), v_old=np64(x["v_old"]), cand_idx=cand)
+    assert_dev_close(dev.cpu().numpy().astype(np.float64), ref_dev)
+    off, sel_off = x["h_cand_off"], PL.offsets(counts)
+    sl, sg = npi(sl), npi(sg)
+    for r in range(wl.n_requests):
+        loc, glob = O.topk_select(ref_dev[off[r]:off[r + 1]], cand[off[r]:off[r + 1]], counts[r])
+        assert np.array_equal(sg[sel_off[r]:sel_off[r + 1]], glob)
+        assert np.array_equal(sl[sel_off[r]:sel_off[r + 1]], loc + off[r])
+    assert np.array_equal(sg, x["planted"])
+
+
+def _blend_one_layer(wl, x, source, with_delta):
+    runner = PL.BlendRunner(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.torch_dtype,
+                            wl.request_lengths, wl.r1_pct, wl.r2_pct, 1, wl.rope_theta,
+                            dev_source=source)
+    xg = {k: (v.to(DEV) if torch.is_tensor(v) else v) for k, v in x.items()}
+    if not with_delta:
+        xg["delta"] = None
+    o = runner.run_layer(0, xg)
+    torch.cuda.synchronize()
+    return runner, xg, o
+
+
+def _oracle_args(wl, x, with_delta):
+    counts = PL.GradualFilter(wl.request_lengths, wl.r1_pct, wl.r2_pct).counts(0)
+    return dict(k_old=np64(x["k_old"]), v_old=np64(x["v_old"]),
+                delta=wl.delta() if with_delta else None, k_new_c=np64(x["k_new_c"]),
+                v_new_c=np64(x["v_new_c"]), q_c=np64(x["q_c"]), cand_idx=npi(x["cand_idx"]),
+                tok_off=wl.tok_off, cand_off=x["h_cand_off"], sel_counts=counts,
+                n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads, theta=wl.rope_theta,
+                scale=1.0 / math.sqrt(wl.head_dim))
+
+
+@pytest.mark.parametrize("source", ["k", "kv"])
+@pytest.mark.parametrize("name", ["tiny", "mistral7b-layer"])
+def test_blend_layer_key_sources_at_new_positions(source, name):
+    """cb_blend_layer with a key-based deviation on a cache whose keys already
+    sit at their new positions (delta NULL): everything against the oracle."""
+    say(f"blend {source} {name} (no re-rotation)")
+    wl = W.make_workload(name)
+    x = W.layer_inputs(wl, W.PlantedSets(wl), 0, k_new="tied")
+    runner, xg, o = _blend_one_layer(wl, x, source, with_delta=False)
+    ref = O.blend_layer(**_oracle_args(wl, x, False), dev_source=source)
+    assert_dev_close(o["dev"].cpu().numpy().astype(np.float64), ref["dev"])
+    assert np.array_equal(npi(o["sel_global"]), ref["sel_global"])
+    assert np.array_equal(npi(o["sel_local"]), ref["sel_local"])
+    assert np.array_equal(ref["sel_global"], x["planted"])
+    assert np.array_equal(np64(xg["k_old"]), ref["k_fused"])      # no rotation: bit-exact
+    assert np.array_equal(np64(xg["v_old"]), ref["v_fused"])
+    err = np.abs(np64(o["out"]) - ref["out"])
+    assert err.max() <= ATTN_ABS, f"attention max err {err.max()}"
+
+
+@pytest.mark.parametrize("source", ["k", "kv"])
+@pytest.mark.parametrize("name", ["tiny", "mistral7b-layer", "7b-32layer-6k"])
+def test_blend_layer_key_deviation_reads_rerotated_keys(source, name):
+    """With re-rotation, the key deviation compares the recomputed keys with
+    the re-rotated cache as stored.  Deviations to 1e-4 relative against the
+    oracle reading its own re-rotated keys rounded to the cache type.  With
+    independent keys the deviations have no planted gap, so near-ties may
+    order either way: the selection must be a valid top-k of the oracle's
+    deviations (every chosen score >= every other, to the same tolerance)."""
+    say(f"blend {source} {name} (after re-rotation)")
+    wl = W.make_workload(name)
+    x = W.layer_inputs(wl, W.PlantedSets(wl), 0)
+    runner, xg, o = _blend_one_layer(wl, x, source, with_delta=True)
+    ref = O.blend_layer(**_oracle_args(wl, x, True), dev_source=source, cache_dtype=wl.dtype,
+                        attend=False)
+    assert_dev_close(o["dev"].cpu().numpy().astype(np.float64), ref["dev"])
+    cand = npi(x["cand_idx"])
+    sl, sg = npi(o["sel_local"]), npi(o["sel_global"])
+    counts = runner.filter.counts(0)
+    off, sel_off = x["h_cand_off"], PL.offsets(counts)
+    for r in range(wl.n_requests):
+        loc = sl[sel_off[r]:sel_off[r + 1]] - off[r]
+        assert len(loc) == counts[r] and np.all(np.diff(loc) > 0)
+        assert np.array_equal(sg[sel_off[r]:sel_off[r + 1]], cand[off[r]:off[r + 1]][loc])
+        d = ref["dev"][off[r]:off[r + 1]]
+        rest = np.delete(d, loc)
+        if len(rest):
+            assert d[loc].min() >= rest.max() * (1 - 2 * DEV_REL)
+    # the fused keys: chosen rows are the recomputed ones, the rest re-rotated
+    kf = np64(xg["k_old"])
+    assert np.array_equal(kf[sg], np64(x["k_new_c"])[sl])
+    mask = np.ones(wl.n_tokens, bool)
+    mask[sg] = False
+    assert_k_close(kf[mask], ref["k_rot"][mask], wl.torch_dtype, "fused K")
+
+
 def test_topk_exact_ties_and_specials():
     say("topk ties / NaN / inf / k in {0, M} / ragged")
     rng = np.random.default_rng(42)

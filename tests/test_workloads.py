@@ -80,3 +80,27 @@ def test_persistence_and_pool():
     chain = W.PlantedSets(wl, "chain")
     assert np.array_equal(chain.layer(1).cand_idx, l0.planted)
     assert np.array_equal(chain.layer(2).cand_idx, chain.layer(1).planted)
+
+
+@pytest.mark.parametrize("name,layer", [("tiny", 0), ("mistral7b-layer", 0), ("7b-32layer-6k", 1)])
+@pytest.mark.parametrize("source", ["k", "kv"])
+def test_tied_keys_carry_the_planted_gap(name, layer, source):
+    """With tied keys and a cache already at the new positions, a key-based
+    deviation selects the planted rows with the same tier gap."""
+    wl = W.make_workload(name)
+    sets = W.PlantedSets(wl)
+    x = W.layer_inputs(wl, sets, layer, k_new="tied")
+    base = W.layer_inputs(wl, sets, layer)
+    for key in ("k_old", "v_old", "v_new_c", "q_c"):            # only K_new changes
+        assert torch.equal(x[key], base[key])
+    cand = x["cand_idx"].numpy().astype(np.int64)
+    dev = O.kv_deviation(source, k_new_c=_np64(x["k_new_c"]), k_cached=_np64(x["k_old"]),
+                         v_new_c=_np64(x["v_new_c"]), v_old=_np64(x["v_old"]), cand_idx=cand)
+    offs = x["h_cand_off"]
+    for r in range(wl.n_requests):
+        _, k = O.layer_plan(layer + 1, wl.request_lengths[r], wl.r1_pct, wl.r2_pct)
+        d_r = dev[offs[r]:offs[r + 1]]
+        _, glob = O.topk_select(d_r, cand[offs[r]:offs[r + 1]], k)
+        assert np.array_equal(glob, x["planted"][x["planted_off"][r]:x["planted_off"][r + 1]])
+        srt = np.sort(d_r)[::-1]
+        assert (srt[k - 1] - srt[k]) / srt[k - 1] > 1e-3
