@@ -6,7 +6,9 @@
 #include <cstdint>
 #include <algorithm>
 #include <cstdio>
+#include <queue>
 #include <string>
+#include <vector>
 
 #include "cacheblend.h"
 #include "cb_launch.hpp"
@@ -245,10 +247,71 @@ cb_status validate_attn(const cb_geom *geom, const cb_ragged *rg, void *out, con
 
 constexpr int kNoSplit = 1 << 30;
 
+// Cost model of one MFMA attention launch, for choosing the key chunk.  The
+// figures were measured on MI355X at head_dim 128 (they scale with head_dim):
+// one 64-key tile of a 256-query unit takes ~2.1 us with every CU busy, a
+// workgroup spends ~3.6 us before its first tile (three dependent loads:
+// request offsets, selected rows, Q) and ~1 us writing an fp32 partial; the
+// combine launch costs ~3 us plus its partials read at ~4.5 TB/s.
+constexpr double kTileUs = 2.1, kSetupUs = 3.6, kPartialUs = 1.0, kCombineUs = 3.0;
+constexpr double kCombineBytesPerUs = 4.5e6;
+// CUs the simulated dispatch fills: 240 of the 256, a margin against plans
+// that fit one more round only if the selected rows sit exactly as assumed.
+constexpr int kSimCUs = 240;
+
+// Estimated duration (us) of the launch with key chunk `kc` (kNoSplit: none),
+// and the number of units that do work.  The selected rows of a request are
+// taken as evenly spread over its tokens, so query tile t ends near position
+// min(k, (t+1) rows) * n / k.  Units are dispatched in the kernel's order
+// (request by request, chunk by chunk, longest tile first), each to the
+// earliest free group of CUs; the n_kv_heads workgroups of a unit run side by
+// side, so one "slot" stands for n_kv_heads CUs.
+double estimate_attn_us(const cb_geom *g, const cb_ragged *rg, int rows, int64_t kc,
+                        int64_t *active) {
+  const int n_slots = std::max(1, kSimCUs / g->n_kv_heads);
+  const double tile_us = kTileUs * g->head_dim / 128.0;
+  std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
+  for (int i = 0; i < n_slots; ++i) free_at.push(0.0);
+  bool split = false;
+  int64_t busy = 0;
+  for (int32_t r = 0; r < rg->n_req; ++r) {
+    const int64_t k = rg->h_sel_off[r + 1] - rg->h_sel_off[r];
+    const int64_t n = rg->h_tok_off[r + 1] - rg->h_tok_off[r];
+    if (k == 0) continue;
+    const int64_t tiles = (k + rows - 1) / rows;
+    const int64_t chunks = (n + kc - 1) / kc;
+    if (chunks > 1) split = true;
+    for (int64_t c = 0; c < chunks; ++c)
+      for (int64_t t = tiles - 1; t >= 0; --t) {
+        const int64_t end = (std::min(k, (t + 1) * rows) * n + k - 1) / k;
+        const int64_t lo = c * kc, hi = std::min(end, lo + kc);
+        if (hi <= lo) continue;
+        const double us = kSetupUs + (double)((hi - lo + 63) / 64) * tile_us +
+                          (chunks > 1 ? kPartialUs : 0.0);
+        const double start = free_at.top();
+        free_at.pop();
+        free_at.push(start + us);
+        ++busy;
+      }
+  }
+  double makespan = 0.0;
+  while (!free_at.empty()) {
+    makespan = std::max(makespan, free_at.top());
+    free_at.pop();
+  }
+  *active = busy;
+  if (split)
+    makespan += kCombineUs + (double)busy * g->n_kv_heads *
+                                 (double)cb::attn_unit_bytes(g->head_dim) / kCombineBytesPerUs;
+  return makespan;
+}
+
 // Tile and key-chunk decomposition of the MFMA attention, from host mirrors
-// only.  Long rows are split over key chunks when the query tiles alone give
-// fewer than 1024 workgroups, aiming at ~2048 units; a split needs
-// `ws_bytes` of workspace and is dropped when `ws_avail` is smaller.
+// only.  When the query tiles alone give fewer than 1024 workgroups, long
+// rows may be split over key chunks (a multiple of 64 keys, at least 256, at
+// most attn_max_chunks() per request); the cost model above picks the chunk
+// count with the shortest estimated launch, among the plans whose workspace
+// fits in `ws_avail`.
 cb::AttnPlan plan_attn(const cb_geom *g, const cb_ragged *rg, size_t ws_avail) {
   cb::AttnPlan pl{};
   pl.rows_per_tile = cb::attn_mfma_rows_per_tile(g->dtype, g->n_q_heads, g->n_kv_heads,
@@ -262,14 +325,7 @@ cb::AttnPlan plan_attn(const cb_geom *g, const cb_ragged *rg, size_t ws_avail) {
     pl.tiles += (kr + rows - 1) / rows;
     if (kr > 0) max_n = std::max<int64_t>(max_n, rg->h_tok_off[r + 1] - rg->h_tok_off[r]);
   }
-  const int64_t blocks = pl.tiles * g->n_kv_heads;
-  if (blocks > 0 && blocks < 1024) {
-    const int64_t want = std::min<int64_t>((2048 + blocks - 1) / blocks, cb::attn_max_chunks());
-    int64_t kc = (max_n + want - 1) / want;
-    kc = std::max<int64_t>(256, (kc + 63) / 64 * 64);
-    if (kc < max_n) pl.key_chunk = (int)kc;
-  }
-  auto count_units = [&](int kc, bool &split) {
+  auto count_units = [&](int64_t kc, bool &split) {
     int64_t units = 0;
     split = false;
     for (int32_t r = 0; r < rg->n_req; ++r) {
@@ -282,15 +338,29 @@ cb::AttnPlan plan_attn(const cb_geom *g, const cb_ragged *rg, size_t ws_avail) {
     }
     return units;
   };
-  pl.units = count_units(pl.key_chunk, pl.split);
-  if (pl.split) {
-    pl.ws_bytes = (size_t)pl.units * g->n_kv_heads * cb::attn_unit_bytes(g->head_dim);
-    if (pl.ws_bytes > ws_avail) {
-      pl.key_chunk = kNoSplit;
-      pl.units = count_units(pl.key_chunk, pl.split);
-      pl.ws_bytes = 0;
+  const int64_t blocks = pl.tiles * g->n_kv_heads;
+  if (blocks > 0 && blocks < 1024) {
+    int64_t active = 0;
+    double best = estimate_attn_us(g, rg, rows, kNoSplit, &active);
+    int64_t prev_kc = 0;
+    for (int c = 2; c <= cb::attn_max_chunks(); ++c) {
+      int64_t kc = (max_n + c - 1) / c;
+      kc = std::max<int64_t>(256, (kc + 63) / 64 * 64);
+      if (kc >= max_n || kc == prev_kc) continue;
+      prev_kc = kc;
+      bool split = false;
+      const size_t ws = (size_t)count_units(kc, split) * g->n_kv_heads *
+                        cb::attn_unit_bytes(g->head_dim);
+      if (ws > ws_avail) continue;
+      const double us = estimate_attn_us(g, rg, rows, kc, &active);
+      if (us < best) {
+        best = us;
+        pl.key_chunk = (int)kc;
+      }
     }
   }
+  pl.units = count_units(pl.key_chunk, pl.split);
+  pl.ws_bytes = pl.split ? (size_t)pl.units * g->n_kv_heads * cb::attn_unit_bytes(g->head_dim) : 0;
   return pl;
 }
 

@@ -69,7 +69,7 @@ struct AttnArgs {
 
 // Host-side decomposition of the MFMA attention launch.
 struct AttnPlan {
-  int rows_per_tile;   // selected rows per query tile (128 query vectors)
+  int rows_per_tile;   // selected rows per query tile (256 query vectors)
   int key_chunk;       // keys per unit (multiple of 64); huge = no split
   bool split;          // some request has more than one chunk
   int64_t tiles;       // query tiles over all requests
@@ -77,7 +77,7 @@ struct AttnPlan {
   size_t ws_bytes;     // workspace the split needs
 };
 
-// Selected rows per MFMA query tile (128 query vectors), or 0 if the MFMA
+// Selected rows per MFMA query tile (256 query vectors), or 0 if the MFMA
 // kernel does not cover this geometry.
 int attn_mfma_rows_per_tile(int dtype, int32_t n_q_heads, int32_t n_kv_heads,
                             int32_t head_dim);

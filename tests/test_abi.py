@@ -178,8 +178,9 @@ def test_zero_sized_calls_are_noops(lib):
 
 
 def test_workspace_size_plan(lib):
-    """The split plan is a pure host computation: small tile counts ask for a
-    workspace, large ones or unsupported geometries do not."""
+    """The split plan is a pure host computation.  Its cost model splits when
+    the query tiles leave the GPU idle or their rows are long, and not when
+    the tiles already fill it or the geometry runs on the plain kernel."""
     def size(g, tok, sel):
         rg, keep = _ragged(tok, tok, sel)
         n = ctypes.c_size_t(123)
@@ -190,6 +191,12 @@ def test_workspace_size_plan(lib):
     # in chunks of 256
     assert size(_geom(), [0, 2048], [0, 308]) == 5 * 8 * 8 * unit
     assert size(_geom(), [0, 65536], [0, 16384]) == 0           # enough tiles already
+    # 922 of 6144 rows: 15 tiles; three chunks of 2048 keys fill two rounds of
+    # the GPU better than eight of 768 (measured 79 against 99 us)
+    assert size(_geom(), [0, 6144], [0, 922]) == 15 * 3 * 8 * unit
+    # 3277 of 32768 rows: 52 tiles of up to 512 key tiles; a split only adds
+    # partial traffic (measured 941 us unsplit against 1018 us in 5 chunks)
+    assert size(_geom(), [0, 32768], [0, 3277]) == 0
     assert size(_geom(dt=B.CB_DTYPE_F32), [0, 2048], [0, 308]) == 0   # plain kernel
     assert size(_geom(d=16), [0, 2048], [0, 308]) == 0
     assert lib.cb_partial_attn_workspace_size(ctypes.byref(_geom()), None, None) == 1

@@ -296,15 +296,15 @@ ATTN_CASES = [
     # (dtype, hq, hkv, d, request lengths, selected per request)
     (torch.bfloat16, 32, 8, 128, [2048], [308]),
     (torch.bfloat16, 64, 8, 128, [700, 1500, 33], [100, 257, 33]),
-    (torch.bfloat16, 8, 8, 64, [500, 90], [64, 1]),
+    (torch.bfloat16, 8, 8, 64, [3000, 90], [64, 1]),
     (torch.bfloat16, 16, 1, 32, [1000], [77]),
     (torch.bfloat16, 4, 2, 128, [129, 64, 1], [65, 64, 1]),
     (torch.bfloat16, 6, 2, 64, [300], [40]),          # group 3: plain kernel
     (torch.bfloat16, 4, 2, 16, [200], [30]),          # head_dim 16: plain kernel
     (torch.float32, 4, 2, 16, [64, 64], [10, 10]),
     (torch.float32, 32, 8, 128, [1000], [50]),
-    (torch.bfloat16, 128, 2, 128, [300, 0, 200], [40, 0, 9]),  # group 64, empty request
-    # 64 requests (longest-first schedule) and 70 (natural order in batches of 64)
+    (torch.bfloat16, 128, 2, 128, [2500, 0, 1200], [40, 0, 9]),  # group 64, empty request
+    # 64 and 70 short requests
     (torch.bfloat16, 8, 2, 64, [(i * 37) % 41 + 1 for i in range(64)],
      [((i * 37) % 41 + 1 + 2) // 3 for i in range(64)]),
     (torch.bfloat16, 8, 2, 128, [(i * 53) % 97 + 1 for i in range(70)],
