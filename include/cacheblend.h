@@ -194,7 +194,7 @@ cb_status cb_fuse_scatter(const cb_geom *geom, void *k_fused, void *v_fused,
  *   q_c    : [M][n_q_heads][head_dim], already rotated at the new positions
  *   workspace, workspace_bytes : optional device scratch owned by the caller
  *            (NULL/0 allowed).  When the query tiles are too few to fill the
- *            GPU, long rows are split over key ranges whose fp32 partials
+ *            GPU, long rows are split over key ranges whose partials
  *            live here; cb_partial_attn_workspace_size() gives the size that
  *            enables the split.  A smaller workspace only disables the split.
  *            Calls that share a workspace must be ordered on one stream.

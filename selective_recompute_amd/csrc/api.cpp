@@ -251,7 +251,7 @@ constexpr int kNoSplit = 1 << 30;
 // figures were measured on MI355X at head_dim 128 (they scale with head_dim):
 // one 64-key tile of a 256-query unit takes ~2.1 us with every CU busy, a
 // workgroup spends ~3.6 us before its first tile (three dependent loads:
-// request offsets, selected rows, Q) and ~1 us writing an fp32 partial; the
+// request offsets, selected rows, Q) and ~1 us writing its partial; the
 // combine launch costs ~3 us plus its partials read at ~4.5 TB/s.
 constexpr double kTileUs = 2.1, kSetupUs = 3.6, kPartialUs = 1.0, kCombineUs = 3.0;
 constexpr double kCombineBytesPerUs = 4.5e6;

@@ -44,8 +44,9 @@ namespace cb {
 //    unit sees in full skip the causal mask.
 //
 // Long rows with too few tiles to fill the chip are split over key chunks of
-// `key_chunk` keys (a multiple of 64); every chunk writes its unnormalised
-// fp32 partial (O, running max, running sum) to the workspace and
+// `key_chunk` keys (a multiple of 64); every chunk writes its partial to the
+// workspace -- O of each query vector divided by its largest |O| as fp16,
+// then the running max, running sum and that largest |O| in fp32 -- and
 // attn_combine_kernel merges them.  Unsplit units write the output directly.
 // Block order: blockIdx % Hkv is the KV head, so with Hkv = 8 the round-robin
 // dispatch over the 8 XCDs keeps each head's K/V stream in one XCD's L2.  In
@@ -63,7 +64,7 @@ struct AttnParams {
   const bf16 *v_fused;
   const int32_t *tok_off;
   const int32_t *sel_off;
-  float *ws;
+  unsigned char *ws;
   int32_t n_req, hq, hkv, group, rows_per_tile, key_chunk;
   float scale_log2;
 };
@@ -78,6 +79,11 @@ constexpr int kMaxChunks = 8;          // key chunks per row (split plan bound)
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// Bytes of one split partial: fp16 O in fragment order, then three fp32
+// values per query vector (running max, running sum, largest |O|).
+template <int HD> constexpr int partial_bytes() { return kQT * HD * 2 + 3 * kQT * 4; }
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void global_cvoid;
@@ -393,32 +399,48 @@ void attn_mfma_kernel(const AttnParams p) {
             *reinterpret_cast<const uint4 *>(stage + v * HD + 8 * (part ^ (v & (CPQ - 1))));
     }
   } else {
-    // Partial in fragment order: store (dt, q) of wave w writes 64 lanes x 16
-    // contiguous bytes at float4 index ((w*NDT + dt)*4 + q)*64 + lane; then
-    // the running max and sum of the 256 query vectors.
-    float *w = p.ws + (int64_t)blockIdx.x * (kQT * HD + 2 * kQT);
+    // Partial in fragment order: store (dt, q) of wave w writes 64 lanes x 8
+    // contiguous bytes at fp16x4 index ((w*NDT + dt)*4 + q)*64 + lane.  Each
+    // query vector's O is divided by its largest |O| (the two lanes l and
+    // l ^ 32 hold its dims), so fp16 keeps 11 significant bits of every
+    // value whatever the scale of V; the combine multiplies it back.
+    unsigned char *w = p.ws + (int64_t)blockIdx.x * partial_bytes<HD>();
+    float amax = 0.f;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<f32x4 *>(w + 4 * ((((wave * NDT + dt) * 4 + q) << 6) + lane)) =
-            f32x4{o[dt][4 * q], o[dt][4 * q + 1], o[dt][4 * q + 2], o[dt][4 * q + 3]};
+      for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(o[dt][e]));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+    const float inv_amax = amax > 0.f ? 1.f / amax : 0.f;
+    f16x4 *wo = reinterpret_cast<f16x4 *>(w);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f16x4 h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = (_Float16)(o[dt][4 * q + i] * inv_amax);
+        wo[(((wave * NDT + dt) * 4 + q) << 6) + lane] = h;
+      }
     if (half == 0) {
-      w[kQT * HD + qv] = m_run;
-      w[kQT * HD + kQT + qv] = l;
+      float *meta = reinterpret_cast<float *>(w + kQT * HD * 2);
+      meta[qv] = m_run;
+      meta[kQT + qv] = l;
+      meta[2 * kQT + qv] = amax;
     }
   }
 }
 
-// Merge the key-chunk partials.  One thread per float4 of a partial, in the
-// partial's fragment order (consecutive threads read consecutive 16 bytes):
-// it loads the running max, running sum and partial O of every chunk at once
-// (unrolled over the chunk bound, inactive chunks clamped to chunk 0 and
-// weighted 0), so each thread waits for a single round of loads.
+// Merge the key-chunk partials.  One thread per 4 dims of a query vector, in
+// the partials' fragment order (consecutive threads read consecutive 8
+// bytes): it loads the running max, running sum, largest |O| and the 4 fp16
+// values of every chunk at once (unrolled over the chunk bound, inactive
+// chunks clamped to chunk 0 and weighted 0), so each thread waits for a
+// single round of loads.
 template <int HD>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   constexpr int QT = kQT;
-  constexpr int UNIT = QT * HD + 2 * QT;
+  constexpr int UNIT = partial_bytes<HD>();
   constexpr int GROUPS = QT * HD / 4 / 256;  // workgroups per (tile, head)
   const int g = blockIdx.x % p.hkv;
   const int rest = blockIdx.x / p.hkv;
@@ -438,7 +460,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   if (r == p.n_req || cr == 1) return;
   const int s0 = p.sel_off[r] + tile * p.rows_per_tile;
   const int ns = min(p.rows_per_tile, p.sel_off[r + 1] - s0);
-  // float4 index f = ((wave*NDT + dt)*4 + q)*64 + lane of the partial holds
+  // fp16x4 index f = ((wave*NDT + dt)*4 + q)*64 + lane of the partial holds
   // dims 32dt + 8q + 4(lane/32) .. +3 of query vector 32*wave + lane%32
   constexpr int NDT = HD / 32;
   const int f = qgroup * 256 + (int)threadIdx.x;
@@ -451,16 +473,18 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   const int p_last = p.sel_global[s0 + ns - 1];
   const int n_active = (p_last - lo) / p.key_chunk + 1;
   // unit of (tile, chunk c) is ubase + c * tr + (tr - 1 - tile)
-  const float *w0 = p.ws + ((ubase + (int64_t)(tr - 1 - tile)) * p.hkv + g) * UNIT;
+  const unsigned char *w0 = p.ws + ((ubase + (int64_t)(tr - 1 - tile)) * p.hkv + g) * UNIT;
   const int64_t ustride = (int64_t)tr * p.hkv * UNIT;
-  float mc[kMaxChunks], lc[kMaxChunks];
-  f32x4 oc[kMaxChunks];
+  float mc[kMaxChunks], lc[kMaxChunks], ac[kMaxChunks];
+  f16x4 oc[kMaxChunks];
 #pragma unroll
   for (int c = 0; c < kMaxChunks; ++c) {
-    const float *w = w0 + (c < n_active ? c : 0) * ustride;
-    mc[c] = w[QT * HD + qv];
-    lc[c] = w[QT * HD + QT + qv];
-    oc[c] = *reinterpret_cast<const f32x4 *>(w + 4 * f);
+    const unsigned char *w = w0 + (c < n_active ? c : 0) * ustride;
+    const float *meta = reinterpret_cast<const float *>(w + QT * HD * 2);
+    mc[c] = meta[qv];
+    lc[c] = meta[QT + qv];
+    ac[c] = meta[2 * QT + qv];
+    oc[c] = reinterpret_cast<const f16x4 *>(w)[f];
   }
   float mx = kNegFloor;
 #pragma unroll
@@ -471,7 +495,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   for (int c = 0; c < kMaxChunks; ++c) {
     const float wgt = c < n_active ? __builtin_amdgcn_exp2f(mc[c] - mx) : 0.f;
     l += lc[c] * wgt;
-    acc += oc[c] * wgt;
+    const float wo = wgt * ac[c];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = fmaf((float)oc[c][i], wo, acc[i]);
   }
   const float inv = 1.f / l;
   bf16x4 o;
@@ -490,7 +516,7 @@ int attn_mfma_rows_per_tile(int dtype, int32_t n_q_heads, int32_t n_kv_heads, in
 }
 
 size_t attn_unit_bytes(int32_t head_dim) {
-  return ((size_t)kQT * head_dim + 2 * kQT) * sizeof(float);
+  return (size_t)kQT * head_dim * 2 + 3 * (size_t)kQT * sizeof(float);
 }
 
 int attn_max_chunks() { return kMaxChunks; }
@@ -506,7 +532,7 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &plan, hipStream_t
   p.v_fused = (const bf16 *)a.v_fused;
   p.tok_off = a.tok_off;
   p.sel_off = a.sel_off;
-  p.ws = (float *)a.workspace;
+  p.ws = (unsigned char *)a.workspace;
   p.n_req = a.n_req;
   p.hq = a.n_q_heads;
   p.hkv = a.n_kv_heads;

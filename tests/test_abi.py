@@ -186,7 +186,7 @@ def test_workspace_size_plan(lib):
         n = ctypes.c_size_t(123)
         assert lib.cb_partial_attn_workspace_size(ctypes.byref(g), ctypes.byref(rg), ctypes.byref(n)) == 0
         return n.value
-    unit = (256 * 128 + 2 * 256) * 4
+    unit = 256 * 128 * 2 + 3 * 256 * 4
     # 256 query vectors per tile: 308 rows / 64 = 5 tiles x 8 heads, 2048 keys
     # in chunks of 256
     assert size(_geom(), [0, 2048], [0, 308]) == 5 * 8 * 8 * unit
