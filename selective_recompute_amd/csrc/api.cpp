@@ -118,13 +118,6 @@ cb_status check_ragged(const cb_ragged *rg, bool want_tok, bool want_cand, bool 
   return CB_OK;
 }
 
-int32_t max_cand(const cb_ragged *rg) {
-  int32_t mx = 0;
-  for (int32_t r = 0; r < rg->n_req; ++r)
-    mx = std::max(mx, rg->h_cand_off[r + 1] - rg->h_cand_off[r]);
-  return mx;
-}
-
 cb_status hip_status(hipError_t e, const char *what) {
   if (e == hipSuccess) return CB_OK;
   return fail(CB_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -414,7 +407,8 @@ CB_EXPORT cb_status cb_kv_deviation_topk(const cb_geom *geom, const cb_ragged *r
                     "deviation"));
   if (rg->h_sel_off[rg->n_req] == 0) return CB_OK;
   return hip_status(cb::launch_topk(rg->n_req, dev, cand_idx, rg->cand_off, rg->sel_off,
-                                    sel_local, sel_global, max_cand(rg), (hipStream_t)stream),
+                                    sel_local, sel_global, rg->h_cand_off, rg->h_sel_off,
+                                    (hipStream_t)stream),
                     "topk");
 }
 
@@ -432,7 +426,8 @@ CB_EXPORT cb_status cb_topk(const cb_ragged *rg, const float *dev, const int32_t
   CB_TRY(validate_topk(rg, dev, cand_idx, sel_local, sel_global));
   if (rg->h_sel_off[rg->n_req] == 0) return CB_OK;
   return hip_status(cb::launch_topk(rg->n_req, dev, cand_idx, rg->cand_off, rg->sel_off,
-                                    sel_local, sel_global, max_cand(rg), (hipStream_t)stream),
+                                    sel_local, sel_global, rg->h_cand_off, rg->h_sel_off,
+                                    (hipStream_t)stream),
                     "topk");
 }
 
@@ -514,7 +509,7 @@ CB_EXPORT cb_status cb_blend_layer(const cb_layer_args *a, void *stream) {
   }
   if (k_total == 0) return CB_OK;
   CB_TRY(hip_status(cb::launch_topk(rg->n_req, a->dev, a->cand_idx, rg->cand_off, rg->sel_off,
-                                    a->sel_local, a->sel_global, max_cand(rg), s),
+                                    a->sel_local, a->sel_global, rg->h_cand_off, rg->h_sel_off, s),
                     "topk"));
   CB_TRY(hip_status(cb::launch_fuse(a->k, a->v, a->k_new_c, a->v_new_c, a->sel_local,
                                     a->sel_global, k_total,

@@ -37,10 +37,11 @@ hipError_t launch_deviation(int dtype, const void *new0, const void *old0, const
                             const void *old1, const int32_t *cand_idx, float *dev, int64_t m,
                             int32_t row_elems, hipStream_t stream);
 
-// max_m: the largest candidate count of any request (host mirror).
+// h_cand_off / h_sel_off: host mirrors of the offsets (grid sizing; a single
+// request's counts also travel as kernel arguments).
 hipError_t launch_topk(int32_t n_req, const float *dev, const int32_t *cand_idx,
-                       const int32_t *cand_off, const int32_t *sel_off,
-                       int32_t *sel_local, int32_t *sel_global, int32_t max_m,
+                       const int32_t *cand_off, const int32_t *sel_off, int32_t *sel_local,
+                       int32_t *sel_global, const int32_t *h_cand_off, const int32_t *h_sel_off,
                        hipStream_t stream);
 
 hipError_t launch_fuse(void *k_fused, void *v_fused, const void *k_new_c,

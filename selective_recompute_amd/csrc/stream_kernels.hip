@@ -3,6 +3,7 @@
 //
 // Pages: [Derivations] = "数学推导" (CacheBlend math derivations page);
 // [KV-blog] = "rag的kvcache问题".
+#include <algorithm>
 #include <climits>
 
 #include "cb_device.hpp"
@@ -345,20 +346,25 @@ __device__ inline void wave_hist_add(uint32_t *hist, int bin) {
   }
 }
 
+// one_m / one_k: for a single request, its candidate and selected counts
+// (known on the host), so the scores are loaded without first waiting for
+// the offsets; -1 with several requests.
 template <int KPT>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     const float *__restrict__ dev, const int32_t *__restrict__ cand_idx,
     const int32_t *__restrict__ cand_off, const int32_t *__restrict__ sel_off,
-    int32_t *__restrict__ sel_local, int32_t *__restrict__ sel_global) {
+    int32_t *__restrict__ sel_local, int32_t *__restrict__ sel_global, int32_t one_m,
+    int32_t one_k) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t sh_digit, sh_above, sh_count;
   __shared__ uint32_t wave_tot[2][kTopkWaves];
 
   const int r = blockIdx.x;
-  const int c0 = cand_off[r];
-  const int m = cand_off[r + 1] - c0;
-  const int s0 = sel_off[r];
-  const int k = sel_off[r + 1] - s0;
+  const bool one = one_m >= 0;
+  const int c0 = one ? 0 : cand_off[r];
+  const int m = one ? one_m : cand_off[r + 1] - c0;
+  const int s0 = one ? 0 : sel_off[r];
+  const int k = one ? one_k : sel_off[r + 1] - s0;
   const int tid = threadIdx.x;
   if (k <= 0) return;
   if (k >= m) {  // every candidate is selected
@@ -459,12 +465,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
 
 hipError_t launch_topk(int32_t n_req, const float *dev, const int32_t *cand_idx,
                        const int32_t *cand_off, const int32_t *sel_off, int32_t *sel_local,
-                       int32_t *sel_global, int32_t max_m, hipStream_t stream) {
+                       int32_t *sel_global, const int32_t *h_cand_off, const int32_t *h_sel_off,
+                       hipStream_t stream) {
   if (n_req == 0) return hipSuccess;
+  int32_t max_m = 0;
+  for (int32_t r = 0; r < n_req; ++r) max_m = std::max(max_m, h_cand_off[r + 1] - h_cand_off[r]);
+  const int32_t one_m = n_req == 1 ? h_cand_off[1] : -1;
+  const int32_t one_k = n_req == 1 ? h_sel_off[1] : -1;
   const int seg = (max_m + kTopkThreads - 1) / kTopkThreads;
 #define CB_TOPK(K)                                                                            \
   hipLaunchKernelGGL(topk_kernel<K>, dim3(n_req), dim3(kTopkThreads), 0, stream, dev, cand_idx, \
-                     cand_off, sel_off, sel_local, sel_global)
+                     cand_off, sel_off, sel_local, sel_global, one_m, one_k)
   if (seg <= 1) CB_TOPK(1);
   else if (seg <= 2) CB_TOPK(2);
   else if (seg <= 4) CB_TOPK(4);
