@@ -431,17 +431,18 @@ void attn_mfma_kernel(const AttnParams p) {
   }
 }
 
-// Merge the key-chunk partials.  One thread per 4 dims of a query vector, in
-// the partials' fragment order (consecutive threads read consecutive 8
-// bytes): it loads the running max, running sum, largest |O| and the 4 fp16
-// values of every chunk at once (unrolled over the chunk bound, inactive
-// chunks clamped to chunk 0 and weighted 0), so each thread waits for a
-// single round of loads.
+// Merge the key-chunk partials.  One thread per 8 dims of a query vector:
+// the two fp16x4 fragments f and f + 64 of the partials' fragment order
+// (dims d and d + 8), so the running max, running sum and largest |O| of each
+// chunk are loaded once for both.  Consecutive threads read consecutive 8
+// bytes.  Every chunk's loads are issued at once (unrolled over the chunk
+// bound, inactive chunks clamped to chunk 0 and weighted 0), so each thread
+// waits for a single round of loads.
 template <int HD>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   constexpr int QT = kQT;
   constexpr int UNIT = partial_bytes<HD>();
-  constexpr int GROUPS = QT * HD / 4 / 256;  // workgroups per (tile, head)
+  constexpr int GROUPS = QT * HD / 8 / 256;  // workgroups per (tile, head): 2 fragments per thread
   const int g = blockIdx.x % p.hkv;
   const int rest = blockIdx.x / p.hkv;
   const int qgroup = rest % GROUPS;
@@ -463,7 +464,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   // fp16x4 index f = ((wave*NDT + dt)*4 + q)*64 + lane of the partial holds
   // dims 32dt + 8q + 4(lane/32) .. +3 of query vector 32*wave + lane%32
   constexpr int NDT = HD / 32;
-  const int f = qgroup * 256 + (int)threadIdx.x;
+  // thread -> fragments f and f + 64 (dims d0 and d0 + 8 of one query vector)
+  const int t = qgroup * 256 + (int)threadIdx.x;
+  const int f = ((t >> 6) << 7) + (t & 63);
   const int lane = f & 63, q = (f >> 6) & 3, dt = (f >> 8) % NDT, wv = (f >> 8) / NDT;
   const int qv = wv * 32 + (lane & 31);
   const int d0 = 32 * dt + 8 * q + 4 * (lane >> 5);
@@ -476,7 +479,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   const unsigned char *w0 = p.ws + ((ubase + (int64_t)(tr - 1 - tile)) * p.hkv + g) * UNIT;
   const int64_t ustride = (int64_t)tr * p.hkv * UNIT;
   float mc[kMaxChunks], lc[kMaxChunks], ac[kMaxChunks];
-  f16x4 oc[kMaxChunks];
+  f16x4 oc[kMaxChunks], oc2[kMaxChunks];
 #pragma unroll
   for (int c = 0; c < kMaxChunks; ++c) {
     const unsigned char *w = w0 + (c < n_active ? c : 0) * ustride;
@@ -485,26 +488,34 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
     lc[c] = meta[QT + qv];
     ac[c] = meta[2 * QT + qv];
     oc[c] = reinterpret_cast<const f16x4 *>(w)[f];
+    oc2[c] = reinterpret_cast<const f16x4 *>(w)[f + 64];
   }
   float mx = kNegFloor;
 #pragma unroll
   for (int c = 0; c < kMaxChunks; ++c) mx = fmaxf(mx, c < n_active ? mc[c] : kNegFloor);
   float l = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < kMaxChunks; ++c) {
     const float wgt = c < n_active ? __builtin_amdgcn_exp2f(mc[c] - mx) : 0.f;
     l += lc[c] * wgt;
     const float wo = wgt * ac[c];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = fmaf((float)oc[c][i], wo, acc[i]);
+    for (int i = 0; i < 4; ++i) {
+      acc[i] = fmaf((float)oc[c][i], wo, acc[i]);
+      acc2[i] = fmaf((float)oc2[c][i], wo, acc2[i]);
+    }
   }
   const float inv = 1.f / l;
-  bf16x4 o;
+  bf16x4 o, o2;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = (bf16)(acc[i] * inv);
-  *reinterpret_cast<bf16x4 *>(p.out + ((int64_t)(s0 + row) * p.hq + g * p.group + hh) * HD +
-                              d0) = o;
+  for (int i = 0; i < 4; ++i) {
+    o[i] = (bf16)(acc[i] * inv);
+    o2[i] = (bf16)(acc2[i] * inv);
+  }
+  bf16 *dst = p.out + ((int64_t)(s0 + row) * p.hq + g * p.group + hh) * HD + d0;
+  *reinterpret_cast<bf16x4 *>(dst) = o;
+  *reinterpret_cast<bf16x4 *>(dst + 8) = o2;
 }
 
 int attn_mfma_rows_per_tile(int dtype, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim) {
@@ -548,7 +559,7 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &plan, hipStream_t
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !plan.split) return e;
-  const int groups = kQT / (256 / (a.head_dim / 4));
+  const int groups = kQT / (512 / (a.head_dim / 4));
   const dim3 cgrid((unsigned)(plan.tiles * a.n_kv_heads * groups)), cblock(256);
   switch (a.head_dim) {
     case 32: hipLaunchKernelGGL(attn_combine_kernel<32>, cgrid, cblock, 0, stream, p); break;
