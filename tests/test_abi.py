@@ -200,3 +200,36 @@ def test_workspace_size_plan(lib):
     assert size(_geom(dt=B.CB_DTYPE_F32), [0, 2048], [0, 308]) == 0   # plain kernel
     assert size(_geom(d=16), [0, 2048], [0, 308]) == 0
     assert lib.cb_partial_attn_workspace_size(ctypes.byref(_geom()), None, None) == 1
+
+
+def test_workspace_plan_properties(lib):
+    """Random ragged batches: a split plan is a whole number of units, and its
+    unit count is that of a chunk the planner may choose (a multiple of 64
+    keys, at least 256, at most 8 chunks for the longest request); query
+    tiles that alone give 1024 or more workgroups are never split."""
+    rng = np.random.default_rng(11)
+    unit = 256 * 128 * 2 + 3 * 256 * 4
+    for _ in range(300):
+        hq, hkv = [(32, 8), (64, 8), (8, 2), (16, 1), (8, 8)][rng.integers(5)]
+        lens = [int(x) for x in rng.integers(1, 40000, size=rng.integers(1, 9))]
+        ks = [min(n, int(n * rng.uniform(0, 0.3))) for n in lens]
+        rg, keep = _ragged(np.concatenate([[0], np.cumsum(lens)]),
+                           np.concatenate([[0], np.cumsum(lens)]),
+                           np.concatenate([[0], np.cumsum(ks)]))
+        g = _geom(hq, hkv, 128)
+        n = ctypes.c_size_t(123)
+        assert lib.cb_partial_attn_workspace_size(ctypes.byref(g), ctypes.byref(rg), ctypes.byref(n)) == 0
+        rows = 256 // (hq // hkv)
+        tiles = [-(-k // rows) for k in ks]
+        if sum(tiles) * hkv >= 1024 or n.value == 0:
+            assert sum(tiles) * hkv < 1024 or n.value == 0
+            continue
+        assert n.value % (hkv * unit) == 0
+        units = n.value // (hkv * unit)
+        max_n = max(nn for nn, k in zip(lens, ks) if k)
+        chunks = set()
+        for c in range(2, 9):
+            kc = max(256, -(-(-(-max_n // c)) // 64) * 64)
+            if kc < max_n:
+                chunks.add(kc)
+        assert any(units == sum(t * -(-nn // kc) for t, nn in zip(tiles, lens)) for kc in chunks)

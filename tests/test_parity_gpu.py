@@ -312,12 +312,11 @@ ATTN_CASES = [
 ]
 
 
-@pytest.mark.parametrize("use_ws", [False, True], ids=["direct", "split"])
-@pytest.mark.parametrize("case", ATTN_CASES, ids=[f"a{i}" for i in range(len(ATTN_CASES))])
-def test_partial_attention_parity(case, use_ws):
+def _attention_case(case, use_ws, seed, max_rows=None):
+    """Run cb_partial_attn on a seeded case; compare every row (or a sample of
+    max_rows plus each request's first and last) with the oracle."""
     dtype, hq, hkv, d, lens, ks = case
-    say(f"attention {case} workspace={use_ws}")
-    rng = np.random.default_rng(sum(lens) + hq)
+    rng = np.random.default_rng(seed)
     t_count = sum(lens)
     tok_off = PL.offsets(lens)
     sel_off = PL.offsets(ks)
@@ -335,16 +334,17 @@ def test_partial_attention_parity(case, use_ws):
     row_start = np.concatenate(row_start)
     m = t_count
     sel_l = sel_g.copy()                                      # candidates = all tokens
-    q = torch.randn(m, hq, d).to(dtype)
-    kf = torch.randn(t_count, hkv, d).to(dtype)
-    vf = torch.randn(t_count, hkv, d).to(dtype)
+    gen = torch.Generator().manual_seed(seed)
+    q = torch.randn(m, hq, d, generator=gen).to(dtype)
+    kf = torch.randn(t_count, hkv, d, generator=gen).to(dtype)
+    vf = torch.randn(t_count, hkv, d, generator=gen).to(dtype)
     rb = B.RaggedBatch(tok_off, tok_off, sel_off, DEV)
     g = B.geom(hq, hkv, d, dtype)
     ws = None
     if use_ws:
         nbytes = B.attn_workspace_bytes(g, rb)
         if nbytes == 0:
-            pytest.skip("this geometry never splits")
+            pytest.skip("the planner does not split this case")
         ws = B.workspace_tensor(nbytes, DEV)
         ws.fill_(0xFF)                                        # NaN garbage: must be overwritten
     out = torch.full((rb.n_sel, hq, d), float("nan"), dtype=dtype, device=DEV)
@@ -352,11 +352,45 @@ def test_partial_attention_parity(case, use_ws):
     B.partial_attn(g, rb, out, q.to(DEV), torch.from_numpy(sel_l).to(DEV),
                    torch.from_numpy(sel_g).to(DEV), kf.to(DEV), vf.to(DEV), scale, workspace=ws)
     torch.cuda.synchronize()
-    ref = O.attention_rows(np64(q), sel_l, sel_g, row_start, np64(kf), np64(vf), hq, hkv, scale)
     got = np64(out)
-    err = np.abs(got - ref)
     assert np.isfinite(got).all()
+    rows = np.arange(len(sel_g))
+    if max_rows is not None and len(rows) > max_rows:
+        ends = np.concatenate([[sel_off[r], sel_off[r + 1] - 1] for r in range(len(ks)) if ks[r]])
+        rows = np.unique(np.concatenate([ends, rng.choice(len(sel_g), max_rows, replace=False)]))
+    ref = O.attention_rows(np64(q), sel_l[rows], sel_g[rows], row_start[rows], np64(kf),
+                           np64(vf), hq, hkv, scale)
+    err = np.abs(got[rows] - ref)
     assert err.max() <= ATTN_ABS, f"max err {err.max()}"
+
+
+@pytest.mark.parametrize("use_ws", [False, True], ids=["direct", "split"])
+@pytest.mark.parametrize("case", ATTN_CASES, ids=[f"a{i}" for i in range(len(ATTN_CASES))])
+def test_partial_attention_parity(case, use_ws):
+    say(f"attention {case} workspace={use_ws}")
+    _attention_case(case, use_ws, sum(case[4]) + case[1])
+
+
+def _random_case(i):
+    """Seeded ragged batch: 1-5 requests of 1-3000 tokens, 0-25% of the rows
+    selected, one of several head geometries (the split planner then chooses
+    freely between no split and 2-8 chunks)."""
+    rng = np.random.default_rng(5000 + i)
+    hq, hkv = [(32, 8), (8, 2), (16, 1), (32, 4), (8, 8)][int(rng.integers(5))]
+    d = [64, 128][int(rng.integers(2))]
+    lens = [int(x) for x in rng.integers(1, 3001, size=int(rng.integers(1, 6)))]
+    ks = [min(n, int(round(n * rng.uniform(0.0, 0.25)))) for n in lens]
+    return (torch.bfloat16, hq, hkv, d, lens, ks)
+
+
+RANDOM_CASES = [_random_case(i) for i in range(8)]
+
+
+@pytest.mark.parametrize("use_ws", [False, True], ids=["direct", "planned"])
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=[f"r{i}" for i in range(len(RANDOM_CASES))])
+def test_attention_random_ragged_batches(case, use_ws):
+    say(f"attention random {case[1:4]} lens={case[4]} ks={case[5]} workspace={use_ws}")
+    _attention_case(case, use_ws, 77 + sum(case[4]), max_rows=96)
 
 
 DENSE = [(32, 8, 128, [2048], 64), (64, 8, 128, [700, 1300], 48), (8, 8, 64, [333], None)]
