@@ -142,8 +142,10 @@ def test_kv_deviation_topk_parity(source, name, layer):
     dev = torch.empty(rb.n_cand, dtype=torch.float32, device=DEV)
     sl = torch.empty(rb.n_sel, dtype=torch.int32, device=DEV)
     sg = torch.empty(rb.n_sel, dtype=torch.int32, device=DEV)
+    # the K score reads no V: its V pointers may be NULL
+    v_new, v_old = (None, None) if source == "k" else (x["v_new_c"].to(DEV), x["v_old"].to(DEV))
     B.kv_deviation_topk(g, rb, B.DEV_SOURCES[source], x["k_new_c"].to(DEV), x["k_old"].to(DEV),
-                        x["v_new_c"].to(DEV), x["v_old"].to(DEV), x["cand_idx"].to(DEV), dev, sl, sg)
+                        v_new, v_old, x["cand_idx"].to(DEV), dev, sl, sg)
     torch.cuda.synchronize()
     cand = npi(x["cand_idx"])
     ref_dev = O.kv_deviation(source, k_new_c=np64(x["k_new_c"]), k_cached=np64(x["k_old"]),
