@@ -391,13 +391,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     return order_key(dev[c0 + jb + i]);
   };
   const int iters = KPT > 0 ? KPT : seg;  // uniform over the workgroup
+  constexpr int kUnroll = KPT > 0 ? KPT : 1;  // register path: fully unrolled
 
   uint32_t prefix = 0, mask = 0, krem = (uint32_t)k;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
-#pragma unroll
+#pragma unroll kUnroll
     for (int i = 0; i < iters; ++i) {
       int bin = -1;
       if (i < n_my) {
@@ -437,7 +438,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   const uint32_t keep_eq = krem;  // keys of the boundary bin to keep, lowest index first
 
   uint32_t n_gt = 0, n_eq = 0;
-#pragma unroll
+#pragma unroll kUnroll
   for (int i = 0; i < iters; ++i) {
     if (i < n_my) {
       const uint32_t km = key_at(i) & mask;
@@ -447,7 +448,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   }
   uint32_t gt_before, eq_before;
   block_excl_scan2(n_gt, n_eq, gt_before, eq_before, wave_tot);
-#pragma unroll
+#pragma unroll kUnroll
   for (int i = 0; i < iters; ++i) {
     if (i < n_my) {
       const uint32_t km = key_at(i) & mask;
