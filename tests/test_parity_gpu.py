@@ -506,6 +506,44 @@ def test_blend_layers_end_to_end(name, layers, n_rows, schedule):
         assert err.max() <= ATTN_ABS, f"attention max err {err.max()}"
 
 
+def test_blend_layer_128k_token_request():
+    """One request of 131072 tokens (16 chunks of 8192; deltas up to 122880),
+    1% selected: the top-k runs its memory path (128 scores per thread), the
+    attention rows reach 131072 keys and the split plan sees its longest rows.
+    Exact selection, deviations to 1e-4, fused rows and sampled attention rows
+    against the oracle."""
+    say("blend 128k-token request")
+    wl = W.Workload("long-128k", 1, ((8192,) * 16,), 32, 8, 128, 10000.0, "bf16", 1, 1, 1, 80,
+                    0xCB10, "one request of 131072 tokens")
+    sets = W.PlantedSets(wl)
+    x = W.layer_inputs(wl, sets, 0, device=DEV)
+    x_cpu = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in x.items()}
+    runner = PL.BlendRunner(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.torch_dtype,
+                            wl.request_lengths, wl.r1_pct, wl.r2_pct, 1, wl.rope_theta)
+    o = runner.run_layer(0, x)
+    torch.cuda.synchronize()
+    counts = runner.filter.counts(0)
+    cand = npi(x_cpu["cand_idx"])
+    n_sel = int(np.sum(counts))
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[0, n_sel - 1], rng.choice(n_sel, 14, replace=False)]))
+    ref = _oracle_layer(wl, x_cpu, cand, counts, rows)
+    assert_dev_close(o["dev"].cpu().numpy().astype(np.float64), ref["dev"])
+    assert np.array_equal(npi(o["sel_global"]), ref["sel_global"])
+    assert np.array_equal(npi(o["sel_local"]), ref["sel_local"])
+    assert np.array_equal(ref["sel_global"], x_cpu["planted"])
+    kf, vf = np64(x["k_old"]), np64(x["v_old"])
+    sel = ref["sel_global"]
+    assert np.array_equal(kf[sel], np64(x_cpu["k_new_c"])[ref["sel_local"]])
+    assert np.array_equal(vf, ref["v_fused"])
+    probe = np.unique(np.concatenate([rng.choice(wl.n_tokens, 4096, replace=False),
+                                      [wl.n_tokens - 1]]))
+    probe = probe[~np.isin(probe, sel)]
+    assert_k_close(kf[probe], ref["k_rot"][probe], wl.torch_dtype, "fused K")
+    err = np.abs(np64(o["out"])[ref["rows"]] - ref["out"])
+    assert err.max() <= ATTN_ABS, f"attention max err {err.max()}"
+
+
 def test_blend_is_deterministic():
     say("determinism mistral7b-layer")
     wl = W.make_workload("mistral7b-layer")
