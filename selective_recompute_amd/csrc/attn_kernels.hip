@@ -272,10 +272,13 @@ void attn_mfma_kernel(const AttnParams p) {
     }
   }
 
-  // Q and the first tiles resident.  Waiting for everything here (instead of
-  // tile 0 only) also tells the compiler that no load of its own is pending
-  // inside the loop, so it adds no waits there.
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  // Q (issued first) and tile 0 resident; the later prefetched tiles may stay
+  // in flight.  The compiler, which does not count the copies into LDS, adds
+  // its own waits before the first uses of Q; it peels them into the first
+  // iteration, so the tile loop keeps only the waits below.
+  if (n_kt >= 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * PER_TILE));
+  else if (n_kt == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(PER_TILE));
+  else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
 
   for (int kt = 0; kt < n_kt; ++kt) {
