@@ -264,8 +264,8 @@ def main():
         print(source_fingerprint())
         return
     if a.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported by this "
-              "single-GPU build (no multi-GPU path exists).", file=sys.stderr)
+        print(f"bench.py measures one GPU: --gpus {a.gpus} is not supported (the library "
+              "has no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
     peaks = attainable_peaks() if a.attainable else None
     if a.prefill:
