@@ -35,8 +35,8 @@ Recipe (per layer l, per request of N tokens):
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field
-from typing import List, Sequence, Tuple
+from dataclasses import dataclass
+from typing import List, Tuple
 
 import numpy as np
 import torch

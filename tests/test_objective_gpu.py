@@ -13,7 +13,6 @@ claim compares GPU results with each other.
 """
 import math
 
-import numpy as np
 import pytest
 import torch
 
