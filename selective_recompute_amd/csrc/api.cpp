@@ -353,6 +353,12 @@ cb::AttnPlan plan_attn(const cb_geom *g, const cb_ragged *rg, size_t ws_avail) {
     }
   }
   pl.units = count_units(pl.key_chunk, pl.split);
+  pl.max_chunks = 1;
+  for (int32_t r = 0; r < rg->n_req; ++r)
+    if (rg->h_sel_off[r + 1] > rg->h_sel_off[r])
+      pl.max_chunks = std::max<int>(pl.max_chunks, (int)(((int64_t)rg->h_tok_off[r + 1] -
+                                                          rg->h_tok_off[r] + pl.key_chunk - 1) /
+                                                         pl.key_chunk));
   pl.ws_bytes = pl.split ? (size_t)pl.units * g->n_kv_heads * cb::attn_unit_bytes(g->head_dim) : 0;
   return pl;
 }

@@ -438,10 +438,10 @@ void attn_mfma_kernel(const AttnParams p) {
 // the two fp16x4 fragments f and f + 64 of the partials' fragment order
 // (dims d and d + 8), so the running max, running sum and largest |O| of each
 // chunk are loaded once for both.  Consecutive threads read consecutive 8
-// bytes.  Every chunk's loads are issued at once (unrolled over the chunk
-// bound, inactive chunks clamped to chunk 0 and weighted 0), so each thread
-// waits for a single round of loads.
-template <int HD>
+// bytes.  Every chunk's loads are issued at once (unrolled over NC, the
+// plan's largest chunk count rounded up to 2, 4 or 8; inactive chunks clamped
+// to chunk 0 and weighted 0), so each thread waits for a single round of loads.
+template <int HD, int NC>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   constexpr int QT = kQT;
   constexpr int UNIT = partial_bytes<HD>();
@@ -481,10 +481,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   // unit of (tile, chunk c) is ubase + c * tr + (tr - 1 - tile)
   const unsigned char *w0 = p.ws + ((ubase + (int64_t)(tr - 1 - tile)) * p.hkv + g) * UNIT;
   const int64_t ustride = (int64_t)tr * p.hkv * UNIT;
-  float mc[kMaxChunks], lc[kMaxChunks], ac[kMaxChunks];
-  f16x4 oc[kMaxChunks], oc2[kMaxChunks];
+  float mc[NC], lc[NC], ac[NC];
+  f16x4 oc[NC], oc2[NC];
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
+  for (int c = 0; c < NC; ++c) {
     const unsigned char *w = w0 + (c < n_active ? c : 0) * ustride;
     const float *meta = reinterpret_cast<const float *>(w + QT * HD * 2);
     mc[c] = meta[qv];
@@ -495,11 +495,11 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   }
   float mx = kNegFloor;
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) mx = fmaxf(mx, c < n_active ? mc[c] : kNegFloor);
+  for (int c = 0; c < NC; ++c) mx = fmaxf(mx, c < n_active ? mc[c] : kNegFloor);
   float l = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
+  for (int c = 0; c < NC; ++c) {
     const float wgt = c < n_active ? __builtin_amdgcn_exp2f(mc[c] - mx) : 0.f;
     l += lc[c] * wgt;
     const float wo = wgt * ac[c];
@@ -564,11 +564,21 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &plan, hipStream_t
   if (e != hipSuccess || !plan.split) return e;
   const int groups = kQT / (512 / (a.head_dim / 4));
   const dim3 cgrid((unsigned)(plan.tiles * a.n_kv_heads * groups)), cblock(256);
+#define CB_COMBINE(HD)                                                                          \
+  do {                                                                                          \
+    if (plan.max_chunks <= 2)                                                                   \
+      hipLaunchKernelGGL((attn_combine_kernel<HD, 2>), cgrid, cblock, 0, stream, p);            \
+    else if (plan.max_chunks <= 4)                                                              \
+      hipLaunchKernelGGL((attn_combine_kernel<HD, 4>), cgrid, cblock, 0, stream, p);            \
+    else                                                                                        \
+      hipLaunchKernelGGL((attn_combine_kernel<HD, kMaxChunks>), cgrid, cblock, 0, stream, p);   \
+  } while (0)
   switch (a.head_dim) {
-    case 32: hipLaunchKernelGGL(attn_combine_kernel<32>, cgrid, cblock, 0, stream, p); break;
-    case 64: hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, cblock, 0, stream, p); break;
-    default: hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, cblock, 0, stream, p); break;
+    case 32: CB_COMBINE(32); break;
+    case 64: CB_COMBINE(64); break;
+    default: CB_COMBINE(128); break;
   }
+#undef CB_COMBINE
   return hipGetLastError();
 }
 

@@ -75,6 +75,7 @@ struct AttnPlan {
   bool split;          // some request has more than one chunk
   int64_t tiles;       // query tiles over all requests
   int64_t units;       // (tile, chunk) units over all requests
+  int max_chunks;      // largest chunk count of any request with selected rows
   size_t ws_bytes;     // workspace the split needs
 };
 
