@@ -15,8 +15,9 @@ kernel (algorithmic work per launch / its average launch time, measured with
 HIP events on the launch stream, against the published peak and against the
 peak measured by the in-tree probe `cb_peaks`), the whole-step roofline
 fraction (streaming bytes at 8 TB/s plus attention flops at the MFMA peak,
-over the step time), per-kernel figures and the CPU oracle timed on the host
-as a reported baseline.
+over the step time), per-kernel figures (each stage's rate and its fraction of
+the published and the measured peak; the top-k also timed on its own) and the
+CPU oracle timed on the host as a reported baseline.
 """
 from __future__ import annotations
 
@@ -365,6 +366,7 @@ def main():
     gref = ctypes.byref(runner.geom)
     rgs = [rb.struct() for rb in runner.batches]
     stage_calls = {s: [[] for _ in range(L)] for s in STAGES}
+    topk_calls = [[] for _ in range(L)]   # the selection half alone, for its own time
     keep = []
     ws_ptr, ws_bytes = B._ws(runner.workspace)
     for cp in copies:
@@ -387,6 +389,9 @@ def main():
                                             x["k_new_c"].data_ptr(), k_ptr,
                                             x["v_new_c"].data_ptr(), v_ptr, cand.data_ptr(),
                                             dev_t.data_ptr(), sl.data_ptr(), sg.data_ptr(), h)))
+            topk_calls[l].append(
+                (lib.cb_topk, (ctypes.byref(rgs[l]), dev_t.data_ptr(), cand.data_ptr(),
+                               sl.data_ptr(), sg.data_ptr(), h)))
             stage_calls["fuse_scatter"][l].append(
                 (lib.cb_fuse_scatter, (gref, k_ptr, v_ptr, x["k_new_c"].data_ptr(),
                                        x["v_new_c"].data_ptr(), sl.data_ptr(), sg.data_ptr(),
@@ -409,6 +414,15 @@ def main():
                         B.check(st)
                 e1.record(stream)
                 events[(l, s)] = (e0, e1)
+            # the top-k again on the scores just computed (same outputs)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for fn, args in topk_calls[l]:
+                st = fn(*args)
+                if st != 0:
+                    B.check(st)
+            e1.record(stream)
+            events[(l, "topk")] = (e0, e1)
         torch.cuda.synchronize()
     stage_ms = {s: sum(events[(l, s)][0].elapsed_time(events[(l, s)][1]) for l in range(L))
                 for s in STAGES}
@@ -427,6 +441,21 @@ def main():
             rate = stage_work[s] / (stage_ms[s] * 1e-3) / 1e9
             kernels[s] = {"avg_us": round(avg_us, 3), "gbs": round(rate, 1),
                           "mb_per_launch": round(stage_work[s] / launches / 1e6, 4)}
+    # each class against its published peak and, when measured, the attainable one
+    # (MFMA probe for the attention, streaming-read probe for the HBM stages)
+    flop_peak_t = BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
+    for s in STAGES:
+        kk = kernels[s]
+        if "tflops" in kk:
+            kk["frac"] = round(kk["tflops"] / flop_peak_t, 5)
+            if peaks and wl.dtype == "bf16":
+                kk["frac_attainable"] = round(kk["tflops"] / peaks["mfma_bf16_32x32x16_tflops"], 5)
+        else:
+            kk["frac"] = round(kk["gbs"] / HBM_PEAK_GBS, 5)
+            if peaks:
+                kk["frac_attainable"] = round(kk["gbs"] / peaks["read_gbs"], 5)
+    topk_ms = sum(events[(l, "topk")][0].elapsed_time(events[(l, "topk")][1]) for l in range(L))
+    kernels["topk"] = {"avg_us": round(topk_ms * 1e3 / launches, 3), "bound": "latency"}
     dominant = max(STAGES, key=lambda s: stage_ms[s])
     if dominant == "partial_attn":
         bf16 = wl.dtype == "bf16"
@@ -442,7 +471,7 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
                 "traffic": recorded_traffic(dominant, wl.name)}
     if peaks:
-        att = peaks["mfma_bf16_32x32x16_tflops"] if roof["unit"] == "TFLOP/s" else peaks["copy_gbs"]
+        att = peaks["mfma_bf16_32x32x16_tflops"] if roof["unit"] == "TFLOP/s" else peaks["read_gbs"]
         if roof["bound"] in ("mfma", "hbm"):
             roof["attainable_peak"] = att
             roof["frac_attainable"] = round(roof["achieved"] / att, 5)
