@@ -18,14 +18,15 @@ def say(msg):
     print(f"[graph-test] {msg}", flush=True)
 
 
-@pytest.mark.parametrize("name", ["mistral7b-layer", "tiny"])
-def test_blend_layer_graph_replays_match_eager(name):
-    say(f"graph replay {name}")
+@pytest.mark.parametrize("name,source", [("mistral7b-layer", "v"), ("tiny", "v"),
+                                         ("mistral7b-layer", "kv")])
+def test_blend_layer_graph_replays_match_eager(name, source):
+    say(f"graph replay {name} deviation source {source}")
     wl = W.make_workload(name)
     sets = W.PlantedSets(wl)
     runner = PL.BlendRunner(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.torch_dtype,
                             wl.request_lengths, wl.r1_pct, wl.r2_pct, 1, wl.rope_theta,
-                            device=DEV)
+                            dev_source=source, device=DEV)
     x = W.layer_inputs(wl, sets, 0, device=DEV)
     k0, v0 = x["k_old"].clone(), x["v_old"].clone()
     o = runner.outs[0]
@@ -34,7 +35,8 @@ def test_blend_layer_graph_replays_match_eager(name):
                            delta=x["delta"], cand_idx=runner.candidates(0),
                            rope_theta=wl.rope_theta, rope_style=B.ROPE_HALF,
                            softmax_scale=runner.scale, dev=o["dev"], sel_local=o["sel_local"],
-                           sel_global=o["sel_global"], out=o["out"], workspace=runner.workspace)
+                           sel_global=o["sel_global"], out=o["out"], workspace=runner.workspace,
+                           dev_source=runner.dev_source)
     outs = [o["dev"], o["sel_local"], o["sel_global"], o["out"], x["k_old"], x["v_old"]]
     stream = torch.cuda.Stream()
 
@@ -50,7 +52,8 @@ def test_blend_layer_graph_replays_match_eager(name):
         prep.launch(stream.cuda_stream)
     torch.cuda.synchronize()
     eager = [t.clone() for t in outs]
-    assert np.array_equal(eager[2].cpu().numpy(), sets.layer(0).planted)
+    if source == "v":       # the inputs plant the deviation tiers in V
+        assert np.array_equal(eager[2].cpu().numpy(), sets.layer(0).planted)
 
     restore()
     graph = torch.cuda.CUDAGraph()
