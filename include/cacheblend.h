@@ -212,6 +212,57 @@ cb_status cb_partial_attn(const cb_geom *geom, const cb_ragged *rg, void *out,
 cb_status cb_partial_attn_workspace_size(const cb_geom *geom,
                                          const cb_ragged *rg, size_t *bytes);
 
+/* How cb_partial_attn decomposes the work for a geometry and batch. */
+typedef struct cb_attn_plan {
+  int32_t mfma;           /* 1: bf16 MFMA query tiles; 0: plain kernel (one
+                             wave per selected row and query head) */
+  int32_t key_split;      /* MFMA: wave groups that split the keys of every
+                             tile (1: 256 query vectors, 64-key tiles;
+                             2: 128 query vectors, 128-key tiles) */
+  int32_t rows_per_tile;  /* MFMA: selected rows per query tile */
+  int32_t key_chunk;      /* MFMA: keys per chunk when long rows are split over
+                             keys (their partials go to the workspace); 0: no split */
+  int64_t tiles;          /* MFMA: query tiles over all requests */
+  int64_t workgroups;     /* workgroups of the attention launch */
+  size_t workspace_bytes; /* workspace the plan uses (<= the size passed in) */
+} cb_attn_plan;
+
+/* The plan cb_partial_attn follows with `workspace_bytes` of workspace
+ * (SIZE_MAX: as with cb_partial_attn_workspace_size()).  The choice is a
+ * host-side cost model of the launch; it reads host mirrors only and
+ * enqueues nothing.  Errors: INVALID_ARG for a NULL plan or invalid
+ * geometry / offsets (the plan is zeroed first). */
+cb_status cb_partial_attn_plan(const cb_geom *geom, const cb_ragged *rg,
+                               size_t workspace_bytes, cb_attn_plan *plan);
+
+/* Completes a pinned plan: reads mfma, key_split and key_chunk, checks them
+ * as cb_partial_attn_with_plan does (same errors; *plan unchanged on error)
+ * and fills the other fields, workspace_bytes included.  Host only. */
+cb_status cb_partial_attn_describe_plan(const cb_geom *geom, const cb_ragged *rg,
+                                        cb_attn_plan *plan);
+
+/*
+ * cb_partial_attn_with_plan -- cb_partial_attn with the decomposition pinned
+ * by the caller instead of chosen by the cost model (tuning, reproducible
+ * launch shapes).  Same operation, arguments and result as cb_partial_attn.
+ * Of *plan only three fields are read:
+ *   mfma      : 0 = plain kernel (any geometry), 1 = MFMA query tiles;
+ *   key_split : 1 or 2 (MFMA); UNSUPPORTED if the group size does not
+ *               divide the 256 / key_split query vectors of a tile;
+ *   key_chunk : 0 = no split over keys, else a positive multiple of
+ *               64 * key_split that splits no request with selected rows
+ *               into more than 8 chunks (INVALID_ARG otherwise).
+ * A split needs the workspace that cb_partial_attn_describe_plan() reports
+ * for the same fields (INVALID_ARG if workspace_bytes is smaller).
+ */
+cb_status cb_partial_attn_with_plan(const cb_geom *geom, const cb_ragged *rg,
+                                    const cb_attn_plan *plan, void *out,
+                                    const void *q_c, const int32_t *sel_local,
+                                    const int32_t *sel_global, const void *k_fused,
+                                    const void *v_fused, float softmax_scale,
+                                    void *workspace, size_t workspace_bytes,
+                                    void *stream);
+
 /* Every argument of one layer of the blend. */
 typedef struct cb_layer_args {
   cb_geom geom;
@@ -251,7 +302,7 @@ const char *cb_last_error(void);
 /* ABI revision of this header (bumped on any incompatible change). */
 int32_t cb_abi_version(void);
 
-#define CB_ABI_VERSION 3
+#define CB_ABI_VERSION 4
 
 #ifdef __cplusplus
 }

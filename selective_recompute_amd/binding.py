@@ -51,6 +51,13 @@ class LayerArgs(ctypes.Structure):
                 ("dev_source", ctypes.c_int32)]
 
 
+class AttnPlan(ctypes.Structure):
+    _fields_ = [("mfma", ctypes.c_int32), ("key_split", ctypes.c_int32),
+                ("rows_per_tile", ctypes.c_int32), ("key_chunk", ctypes.c_int32),
+                ("tiles", ctypes.c_int64), ("workgroups", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
 class CbError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{_STATUS.get(status, status)}: {message}")
@@ -81,6 +88,15 @@ _SIGNATURES = {
                         ctypes.c_void_p],
     "cb_partial_attn_workspace_size": [ctypes.POINTER(Geom), ctypes.POINTER(Ragged),
                                        ctypes.POINTER(ctypes.c_size_t)],
+    "cb_partial_attn_plan": [ctypes.POINTER(Geom), ctypes.POINTER(Ragged), ctypes.c_size_t,
+                             ctypes.POINTER(AttnPlan)],
+    "cb_partial_attn_describe_plan": [ctypes.POINTER(Geom), ctypes.POINTER(Ragged),
+                                      ctypes.POINTER(AttnPlan)],
+    "cb_partial_attn_with_plan": [ctypes.POINTER(Geom), ctypes.POINTER(Ragged),
+                                  ctypes.POINTER(AttnPlan), ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
+                                  ctypes.c_size_t, ctypes.c_void_p],
     "cb_blend_layer": [ctypes.POINTER(LayerArgs), ctypes.c_void_p],
 }
 
@@ -223,6 +239,26 @@ def attn_workspace_bytes(g: Geom, rb: RaggedBatch) -> int:
     return int(n.value)
 
 
+def attn_plan(g: Geom, rb: RaggedBatch, workspace_bytes: Optional[int] = None) -> dict:
+    """The decomposition cb_partial_attn uses (cb_attn_plan as a dict);
+    workspace_bytes None = as much as the plan can use."""
+    plan = AttnPlan()
+    rg = rb.struct()
+    ws = ctypes.c_size_t(-1).value if workspace_bytes is None else workspace_bytes
+    check(lib().cb_partial_attn_plan(ctypes.byref(g), ctypes.byref(rg), ws, ctypes.byref(plan)))
+    return {name: getattr(plan, name) for name, _ in AttnPlan._fields_}
+
+
+def describe_plan(g: Geom, rb: RaggedBatch, mfma: int = 1, key_split: int = 1,
+                  key_chunk: int = 0) -> dict:
+    """A pinned plan with its derived fields (cb_partial_attn_describe_plan)."""
+    plan = AttnPlan(mfma, key_split, 0, key_chunk, 0, 0, 0)
+    rg = rb.struct()
+    check(lib().cb_partial_attn_describe_plan(ctypes.byref(g), ctypes.byref(rg),
+                                              ctypes.byref(plan)))
+    return {name: getattr(plan, name) for name, _ in AttnPlan._fields_}
+
+
 def workspace_tensor(nbytes: int, device="cuda") -> Optional[torch.Tensor]:
     """A device buffer of at least nbytes (16-byte aligned), or None for 0."""
     if nbytes <= 0:
@@ -242,6 +278,20 @@ def partial_attn(g: Geom, rb: RaggedBatch, out, q_c, sel_local, sel_global, k_fu
                                 _dev(sel_local, torch.int32), _dev(sel_global, torch.int32),
                                 _dev(k_fused), _dev(v_fused), softmax_scale, ws_ptr, ws_bytes,
                                 _stream(stream)))
+
+
+def partial_attn_with_plan(g: Geom, rb: RaggedBatch, plan: dict, out, q_c, sel_local,
+                           sel_global, k_fused, v_fused, softmax_scale: float,
+                           workspace: Optional[torch.Tensor] = None, stream=None):
+    """cb_partial_attn with a pinned plan (a dict with mfma, key_split, key_chunk)."""
+    p = AttnPlan(plan["mfma"], plan.get("key_split", 1), 0, plan.get("key_chunk", 0), 0, 0, 0)
+    rg = rb.struct()
+    ws_ptr, ws_bytes = _ws(workspace)
+    check(lib().cb_partial_attn_with_plan(ctypes.byref(g), ctypes.byref(rg), ctypes.byref(p),
+                                          _dev(out), _dev(q_c), _dev(sel_local, torch.int32),
+                                          _dev(sel_global, torch.int32), _dev(k_fused),
+                                          _dev(v_fused), softmax_scale, ws_ptr, ws_bytes,
+                                          _stream(stream)))
 
 
 def blend_layer(g: Geom, rb: RaggedBatch, *, k, v, k_new_c, v_new_c, q_c, delta, cand_idx,

@@ -240,29 +240,35 @@ cb_status validate_attn(const cb_geom *geom, const cb_ragged *rg, void *out, con
 
 constexpr int kNoSplit = 1 << 30;
 
-// Cost model of one MFMA attention launch, for choosing the key chunk.  The
-// figures were measured on MI355X at head_dim 128 (they scale with head_dim):
-// one 64-key tile of a 256-query unit takes ~2.1 us with every CU busy, a
-// workgroup spends ~3.6 us before its first tile (three dependent loads:
-// request offsets, selected rows, Q) and ~1 us writing its partial; the
-// combine launch costs ~3 us plus its partials read at ~4.5 TB/s.
+// Cost model of one MFMA attention launch, for choosing the key split and
+// the key chunk.  The figures were measured on MI355X at head_dim 128 (they
+// scale with head_dim): 64 keys of a 256-query unit take ~2.1 us with every
+// CU busy, and kKeySplitTile of that for a 128-query unit whose 128-key
+// tiles are split over two wave groups; a workgroup spends ~3.6 us before
+// its first tile (three dependent loads: request offsets, selected rows, Q)
+// and ~1 us writing its partial; the combine launch costs ~3 us plus its
+// partials read at ~4.5 TB/s.
 constexpr double kTileUs = 2.1, kSetupUs = 3.6, kPartialUs = 1.0, kCombineUs = 3.0;
+constexpr double kKeySplitTile = 0.55;
 constexpr double kCombineBytesPerUs = 4.5e6;
 // CUs the simulated dispatch fills: 240 of the 256, a margin against plans
 // that fit one more round only if the selected rows sit exactly as assumed.
 constexpr int kSimCUs = 240;
 
-// Estimated duration (us) of the launch with key chunk `kc` (kNoSplit: none),
-// and the number of units that do work.  The selected rows of a request are
-// taken as evenly spread over its tokens, so query tile t ends near position
-// min(k, (t+1) rows) * n / k.  Units are dispatched in the kernel's order
-// (request by request, chunk by chunk, longest tile first), each to the
-// earliest free group of CUs; the n_kv_heads workgroups of a unit run side by
-// side, so one "slot" stands for n_kv_heads CUs.
-double estimate_attn_us(const cb_geom *g, const cb_ragged *rg, int rows, int64_t kc,
+// Estimated duration (us) of the launch with key split `ks`, `rows` selected
+// rows per tile and key chunk `kc` (kNoSplit: none), and the number of units
+// that do work.  The selected rows of a request are taken as evenly spread
+// over its tokens, so query tile t ends near position min(k, (t+1) rows) n / k.
+// Units are dispatched in the kernel's order (request by request, chunk by
+// chunk, longest tile first), each to the earliest free group of CUs; the
+// n_kv_heads workgroups of a unit run side by side, so one "slot" stands for
+// n_kv_heads CUs.
+double estimate_attn_us(const cb_geom *g, const cb_ragged *rg, int ks, int rows, int64_t kc,
                         int64_t *active) {
   const int n_slots = std::max(1, kSimCUs / g->n_kv_heads);
-  const double tile_us = kTileUs * g->head_dim / 128.0;
+  const double tile_us = kTileUs * g->head_dim / 128.0 * (ks == 2 ? kKeySplitTile : 1.0);
+  const double partial_us = kPartialUs / ks;
+  const int64_t kt = 64 * ks;  // keys per tile
   std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
   for (int i = 0; i < n_slots; ++i) free_at.push(0.0);
   bool split = false;
@@ -279,8 +285,8 @@ double estimate_attn_us(const cb_geom *g, const cb_ragged *rg, int rows, int64_t
         const int64_t end = (std::min(k, (t + 1) * rows) * n + k - 1) / k;
         const int64_t lo = c * kc, hi = std::min(end, lo + kc);
         if (hi <= lo) continue;
-        const double us = kSetupUs + (double)((hi - lo + 63) / 64) * tile_us +
-                          (chunks > 1 ? kPartialUs : 0.0);
+        const double us = kSetupUs + (double)((hi - lo + kt - 1) / kt * ks) * tile_us +
+                          (chunks > 1 ? partial_us : 0.0);
         const double start = free_at.top();
         free_at.pop();
         free_at.push(start + us);
@@ -295,30 +301,55 @@ double estimate_attn_us(const cb_geom *g, const cb_ragged *rg, int rows, int64_t
   *active = busy;
   if (split)
     makespan += kCombineUs + (double)busy * g->n_kv_heads *
-                                 (double)cb::attn_unit_bytes(g->head_dim) / kCombineBytesPerUs;
+                                 (double)cb::attn_unit_bytes(g->head_dim, ks) / kCombineBytesPerUs;
   return makespan;
 }
 
-// Tile and key-chunk decomposition of the MFMA attention, from host mirrors
-// only.  When the query tiles alone give fewer than 1024 workgroups, long
-// rows may be split over key chunks (a multiple of 64 keys, at least 256, at
-// most attn_max_chunks() per request); the cost model above picks the chunk
-// count with the shortest estimated launch, among the plans whose workspace
-// fits in `ws_avail`.
-cb::AttnPlan plan_attn(const cb_geom *g, const cb_ragged *rg, size_t ws_avail) {
-  cb::AttnPlan pl{};
-  pl.rows_per_tile = cb::attn_mfma_rows_per_tile(g->dtype, g->n_q_heads, g->n_kv_heads,
-                                                 g->head_dim);
-  pl.key_chunk = kNoSplit;
-  if (pl.rows_per_tile == 0) return pl;
+// Fills the counts of an MFMA plan whose key split, rows per tile and key
+// chunk are set: tiles, units, split, largest chunk count, workspace.
+void finish_plan(const cb_geom *g, const cb_ragged *rg, cb::AttnPlan &pl) {
   const int rows = pl.rows_per_tile;
-  int64_t max_n = 0;
+  pl.tiles = pl.units = 0;
+  pl.split = false;
+  pl.max_chunks = 1;
   for (int32_t r = 0; r < rg->n_req; ++r) {
     const int64_t kr = rg->h_sel_off[r + 1] - rg->h_sel_off[r];
-    pl.tiles += (kr + rows - 1) / rows;
-    if (kr > 0) max_n = std::max<int64_t>(max_n, rg->h_tok_off[r + 1] - rg->h_tok_off[r]);
+    const int64_t n = rg->h_tok_off[r + 1] - rg->h_tok_off[r];
+    const int64_t tr = (kr + rows - 1) / rows;
+    const int64_t cr = (n + pl.key_chunk - 1) / pl.key_chunk;
+    pl.tiles += tr;
+    pl.units += tr * cr;
+    if (tr > 0) {
+      if (cr > 1) pl.split = true;
+      pl.max_chunks = std::max<int>(pl.max_chunks, (int)cr);
+    }
   }
-  auto count_units = [&](int64_t kc, bool &split) {
+  pl.ws_bytes = pl.split ? (size_t)pl.units * g->n_kv_heads *
+                               cb::attn_unit_bytes(g->head_dim, pl.key_split)
+                         : 0;
+}
+
+// Decomposition of the MFMA attention, from host mirrors only.  When the
+// query tiles of 256 query vectors give 1024 workgroups or more, that is the
+// plan.  Otherwise the cost model above picks, among the plans whose
+// workspace fits in `ws_avail`, the shortest of: key split 1 or 2 (2 only
+// when its working workgroups fit on the CUs at once), each either unsplit
+// or with long rows split over key chunks (a multiple of the tile, 64 or 128
+// keys, at least 256, at most attn_max_chunks() per request).
+cb::AttnPlan plan_attn(const cb_geom *g, const cb_ragged *rg, size_t ws_avail) {
+  cb::AttnPlan pl{};
+  pl.key_split = 1;
+  pl.key_chunk = kNoSplit;
+  pl.rows_per_tile = cb::attn_mfma_rows_per_tile(g->dtype, g->n_q_heads, g->n_kv_heads,
+                                                 g->head_dim, 1);
+  if (pl.rows_per_tile == 0) return pl;
+  auto count_tiles = [&](int rows) {
+    int64_t tiles = 0;
+    for (int32_t r = 0; r < rg->n_req; ++r)
+      tiles += (rg->h_sel_off[r + 1] - rg->h_sel_off[r] + rows - 1) / rows;
+    return tiles;
+  };
+  auto count_units = [&](int rows, int64_t kc, bool &split) {
     int64_t units = 0;
     split = false;
     for (int32_t r = 0; r < rg->n_req; ++r) {
@@ -331,42 +362,97 @@ cb::AttnPlan plan_attn(const cb_geom *g, const cb_ragged *rg, size_t ws_avail) {
     }
     return units;
   };
-  const int64_t blocks = pl.tiles * g->n_kv_heads;
+  int64_t max_n = 0;
+  for (int32_t r = 0; r < rg->n_req; ++r)
+    if (rg->h_sel_off[r + 1] > rg->h_sel_off[r])
+      max_n = std::max<int64_t>(max_n, rg->h_tok_off[r + 1] - rg->h_tok_off[r]);
+  const int64_t blocks = count_tiles(pl.rows_per_tile) * g->n_kv_heads;
   if (blocks > 0 && blocks < 1024) {
     int64_t active = 0;
-    double best = estimate_attn_us(g, rg, rows, kNoSplit, &active);
-    int64_t prev_kc = 0;
-    for (int c = 2; c <= cb::attn_max_chunks(); ++c) {
-      int64_t kc = (max_n + c - 1) / c;
-      kc = std::max<int64_t>(256, (kc + 63) / 64 * 64);
-      if (kc >= max_n || kc == prev_kc) continue;
-      prev_kc = kc;
+    double best = estimate_attn_us(g, rg, 1, pl.rows_per_tile, kNoSplit, &active);
+    auto consider = [&](int ks, int rows, int64_t kc) {
       bool split = false;
-      const size_t ws = (size_t)count_units(kc, split) * g->n_kv_heads *
-                        cb::attn_unit_bytes(g->head_dim);
-      if (ws > ws_avail) continue;
-      const double us = estimate_attn_us(g, rg, rows, kc, &active);
+      const int64_t units = count_units(rows, kc, split);
+      const size_t ws =
+          split ? (size_t)units * g->n_kv_heads * cb::attn_unit_bytes(g->head_dim, ks) : 0;
+      if (ws > ws_avail) return;
+      const double us = estimate_attn_us(g, rg, ks, rows, kc, &active);
+      // Key split 2 only where its working units fit in one round of the CUs:
+      // there the shorter units decide; with more rounds its ~5% higher cost
+      // per flop and its doubled K/V reads through L2 decide against it (in
+      // the full blend step: -4% at 2k tokens and one round, +1.5% at 6k
+      // tokens and two rounds).
+      if (ks == 2 && active * g->n_kv_heads > kSimCUs) return;
       if (us < best) {
         best = us;
-        pl.key_chunk = (int)kc;
+        pl.key_split = ks;
+        pl.rows_per_tile = rows;
+        pl.key_chunk = (int)std::min<int64_t>(kc, kNoSplit);
+      }
+    };
+    for (int ks = 1; ks <= 2; ++ks) {
+      const int rows = cb::attn_mfma_rows_per_tile(g->dtype, g->n_q_heads, g->n_kv_heads,
+                                                   g->head_dim, ks);
+      if (rows == 0) continue;
+      if (ks > 1) consider(ks, rows, kNoSplit);
+      int64_t prev_kc = 0;
+      for (int c = 2; c <= cb::attn_max_chunks(); ++c) {
+        int64_t kc = (max_n + c - 1) / c;
+        kc = std::max<int64_t>(256, (kc + 64 * ks - 1) / (64 * ks) * (64 * ks));
+        if (kc >= max_n || kc == prev_kc) continue;
+        prev_kc = kc;
+        consider(ks, rows, kc);
       }
     }
   }
-  pl.units = count_units(pl.key_chunk, pl.split);
-  pl.max_chunks = 1;
-  for (int32_t r = 0; r < rg->n_req; ++r)
-    if (rg->h_sel_off[r + 1] > rg->h_sel_off[r])
-      pl.max_chunks = std::max<int>(pl.max_chunks, (int)(((int64_t)rg->h_tok_off[r + 1] -
-                                                          rg->h_tok_off[r] + pl.key_chunk - 1) /
-                                                         pl.key_chunk));
-  pl.ws_bytes = pl.split ? (size_t)pl.units * g->n_kv_heads * cb::attn_unit_bytes(g->head_dim) : 0;
+  finish_plan(g, rg, pl);
   return pl;
 }
 
-cb_status run_attn(const cb_geom *geom, const cb_ragged *rg, void *out, const void *q_c,
-                   const int32_t *sel_local, const int32_t *sel_global, const void *k_fused,
-                   const void *v_fused, float softmax_scale, void *workspace,
-                   size_t workspace_bytes, hipStream_t stream) {
+// A plan the caller pins (cb_partial_attn_with_plan): only mfma, key_split
+// and key_chunk are read; the rest is derived as for a chosen plan.
+cb_status pinned_plan(const cb_geom *g, const cb_ragged *rg, const cb_attn_plan *in,
+                      size_t ws_avail, cb::AttnPlan &pl) {
+  pl = cb::AttnPlan{};
+  pl.key_split = 1;
+  pl.key_chunk = kNoSplit;
+  if (in->mfma == 0) return CB_OK;  // plain kernel: any geometry
+  if (in->mfma != 1) return fail(CB_ERR_INVALID_ARG, "plan.mfma must be 0 or 1");
+  if (in->key_split != 1 && in->key_split != 2)
+    return fail(CB_ERR_INVALID_ARG, "plan.key_split must be 1 or 2");
+  pl.key_split = in->key_split;
+  pl.rows_per_tile = cb::attn_mfma_rows_per_tile(g->dtype, g->n_q_heads, g->n_kv_heads,
+                                                 g->head_dim, pl.key_split);
+  if (pl.rows_per_tile == 0)
+    return fail(CB_ERR_UNSUPPORTED,
+                "the MFMA kernel does not cover this geometry with key split %d (bf16, "
+                "head_dim 32/64/128, a group size dividing %d query vectors)",
+                pl.key_split, 256 / pl.key_split);
+  const int tile_keys = 64 * pl.key_split;
+  if (in->key_chunk < 0 || in->key_chunk % tile_keys != 0)
+    return fail(CB_ERR_INVALID_ARG, "plan.key_chunk %d must be 0 or a positive multiple of %d",
+                in->key_chunk, tile_keys);
+  if (in->key_chunk > 0) {
+    pl.key_chunk = in->key_chunk;
+    for (int32_t r = 0; r < rg->n_req; ++r) {
+      const int64_t n = rg->h_tok_off[r + 1] - rg->h_tok_off[r];
+      if (rg->h_sel_off[r + 1] > rg->h_sel_off[r] &&
+          (n + pl.key_chunk - 1) / pl.key_chunk > cb::attn_max_chunks())
+        return fail(CB_ERR_INVALID_ARG, "plan.key_chunk splits request %d into more than %d chunks",
+                    (int)r, cb::attn_max_chunks());
+    }
+  }
+  finish_plan(g, rg, pl);
+  if (pl.ws_bytes > ws_avail)
+    return fail(CB_ERR_INVALID_ARG, "workspace_bytes %zu is smaller than the plan's %zu",
+                ws_avail, pl.ws_bytes);
+  return CB_OK;
+}
+
+cb_status run_attn(const cb_geom *geom, const cb_ragged *rg, const cb::AttnPlan &plan,
+                   void *out, const void *q_c, const int32_t *sel_local,
+                   const int32_t *sel_global, const void *k_fused, const void *v_fused,
+                   float softmax_scale, void *workspace, hipStream_t stream) {
   cb::AttnArgs a;
   a.out = out; a.q_c = q_c; a.sel_local = sel_local; a.sel_global = sel_global;
   a.k_fused = k_fused; a.v_fused = v_fused; a.tok_off = rg->tok_off; a.sel_off = rg->sel_off;
@@ -375,7 +461,6 @@ cb_status run_attn(const cb_geom *geom, const cb_ragged *rg, void *out, const vo
   a.n_q_heads = geom->n_q_heads; a.n_kv_heads = geom->n_kv_heads; a.head_dim = geom->head_dim;
   a.softmax_scale = softmax_scale;
   if (a.k_total == 0) return CB_OK;
-  const cb::AttnPlan plan = plan_attn(geom, rg, workspace ? workspace_bytes : 0);
   if (plan.rows_per_tile > 0) {
     if (plan.units * geom->n_kv_heads > INT32_MAX)
       return fail(CB_ERR_UNSUPPORTED, "too many attention work units");
@@ -459,8 +544,27 @@ CB_EXPORT cb_status cb_partial_attn(const cb_geom *geom, const cb_ragged *rg, vo
   CB_TRY(validate_attn(geom, rg, out, q_c, sel_local, sel_global, k_fused, v_fused,
                        softmax_scale));
   CB_TRY(need_ptr(workspace, "workspace", workspace_bytes > 0));
-  return run_attn(geom, rg, out, q_c, sel_local, sel_global, k_fused, v_fused, softmax_scale,
-                  workspace, workspace_bytes, (hipStream_t)stream);
+  const cb::AttnPlan plan = plan_attn(geom, rg, workspace ? workspace_bytes : 0);
+  return run_attn(geom, rg, plan, out, q_c, sel_local, sel_global, k_fused, v_fused,
+                  softmax_scale, workspace, (hipStream_t)stream);
+}
+
+CB_EXPORT cb_status cb_partial_attn_with_plan(const cb_geom *geom, const cb_ragged *rg,
+                                              const cb_attn_plan *plan, void *out,
+                                              const void *q_c, const int32_t *sel_local,
+                                              const int32_t *sel_global, const void *k_fused,
+                                              const void *v_fused, float softmax_scale,
+                                              void *workspace, size_t workspace_bytes,
+                                              void *stream) {
+  g_last_error.clear();
+  if (!plan) return fail(CB_ERR_INVALID_ARG, "plan is NULL");
+  CB_TRY(validate_attn(geom, rg, out, q_c, sel_local, sel_global, k_fused, v_fused,
+                       softmax_scale));
+  CB_TRY(need_ptr(workspace, "workspace", workspace_bytes > 0));
+  cb::AttnPlan pl;
+  CB_TRY(pinned_plan(geom, rg, plan, workspace ? workspace_bytes : 0, pl));
+  return run_attn(geom, rg, pl, out, q_c, sel_local, sel_global, k_fused, v_fused,
+                  softmax_scale, workspace, (hipStream_t)stream);
 }
 
 CB_EXPORT cb_status cb_partial_attn_workspace_size(const cb_geom *geom, const cb_ragged *rg,
@@ -471,6 +575,47 @@ CB_EXPORT cb_status cb_partial_attn_workspace_size(const cb_geom *geom, const cb
   CB_TRY(check_geom(geom));
   CB_TRY(check_ragged(rg, true, false, true));
   *bytes = plan_attn(geom, rg, SIZE_MAX).ws_bytes;
+  return CB_OK;
+}
+
+namespace {
+void export_plan(const cb_geom *geom, const cb_ragged *rg, const cb::AttnPlan &pl,
+                 cb_attn_plan *plan) {
+  *plan = cb_attn_plan{};
+  if (pl.rows_per_tile == 0) {
+    plan->workgroups = (int64_t)rg->h_sel_off[rg->n_req] * geom->n_q_heads;
+    return;
+  }
+  plan->mfma = 1;
+  plan->key_split = pl.key_split;
+  plan->rows_per_tile = pl.rows_per_tile;
+  plan->key_chunk = pl.split ? pl.key_chunk : 0;
+  plan->tiles = pl.tiles;
+  plan->workgroups = pl.units * geom->n_kv_heads;
+  plan->workspace_bytes = pl.ws_bytes;
+}
+}  // namespace
+
+CB_EXPORT cb_status cb_partial_attn_plan(const cb_geom *geom, const cb_ragged *rg,
+                                         size_t workspace_bytes, cb_attn_plan *plan) {
+  g_last_error.clear();
+  if (!plan) return fail(CB_ERR_INVALID_ARG, "plan is NULL");
+  *plan = cb_attn_plan{};
+  CB_TRY(check_geom(geom));
+  CB_TRY(check_ragged(rg, true, false, true));
+  export_plan(geom, rg, plan_attn(geom, rg, workspace_bytes), plan);
+  return CB_OK;
+}
+
+CB_EXPORT cb_status cb_partial_attn_describe_plan(const cb_geom *geom, const cb_ragged *rg,
+                                                  cb_attn_plan *plan) {
+  g_last_error.clear();
+  if (!plan) return fail(CB_ERR_INVALID_ARG, "plan is NULL");
+  CB_TRY(check_geom(geom));
+  CB_TRY(check_ragged(rg, true, false, true));
+  cb::AttnPlan pl;
+  CB_TRY(pinned_plan(geom, rg, plan, SIZE_MAX, pl));
+  export_plan(geom, rg, pl, plan);
   return CB_OK;
 }
 
@@ -521,8 +666,9 @@ CB_EXPORT cb_status cb_blend_layer(const cb_layer_args *a, void *stream) {
                                     a->sel_global, k_total,
                                     (int32_t)(row_elems(geom) * elem_size(geom->dtype)), s),
                     "fuse_scatter"));
-  return run_attn(geom, rg, a->out, a->q_c, a->sel_local, a->sel_global, a->k, a->v,
-                  a->softmax_scale, a->workspace, a->workspace_bytes, s);
+  const cb::AttnPlan plan = plan_attn(geom, rg, a->workspace ? a->workspace_bytes : 0);
+  return run_attn(geom, rg, plan, a->out, a->q_c, a->sel_local, a->sel_global, a->k, a->v,
+                  a->softmax_scale, a->workspace, s);
 }
 
 CB_EXPORT const char *cb_status_str(cb_status status) {

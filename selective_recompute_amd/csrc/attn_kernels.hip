@@ -15,22 +15,31 @@ namespace cb {
 // ---------------------------------------------------------------------------
 // MFMA kernel (bf16, head_dim HD in {32, 64, 128}).
 //
-// Work unit = (query tile, KV head g, key chunk).  A query tile holds 128
-// query vectors: rows_per_tile selected rows of one request times the
+// Work unit = (query tile, KV head g, key chunk).  A query tile holds the
+// query vectors of rows_per_tile selected rows of one request times the
 // G = Hq/Hkv query heads that read KV head g, so one K/V stream serves all of
-// them.  A workgroup of 4 waves owns a unit; each wave owns 32 query vectors.
-// Keys stream through LDS in tiles of 64.  All products use
+// them.  A workgroup of 8 waves (two per SIMD) owns a unit; each wave owns 32
+// query vectors.  Keys stream through LDS in tiles of 64.  All products use
 // v_mfma_f32_32x32x16_bf16, which on gfx950 sustains about twice the rate of
 // the 16x16x32 form.  Lane l of a 32x32 result holds rows
 // 8(r/4) + 4(l/32) + r%4 (r = 0..15) of column l%32.
 //
+//  * Key split KS: with KS = 1 the 8 waves cover 256 query vectors over
+//    64-key tiles in 4 LDS stages; with KS = 2 they form two key groups over
+//    the same 128 query vectors and 128-key tiles in 2 stages (the same LDS
+//    bytes), group h taking keys 64h .. 64h+63 of every tile, so each wave
+//    does the same work between two barriers; group 1 hands its (max, sum,
+//    O) to group 0 through LDS at the end.  KS = 2 halves the time of a unit
+//    over the same keys (the longest unit bounds small launches) without any
+//    partial in global memory, at the price of twice the K/V staging per
+//    query and a shallower prefetch.
 //  * Staging: K and V tiles go global -> LDS with global_load_lds_dwordx4
-//    (no registers), two stages: while tile t is multiplied, tile t+1 is in
-//    flight.  The LDS tiles are row-major with an XOR swizzle of the 16-byte
-//    chunks of each key row (different for K and V) so that the two read
-//    patterns below are free of bank conflicts.
-//  * S^T = K Q^T (keys on the M side, queries on the N side) in two 32-key
-//    blocks: a lane's 32 scores all belong to one query column, so the
+//    (no registers) through the LDS stages: tile t + stages - 1 is issued
+//    while tile t is multiplied.  The LDS tiles are row-major with an XOR
+//    swizzle of the 16-byte chunks of each key row (different for K and V)
+//    so that the two read patterns below are free of bank conflicts.
+//  * S^T = K Q^T (keys on the M side, queries on the N side) in 32-key
+//    blocks: a lane's scores all belong to one query column, so the
 //    online-softmax statistics stay in the lane and its partner l^32, and the
 //    probabilities of 16 consecutive keys are 8 consecutive accumulator
 //    registers -- already the B operand of the second product.
@@ -81,9 +90,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
-// Bytes of one split partial: fp16 O in fragment order, then three fp32
-// values per query vector (running max, running sum, largest |O|).
-template <int HD> constexpr int partial_bytes() { return kQT * HD * 2 + 3 * kQT * 4; }
+// Bytes of one split partial of QT query vectors: fp16 O in fragment order,
+// then three fp32 values per query vector (running max, running sum, largest
+// |O|).
+template <int HD, int QT> constexpr int partial_bytes() { return QT * HD * 2 + 3 * QT * 4; }
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void global_cvoid;
@@ -169,22 +179,29 @@ __device__ inline void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int HD>
+template <int HD, int KS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_mfma_kernel(const AttnParams p) {
+  static_assert(KS == 1 || KS == 2, "key split of 1 or 2 groups");
+  constexpr int QT = kQT / KS;            // query vectors per unit
+  constexpr int WPG = kWaves / KS;        // waves per key group
+  constexpr int KT = kKeyTile * KS;       // keys per tile: 64 per key group
+  constexpr int STAGES = kStages / KS;    // tiles resident in LDS (the same bytes)
+  constexpr int NSB = 2;                  // 32-key blocks per wave and tile
   constexpr int NKS = HD / 16;            // 16-wide contraction steps of S over head_dim
   constexpr int NDT = HD / 32;            // 32-dim output blocks
   constexpr int CPR = HD / 8;             // 16-byte chunks per key row
-  constexpr int TILE = kKeyTile * HD;     // elements per tensor per stage
+  constexpr int TILE = KT * HD;           // elements per tensor per stage
   constexpr int NI = TILE / 512;          // 1 KiB DMA instructions per tensor per tile
   constexpr int DMA_WAVES = NI < kWaves ? NI : kWaves;
   constexpr int IPW = NI / DMA_WAVES;     // per issuing wave and tensor
   constexpr int PER_TILE = 2 * IPW;       // vector-memory ops per tile and issuing wave
-  __shared__ __attribute__((aligned(1024))) bf16 kst[kStages][TILE];
-  __shared__ __attribute__((aligned(1024))) bf16 vst[kStages][TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 kst[STAGES][TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 vst[STAGES][TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
+  const int kg = wave / WPG;              // key group: keys 64kg .. 64kg+63 of each tile
   const int g = blockIdx.x % p.hkv;
   int r, tile, chunk, nchunks;
   if (!locate_unit(p, (int)(blockIdx.x / p.hkv), r, tile, chunk, nchunks)) return;
@@ -197,7 +214,7 @@ void attn_mfma_kernel(const AttnParams p) {
   if (kb > p_last) return;  // whole chunk after the tile's last row (uniform)
   const int k_begin = (int)kb;
   const int k_end = (int)min((int64_t)p_last + 1, kb + p.key_chunk);
-  const int n_kt = (k_end - k_begin + kKeyTile - 1) / kKeyTile;
+  const int n_kt = (k_end - k_begin + KT - 1) / KT;
 
   // DMA slots of this wave: instruction i writes 64 consecutive 16-byte chunks
   // of the tile; lane -> (row, physical chunk) -> logical chunk.  Rows past
@@ -218,11 +235,11 @@ void attn_mfma_kernel(const AttnParams p) {
   const char *vbase = (const char *)(p.v_fused + (int64_t)g * HD);
   auto issue_tile = [&](int t) {
     if (!dma_wave) return;
-    const int k0 = k_begin + t * kKeyTile;
+    const int k0 = k_begin + t * KT;
     const int64_t tb = (int64_t)k0 * rs * 2;
-    const bool clamp = k0 + kKeyTile - 1 > p_last;
-    const uint32_t kd = lds_addr(kst[t % kStages]) + wave * IPW * 1024;
-    const uint32_t vd = lds_addr(vst[t % kStages]) + wave * IPW * 1024;
+    const bool clamp = k0 + KT - 1 > p_last;
+    const uint32_t kd = lds_addr(kst[t % STAGES]) + wave * IPW * 1024;
+    const uint32_t vd = lds_addr(vst[t % STAGES]) + wave * IPW * 1024;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       uint32_t back = 0;
@@ -234,7 +251,7 @@ void attn_mfma_kernel(const AttnParams p) {
 
   // This lane's query column.  Padding columns (past the tile's last row)
   // see every key; their results are dropped.
-  const int qv = wave * 32 + col;
+  const int qv = (wave - kg * WPG) * 32 + col;
   const int qrow = qv / p.group, qhh = qv - qrow * p.group;
   const bool qvalid = qrow < ns;
   int p_q;
@@ -246,7 +263,7 @@ void attn_mfma_kernel(const AttnParams p) {
 #pragma unroll
     for (int st = 0; st < NKS; ++st) qreg[st] = *reinterpret_cast<const bf16x8 *>(qp + 16 * st);
   }
-  for (int t = 0; t < kStages - 1 && t < n_kt; ++t) issue_tile(t);
+  for (int t = 0; t < STAGES - 1 && t < n_kt; ++t) issue_tile(t);
 
   f32x16 o[NDT];
 #pragma unroll
@@ -276,53 +293,57 @@ void attn_mfma_kernel(const AttnParams p) {
   // in flight.  The compiler, which does not count the copies into LDS, adds
   // its own waits before the first uses of Q; it peels them into the first
   // iteration, so the tile loop keeps only the waits below.
-  if (n_kt >= 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * PER_TILE));
-  else if (n_kt == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(PER_TILE));
+  const int ahead0 = min(STAGES - 2, n_kt - 1);  // tiles issued after tile 0
+  if (ahead0 >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * PER_TILE));
+  else if (ahead0 == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(PER_TILE));
   else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
 
   for (int kt = 0; kt < n_kt; ++kt) {
-    const int k0 = k_begin + kt * kKeyTile;
+    const int k0 = k_begin + kt * KT;
     // Tile kt has landed for this wave's share; the tiles issued after it
-    // (up to kStages - 2 of them) may stay in flight.  The barrier then makes
+    // (up to STAGES - 2 of them) may stay in flight.  The barrier then makes
     // every wave's share visible and tells that all waves are done with tile
-    // kt - 1, whose stage is refilled with tile kt + kStages - 1.
+    // kt - 1, whose stage is refilled with tile kt + STAGES - 1.
     if (kt > 0) {
-      const int ahead = min(kt + kStages - 2, n_kt - 1) - kt;
+      const int ahead = min(kt + STAGES - 2, n_kt - 1) - kt;
       if (ahead >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * PER_TILE));
       else if (ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(PER_TILE));
       else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
     phase_barrier();
-    if (kt + kStages - 1 < n_kt) issue_tile(kt + kStages - 1);
-    const bf16 *ks = kst[kt % kStages];
-    const bf16 *vs = vst[kt % kStages];
+    if (kt + STAGES - 1 < n_kt) issue_tile(kt + STAGES - 1);
+    const bf16 *ks = kst[kt % STAGES];
+    const bf16 *vs = vst[kt % STAGES];
 
-    // S^T: sacc[sb][r] = score(key k0 + 32sb + 8(r/4) + 4*half + r%4, column).
-    f32x16 sacc[2];
+    // S^T: sacc[sb][r] = score(key kg0 + 32sb + 8(r/4) + 4*half + r%4, column)
+    // for this wave's key group (kg0 = first key of the group in the tile).
+    const int kg0 = k0 + 32 * NSB * kg;
+    const bf16 *ksg = ks + NSB * kg * 32 * HD;
+    f32x16 sacc[NSB];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+    for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[sb][e] = 0.f;
 #pragma unroll
     for (int st = 0; st < NKS; ++st) {
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(ks + koff[st] + sb * 32 * HD);
+      for (int sb = 0; sb < NSB; ++sb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(ksg + koff[st] + sb * 32 * HD);
         sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[st], sacc[sb], 0, 0, 0);
       }
     }
 
-    if (k0 + kKeyTile - 1 > p_first) {  // causal mask (tiles past the first row)
+    if (kg0 + 32 * NSB - 1 > p_first) {  // causal mask (key blocks past the first row)
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+      for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          if (k0 + 32 * sb + 8 * (e >> 2) + 4 * half + (e & 3) > p_q) sacc[sb][e] = -INFINITY;
+          if (kg0 + 32 * sb + 8 * (e >> 2) + 4 * half + (e & 3) > p_q) sacc[sb][e] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+    for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[sb][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
@@ -337,9 +358,9 @@ void attn_mfma_kernel(const AttnParams p) {
       for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
     }
     const float neg_m = -m_run;
-    bf16x8 bp[4];  // probabilities of keys 16c .. 16c+15 of the tile
+    bf16x8 bp[2 * NSB];  // probabilities of keys kg0 + 16c .. kg0 + 16c + 15
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+    for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
       for (int e = 0; e < 16; ++e)
         bp[2 * sb + (e >> 3)][e & 7] =
@@ -348,7 +369,7 @@ void attn_mfma_kernel(const AttnParams p) {
     // (bf16), two per v_dot2c_f32_bf16, in two independent chains.
     float ps[2] = {0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < 2 * NSB; ++c)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         ps[i & 1] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{bp[c][2 * i], bp[c][2 * i + 1]},
@@ -356,11 +377,12 @@ void attn_mfma_kernel(const AttnParams p) {
     l_run += ps[0] + ps[1];
 
     // O^T += V^T P^T: per 16-key step c, one transposed V fragment per dim block.
+    const bf16 *vsg = vs + 2 * NSB * kg * 16 * HD;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < 2 * NSB; ++c) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const bf16 *vp = vs + voff[dt] + c * 16 * HD;
+        const bf16 *vp = vsg + voff[dt] + c * 16 * HD;
         const bf16x4 lo4 = lds_read_tr(vp);
         const bf16x4 hi4 = lds_read_tr(vp + 8 * HD);
         const bf16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -370,30 +392,72 @@ void attn_mfma_kernel(const AttnParams p) {
   }
 
   float l = l_run + __shfl_xor(l_run, 32, kWave);
+  if constexpr (KS == 2) {
+    // Key group 1 hands (running max, running sum, O) of its query vectors to
+    // group 0 through LDS (the stage buffers are free once every wave is past
+    // its last tile): O in fragment order, 16 bytes per lane and store.
+    static_assert(STAGES * TILE * 2 >= WPG * NDT * 16 * 64 * 4, "O exchange does not fit");
+    float *xo = reinterpret_cast<float *>(&vst[0][0]);
+    float *xm = reinterpret_cast<float *>(&kst[0][0]);
+    phase_barrier();
+    if (kg == 1) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 w = {o[dt][4 * q], o[dt][4 * q + 1], o[dt][4 * q + 2], o[dt][4 * q + 3]};
+          *reinterpret_cast<f32x4 *>(xo + 4 * ((((wave - WPG) * NDT + dt) * 4 + q) * 64 + lane)) = w;
+        }
+      if (half == 0) {
+        xm[qv] = m_run;
+        xm[QT + qv] = l;
+      }
+    }
+    phase_barrier();
+    if (kg == 0) {
+      const float mb = xm[qv], lb = xm[QT + qv];
+      const float mm = fmaxf(m_run, mb);
+      const float wa = __builtin_amdgcn_exp2f(m_run - mm), wb = __builtin_amdgcn_exp2f(mb - mm);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 w = *reinterpret_cast<const f32x4 *>(
+              xo + 4 * (((wave * NDT + dt) * 4 + q) * 64 + lane));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[dt][4 * q + i] = fmaf(o[dt][4 * q + i], wa, w[i] * wb);
+        }
+      l = fmaf(l, wa, lb * wb);
+      m_run = mm;
+    }
+  }
   if (nchunks == 1) {
     // Output through LDS (the K stage buffers are free once every wave is
-    // past its last tile): each wave writes its normalised bf16 rows (16-byte
-    // chunk index XOR-swizzled by the query vector against bank conflicts),
-    // then the workgroup stores 16-byte chunks in output order -- the G query
-    // heads of one selected row are adjacent in `out`, so a wave writes whole
-    // 1 KiB runs instead of 8 bytes per lane 256 bytes apart.
+    // past its last tile): each wave of key group 0 writes its normalised
+    // bf16 rows (16-byte chunk index XOR-swizzled by the query vector against
+    // bank conflicts), then the workgroup stores 16-byte chunks in output
+    // order -- the G query heads of one selected row are adjacent in `out`,
+    // so a wave writes whole 1 KiB runs instead of 8 bytes per lane 256
+    // bytes apart.
     constexpr int CPQ = HD / 8;  // 16-byte chunks per query vector
     bf16 *stage = &kst[0][0];
-    static_assert(kStages * TILE >= kQT * HD, "output staging does not fit");
+    static_assert(STAGES * TILE >= QT * HD, "output staging does not fit");
     phase_barrier();
-    const float inv = 1.f / l;
+    if (kg == 0) {
+      const float inv = 1.f / l;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        bf16x4 w;
+        for (int q = 0; q < 4; ++q) {
+          bf16x4 w;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = (bf16)(o[dt][4 * q + i] * inv);
-        const int chunk = (4 * dt + q) ^ (qv & (CPQ - 1));
-        *reinterpret_cast<bf16x4 *>(stage + qv * HD + 8 * chunk + 4 * half) = w;
-      }
+          for (int i = 0; i < 4; ++i) w[i] = (bf16)(o[dt][4 * q + i] * inv);
+          const int chunk = (4 * dt + q) ^ (qv & (CPQ - 1));
+          *reinterpret_cast<bf16x4 *>(stage + qv * HD + 8 * chunk + 4 * half) = w;
+        }
+    }
     phase_barrier();
-    for (int c = tid; c < kQT * CPQ; c += 64 * kWaves) {
+    for (int c = tid; c < QT * CPQ; c += 64 * kWaves) {
       const int v = c / CPQ, part = c - v * CPQ;
       const int vrow = v / p.group, vh = v - vrow * p.group;
       if (vrow < ns)
@@ -401,13 +465,13 @@ void attn_mfma_kernel(const AttnParams p) {
                                    8 * part) =
             *reinterpret_cast<const uint4 *>(stage + v * HD + 8 * (part ^ (v & (CPQ - 1))));
     }
-  } else {
+  } else if (kg == 0) {
     // Partial in fragment order: store (dt, q) of wave w writes 64 lanes x 8
     // contiguous bytes at fp16x4 index ((w*NDT + dt)*4 + q)*64 + lane.  Each
     // query vector's O is divided by its largest |O| (the two lanes l and
     // l ^ 32 hold its dims), so fp16 keeps 11 significant bits of every
     // value whatever the scale of V; the combine multiplies it back.
-    unsigned char *w = p.ws + (int64_t)blockIdx.x * partial_bytes<HD>();
+    unsigned char *w = p.ws + (int64_t)blockIdx.x * partial_bytes<HD, QT>();
     float amax = 0.f;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -426,10 +490,10 @@ void attn_mfma_kernel(const AttnParams p) {
         wo[(((wave * NDT + dt) * 4 + q) << 6) + lane] = h;
       }
     if (half == 0) {
-      float *meta = reinterpret_cast<float *>(w + kQT * HD * 2);
+      float *meta = reinterpret_cast<float *>(w + QT * HD * 2);
       meta[qv] = m_run;
-      meta[kQT + qv] = l;
-      meta[2 * kQT + qv] = amax;
+      meta[QT + qv] = l;
+      meta[2 * QT + qv] = amax;
     }
   }
 }
@@ -441,10 +505,9 @@ void attn_mfma_kernel(const AttnParams p) {
 // bytes.  Every chunk's loads are issued at once (unrolled over NC, the
 // plan's largest chunk count rounded up to 2, 4 or 8; inactive chunks clamped
 // to chunk 0 and weighted 0), so each thread waits for a single round of loads.
-template <int HD, int NC>
+template <int HD, int QT, int NC>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
-  constexpr int QT = kQT;
-  constexpr int UNIT = partial_bytes<HD>();
+  constexpr int UNIT = partial_bytes<HD, QT>();
   constexpr int GROUPS = QT * HD / 8 / 256;  // workgroups per (tile, head): 2 fragments per thread
   const int g = blockIdx.x % p.hkv;
   const int rest = blockIdx.x / p.hkv;
@@ -521,19 +584,47 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   *reinterpret_cast<bf16x4 *>(dst + 8) = o2;
 }
 
-int attn_mfma_rows_per_tile(int dtype, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim) {
+int attn_mfma_rows_per_tile(int dtype, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                            int key_split) {
   if (dtype != kBF16) return 0;
   if (head_dim != 32 && head_dim != 64 && head_dim != 128) return 0;
+  if (key_split != 1 && key_split != 2) return 0;
+  const int qt = kQT / key_split;
   const int group = n_q_heads / n_kv_heads;
-  if (group < 1 || group > kQT || kQT % group != 0) return 0;
-  return kQT / group;
+  if (group < 1 || group > qt || qt % group != 0) return 0;
+  return qt / group;
 }
 
-size_t attn_unit_bytes(int32_t head_dim) {
-  return (size_t)kQT * head_dim * 2 + 3 * (size_t)kQT * sizeof(float);
+size_t attn_unit_bytes(int32_t head_dim, int key_split) {
+  const size_t qt = (size_t)(kQT / key_split);
+  return qt * head_dim * 2 + 3 * qt * sizeof(float);
 }
 
 int attn_max_chunks() { return kMaxChunks; }
+
+template <int HD, int KS>
+static void launch_combine(const AttnParams &p, const AttnPlan &plan, int n_kv_heads,
+                           hipStream_t stream) {
+  constexpr int QT = kQT / KS;
+  const dim3 grid((unsigned)(plan.tiles * n_kv_heads * (QT * HD / 2048))), block(256);
+  if (plan.max_chunks <= 2)
+    hipLaunchKernelGGL((attn_combine_kernel<HD, QT, 2>), grid, block, 0, stream, p);
+  else if (plan.max_chunks <= 4)
+    hipLaunchKernelGGL((attn_combine_kernel<HD, QT, 4>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<HD, QT, kMaxChunks>), grid, block, 0, stream, p);
+}
+
+template <int HD, int KS>
+static hipError_t launch_hd(const AttnParams &p, const AttnPlan &plan, int n_kv_heads,
+                            hipStream_t stream) {
+  const dim3 grid((unsigned)(plan.units * n_kv_heads)), block(64 * kWaves);
+  hipLaunchKernelGGL((attn_mfma_kernel<HD, KS>), grid, block, 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !plan.split) return e;
+  launch_combine<HD, KS>(p, plan, n_kv_heads, stream);
+  return hipGetLastError();
+}
 
 hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &plan, hipStream_t stream) {
   if (plan.units == 0) return hipSuccess;
@@ -554,32 +645,20 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &plan, hipStream_t
   p.rows_per_tile = plan.rows_per_tile;
   p.key_chunk = plan.key_chunk;
   p.scale_log2 = a.softmax_scale * 1.4426950408889634f;
-  const dim3 grid((unsigned)(plan.units * a.n_kv_heads)), block(64 * kWaves);
-  switch (a.head_dim) {
-    case 32: hipLaunchKernelGGL(attn_mfma_kernel<32>, grid, block, 0, stream, p); break;
-    case 64: hipLaunchKernelGGL(attn_mfma_kernel<64>, grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL(attn_mfma_kernel<128>, grid, block, 0, stream, p); break;
+  const int h = a.n_kv_heads;
+  if (plan.key_chunk % (kKeyTile * plan.key_split) != 0) return hipErrorInvalidValue;
+  if (plan.key_split == 2) {
+    switch (a.head_dim) {
+      case 32: return launch_hd<32, 2>(p, plan, h, stream);
+      case 64: return launch_hd<64, 2>(p, plan, h, stream);
+      default: return launch_hd<128, 2>(p, plan, h, stream);
+    }
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !plan.split) return e;
-  const int groups = kQT / (512 / (a.head_dim / 4));
-  const dim3 cgrid((unsigned)(plan.tiles * a.n_kv_heads * groups)), cblock(256);
-#define CB_COMBINE(HD)                                                                          \
-  do {                                                                                          \
-    if (plan.max_chunks <= 2)                                                                   \
-      hipLaunchKernelGGL((attn_combine_kernel<HD, 2>), cgrid, cblock, 0, stream, p);            \
-    else if (plan.max_chunks <= 4)                                                              \
-      hipLaunchKernelGGL((attn_combine_kernel<HD, 4>), cgrid, cblock, 0, stream, p);            \
-    else                                                                                        \
-      hipLaunchKernelGGL((attn_combine_kernel<HD, kMaxChunks>), cgrid, cblock, 0, stream, p);   \
-  } while (0)
   switch (a.head_dim) {
-    case 32: CB_COMBINE(32); break;
-    case 64: CB_COMBINE(64); break;
-    default: CB_COMBINE(128); break;
+    case 32: return launch_hd<32, 1>(p, plan, h, stream);
+    case 64: return launch_hd<64, 1>(p, plan, h, stream);
+    default: return launch_hd<128, 1>(p, plan, h, stream);
   }
-#undef CB_COMBINE
-  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -70,8 +70,9 @@ struct AttnArgs {
 
 // Host-side decomposition of the MFMA attention launch.
 struct AttnPlan {
-  int rows_per_tile;   // selected rows per query tile (256 query vectors)
-  int key_chunk;       // keys per unit (multiple of 64); huge = no split
+  int key_split;       // key groups per workgroup (1: 256, 2: 128 query vectors per tile)
+  int rows_per_tile;   // selected rows per query tile
+  int key_chunk;       // keys per unit (multiple of the 64 * key_split keys of a tile); huge = no split
   bool split;          // some request has more than one chunk
   int64_t tiles;       // query tiles over all requests
   int64_t units;       // (tile, chunk) units over all requests
@@ -79,12 +80,12 @@ struct AttnPlan {
   size_t ws_bytes;     // workspace the split needs
 };
 
-// Selected rows per MFMA query tile (256 query vectors), or 0 if the MFMA
-// kernel does not cover this geometry.
+// Selected rows per MFMA query tile (256 / key_split query vectors), or 0 if
+// the MFMA kernel does not cover this geometry with that key split (1 or 2).
 int attn_mfma_rows_per_tile(int dtype, int32_t n_q_heads, int32_t n_kv_heads,
-                            int32_t head_dim);
+                            int32_t head_dim, int key_split);
 // Workspace bytes of one split unit.
-size_t attn_unit_bytes(int32_t head_dim);
+size_t attn_unit_bytes(int32_t head_dim, int key_split);
 // Most key chunks one row may be split into.
 int attn_max_chunks();
 

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
             "cb_blend_layer"} <= declared
     for name in sorted(declared):
         assert hasattr(lib, name), name
-    assert lib.cb_abi_version() == 3
+    assert lib.cb_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -177,59 +177,159 @@ def test_zero_sized_calls_are_noops(lib):
     assert lib.cb_last_error() == b""
 
 
-def test_workspace_size_plan(lib):
-    """The split plan is a pure host computation.  Its cost model splits when
-    the query tiles leave the GPU idle or their rows are long, and not when
-    the tiles already fill it or the geometry runs on the plain kernel."""
-    def size(g, tok, sel):
-        rg, keep = _ragged(tok, tok, sel)
-        n = ctypes.c_size_t(123)
-        assert lib.cb_partial_attn_workspace_size(ctypes.byref(g), ctypes.byref(rg), ctypes.byref(n)) == 0
-        return n.value
-    unit = 256 * 128 * 2 + 3 * 256 * 4
-    # 256 query vectors per tile: 308 rows / 64 = 5 tiles x 8 heads, 2048 keys
-    # in chunks of 256
-    assert size(_geom(), [0, 2048], [0, 308]) == 5 * 8 * 8 * unit
-    assert size(_geom(), [0, 65536], [0, 16384]) == 0           # enough tiles already
-    # 922 of 6144 rows: 15 tiles; three chunks of 2048 keys fill two rounds of
-    # the GPU better than eight of 768 (measured 79 against 99 us)
-    assert size(_geom(), [0, 6144], [0, 922]) == 15 * 3 * 8 * unit
-    # 3277 of 32768 rows: 52 tiles of up to 512 key tiles; a split only adds
-    # partial traffic (measured 941 us unsplit against 1018 us in 5 chunks)
-    assert size(_geom(), [0, 32768], [0, 3277]) == 0
-    assert size(_geom(dt=B.CB_DTYPE_F32), [0, 2048], [0, 308]) == 0   # plain kernel
-    assert size(_geom(d=16), [0, 2048], [0, 308]) == 0
+SIZE_MAX = ctypes.c_size_t(-1).value
+
+
+def _unit(ks, d=128):
+    """Workspace bytes of one split unit: fp16 O of 256 / ks query vectors plus
+    three fp32 values per vector."""
+    q = 256 // ks
+    return q * d * 2 + 3 * q * 4
+
+
+def _plan(lib, g, tok, sel, ws=SIZE_MAX):
+    rg, keep = _ragged(tok, tok, sel)
+    p = B.AttnPlan()
+    assert lib.cb_partial_attn_plan(ctypes.byref(g), ctypes.byref(rg), ws, ctypes.byref(p)) == 0
+    n = ctypes.c_size_t(123)
+    assert lib.cb_partial_attn_workspace_size(ctypes.byref(g), ctypes.byref(rg), ctypes.byref(n)) == 0
+    if ws == SIZE_MAX:
+        assert n.value == p.workspace_bytes
+    return p
+
+
+def test_attention_plan_choices(lib):
+    """The plan is a pure host computation.  Its cost model (fitted to MI355X
+    timings of these shapes) splits the keys of each tile over two wave
+    groups and / or long rows over key chunks when the query tiles leave the
+    GPU idle, and does neither when the tiles fill it or the geometry runs on
+    the plain kernel."""
+    def fields(p):
+        return (p.mfma, p.key_split, p.rows_per_tile, p.key_chunk, p.tiles, p.workgroups)
+    # 308 of 2048 rows: key split 2 (32 rows per tile, 10 tiles), 4 chunks of
+    # 512 keys, 216 working workgroups: measured 20.1 us against 22.2 for the
+    # best key-split-1 plan (8 chunks of 256 keys) and 35.1 unsplit
+    p = _plan(lib, _geom(), [0, 2048], [0, 308])
+    assert fields(p) == (1, 2, 32, 512, 10, 320) and p.workspace_bytes == 320 * _unit(2)
+    # without workspace the same batch stays unsplit, still with key split 2
+    p = _plan(lib, _geom(), [0, 2048], [0, 308], ws=0)
+    assert fields(p) == (1, 2, 32, 0, 10, 80) and p.workspace_bytes == 0
+    # 1844 of 6144 rows: two chunks of 3072 keys (the key-split-2 plans need
+    # more than one round of the CUs, where they lose in the full step)
+    p = _plan(lib, _geom(), [0, 6144], [0, 1844])
+    assert fields(p) == (1, 1, 64, 3072, 29, 464) and p.workspace_bytes == 464 * _unit(1)
+    # 922 of 6144 rows: three chunks of 2048 keys (the 6k-token blend step:
+    # 2.88 ms against 2.92 with key split 2 in two chunks of 3072 keys)
+    p = _plan(lib, _geom(), [0, 6144], [0, 922])
+    assert fields(p) == (1, 1, 64, 2048, 15, 360) and p.workspace_bytes == 360 * _unit(1)
+    # 3277 of 32768 rows: 52 tiles, unsplit (978 us against 1027 with key split 2)
+    p = _plan(lib, _geom(), [0, 32768], [0, 3277])
+    assert fields(p) == (1, 1, 64, 0, 52, 416)
+    # 1024 workgroups or more: always key split 1 unsplit
+    p = _plan(lib, _geom(), [0, 65536], [0, 16384])
+    assert fields(p) == (1, 1, 64, 0, 256, 2048) and p.workspace_bytes == 0
+    # the plain kernel: one workgroup per selected row and query head
+    for g in (_geom(dt=B.CB_DTYPE_F32), _geom(d=16), _geom(24, 8, 128)):
+        p = _plan(lib, g, [0, 2048], [0, 308])
+        assert fields(p) == (0, 0, 0, 0, 0, 308 * g.n_q_heads) and p.workspace_bytes == 0
+    rg, keep = _ragged([0, 2048], [0, 2048], [0, 308])
     assert lib.cb_partial_attn_workspace_size(ctypes.byref(_geom()), None, None) == 1
+    assert lib.cb_partial_attn_plan(ctypes.byref(_geom()), ctypes.byref(rg), SIZE_MAX, None) == 1
+    assert b"plan" in lib.cb_last_error()
 
 
 def test_workspace_plan_properties(lib):
-    """Random ragged batches: a split plan is a whole number of units, and its
-    unit count is that of a chunk the planner may choose (a multiple of 64
-    keys, at least 256, at most 8 chunks for the longest request); query
-    tiles that alone give 1024 or more workgroups are never split."""
+    """Random ragged batches: the plan's tiles, workgroups and workspace follow
+    from its key split and key chunk (a multiple of the 64 * key_split keys
+    of a tile, at least 256, at most 8 chunks for the longest request, one of
+    the chunk counts 2..8); query tiles that alone give 1024 or more
+    workgroups are never split; a workspace limit is respected."""
     rng = np.random.default_rng(11)
-    unit = 256 * 128 * 2 + 3 * 256 * 4
-    for _ in range(300):
+    seen = set()
+    for i in range(300):
         hq, hkv = [(32, 8), (64, 8), (8, 2), (16, 1), (8, 8)][rng.integers(5)]
-        lens = [int(x) for x in rng.integers(1, 40000, size=rng.integers(1, 9))]
+        lens = [int(x) for x in rng.integers(1, [40000, 4000][i % 2], size=rng.integers(1, 9))]
         ks = [min(n, int(n * rng.uniform(0, 0.3))) for n in lens]
-        rg, keep = _ragged(np.concatenate([[0], np.cumsum(lens)]),
-                           np.concatenate([[0], np.cumsum(lens)]),
-                           np.concatenate([[0], np.cumsum(ks)]))
+        tok = np.concatenate([[0], np.cumsum(lens)])
+        sel = np.concatenate([[0], np.cumsum(ks)])
         g = _geom(hq, hkv, 128)
-        n = ctypes.c_size_t(123)
-        assert lib.cb_partial_attn_workspace_size(ctypes.byref(g), ctypes.byref(rg), ctypes.byref(n)) == 0
-        rows = 256 // (hq // hkv)
+        p = _plan(lib, g, tok, sel)
+        assert p.mfma == 1 and p.key_split in (1, 2)
+        rows = 256 // p.key_split // (hq // hkv)
+        assert p.rows_per_tile == rows
         tiles = [-(-k // rows) for k in ks]
-        if sum(tiles) * hkv >= 1024 or n.value == 0:
-            assert sum(tiles) * hkv < 1024 or n.value == 0
+        assert p.tiles == sum(tiles)
+        tiles1 = sum(-(-k // (256 // (hq // hkv))) for k in ks)
+        if tiles1 * hkv >= 1024:
+            assert (p.key_split, p.key_chunk, p.workspace_bytes) == (1, 0, 0)
+        seen.add((p.key_split, p.key_chunk > 0))
+        if p.key_chunk == 0:
+            assert p.workgroups == p.tiles * hkv and p.workspace_bytes == 0
             continue
-        assert n.value % (hkv * unit) == 0
-        units = n.value // (hkv * unit)
+        kt = 64 * p.key_split
         max_n = max(nn for nn, k in zip(lens, ks) if k)
-        chunks = set()
-        for c in range(2, 9):
-            kc = max(256, -(-(-(-max_n // c)) // 64) * 64)
-            if kc < max_n:
-                chunks.add(kc)
-        assert any(units == sum(t * -(-nn // kc) for t, nn in zip(tiles, lens)) for kc in chunks)
+        chunks = {max(256, -(-(-(-max_n // c)) // kt) * kt) for c in range(2, 9)}
+        assert p.key_chunk in chunks and p.key_chunk < max_n
+        units = sum(t * -(-nn // p.key_chunk) for t, nn in zip(tiles, lens))
+        assert p.workgroups == units * hkv
+        assert p.workspace_bytes == units * hkv * _unit(p.key_split)
+        # a smaller workspace gives a plan that fits it
+        q = _plan(lib, g, tok, sel, ws=p.workspace_bytes - 1)
+        assert q.workspace_bytes <= p.workspace_bytes - 1
+    assert seen == {(1, False), (1, True), (2, False), (2, True)}
+
+
+def test_pinned_plans(lib):
+    """cb_partial_attn_describe_plan completes a pinned plan with the same
+    counts as a chosen one, and it and cb_partial_attn_with_plan reject every
+    invalid field on the host (fake device pointers: nothing may launch)."""
+    tok, sel = [0, 3000, 3100], [0, 450, 470]
+    rg, keep = _ragged(tok, tok, sel)
+
+    def describe(g, mfma, ks, kc):
+        p = B.AttnPlan(mfma, ks, 0, kc, 0, 0, 0)
+        st = lib.cb_partial_attn_describe_plan(ctypes.byref(g), ctypes.byref(rg), ctypes.byref(p))
+        return st, p
+
+    for ks in (1, 2):
+        rows = 64 // ks
+        tiles = -(-450 // rows) + 1
+        st, p = describe(_geom(), 1, ks, 0)
+        assert st == 0 and (p.rows_per_tile, p.tiles, p.workgroups, p.workspace_bytes) == (rows, tiles, 8 * tiles, 0)
+        for kc in (384, 768, 1024, 3072):
+            if kc % (64 * ks):
+                continue
+            st, p = describe(_geom(), 1, ks, kc)
+            units = -(-450 // rows) * -(-3000 // kc) + -(-100 // kc)
+            split = -(-3000 // kc) > 1
+            assert st == 0 and p.workgroups == 8 * units and p.key_chunk == (kc if split else 0)
+            assert p.workspace_bytes == (8 * units * _unit(ks) if split else 0)
+    st, p = describe(_geom(dt=B.CB_DTYPE_F32), 0, 0, 0)
+    assert st == 0 and (p.mfma, p.workgroups) == (0, 470 * 32)
+    bad = [
+        (_geom(), 2, 1, 0, 1, "mfma"),
+        (_geom(), 1, 3, 0, 1, "key_split"),
+        (_geom(), 1, 1, 100, 1, "multiple of 64"),
+        (_geom(), 1, 2, 192, 1, "multiple of 128"),
+        (_geom(), 1, 1, -64, 1, "multiple"),
+        (_geom(), 1, 1, 256, 1, "more than 8 chunks"),
+        (_geom(dt=B.CB_DTYPE_F32), 1, 1, 0, 2, "MFMA"),
+        (_geom(256, 1, 64), 1, 2, 0, 2, "key split 2"),
+        (_geom(24, 8, 128), 1, 1, 0, 2, "MFMA"),
+    ]
+    for g, mfma, ks, kc, status, needle in bad:
+        p = B.AttnPlan(mfma, ks, 7, kc, 7, 7, 7)
+        assert lib.cb_partial_attn_describe_plan(ctypes.byref(g), ctypes.byref(rg), ctypes.byref(p)) == status
+        assert needle.encode() in lib.cb_last_error(), lib.cb_last_error()
+        assert (p.rows_per_tile, p.tiles, p.workgroups, p.workspace_bytes) == (7, 7, 7, 7)
+        assert lib.cb_partial_attn_with_plan(ctypes.byref(g), ctypes.byref(rg), ctypes.byref(p), P, P, P, P,
+                                             P, P, 0.1, None, 0, None) == status
+        assert needle.encode() in lib.cb_last_error()
+    # a split needs its workspace
+    p = B.AttnPlan(1, 1, 0, 1024, 0, 0, 0)
+    assert lib.cb_partial_attn_with_plan(ctypes.byref(_geom()), ctypes.byref(rg), ctypes.byref(p), P, P, P, P,
+                                         P, P, 0.1, P2, 4096, None) == 1
+    assert b"smaller than the plan" in lib.cb_last_error()
+    assert lib.cb_partial_attn_with_plan(ctypes.byref(_geom()), ctypes.byref(rg), None, P, P, P, P,
+                                         P, P, 0.1, None, 0, None) == 1
+    assert lib.cb_partial_attn_describe_plan(ctypes.byref(_geom()), ctypes.byref(rg), None) == 1

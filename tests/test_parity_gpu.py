@@ -314,9 +314,10 @@ ATTN_CASES = [
 ]
 
 
-def _attention_case(case, use_ws, seed, max_rows=None):
-    """Run cb_partial_attn on a seeded case; compare every row (or a sample of
-    max_rows plus each request's first and last) with the oracle."""
+def _attention_case(case, use_ws, seed, max_rows=None, plan=None):
+    """Run cb_partial_attn (or, given `plan`, cb_partial_attn_with_plan) on a
+    seeded case; compare every row (or a sample of max_rows plus each
+    request's first and last) with the oracle."""
     dtype, hq, hkv, d, lens, ks = case
     rng = np.random.default_rng(seed)
     t_count = sum(lens)
@@ -343,7 +344,12 @@ def _attention_case(case, use_ws, seed, max_rows=None):
     rb = B.RaggedBatch(tok_off, tok_off, sel_off, DEV)
     g = B.geom(hq, hkv, d, dtype)
     ws = None
-    if use_ws:
+    if plan is not None:
+        full = B.describe_plan(g, rb, **plan)
+        ws = B.workspace_tensor(full["workspace_bytes"], DEV)
+        if ws is not None:
+            ws.fill_(0xFF)
+    elif use_ws:
         nbytes = B.attn_workspace_bytes(g, rb)
         if nbytes == 0:
             pytest.skip("the planner does not split this case")
@@ -351,8 +357,12 @@ def _attention_case(case, use_ws, seed, max_rows=None):
         ws.fill_(0xFF)                                        # NaN garbage: must be overwritten
     out = torch.full((rb.n_sel, hq, d), float("nan"), dtype=dtype, device=DEV)
     scale = 1.0 / math.sqrt(d)
-    B.partial_attn(g, rb, out, q.to(DEV), torch.from_numpy(sel_l).to(DEV),
-                   torch.from_numpy(sel_g).to(DEV), kf.to(DEV), vf.to(DEV), scale, workspace=ws)
+    args = (out, q.to(DEV), torch.from_numpy(sel_l).to(DEV), torch.from_numpy(sel_g).to(DEV),
+            kf.to(DEV), vf.to(DEV), scale)
+    if plan is not None:
+        B.partial_attn_with_plan(g, rb, plan, *args, workspace=ws)
+    else:
+        B.partial_attn(g, rb, *args, workspace=ws)
     torch.cuda.synchronize()
     got = np64(out)
     assert np.isfinite(got).all()
@@ -393,6 +403,32 @@ RANDOM_CASES = [_random_case(i) for i in range(8)]
 def test_attention_random_ragged_batches(case, use_ws):
     say(f"attention random {case[1:4]} lens={case[4]} ks={case[5]} workspace={use_ws}")
     _attention_case(case, use_ws, 77 + sum(case[4]), max_rows=96)
+
+
+# Every decomposition of the MFMA kernel on each head_dim, whatever the cost
+# model would choose: key split 1 / 2, unsplit and over key chunks (64-key
+# multiples that are not 128-key multiples only for key split 1), and the
+# plain kernel.  Ragged batch with a fully selected short request.
+PINNED_PLANS = [dict(mfma=0), dict(mfma=1, key_split=1, key_chunk=0),
+                dict(mfma=1, key_split=1, key_chunk=256), dict(mfma=1, key_split=1, key_chunk=576),
+                dict(mfma=1, key_split=2, key_chunk=0), dict(mfma=1, key_split=2, key_chunk=384),
+                dict(mfma=1, key_split=2, key_chunk=1024)]
+PINNED_GEOMS = [(32, 8, 128), (8, 2, 64), (16, 1, 32), (8, 8, 128)]
+
+
+@pytest.mark.parametrize("plan", PINNED_PLANS,
+                         ids=["plain", "ks1", "ks1c256", "ks1c576", "ks2", "ks2c384", "ks2c1024"])
+@pytest.mark.parametrize("geo", PINNED_GEOMS, ids=[f"h{a}-{b}-d{c}" for a, b, c in PINNED_GEOMS])
+def test_attention_pinned_plans(geo, plan):
+    hq, hkv, d = geo
+    case = (torch.bfloat16, hq, hkv, d, [1500, 700, 33], [230, 100, 33])
+    say(f"attention pinned plan {plan} geometry {geo}")
+    full = B.describe_plan(B.geom(hq, hkv, d, torch.bfloat16),
+                           B.RaggedBatch(PL.offsets(case[4]), PL.offsets(case[4]),
+                                         PL.offsets(case[5]), DEV), **plan)
+    if plan.get("key_chunk"):
+        assert full["key_chunk"] == plan["key_chunk"] and full["workspace_bytes"] > 0
+    _attention_case(case, False, 4242 + d + hq, max_rows=120, plan=plan)
 
 
 DENSE = [(32, 8, 128, [2048], 64), (64, 8, 128, [700, 1300], 48), (8, 8, 64, [333], None)]
