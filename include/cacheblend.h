@@ -195,8 +195,11 @@ cb_status cb_fuse_scatter(const cb_geom *geom, void *k_fused, void *v_fused,
  *   workspace, workspace_bytes : optional device scratch owned by the caller
  *            (NULL/0 allowed).  When the query tiles are too few to fill the
  *            GPU, long rows are split over key ranges whose partials
- *            live here; cb_partial_attn_workspace_size() gives the size that
- *            enables the split.  A smaller workspace only disables the split.
+ *            live here, with one arrival counter per query tile and KV head
+ *            (the last chunk to arrive merges them; the call clears the
+ *            counters first, so the contents need no initialisation);
+ *            cb_partial_attn_workspace_size() gives the size that enables
+ *            the split.  A smaller workspace only disables the split.
  *            Calls that share a workspace must be ordered on one stream.
  * bf16 uses MFMA products with fp32 accumulation and an fp32 online softmax.
  */

@@ -246,11 +246,12 @@ constexpr int kNoSplit = 1 << 30;
 // CU busy, and kKeySplitTile of that for a 128-query unit whose 128-key
 // tiles are split over two wave groups; a workgroup spends ~3.6 us before
 // its first tile (three dependent loads: request offsets, selected rows, Q)
-// and ~1 us writing its partial; the combine launch costs ~3 us plus its
-// partials read at ~4.5 TB/s.
-constexpr double kTileUs = 2.1, kSetupUs = 3.6, kPartialUs = 1.0, kCombineUs = 3.0;
+// and, when split, ~1 us storing its partial; the last working unit of a
+// split tile then spends kMergeUs arriving (fences and the counter) plus
+// kMergePairUs per two other partials it loads and merges.
+constexpr double kTileUs = 2.1, kSetupUs = 3.6, kPartialUs = 1.0;
 constexpr double kKeySplitTile = 0.55;
-constexpr double kCombineBytesPerUs = 4.5e6;
+constexpr double kMergeUs = 1.0, kMergePairUs = 1.0;
 // CUs the simulated dispatch fills: 240 of the 256, a margin against plans
 // that fit one more round only if the selected rows sit exactly as assumed.
 constexpr int kSimCUs = 240;
@@ -262,7 +263,7 @@ constexpr int kSimCUs = 240;
 // Units are dispatched in the kernel's order (request by request, chunk by
 // chunk, longest tile first), each to the earliest free group of CUs; the
 // n_kv_heads workgroups of a unit run side by side, so one "slot" stands for
-// n_kv_heads CUs.
+// n_kv_heads CUs.  A split tile ends when its last unit has merged.
 double estimate_attn_us(const cb_geom *g, const cb_ragged *rg, int ks, int rows, int64_t kc,
                         int64_t *active) {
   const int n_slots = std::max(1, kSimCUs / g->n_kv_heads);
@@ -271,15 +272,18 @@ double estimate_attn_us(const cb_geom *g, const cb_ragged *rg, int ks, int rows,
   const int64_t kt = 64 * ks;  // keys per tile
   std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
   for (int i = 0; i < n_slots; ++i) free_at.push(0.0);
-  bool split = false;
   int64_t busy = 0;
+  double makespan = 0.0;
+  std::vector<double> tile_end;
+  std::vector<int> tile_units;
   for (int32_t r = 0; r < rg->n_req; ++r) {
     const int64_t k = rg->h_sel_off[r + 1] - rg->h_sel_off[r];
     const int64_t n = rg->h_tok_off[r + 1] - rg->h_tok_off[r];
     if (k == 0) continue;
     const int64_t tiles = (k + rows - 1) / rows;
     const int64_t chunks = (n + kc - 1) / kc;
-    if (chunks > 1) split = true;
+    tile_end.assign((size_t)tiles, 0.0);
+    tile_units.assign((size_t)tiles, 0);
     for (int64_t c = 0; c < chunks; ++c)
       for (int64_t t = tiles - 1; t >= 0; --t) {
         const int64_t end = (std::min(k, (t + 1) * rows) * n + k - 1) / k;
@@ -290,28 +294,36 @@ double estimate_attn_us(const cb_geom *g, const cb_ragged *rg, int ks, int rows,
         const double start = free_at.top();
         free_at.pop();
         free_at.push(start + us);
+        tile_end[(size_t)t] = std::max(tile_end[(size_t)t], start + us);
+        ++tile_units[(size_t)t];
         ++busy;
       }
-  }
-  double makespan = 0.0;
-  while (!free_at.empty()) {
-    makespan = std::max(makespan, free_at.top());
-    free_at.pop();
+    for (int64_t t = 0; t < tiles; ++t) {
+      const int u = tile_units[(size_t)t];
+      const double merge = u > 1 ? kMergeUs + (double)(u / 2) * kMergePairUs : 0.0;
+      makespan = std::max(makespan, tile_end[(size_t)t] + merge);
+    }
   }
   *active = busy;
-  if (split)
-    makespan += kCombineUs + (double)busy * g->n_kv_heads *
-                                 (double)cb::attn_unit_bytes(g->head_dim, ks) / kCombineBytesPerUs;
   return makespan;
 }
 
+// Workspace of a split: the partials of every workgroup, then (256-byte
+// aligned) one arrival counter per (tile, KV head).
+size_t split_ws_bytes(const cb_geom *g, int ks, int64_t units, int64_t tiles,
+                      size_t *cnt_offset = nullptr) {
+  const size_t partials = (size_t)units * g->n_kv_heads * cb::attn_unit_bytes(g->head_dim, ks);
+  const size_t off = (partials + 255) / 256 * 256;
+  if (cnt_offset) *cnt_offset = off;
+  return off + (size_t)tiles * g->n_kv_heads * sizeof(uint32_t);
+}
+
 // Fills the counts of an MFMA plan whose key split, rows per tile and key
-// chunk are set: tiles, units, split, largest chunk count, workspace.
+// chunk are set: tiles, units, split, counters, workspace.
 void finish_plan(const cb_geom *g, const cb_ragged *rg, cb::AttnPlan &pl) {
   const int rows = pl.rows_per_tile;
   pl.tiles = pl.units = 0;
   pl.split = false;
-  pl.max_chunks = 1;
   for (int32_t r = 0; r < rg->n_req; ++r) {
     const int64_t kr = rg->h_sel_off[r + 1] - rg->h_sel_off[r];
     const int64_t n = rg->h_tok_off[r + 1] - rg->h_tok_off[r];
@@ -319,14 +331,11 @@ void finish_plan(const cb_geom *g, const cb_ragged *rg, cb::AttnPlan &pl) {
     const int64_t cr = (n + pl.key_chunk - 1) / pl.key_chunk;
     pl.tiles += tr;
     pl.units += tr * cr;
-    if (tr > 0) {
-      if (cr > 1) pl.split = true;
-      pl.max_chunks = std::max<int>(pl.max_chunks, (int)cr);
-    }
+    if (tr > 0 && cr > 1) pl.split = true;
   }
-  pl.ws_bytes = pl.split ? (size_t)pl.units * g->n_kv_heads *
-                               cb::attn_unit_bytes(g->head_dim, pl.key_split)
-                         : 0;
+  pl.cnt_offset = 0;
+  pl.n_cnt = pl.split ? pl.tiles * g->n_kv_heads : 0;
+  pl.ws_bytes = pl.split ? split_ws_bytes(g, pl.key_split, pl.units, pl.tiles, &pl.cnt_offset) : 0;
 }
 
 // Decomposition of the MFMA attention, from host mirrors only.  When the
@@ -373,8 +382,7 @@ cb::AttnPlan plan_attn(const cb_geom *g, const cb_ragged *rg, size_t ws_avail) {
     auto consider = [&](int ks, int rows, int64_t kc) {
       bool split = false;
       const int64_t units = count_units(rows, kc, split);
-      const size_t ws =
-          split ? (size_t)units * g->n_kv_heads * cb::attn_unit_bytes(g->head_dim, ks) : 0;
+      const size_t ws = split ? split_ws_bytes(g, ks, units, count_tiles(rows)) : 0;
       if (ws > ws_avail) return;
       const double us = estimate_attn_us(g, rg, ks, rows, kc, &active);
       // Key split 2 only where its working units fit in one round of the CUs:
@@ -449,10 +457,13 @@ cb_status pinned_plan(const cb_geom *g, const cb_ragged *rg, const cb_attn_plan 
   return CB_OK;
 }
 
+// counters_zero: the split's arrival counters in the workspace are known to
+// be zero (cb_blend_layer's fuse launch clears them).
 cb_status run_attn(const cb_geom *geom, const cb_ragged *rg, const cb::AttnPlan &plan,
                    void *out, const void *q_c, const int32_t *sel_local,
                    const int32_t *sel_global, const void *k_fused, const void *v_fused,
-                   float softmax_scale, void *workspace, hipStream_t stream) {
+                   float softmax_scale, void *workspace, bool counters_zero,
+                   hipStream_t stream) {
   cb::AttnArgs a;
   a.out = out; a.q_c = q_c; a.sel_local = sel_local; a.sel_global = sel_global;
   a.k_fused = k_fused; a.v_fused = v_fused; a.tok_off = rg->tok_off; a.sel_off = rg->sel_off;
@@ -464,7 +475,7 @@ cb_status run_attn(const cb_geom *geom, const cb_ragged *rg, const cb::AttnPlan 
   if (plan.rows_per_tile > 0) {
     if (plan.units * geom->n_kv_heads > INT32_MAX)
       return fail(CB_ERR_UNSUPPORTED, "too many attention work units");
-    return hip_status(cb::launch_attn_mfma(a, plan, stream), "partial_attn");
+    return hip_status(cb::launch_attn_mfma(a, plan, counters_zero, stream), "partial_attn");
   }
   return hip_status(cb::launch_attn_simple(geom->dtype, a, stream), "partial_attn");
 }
@@ -531,7 +542,7 @@ CB_EXPORT cb_status cb_fuse_scatter(const cb_geom *geom, void *k_fused, void *v_
   if (k_total == 0) return CB_OK;
   return hip_status(cb::launch_fuse(k_fused, v_fused, k_new_c, v_new_c, sel_local, sel_global,
                                     k_total, (int32_t)(row_elems(geom) * elem_size(geom->dtype)),
-                                    (hipStream_t)stream),
+                                    nullptr, 0, (hipStream_t)stream),
                     "fuse_scatter");
 }
 
@@ -546,7 +557,7 @@ CB_EXPORT cb_status cb_partial_attn(const cb_geom *geom, const cb_ragged *rg, vo
   CB_TRY(need_ptr(workspace, "workspace", workspace_bytes > 0));
   const cb::AttnPlan plan = plan_attn(geom, rg, workspace ? workspace_bytes : 0);
   return run_attn(geom, rg, plan, out, q_c, sel_local, sel_global, k_fused, v_fused,
-                  softmax_scale, workspace, (hipStream_t)stream);
+                  softmax_scale, workspace, false, (hipStream_t)stream);
 }
 
 CB_EXPORT cb_status cb_partial_attn_with_plan(const cb_geom *geom, const cb_ragged *rg,
@@ -564,7 +575,7 @@ CB_EXPORT cb_status cb_partial_attn_with_plan(const cb_geom *geom, const cb_ragg
   cb::AttnPlan pl;
   CB_TRY(pinned_plan(geom, rg, plan, workspace ? workspace_bytes : 0, pl));
   return run_attn(geom, rg, pl, out, q_c, sel_local, sel_global, k_fused, v_fused,
-                  softmax_scale, workspace, (hipStream_t)stream);
+                  softmax_scale, workspace, false, (hipStream_t)stream);
 }
 
 CB_EXPORT cb_status cb_partial_attn_workspace_size(const cb_geom *geom, const cb_ragged *rg,
@@ -662,13 +673,17 @@ CB_EXPORT cb_status cb_blend_layer(const cb_layer_args *a, void *stream) {
   CB_TRY(hip_status(cb::launch_topk(rg->n_req, a->dev, a->cand_idx, rg->cand_off, rg->sel_off,
                                     a->sel_local, a->sel_global, rg->h_cand_off, rg->h_sel_off, s),
                     "topk"));
-  CB_TRY(hip_status(cb::launch_fuse(a->k, a->v, a->k_new_c, a->v_new_c, a->sel_local,
-                                    a->sel_global, k_total,
-                                    (int32_t)(row_elems(geom) * elem_size(geom->dtype)), s),
-                    "fuse_scatter"));
+  // The fuse launch also clears the attention's arrival counters.
   const cb::AttnPlan plan = plan_attn(geom, rg, a->workspace ? a->workspace_bytes : 0);
+  const bool clear = plan.rows_per_tile > 0 && plan.split;
+  CB_TRY(hip_status(
+      cb::launch_fuse(a->k, a->v, a->k_new_c, a->v_new_c, a->sel_local, a->sel_global, k_total,
+                      (int32_t)(row_elems(geom) * elem_size(geom->dtype)),
+                      clear ? (uint32_t *)((char *)a->workspace + plan.cnt_offset) : nullptr,
+                      clear ? plan.n_cnt : 0, s),
+      "fuse_scatter"));
   return run_attn(geom, rg, plan, a->out, a->q_c, a->sel_local, a->sel_global, a->k, a->v,
-                  a->softmax_scale, a->workspace, s);
+                  a->softmax_scale, a->workspace, clear, s);
 }
 
 CB_EXPORT const char *cb_status_str(cb_status status) {

@@ -5,6 +5,7 @@
 // [KV-blog] = "rag的kvcache问题": section "阶段二：注意力分数计算阶段" (each
 // query row only needs its own q and all of K) and section
 // "transformer训练与推理并行计算的差异" (causal mask: no key after the query).
+#include <algorithm>
 #include <cmath>
 
 #include "cb_device.hpp"
@@ -73,7 +74,8 @@ struct AttnParams {
   const bf16 *v_fused;
   const int32_t *tok_off;
   const int32_t *sel_off;
-  unsigned char *ws;
+  unsigned char *ws;     // split partials, one per workgroup of the launch
+  unsigned *cnt;         // arrival counter per (query tile, KV head); zero at launch
   int32_t n_req, hq, hkv, group, rows_per_tile, key_chunk;
   float scale_log2;
 };
@@ -120,12 +122,18 @@ template <int HD> __device__ constexpr int swz_v(int r) {
   else return 2 * ((r >> 1) & 1);
 }
 
-// Unit u -> (request r, tile, chunk): within a request, chunk-major, tiles
-// from last to first.  Returns false past the last unit.
-__device__ inline bool locate_unit(const AttnParams &p, int u, int &r, int &tile, int &chunk,
-                                   int &nchunks) {
-  int64_t ubase = 0;
-  for (r = 0; r < p.n_req; ++r) {
+// Where a unit sits: request r, its query tile and key chunk, the request's
+// tile and chunk counts, and the units and tiles of the requests before it.
+struct UnitPos {
+  int r, tile, chunk, tr, nchunks;
+  int64_t ubase, tbase;
+};
+
+// Unit u -> its position: within a request, chunk-major, tiles from last to
+// first.  Returns false past the last unit.
+__device__ inline bool locate_unit(const AttnParams &p, int u, UnitPos &up) {
+  int64_t ubase = 0, tbase = 0;
+  for (int r = 0; r < p.n_req; ++r) {
     const int kr = p.sel_off[r + 1] - p.sel_off[r];
     const int n = p.tok_off[r + 1] - p.tok_off[r];
     const int tr = (kr + p.rows_per_tile - 1) / p.rows_per_tile;
@@ -133,12 +141,17 @@ __device__ inline bool locate_unit(const AttnParams &p, int u, int &r, int &tile
     const int64_t nu = (int64_t)tr * cr;
     if (u < ubase + nu) {
       const int ul = (int)(u - ubase);
-      chunk = ul / tr;
-      tile = tr - 1 - (ul - chunk * tr);
-      nchunks = cr;
+      up.r = r;
+      up.chunk = ul / tr;
+      up.tile = tr - 1 - (ul - up.chunk * tr);
+      up.tr = tr;
+      up.nchunks = cr;
+      up.ubase = ubase;
+      up.tbase = tbase;
       return true;
     }
     ubase += nu;
+    tbase += tr;
   }
   return false;
 }
@@ -162,6 +175,19 @@ __device__ inline void dma16(const char *base, uint32_t off, uint32_t lds_byte) 
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
+
+// Split partials pass between workgroups on different XCDs, whose L2 caches
+// are not coherent with each other.  They are stored and loaded only as
+// relaxed agent-scope atomics, which the hardware performs at the coherence
+// point all XCDs share; the arrival counter is such an atomic too.  So no
+// fence has to write back or invalidate a whole L2 (an agent-scope fence
+// does both, and in every workgroup it tripled the launch time).
+template <typename T> __device__ inline void store_agent(T *p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T> __device__ inline T load_agent(const T *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __device__ inline uint32_t lds_addr(const bf16 *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) bf16 *)p;
@@ -203,8 +229,9 @@ void attn_mfma_kernel(const AttnParams p) {
   const int col = lane & 31, half = lane >> 5;
   const int kg = wave / WPG;              // key group: keys 64kg .. 64kg+63 of each tile
   const int g = blockIdx.x % p.hkv;
-  int r, tile, chunk, nchunks;
-  if (!locate_unit(p, (int)(blockIdx.x / p.hkv), r, tile, chunk, nchunks)) return;
+  UnitPos up;
+  if (!locate_unit(p, (int)(blockIdx.x / p.hkv), up)) return;
+  const int r = up.r, tile = up.tile, chunk = up.chunk;
   const int s0 = p.sel_off[r] + tile * p.rows_per_tile;
   const int ns = min(p.rows_per_tile, p.sel_off[r + 1] - s0);
   const int lo = p.tok_off[r];
@@ -431,157 +458,161 @@ void attn_mfma_kernel(const AttnParams p) {
       m_run = mm;
     }
   }
-  if (nchunks == 1) {
-    // Output through LDS (the K stage buffers are free once every wave is
-    // past its last tile): each wave of key group 0 writes its normalised
-    // bf16 rows (16-byte chunk index XOR-swizzled by the query vector against
-    // bank conflicts), then the workgroup stores 16-byte chunks in output
-    // order -- the G query heads of one selected row are adjacent in `out`,
-    // so a wave writes whole 1 KiB runs instead of 8 bytes per lane 256
-    // bytes apart.
-    constexpr int CPQ = HD / 8;  // 16-byte chunks per query vector
-    bf16 *stage = &kst[0][0];
-    static_assert(STAGES * TILE >= QT * HD, "output staging does not fit");
-    phase_barrier();
+  // Split over keys: every working chunk of the tile stores its partial;
+  // the last to arrive merges all of them and writes the output.  A tile
+  // whose rows all lie in its first chunk has one working unit and no merge.
+  const int n_active = (int)((p_last - lo) / p.key_chunk) + 1;
+  if (n_active > 1) {
+    constexpr int UNIT = partial_bytes<HD, QT>();
     if (kg == 0) {
-      const float inv = 1.f / l;
+      // Partial in fragment order: store (dt, q) of wave w writes 64 lanes x 8
+      // contiguous bytes at fp16x4 index ((w*NDT + dt)*4 + q)*64 + lane.  Each
+      // query vector's O is divided by its largest |O| (the two lanes l and
+      // l ^ 32 hold its dims), so fp16 keeps 11 significant bits of every
+      // value whatever the scale of V; the merge multiplies it back.
+      unsigned char *w = p.ws + (int64_t)blockIdx.x * UNIT;
+      float amax = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(o[dt][e]));
+      amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+      const float inv_amax = amax > 0.f ? 1.f / amax : 0.f;
+      uint64_t *wo = reinterpret_cast<uint64_t *>(w);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          bf16x4 w;
+          f16x4 h;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) w[i] = (bf16)(o[dt][4 * q + i] * inv);
-          const int chunk = (4 * dt + q) ^ (qv & (CPQ - 1));
-          *reinterpret_cast<bf16x4 *>(stage + qv * HD + 8 * chunk + 4 * half) = w;
+          for (int i = 0; i < 4; ++i) h[i] = (_Float16)(o[dt][4 * q + i] * inv_amax);
+          store_agent(wo + (((wave * NDT + dt) * 4 + q) << 6) + lane, __builtin_bit_cast(uint64_t, h));
         }
+      if (half == 0) {
+        uint32_t *meta = reinterpret_cast<uint32_t *>(w + QT * HD * 2);
+        store_agent(meta + qv, __builtin_bit_cast(uint32_t, m_run));
+        store_agent(meta + QT + qv, __builtin_bit_cast(uint32_t, l));
+        store_agent(meta + 2 * QT + qv, __builtin_bit_cast(uint32_t, amax));
+      }
+    }
+    // Arrival: every store of the partial has completed at the coherence
+    // point shared by all XCDs before the arrival is counted; the workgroup
+    // that brings the count to n_active goes on.
+    __shared__ int s_last;
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    phase_barrier();
+    if (tid == 0) {
+      const unsigned prev = __hip_atomic_fetch_add(p.cnt + (up.tbase + tile) * p.hkv + g, 1u,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = prev == (unsigned)(n_active - 1);
     }
     phase_barrier();
-    for (int c = tid; c < QT * CPQ; c += 64 * kWaves) {
-      const int v = c / CPQ, part = c - v * CPQ;
-      const int vrow = v / p.group, vh = v - vrow * p.group;
-      if (vrow < ns)
-        *reinterpret_cast<uint4 *>(p.out + ((int64_t)(s0 + vrow) * p.hq + g * p.group + vh) * HD +
-                                   8 * part) =
-            *reinterpret_cast<const uint4 *>(stage + v * HD + 8 * (part ^ (v & (CPQ - 1))));
+    if (!s_last) return;  // uniform
+    if (kg == 0) {
+      // Merge every working chunk's stored partial, this one's included, in
+      // chunk order: the result does not depend on which chunk arrived last.
+      // Unit of (tile, chunk c): ubase + c * tr + (tr - 1 - tile).
+      const unsigned char *w0 =
+          p.ws + ((up.ubase + (int64_t)(up.tr - 1 - tile)) * p.hkv + g) * UNIT;
+      const int64_t ustride = (int64_t)up.tr * p.hkv * UNIT;
+      // Running max, running sum and largest |O| of every chunk, all loads in
+      // one round (chunks past n_active weigh nothing).
+      float mc[kMaxChunks], lc[kMaxChunks], ac[kMaxChunks];
+#pragma unroll
+      for (int c = 0; c < kMaxChunks; ++c) {
+        mc[c] = kNegFloor;
+        lc[c] = ac[c] = 0.f;
+        if (c < n_active) {
+          const uint32_t *mt = reinterpret_cast<const uint32_t *>(w0 + c * ustride + QT * HD * 2);
+          mc[c] = __builtin_bit_cast(float, load_agent(mt + qv));
+          lc[c] = __builtin_bit_cast(float, load_agent(mt + QT + qv));
+          ac[c] = __builtin_bit_cast(float, load_agent(mt + 2 * QT + qv));
+        }
+      }
+      float mx = kNegFloor;
+#pragma unroll
+      for (int c = 0; c < kMaxChunks; ++c) mx = fmaxf(mx, mc[c]);
+      float wgt[kMaxChunks];
+      l = 0.f;
+#pragma unroll
+      for (int c = 0; c < kMaxChunks; ++c) {
+        wgt[c] = c < n_active ? __builtin_amdgcn_exp2f(mc[c] - mx) : 0.f;
+        l = fmaf(lc[c], wgt[c], l);
+        wgt[c] *= ac[c];
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] = 0.f;
+      auto load = [&](int c, f16x4 (&h)[NDT * 4]) {
+        const uint64_t *src = reinterpret_cast<const uint64_t *>(w0 + c * ustride);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            h[dt * 4 + q] = __builtin_bit_cast(
+                f16x4, load_agent(src + (((wave * NDT + dt) * 4 + q) << 6) + lane));
+      };
+      auto add = [&](float wo, const f16x4 (&h)[NDT * 4]) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              o[dt][4 * q + i] = fmaf((float)h[dt * 4 + q][i], wo, o[dt][4 * q + i]);
+      };
+      // O in chunk order, two chunks' loads in flight (weights indexed by
+      // unrolled constants only, so they stay in registers)
+#pragma unroll
+      for (int c = 0; c < kMaxChunks; c += 2) {
+        if (c < n_active) {
+          f16x4 h0[NDT * 4], h1[NDT * 4];
+          load(c, h0);
+          if (c + 1 < n_active) load(c + 1, h1);
+          add(wgt[c], h0);
+          if (c + 1 < n_active) add(wgt[c + 1], h1);
+        }
+      }
     }
-  } else if (kg == 0) {
-    // Partial in fragment order: store (dt, q) of wave w writes 64 lanes x 8
-    // contiguous bytes at fp16x4 index ((w*NDT + dt)*4 + q)*64 + lane.  Each
-    // query vector's O is divided by its largest |O| (the two lanes l and
-    // l ^ 32 hold its dims), so fp16 keeps 11 significant bits of every
-    // value whatever the scale of V; the combine multiplies it back.
-    unsigned char *w = p.ws + (int64_t)blockIdx.x * partial_bytes<HD, QT>();
-    float amax = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(o[dt][e]));
-    amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
-    const float inv_amax = amax > 0.f ? 1.f / amax : 0.f;
-    f16x4 *wo = reinterpret_cast<f16x4 *>(w);
+  }
+
+  // Output through LDS (the K stage buffers are free once every wave is past
+  // its last tile): each wave of key group 0 writes its normalised bf16 rows
+  // (16-byte chunk index XOR-swizzled by the query vector against bank
+  // conflicts), then the workgroup stores 16-byte chunks in output order --
+  // the G query heads of one selected row are adjacent in `out`, so a wave
+  // writes whole 1 KiB runs instead of 8 bytes per lane 256 bytes apart.
+  constexpr int CPQ = HD / 8;  // 16-byte chunks per query vector
+  bf16 *stage = &kst[0][0];
+  static_assert(STAGES * TILE >= QT * HD, "output staging does not fit");
+  phase_barrier();
+  if (kg == 0) {
+    const float inv = 1.f / l;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        f16x4 h;
+        bf16x4 w;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) h[i] = (_Float16)(o[dt][4 * q + i] * inv_amax);
-        wo[(((wave * NDT + dt) * 4 + q) << 6) + lane] = h;
+        for (int i = 0; i < 4; ++i) w[i] = (bf16)(o[dt][4 * q + i] * inv);
+        const int cq = (4 * dt + q) ^ (qv & (CPQ - 1));
+        *reinterpret_cast<bf16x4 *>(stage + qv * HD + 8 * cq + 4 * half) = w;
       }
-    if (half == 0) {
-      float *meta = reinterpret_cast<float *>(w + QT * HD * 2);
-      meta[qv] = m_run;
-      meta[QT + qv] = l;
-      meta[2 * QT + qv] = amax;
-    }
+  }
+  phase_barrier();
+  for (int c = tid; c < QT * CPQ; c += 64 * kWaves) {
+    const int v = c / CPQ, part = c - v * CPQ;
+    const int vrow = v / p.group, vh = v - vrow * p.group;
+    if (vrow < ns)
+      *reinterpret_cast<uint4 *>(p.out + ((int64_t)(s0 + vrow) * p.hq + g * p.group + vh) * HD +
+                                 8 * part) =
+          *reinterpret_cast<const uint4 *>(stage + v * HD + 8 * (part ^ (v & (CPQ - 1))));
   }
 }
 
-// Merge the key-chunk partials.  One thread per 8 dims of a query vector:
-// the two fp16x4 fragments f and f + 64 of the partials' fragment order
-// (dims d and d + 8), so the running max, running sum and largest |O| of each
-// chunk are loaded once for both.  Consecutive threads read consecutive 8
-// bytes.  Every chunk's loads are issued at once (unrolled over NC, the
-// plan's largest chunk count rounded up to 2, 4 or 8; inactive chunks clamped
-// to chunk 0 and weighted 0), so each thread waits for a single round of loads.
-template <int HD, int QT, int NC>
-__global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
-  constexpr int UNIT = partial_bytes<HD, QT>();
-  constexpr int GROUPS = QT * HD / 8 / 256;  // workgroups per (tile, head): 2 fragments per thread
-  const int g = blockIdx.x % p.hkv;
-  const int rest = blockIdx.x / p.hkv;
-  const int qgroup = rest % GROUPS;
-  const int tile_u = rest / GROUPS;
-  int r, tile = 0, cr = 1, tr = 0;
-  int64_t ubase = 0, tbase = 0;
-  for (r = 0; r < p.n_req; ++r) {
-    const int kr = p.sel_off[r + 1] - p.sel_off[r];
-    const int n = p.tok_off[r + 1] - p.tok_off[r];
-    tr = (kr + p.rows_per_tile - 1) / p.rows_per_tile;
-    cr = (int)(((int64_t)n + p.key_chunk - 1) / p.key_chunk);
-    if (tile_u < tbase + tr) { tile = (int)(tile_u - tbase); break; }
-    tbase += tr;
-    ubase += (int64_t)tr * cr;
-  }
-  if (r == p.n_req || cr == 1) return;
-  const int s0 = p.sel_off[r] + tile * p.rows_per_tile;
-  const int ns = min(p.rows_per_tile, p.sel_off[r + 1] - s0);
-  // fp16x4 index f = ((wave*NDT + dt)*4 + q)*64 + lane of the partial holds
-  // dims 32dt + 8q + 4(lane/32) .. +3 of query vector 32*wave + lane%32
-  constexpr int NDT = HD / 32;
-  // thread -> fragments f and f + 64 (dims d0 and d0 + 8 of one query vector)
-  const int t = qgroup * 256 + (int)threadIdx.x;
-  const int f = ((t >> 6) << 7) + (t & 63);
-  const int lane = f & 63, q = (f >> 6) & 3, dt = (f >> 8) % NDT, wv = (f >> 8) / NDT;
-  const int qv = wv * 32 + (lane & 31);
-  const int d0 = 32 * dt + 8 * q + 4 * (lane >> 5);
-  const int row = qv / p.group, hh = qv - row * p.group;
-  if (row >= ns) return;
-  const int lo = p.tok_off[r];
-  const int p_last = p.sel_global[s0 + ns - 1];
-  const int n_active = (p_last - lo) / p.key_chunk + 1;
-  // unit of (tile, chunk c) is ubase + c * tr + (tr - 1 - tile)
-  const unsigned char *w0 = p.ws + ((ubase + (int64_t)(tr - 1 - tile)) * p.hkv + g) * UNIT;
-  const int64_t ustride = (int64_t)tr * p.hkv * UNIT;
-  float mc[NC], lc[NC], ac[NC];
-  f16x4 oc[NC], oc2[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const unsigned char *w = w0 + (c < n_active ? c : 0) * ustride;
-    const float *meta = reinterpret_cast<const float *>(w + QT * HD * 2);
-    mc[c] = meta[qv];
-    lc[c] = meta[QT + qv];
-    ac[c] = meta[2 * QT + qv];
-    oc[c] = reinterpret_cast<const f16x4 *>(w)[f];
-    oc2[c] = reinterpret_cast<const f16x4 *>(w)[f + 64];
-  }
-  float mx = kNegFloor;
-#pragma unroll
-  for (int c = 0; c < NC; ++c) mx = fmaxf(mx, c < n_active ? mc[c] : kNegFloor);
-  float l = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const float wgt = c < n_active ? __builtin_amdgcn_exp2f(mc[c] - mx) : 0.f;
-    l += lc[c] * wgt;
-    const float wo = wgt * ac[c];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[i] = fmaf((float)oc[c][i], wo, acc[i]);
-      acc2[i] = fmaf((float)oc2[c][i], wo, acc2[i]);
-    }
-  }
-  const float inv = 1.f / l;
-  bf16x4 o, o2;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    o[i] = (bf16)(acc[i] * inv);
-    o2[i] = (bf16)(acc2[i] * inv);
-  }
-  bf16 *dst = p.out + ((int64_t)(s0 + row) * p.hq + g * p.group + hh) * HD + d0;
-  *reinterpret_cast<bf16x4 *>(dst) = o;
-  *reinterpret_cast<bf16x4 *>(dst + 8) = o2;
+// Arrival counters of a split launch back to zero (standalone calls; inside
+// cb_blend_layer the fuse launch clears them).
+__global__ __launch_bounds__(256) void attn_clear_kernel(unsigned *cnt, int32_t n) {
+  for (int i = blockIdx.x * 256 + (int)threadIdx.x; i < n; i += gridDim.x * 256) cnt[i] = 0;
 }
 
 int attn_mfma_rows_per_tile(int dtype, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
@@ -603,30 +634,15 @@ size_t attn_unit_bytes(int32_t head_dim, int key_split) {
 int attn_max_chunks() { return kMaxChunks; }
 
 template <int HD, int KS>
-static void launch_combine(const AttnParams &p, const AttnPlan &plan, int n_kv_heads,
-                           hipStream_t stream) {
-  constexpr int QT = kQT / KS;
-  const dim3 grid((unsigned)(plan.tiles * n_kv_heads * (QT * HD / 2048))), block(256);
-  if (plan.max_chunks <= 2)
-    hipLaunchKernelGGL((attn_combine_kernel<HD, QT, 2>), grid, block, 0, stream, p);
-  else if (plan.max_chunks <= 4)
-    hipLaunchKernelGGL((attn_combine_kernel<HD, QT, 4>), grid, block, 0, stream, p);
-  else
-    hipLaunchKernelGGL((attn_combine_kernel<HD, QT, kMaxChunks>), grid, block, 0, stream, p);
-}
-
-template <int HD, int KS>
 static hipError_t launch_hd(const AttnParams &p, const AttnPlan &plan, int n_kv_heads,
                             hipStream_t stream) {
   const dim3 grid((unsigned)(plan.units * n_kv_heads)), block(64 * kWaves);
   hipLaunchKernelGGL((attn_mfma_kernel<HD, KS>), grid, block, 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !plan.split) return e;
-  launch_combine<HD, KS>(p, plan, n_kv_heads, stream);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &plan, hipStream_t stream) {
+hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &plan, bool counters_zero,
+                            hipStream_t stream) {
   if (plan.units == 0) return hipSuccess;
   AttnParams p;
   p.out = (bf16 *)a.out;
@@ -638,6 +654,7 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &plan, hipStream_t
   p.tok_off = a.tok_off;
   p.sel_off = a.sel_off;
   p.ws = (unsigned char *)a.workspace;
+  p.cnt = plan.split ? (unsigned *)((char *)a.workspace + plan.cnt_offset) : nullptr;
   p.n_req = a.n_req;
   p.hq = a.n_q_heads;
   p.hkv = a.n_kv_heads;
@@ -645,8 +662,15 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &plan, hipStream_t
   p.rows_per_tile = plan.rows_per_tile;
   p.key_chunk = plan.key_chunk;
   p.scale_log2 = a.softmax_scale * 1.4426950408889634f;
-  const int h = a.n_kv_heads;
   if (plan.key_chunk % (kKeyTile * plan.key_split) != 0) return hipErrorInvalidValue;
+  if (plan.split && !counters_zero) {
+    const int blocks = (int)std::min<int64_t>((plan.n_cnt + 255) / 256, 64);
+    hipLaunchKernelGGL(attn_clear_kernel, dim3(blocks), dim3(256), 0, stream, p.cnt,
+                       (int32_t)plan.n_cnt);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int h = a.n_kv_heads;
   if (plan.key_split == 2) {
     switch (a.head_dim) {
       case 32: return launch_hd<32, 2>(p, plan, h, stream);

@@ -44,10 +44,13 @@ hipError_t launch_topk(int32_t n_req, const float *dev, const int32_t *cand_idx,
                        int32_t *sel_global, const int32_t *h_cand_off, const int32_t *h_sel_off,
                        hipStream_t stream);
 
+// Also sets clear[0 .. n_clear) to zero (the attention's arrival counters;
+// clear may be NULL when n_clear is 0).
 hipError_t launch_fuse(void *k_fused, void *v_fused, const void *k_new_c,
                        const void *v_new_c, const int32_t *sel_local,
                        const int32_t *sel_global, int64_t k_total,
-                       int32_t row_bytes, hipStream_t stream);
+                       int32_t row_bytes, uint32_t *clear, int64_t n_clear,
+                       hipStream_t stream);
 
 // Partial attention.
 struct AttnArgs {
@@ -76,8 +79,9 @@ struct AttnPlan {
   bool split;          // some request has more than one chunk
   int64_t tiles;       // query tiles over all requests
   int64_t units;       // (tile, chunk) units over all requests
-  int max_chunks;      // largest chunk count of any request with selected rows
-  size_t ws_bytes;     // workspace the split needs
+  size_t cnt_offset;   // split: byte offset of the arrival counters in the workspace
+  int64_t n_cnt;       // split: arrival counters, one per (tile, KV head)
+  size_t ws_bytes;     // workspace the split needs: partials, then counters
 };
 
 // Selected rows per MFMA query tile (256 / key_split query vectors), or 0 if
@@ -89,7 +93,10 @@ size_t attn_unit_bytes(int32_t head_dim, int key_split);
 // Most key chunks one row may be split into.
 int attn_max_chunks();
 
-hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &plan, hipStream_t stream);
+// counters_zero: the split's arrival counters are already zero (cleared by
+// the preceding fuse launch); otherwise a clear launch goes first.
+hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &plan, bool counters_zero,
+                            hipStream_t stream);
 
 hipError_t launch_attn_simple(int dtype, const AttnArgs &a, hipStream_t stream);
 

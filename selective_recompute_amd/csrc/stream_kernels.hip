@@ -497,10 +497,12 @@ __global__ __launch_bounds__(256) void fuse_kernel(
     uint4 *__restrict__ k_fused, uint4 *__restrict__ v_fused,
     const uint4 *__restrict__ k_new_c, const uint4 *__restrict__ v_new_c,
     const int32_t *__restrict__ sel_local, const int32_t *__restrict__ sel_global,
-    int64_t k_total, int32_t row_vec) {
+    int64_t k_total, int32_t row_vec, uint32_t *__restrict__ clear, int64_t n_clear) {
   const int64_t total = k_total * row_vec;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+  const int64_t first = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (int64_t i = first; i < n_clear; i += stride) clear[i] = 0;
+  for (int64_t i = first; i < total; i += stride) {
     const int64_t s = i / row_vec;
     const int c = (int)(i - s * row_vec);
     const int64_t src = (int64_t)sel_local[s] * row_vec + c;
@@ -512,15 +514,15 @@ __global__ __launch_bounds__(256) void fuse_kernel(
 
 hipError_t launch_fuse(void *k_fused, void *v_fused, const void *k_new_c, const void *v_new_c,
                        const int32_t *sel_local, const int32_t *sel_global, int64_t k_total,
-                       int32_t row_bytes, hipStream_t stream) {
+                       int32_t row_bytes, uint32_t *clear, int64_t n_clear, hipStream_t stream) {
   const int32_t row_vec = row_bytes / 16;
   const int64_t total = k_total * row_vec;
-  if (total == 0) return hipSuccess;
-  int64_t blocks = (total + 255) / 256;
+  if (total == 0 && n_clear == 0) return hipSuccess;
+  int64_t blocks = (std::max(total, n_clear) + 255) / 256;
   if (blocks > 16384) blocks = 16384;
   hipLaunchKernelGGL(fuse_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (uint4 *)k_fused,
                      (uint4 *)v_fused, (const uint4 *)k_new_c, (const uint4 *)v_new_c, sel_local,
-                     sel_global, k_total, row_vec);
+                     sel_global, k_total, row_vec, clear, n_clear);
   return hipGetLastError();
 }
 

@@ -187,6 +187,12 @@ def _unit(ks, d=128):
     return q * d * 2 + 3 * q * 4
 
 
+def _split_ws(ks, workgroups, tiles, hkv, d=128):
+    """A split's workspace: every workgroup's partial, then (256-byte aligned)
+    one 4-byte arrival counter per (tile, KV head)."""
+    return -(-workgroups * _unit(ks, d) // 256) * 256 + 4 * tiles * hkv
+
+
 def _plan(lib, g, tok, sel, ws=SIZE_MAX):
     rg, keep = _ragged(tok, tok, sel)
     p = B.AttnPlan()
@@ -210,18 +216,18 @@ def test_attention_plan_choices(lib):
     # 512 keys, 216 working workgroups: measured 20.1 us against 22.2 for the
     # best key-split-1 plan (8 chunks of 256 keys) and 35.1 unsplit
     p = _plan(lib, _geom(), [0, 2048], [0, 308])
-    assert fields(p) == (1, 2, 32, 512, 10, 320) and p.workspace_bytes == 320 * _unit(2)
+    assert fields(p) == (1, 2, 32, 512, 10, 320) and p.workspace_bytes == _split_ws(2, 320, 10, 8)
     # without workspace the same batch stays unsplit, still with key split 2
     p = _plan(lib, _geom(), [0, 2048], [0, 308], ws=0)
     assert fields(p) == (1, 2, 32, 0, 10, 80) and p.workspace_bytes == 0
     # 1844 of 6144 rows: two chunks of 3072 keys (the key-split-2 plans need
     # more than one round of the CUs, where they lose in the full step)
     p = _plan(lib, _geom(), [0, 6144], [0, 1844])
-    assert fields(p) == (1, 1, 64, 3072, 29, 464) and p.workspace_bytes == 464 * _unit(1)
+    assert fields(p) == (1, 1, 64, 3072, 29, 464) and p.workspace_bytes == _split_ws(1, 464, 29, 8)
     # 922 of 6144 rows: three chunks of 2048 keys (the 6k-token blend step:
     # 2.88 ms against 2.92 with key split 2 in two chunks of 3072 keys)
     p = _plan(lib, _geom(), [0, 6144], [0, 922])
-    assert fields(p) == (1, 1, 64, 2048, 15, 360) and p.workspace_bytes == 360 * _unit(1)
+    assert fields(p) == (1, 1, 64, 2048, 15, 360) and p.workspace_bytes == _split_ws(1, 360, 15, 8)
     # 3277 of 32768 rows: 52 tiles, unsplit (978 us against 1027 with key split 2)
     p = _plan(lib, _geom(), [0, 32768], [0, 3277])
     assert fields(p) == (1, 1, 64, 0, 52, 416)
@@ -272,7 +278,7 @@ def test_workspace_plan_properties(lib):
         assert p.key_chunk in chunks and p.key_chunk < max_n
         units = sum(t * -(-nn // p.key_chunk) for t, nn in zip(tiles, lens))
         assert p.workgroups == units * hkv
-        assert p.workspace_bytes == units * hkv * _unit(p.key_split)
+        assert p.workspace_bytes == _split_ws(p.key_split, units * hkv, p.tiles, hkv)
         # a smaller workspace gives a plan that fits it
         q = _plan(lib, g, tok, sel, ws=p.workspace_bytes - 1)
         assert q.workspace_bytes <= p.workspace_bytes - 1
@@ -303,7 +309,7 @@ def test_pinned_plans(lib):
             units = -(-450 // rows) * -(-3000 // kc) + -(-100 // kc)
             split = -(-3000 // kc) > 1
             assert st == 0 and p.workgroups == 8 * units and p.key_chunk == (kc if split else 0)
-            assert p.workspace_bytes == (8 * units * _unit(ks) if split else 0)
+            assert p.workspace_bytes == (_split_ws(ks, 8 * units, p.tiles, 8) if split else 0)
     st, p = describe(_geom(dt=B.CB_DTYPE_F32), 0, 0, 0)
     assert st == 0 and (p.mfma, p.workgroups) == (0, 470 * 32)
     bad = [
