@@ -7,6 +7,7 @@
 // "transformer训练与推理并行计算的差异" (causal mask: no key after the query).
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 #include "cb_device.hpp"
 #include "cb_launch.hpp"
@@ -462,6 +463,15 @@ void attn_mfma_kernel(const AttnParams p) {
   // the last to arrive merges all of them and writes the output.  A tile
   // whose rows all lie in its first chunk has one working unit and no merge.
   const int n_active = (int)((p_last - lo) / p.key_chunk) + 1;
+  // The merge of a split tile: with key split 2 both wave groups take part,
+  // each on half of the dim blocks of its query vectors (one dim block:
+  // group 0 alone); with key split 1 every wave on its own vectors.
+  constexpr int MSPLIT = (KS == 2 && NDT >= 2) ? 2 : 1;
+  constexpr int MDT = NDT / MSPLIT;          // dim blocks merged per wave
+  constexpr int MCH = MDT * 4 <= 8 ? 4 : 2;  // chunks whose loads are in flight at once
+  const bool merging = KS == 1 || MSPLIT == 2 || kg == 0;
+  const int dt_lo = MSPLIT == 2 ? kg * MDT : 0;
+  bool merged = false;
   if (n_active > 1) {
     constexpr int UNIT = partial_bytes<HD, QT>();
     if (kg == 0) {
@@ -508,87 +518,109 @@ void attn_mfma_kernel(const AttnParams p) {
     }
     phase_barrier();
     if (!s_last) return;  // uniform
-    if (kg == 0) {
-      // Merge every working chunk's stored partial, this one's included, in
-      // chunk order: the result does not depend on which chunk arrived last.
-      // Unit of (tile, chunk c): ubase + c * tr + (tr - 1 - tile).
+    merged = true;
+    // Merge every working chunk's stored partial, this one's included, in
+    // chunk order: the result does not depend on which chunk arrived last.
+    // Unit of (tile, chunk c): ubase + c * tr + (tr - 1 - tile).
+    if (merging) {
       const unsigned char *w0 =
           p.ws + ((up.ubase + (int64_t)(up.tr - 1 - tile)) * p.hkv + g) * UNIT;
       const int64_t ustride = (int64_t)up.tr * p.hkv * UNIT;
-      // Running max, running sum and largest |O| of every chunk, all loads in
-      // one round (chunks past n_active weigh nothing).
-      float mc[kMaxChunks], lc[kMaxChunks], ac[kMaxChunks];
+      const int fw = wave - kg * WPG;  // query block of this wave in the fragment order
+      // One round of loads for up to MCH chunks: the running max, running
+      // sum and largest |O| of every chunk, then the first MCH chunks' O
+      // fragments (issued before any of them is used), then a round per
+      // further MCH chunks.  O of the dim blocks D0 .. D0 + MDT - 1 adds up in
+      // chunk order; all indices are unrolled constants, so nothing leaves
+      // the registers.
+      auto merge_dims = [&](auto d0) {
+        constexpr int D0 = decltype(d0)::value;
+        float mc[kMaxChunks], lc[kMaxChunks], ac[kMaxChunks];
 #pragma unroll
-      for (int c = 0; c < kMaxChunks; ++c) {
-        mc[c] = kNegFloor;
-        lc[c] = ac[c] = 0.f;
-        if (c < n_active) {
-          const uint32_t *mt = reinterpret_cast<const uint32_t *>(w0 + c * ustride + QT * HD * 2);
-          mc[c] = __builtin_bit_cast(float, load_agent(mt + qv));
-          lc[c] = __builtin_bit_cast(float, load_agent(mt + QT + qv));
-          ac[c] = __builtin_bit_cast(float, load_agent(mt + 2 * QT + qv));
+        for (int c = 0; c < kMaxChunks; ++c) {
+          mc[c] = kNegFloor;
+          lc[c] = ac[c] = 0.f;
+          if (c < n_active) {
+            const uint32_t *mt =
+                reinterpret_cast<const uint32_t *>(w0 + c * ustride + QT * HD * 2);
+            mc[c] = __builtin_bit_cast(float, load_agent(mt + qv));
+            lc[c] = __builtin_bit_cast(float, load_agent(mt + QT + qv));
+            ac[c] = __builtin_bit_cast(float, load_agent(mt + 2 * QT + qv));
+          }
         }
-      }
-      float mx = kNegFloor;
+        f16x4 h[MCH][MDT * 4];
+        auto load_group = [&](int c0) {
 #pragma unroll
-      for (int c = 0; c < kMaxChunks; ++c) mx = fmaxf(mx, mc[c]);
-      float wgt[kMaxChunks];
-      l = 0.f;
+          for (int j = 0; j < MCH; ++j) {
+            if (c0 + j < n_active) {
+              const uint64_t *src = reinterpret_cast<const uint64_t *>(w0 + (c0 + j) * ustride);
 #pragma unroll
-      for (int c = 0; c < kMaxChunks; ++c) {
-        wgt[c] = c < n_active ? __builtin_amdgcn_exp2f(mc[c] - mx) : 0.f;
-        l = fmaf(lc[c], wgt[c], l);
-        wgt[c] *= ac[c];
-      }
+              for (int dl = 0; dl < MDT; ++dl)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt] = 0.f;
-      auto load = [&](int c, f16x4 (&h)[NDT * 4]) {
-        const uint64_t *src = reinterpret_cast<const uint64_t *>(w0 + c * ustride);
+                for (int q = 0; q < 4; ++q)
+                  h[j][dl * 4 + q] = __builtin_bit_cast(
+                      f16x4, load_agent(src + (((fw * NDT + D0 + dl) * 4 + q) << 6) + lane));
+            }
+          }
+        };
+        load_group(0);
+        float mx = kNegFloor;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
+        for (int c = 0; c < kMaxChunks; ++c) mx = fmaxf(mx, mc[c]);
+        float wgt[kMaxChunks];
+        l = 0.f;
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            h[dt * 4 + q] = __builtin_bit_cast(
-                f16x4, load_agent(src + (((wave * NDT + dt) * 4 + q) << 6) + lane));
-      };
-      auto add = [&](float wo, const f16x4 (&h)[NDT * 4]) {
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              o[dt][4 * q + i] = fmaf((float)h[dt * 4 + q][i], wo, o[dt][4 * q + i]);
-      };
-      // O in chunk order, two chunks' loads in flight (weights indexed by
-      // unrolled constants only, so they stay in registers)
-#pragma unroll
-      for (int c = 0; c < kMaxChunks; c += 2) {
-        if (c < n_active) {
-          f16x4 h0[NDT * 4], h1[NDT * 4];
-          load(c, h0);
-          if (c + 1 < n_active) load(c + 1, h1);
-          add(wgt[c], h0);
-          if (c + 1 < n_active) add(wgt[c + 1], h1);
+        for (int c = 0; c < kMaxChunks; ++c) {
+          wgt[c] = c < n_active ? __builtin_amdgcn_exp2f(mc[c] - mx) : 0.f;
+          l = fmaf(lc[c], wgt[c], l);
+          wgt[c] *= ac[c];
         }
-      }
+#pragma unroll
+        for (int dl = 0; dl < MDT; ++dl) o[D0 + dl] = 0.f;
+#pragma unroll
+        for (int c0 = 0; c0 < kMaxChunks; c0 += MCH) {
+          if (c0 < n_active) {
+            if (c0 > 0) load_group(c0);
+#pragma unroll
+            for (int j = 0; j < MCH; ++j) {
+              if (c0 + j < n_active) {
+#pragma unroll
+                for (int dl = 0; dl < MDT; ++dl)
+#pragma unroll
+                  for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                      o[D0 + dl][4 * q + i] =
+                          fmaf((float)h[j][dl * 4 + q][i], wgt[c0 + j], o[D0 + dl][4 * q + i]);
+              }
+            }
+          }
+        }
+      };
+      if (dt_lo == 0) merge_dims(std::integral_constant<int, 0>{});
+      else merge_dims(std::integral_constant<int, MDT>{});
     }
   }
 
   // Output through LDS (the K stage buffers are free once every wave is past
-  // its last tile): each wave of key group 0 writes its normalised bf16 rows
-  // (16-byte chunk index XOR-swizzled by the query vector against bank
+  // its last tile): each wave holding results writes its normalised bf16
+  // rows (16-byte chunk index XOR-swizzled by the query vector against bank
   // conflicts), then the workgroup stores 16-byte chunks in output order --
   // the G query heads of one selected row are adjacent in `out`, so a wave
   // writes whole 1 KiB runs instead of 8 bytes per lane 256 bytes apart.
+  // Unmerged, key group 0 holds every dim block; merged, each merging wave
+  // holds its own.
   constexpr int CPQ = HD / 8;  // 16-byte chunks per query vector
   bf16 *stage = &kst[0][0];
   static_assert(STAGES * TILE >= QT * HD, "output staging does not fit");
   phase_barrier();
-  if (kg == 0) {
+  const bool writer = merged ? merging : kg == 0;
+  const int w_lo = merged ? dt_lo : 0, w_hi = merged ? dt_lo + MDT : NDT;
+  if (writer) {
     const float inv = 1.f / l;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+    for (int dt = 0; dt < NDT; ++dt) {
+      if (dt < w_lo || dt >= w_hi) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         bf16x4 w;
@@ -597,6 +629,7 @@ void attn_mfma_kernel(const AttnParams p) {
         const int cq = (4 * dt + q) ^ (qv & (CPQ - 1));
         *reinterpret_cast<bf16x4 *>(stage + qv * HD + 8 * cq + 4 * half) = w;
       }
+    }
   }
   phase_barrier();
   for (int c = tid; c < QT * CPQ; c += 64 * kWaves) {
