@@ -376,9 +376,9 @@ void attn_mfma_kernel(const AttnParams p) {
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[sb][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
     const float mxs = mx * p.scale_log2;
-    const bool up = mxs > m_run + kRescaleSlack;
-    if (__any(up)) {
-      const float m_new = up ? mxs : m_run;
+    const bool raise = mxs > m_run + kRescaleSlack;
+    if (__any(raise)) {
+      const float m_new = raise ? mxs : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;

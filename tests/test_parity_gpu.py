@@ -364,6 +364,14 @@ def _attention_case(case, use_ws, seed, max_rows=None, plan=None):
     else:
         B.partial_attn(g, rb, *args, workspace=ws)
     torch.cuda.synchronize()
+    if plan is not None:
+        # the same call again on the used workspace: a split's merge order is
+        # fixed, so the output repeats bit for bit
+        first = out.clone()
+        out.fill_(float("nan"))
+        B.partial_attn_with_plan(g, rb, plan, *args, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out, first)
     got = np64(out)
     assert np.isfinite(got).all()
     rows = np.arange(len(sel_g))
