@@ -55,10 +55,11 @@ namespace cb {
 //    unit sees in full skip the causal mask.
 //
 // Long rows with too few tiles to fill the chip are split over key chunks of
-// `key_chunk` keys (a multiple of 64); every chunk writes its partial to the
-// workspace -- O of each query vector divided by its largest |O| as fp16,
-// then the running max, running sum and that largest |O| in fp32 -- and
-// attn_combine_kernel merges them.  Unsplit units write the output directly.
+// `key_chunk` keys (a multiple of the tile); every working chunk writes its
+// partial to the workspace -- O of each query vector divided by its largest
+// |O| as fp16, then the running max, running sum and that largest |O| in
+// fp32 -- and the last chunk of the tile to arrive merges them (see the end
+// of the kernel).  Unsplit units write the output directly.
 // Block order: blockIdx % Hkv is the KV head, so with Hkv = 8 the round-robin
 // dispatch over the 8 XCDs keeps each head's K/V stream in one XCD's L2.  In
 // a request, units go chunk by chunk and, within a chunk, from the last
