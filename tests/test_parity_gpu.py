@@ -498,19 +498,25 @@ def _oracle_layer(wl, x, cand, counts, attend_rows=None):
                 v_fused=v_fused, out=out, rows=rows)
 
 
-E2E = [("tiny", [0], None, "pool"), ("mistral7b-layer", [0], None, "pool"), ("7b-32layer-6k", [0, 1, 2], 96, "pool"),
-       ("7b-32layer-6k", [0, 1, 2, 3], 96, "chain"), ("7b-32layer-32k", [0, 1], 24, "pool"), ("70b-80layer-8req", [0, 1], 24, "pool")]
+E2E = [("tiny", [0], None, "pool", True), ("mistral7b-layer", [0], None, "pool", True),
+       ("mistral7b-layer", [0], None, "pool", False), ("7b-32layer-6k", [0, 1, 2], 96, "pool", True),
+       ("7b-32layer-6k", [0, 1], 96, "pool", False), ("7b-32layer-6k", [0, 1, 2, 3], 96, "chain", True),
+       ("7b-32layer-32k", [0, 1], 24, "pool", True), ("70b-80layer-8req", [0, 1], 24, "pool", True)]
 
 
-@pytest.mark.parametrize("name,layers,n_rows,schedule", E2E,
-                         ids=[f"{e[0]}-{e[3]}" for e in E2E])
-def test_blend_layers_end_to_end(name, layers, n_rows, schedule):
+@pytest.mark.parametrize("name,layers,n_rows,schedule,use_ws", E2E,
+                         ids=[f"{e[0]}-{e[3]}{'' if e[4] else '-noworkspace'}" for e in E2E])
+def test_blend_layers_end_to_end(name, layers, n_rows, schedule, use_ws):
+    """Whole layers through cb_blend_layer against the oracle; without a
+    workspace the attention runs unsplit."""
     wl = W.make_workload(name)
     sets = W.PlantedSets(wl, schedule)
     gen_dev = "cpu" if wl.n_tokens <= 8192 else DEV
     runner = PL.BlendRunner(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.torch_dtype,
                             wl.request_lengths, wl.r1_pct, wl.r2_pct, max(layers) + 1,
                             wl.rope_theta, schedule=schedule)
+    if not use_ws:
+        runner.workspace = None
     for layer in layers:
         say(f"blend {name} layer {layer}")
         x = W.layer_inputs(wl, sets, layer, device=gen_dev)
