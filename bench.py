@@ -368,7 +368,21 @@ def main():
     stage_calls = {s: [[] for _ in range(L)] for s in STAGES}
     topk_calls = [[] for _ in range(L)]   # the selection half alone, for its own time
     keep = []
-    ws_ptr, ws_bytes = B._ws(runner.workspace)
+    # The attention is timed as the launch cb_blend_layer makes: the plan
+    # cb_partial_attn chooses, pinned, on a workspace zero-filled once per
+    # distinct plan (every call leaves its counters at zero), so no call
+    # needs the launch that clears them.
+    ws_bytes = 0 if runner.workspace is None else runner.workspace.numel()
+    attn_plans, plan_ws = [], {}
+    for l in range(L):
+        pd = B.attn_plan(runner.geom, runner.batches[l], ws_bytes)
+        key = (pd["mfma"], pd["key_split"], pd["key_chunk"])
+        if key not in plan_ws:
+            plan_ws[key] = B.workspace_tensor(pd["workspace_bytes"], "cuda")
+            if plan_ws[key] is not None:
+                plan_ws[key].zero_()
+        attn_plans.append((B.AttnPlan(key[0], key[1], 0, key[2], 0, 0, 0),
+                           *B._ws(plan_ws[key])))
     for cp in copies:
         sels = []
         for l, x in enumerate(cp):
@@ -396,11 +410,13 @@ def main():
                 (lib.cb_fuse_scatter, (gref, k_ptr, v_ptr, x["k_new_c"].data_ptr(),
                                        x["v_new_c"].data_ptr(), sl.data_ptr(), sg.data_ptr(),
                                        rb.n_sel, h)))
+            plan, pws_ptr, pws_bytes = attn_plans[l]
             stage_calls["partial_attn"][l].append(
-                (lib.cb_partial_attn, (gref, ctypes.byref(rgs[l]),
-                                       runner.outs[l]["out"].data_ptr(), x["q_c"].data_ptr(),
-                                       sl.data_ptr(), sg.data_ptr(), k_ptr, v_ptr,
-                                       runner.scale, ws_ptr, ws_bytes, h)))
+                (lib.cb_partial_attn_with_plan,
+                 (gref, ctypes.byref(rgs[l]), ctypes.byref(plan),
+                  runner.outs[l]["out"].data_ptr(), x["q_c"].data_ptr(), sl.data_ptr(),
+                  sg.data_ptr(), k_ptr, v_ptr, runner.scale, pws_ptr, pws_bytes,
+                  B.CB_ATTN_COUNTERS_ZERO, h)))
     events = {}
     with torch.cuda.stream(stream):
         torch.cuda.synchronize()

@@ -196,8 +196,9 @@ cb_status cb_fuse_scatter(const cb_geom *geom, void *k_fused, void *v_fused,
  *            (NULL/0 allowed).  When the query tiles are too few to fill the
  *            GPU, long rows are split over key ranges whose partials
  *            live here, with one arrival counter per query tile and KV head
- *            (the last chunk to arrive merges them; the call clears the
- *            counters first, so the contents need no initialisation);
+ *            (the last chunk to arrive merges them and sets its counter
+ *            back to zero; the call clears the counters first, so the
+ *            contents need no initialisation);
  *            cb_partial_attn_workspace_size() gives the size that enables
  *            the split.  A smaller workspace only disables the split.
  *            Calls that share a workspace must be ordered on one stream.
@@ -257,14 +258,26 @@ cb_status cb_partial_attn_describe_plan(const cb_geom *geom, const cb_ragged *rg
  *               into more than 8 chunks (INVALID_ARG otherwise).
  * A split needs the workspace that cb_partial_attn_describe_plan() reports
  * for the same fields (INVALID_ARG if workspace_bytes is smaller).
+ *
+ * flags : 0 or CB_ATTN_COUNTERS_ZERO (other bits: INVALID_ARG).  Without it
+ *   a split plan first clears its arrival counters with a small launch of
+ *   its own, as cb_partial_attn does.  Every call leaves its plan's counters
+ *   at zero, so a caller that fills the workspace with zeros once and then
+ *   calls with one plan on it may pass the flag and save that launch.  The
+ *   partials of a different split plan on the same workspace can overwrite
+ *   this plan's counters: after such a call fill with zeros again, or omit
+ *   the flag.  Counters that are not zero under the flag give wrong output
+ *   rows (a tile merged early or never); nothing waits on them, so nothing
+ *   hangs.  Unsplit plans use no counters and ignore the flag.
  */
+#define CB_ATTN_COUNTERS_ZERO 1u
 cb_status cb_partial_attn_with_plan(const cb_geom *geom, const cb_ragged *rg,
                                     const cb_attn_plan *plan, void *out,
                                     const void *q_c, const int32_t *sel_local,
                                     const int32_t *sel_global, const void *k_fused,
                                     const void *v_fused, float softmax_scale,
                                     void *workspace, size_t workspace_bytes,
-                                    void *stream);
+                                    uint32_t flags, void *stream);
 
 /* Every argument of one layer of the blend. */
 typedef struct cb_layer_args {
@@ -305,7 +318,7 @@ const char *cb_last_error(void);
 /* ABI revision of this header (bumped on any incompatible change). */
 int32_t cb_abi_version(void);
 
-#define CB_ABI_VERSION 4
+#define CB_ABI_VERSION 5
 
 #ifdef __cplusplus
 }

@@ -21,6 +21,7 @@ CB_OK, CB_ERR_INVALID_ARG, CB_ERR_UNSUPPORTED, CB_ERR_HIP = 0, 1, 2, 3
 CB_DTYPE_F32, CB_DTYPE_BF16 = 0, 1
 ROPE_HALF, ROPE_INTERLEAVED = 0, 1
 CB_DEV_V, CB_DEV_K, CB_DEV_KV = 0, 1, 2
+CB_ATTN_COUNTERS_ZERO = 1
 DEV_SOURCES = {"v": CB_DEV_V, "k": CB_DEV_K, "kv": CB_DEV_KV}
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -96,7 +97,7 @@ _SIGNATURES = {
                                   ctypes.POINTER(AttnPlan), ctypes.c_void_p, ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
-                                  ctypes.c_size_t, ctypes.c_void_p],
+                                  ctypes.c_size_t, ctypes.c_uint32, ctypes.c_void_p],
     "cb_blend_layer": [ctypes.POINTER(LayerArgs), ctypes.c_void_p],
 }
 
@@ -282,16 +283,20 @@ def partial_attn(g: Geom, rb: RaggedBatch, out, q_c, sel_local, sel_global, k_fu
 
 def partial_attn_with_plan(g: Geom, rb: RaggedBatch, plan: dict, out, q_c, sel_local,
                            sel_global, k_fused, v_fused, softmax_scale: float,
-                           workspace: Optional[torch.Tensor] = None, stream=None):
-    """cb_partial_attn with a pinned plan (a dict with mfma, key_split, key_chunk)."""
+                           workspace: Optional[torch.Tensor] = None, stream=None,
+                           counters_zero: bool = False):
+    """cb_partial_attn with a pinned plan (a dict with mfma, key_split, key_chunk).
+    counters_zero: pass CB_ATTN_COUNTERS_ZERO (the workspace was zero-filled and
+    has since been used only with this plan)."""
     p = AttnPlan(plan["mfma"], plan.get("key_split", 1), 0, plan.get("key_chunk", 0), 0, 0, 0)
     rg = rb.struct()
     ws_ptr, ws_bytes = _ws(workspace)
+    flags = CB_ATTN_COUNTERS_ZERO if counters_zero else 0
     check(lib().cb_partial_attn_with_plan(ctypes.byref(g), ctypes.byref(rg), ctypes.byref(p),
                                           _dev(out), _dev(q_c), _dev(sel_local, torch.int32),
                                           _dev(sel_global, torch.int32), _dev(k_fused),
                                           _dev(v_fused), softmax_scale, ws_ptr, ws_bytes,
-                                          _stream(stream)))
+                                          flags, _stream(stream)))
 
 
 def blend_layer(g: Geom, rb: RaggedBatch, *, k, v, k_new_c, v_new_c, q_c, delta, cand_idx,

@@ -458,7 +458,8 @@ cb_status pinned_plan(const cb_geom *g, const cb_ragged *rg, const cb_attn_plan 
 }
 
 // counters_zero: the split's arrival counters in the workspace are known to
-// be zero (cb_blend_layer's fuse launch clears them).
+// be zero (cb_blend_layer's fuse launch clears them, or the caller vouches
+// for them with CB_ATTN_COUNTERS_ZERO).
 cb_status run_attn(const cb_geom *geom, const cb_ragged *rg, const cb::AttnPlan &plan,
                    void *out, const void *q_c, const int32_t *sel_local,
                    const int32_t *sel_global, const void *k_fused, const void *v_fused,
@@ -566,16 +567,19 @@ CB_EXPORT cb_status cb_partial_attn_with_plan(const cb_geom *geom, const cb_ragg
                                               const int32_t *sel_global, const void *k_fused,
                                               const void *v_fused, float softmax_scale,
                                               void *workspace, size_t workspace_bytes,
-                                              void *stream) {
+                                              uint32_t flags, void *stream) {
   g_last_error.clear();
   if (!plan) return fail(CB_ERR_INVALID_ARG, "plan is NULL");
+  if (flags & ~CB_ATTN_COUNTERS_ZERO)
+    return fail(CB_ERR_INVALID_ARG, "unknown flags 0x%x", (unsigned)flags);
   CB_TRY(validate_attn(geom, rg, out, q_c, sel_local, sel_global, k_fused, v_fused,
                        softmax_scale));
   CB_TRY(need_ptr(workspace, "workspace", workspace_bytes > 0));
   cb::AttnPlan pl;
   CB_TRY(pinned_plan(geom, rg, plan, workspace ? workspace_bytes : 0, pl));
   return run_attn(geom, rg, pl, out, q_c, sel_local, sel_global, k_fused, v_fused,
-                  softmax_scale, workspace, false, (hipStream_t)stream);
+                  softmax_scale, workspace, (flags & CB_ATTN_COUNTERS_ZERO) != 0,
+                  (hipStream_t)stream);
 }
 
 CB_EXPORT cb_status cb_partial_attn_workspace_size(const cb_geom *geom, const cb_ragged *rg,

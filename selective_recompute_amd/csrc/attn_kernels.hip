@@ -77,7 +77,7 @@ struct AttnParams {
   const int32_t *tok_off;
   const int32_t *sel_off;
   unsigned char *ws;     // split partials, one per workgroup of the launch
-  unsigned *cnt;         // arrival counter per (query tile, KV head); zero at launch
+  unsigned *cnt;         // arrival counter per (query tile, KV head); zero at launch and at exit
   int32_t n_req, hq, hkv, group, rows_per_tile, key_chunk;
   float scale_log2;
 };
@@ -508,14 +508,18 @@ void attn_mfma_kernel(const AttnParams p) {
     }
     // Arrival: every store of the partial has completed at the coherence
     // point shared by all XCDs before the arrival is counted; the workgroup
-    // that brings the count to n_active goes on.
+    // that brings the count to n_active goes on.  It is the last to touch
+    // the counter in this launch, so it sets it back to zero: every launch
+    // leaves its counters as it needs to find them.
     __shared__ int s_last;
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     phase_barrier();
     if (tid == 0) {
-      const unsigned prev = __hip_atomic_fetch_add(p.cnt + (up.tbase + tile) * p.hkv + g, 1u,
-                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      unsigned *const cnt = p.cnt + (up.tbase + tile) * p.hkv + g;
+      const unsigned prev =
+          __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_last = prev == (unsigned)(n_active - 1);
+      if (s_last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     phase_barrier();
     if (!s_last) return;  // uniform
@@ -643,8 +647,9 @@ void attn_mfma_kernel(const AttnParams p) {
   }
 }
 
-// Arrival counters of a split launch back to zero (standalone calls; inside
-// cb_blend_layer the fuse launch clears them).
+// Arrival counters of a split launch set to zero before it (standalone calls
+// on a workspace of unknown contents; inside cb_blend_layer the fuse launch
+// clears them).
 __global__ __launch_bounds__(256) void attn_clear_kernel(unsigned *cnt, int32_t n) {
   for (int i = blockIdx.x * 256 + (int)threadIdx.x; i < n; i += gridDim.x * 256) cnt[i] = 0;
 }

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
             "cb_blend_layer"} <= declared
     for name in sorted(declared):
         assert hasattr(lib, name), name
-    assert lib.cb_abi_version() == 4
+    assert lib.cb_abi_version() == 5
 
 
 def test_status_strings(lib):
@@ -329,13 +329,19 @@ def test_pinned_plans(lib):
         assert needle.encode() in lib.cb_last_error(), lib.cb_last_error()
         assert (p.rows_per_tile, p.tiles, p.workgroups, p.workspace_bytes) == (7, 7, 7, 7)
         assert lib.cb_partial_attn_with_plan(ctypes.byref(g), ctypes.byref(rg), ctypes.byref(p), P, P, P, P,
-                                             P, P, 0.1, None, 0, None) == status
+                                             P, P, 0.1, None, 0, 0, None) == status
         assert needle.encode() in lib.cb_last_error()
     # a split needs its workspace
     p = B.AttnPlan(1, 1, 0, 1024, 0, 0, 0)
     assert lib.cb_partial_attn_with_plan(ctypes.byref(_geom()), ctypes.byref(rg), ctypes.byref(p), P, P, P, P,
-                                         P, P, 0.1, P2, 4096, None) == 1
+                                         P, P, 0.1, P2, 4096, B.CB_ATTN_COUNTERS_ZERO, None) == 1
     assert b"smaller than the plan" in lib.cb_last_error()
     assert lib.cb_partial_attn_with_plan(ctypes.byref(_geom()), ctypes.byref(rg), None, P, P, P, P,
-                                         P, P, 0.1, None, 0, None) == 1
+                                         P, P, 0.1, None, 0, 0, None) == 1
+    # flags other than CB_ATTN_COUNTERS_ZERO
+    for flags in (2, 0x80000000, 3):
+        p = B.AttnPlan(1, 1, 0, 0, 0, 0, 0)
+        assert lib.cb_partial_attn_with_plan(ctypes.byref(_geom()), ctypes.byref(rg), ctypes.byref(p), P, P, P, P,
+                                             P, P, 0.1, None, 0, flags, None) == 1
+        assert b"unknown flags" in lib.cb_last_error()
     assert lib.cb_partial_attn_describe_plan(ctypes.byref(_geom()), ctypes.byref(rg), None) == 1

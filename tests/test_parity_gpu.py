@@ -314,6 +314,14 @@ ATTN_CASES = [
 ]
 
 
+def _counters(ws, plan, hkv):
+    """The arrival counters of a split plan: the last 4 * tiles * hkv bytes of
+    its workspace (one uint32 per query tile and KV head)."""
+    n = plan["tiles"] * hkv
+    end = plan["workspace_bytes"]
+    return ws[end - 4 * n:end].view(torch.int32)
+
+
 def _attention_case(case, use_ws, seed, max_rows=None, plan=None):
     """Run cb_partial_attn (or, given `plan`, cb_partial_attn_with_plan) on a
     seeded case; compare every row (or a sample of max_rows plus each
@@ -364,14 +372,22 @@ def _attention_case(case, use_ws, seed, max_rows=None, plan=None):
     else:
         B.partial_attn(g, rb, *args, workspace=ws)
     torch.cuda.synchronize()
+    used = full if plan is not None else (B.attn_plan(g, rb, ws.numel()) if use_ws else None)
+    if used is not None and used["key_chunk"]:
+        # every merging workgroup sets its arrival counter back to zero
+        assert not _counters(ws, used, hkv).any()
     if plan is not None:
         # the same call again on the used workspace: a split's merge order is
-        # fixed, so the output repeats bit for bit
+        # fixed, so the output repeats bit for bit; with the counters vouched
+        # for (no clearing launch) too
         first = out.clone()
-        out.fill_(float("nan"))
-        B.partial_attn_with_plan(g, rb, plan, *args, workspace=ws)
-        torch.cuda.synchronize()
-        assert torch.equal(out, first)
+        for counters_zero in (False, True, True):
+            out.fill_(float("nan"))
+            B.partial_attn_with_plan(g, rb, plan, *args, workspace=ws, counters_zero=counters_zero)
+            torch.cuda.synchronize()
+            assert torch.equal(out, first)
+            if full["key_chunk"]:
+                assert not _counters(ws, full, hkv).any()
     got = np64(out)
     assert np.isfinite(got).all()
     rows = np.arange(len(sel_g))
