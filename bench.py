@@ -39,6 +39,8 @@ FP32_PEAK_TFLOPS = 157.3       # fp32 vector
 DEFAULT_STEPS = {"tiny": (200, 20), "mistral7b-layer": (200, 20), "7b-32layer-6k": (20, 3),
                  "7b-32layer-32k": (4, 1), "70b-80layer-8req": (2, 1)}
 STAGES = ("rerotate", "deviation_topk", "fuse_scatter", "partial_attn")
+# the order that scores and selects first, then rotates-or-replaces in one pass
+STAGES_AFTER = ("deviation_topk", "rerotate_fuse", "partial_attn")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -100,6 +102,10 @@ def parse_args():
     ap.add_argument("--dev-source", default="v", choices=["v", "k", "kv"],
                     help="what the token deviation measures: V (default), K at the new "
                          "position, or the K and V rows as one vector")
+    ap.add_argument("--order", default="auto", choices=["auto", "rotate-first", "select-first"],
+                    help="step order of cb_blend_layer: select-first scores V and selects "
+                         "first, then one launch writes the rows of S and re-rotates only the "
+                         "others; auto lets the library choose")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="budget of the CPU oracle baseline (0 disables it)")
     ap.add_argument("--attainable", type=int, default=1,
@@ -131,7 +137,8 @@ def algorithmic_work(wl, runner, selected_per_layer, dev_tensors=1):
     elem = 2 if wl.dtype == "bf16" else 4
     row = wl.n_kv_heads * wl.head_dim * elem
     t_count = wl.n_tokens
-    nz = int(np.count_nonzero(wl.delta()))
+    delta = wl.delta()
+    nz = int(np.count_nonzero(delta))
     tok_off = wl.tok_off
     work = []
     for layer in range(wl.n_layers):
@@ -145,6 +152,9 @@ def algorithmic_work(wl, runner, selected_per_layer, dev_tensors=1):
             "rerotate": 2.0 * row * nz + 4.0 * t_count,
             "deviation_topk": 2.0 * dev_tensors * row * m + 8.0 * m,
             "fuse_scatter": 4.0 * row * k + 8.0 * k,
+            # rotate-or-replace: kept rows with delta != 0 turned, rows of S written
+            "rerotate_fuse": 2.0 * row * (nz - int(np.count_nonzero(delta[sel]))) + 4.0 * t_count
+                             + 4.0 * row * k + 8.0 * k,
             "partial_attn": flops,
         })
     return work
@@ -289,7 +299,11 @@ def main():
     sets = W.PlantedSets(wl, a.schedule)
     runner = PL.BlendRunner(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.torch_dtype,
                             wl.request_lengths, wl.r1_pct, wl.r2_pct, L, wl.rope_theta,
-                            schedule=a.schedule, dev_source=a.dev_source, device="cuda")
+                            schedule=a.schedule, dev_source=a.dev_source, device="cuda",
+                            order=a.order)
+    if a.order == "select-first" and a.dev_source != "v":
+        raise SystemExit("--order select-first scores V only (a key deviation reads the "
+                         "re-rotated keys)")
     stream = torch.cuda.Stream()
     h = stream.cuda_stream
 
@@ -316,8 +330,13 @@ def main():
                                        softmax_scale=runner.scale, dev=o["dev"],
                                        sel_local=o["sel_local"], sel_global=o["sel_global"],
                                        out=o["out"], workspace=runner.workspace,
-                                       dev_source=runner.dev_source))
+                                       dev_source=runner.dev_source,
+                                       order=runner.order))
         prepared.append(row)
+    # the attribution pass times the entry points of the order the library runs
+    # (the same for every layer: it depends on the cache size and the source)
+    select_first = prepared[0][0].resolved_order() == B.CB_ORDER_SELECT_FIRST
+    stages = STAGES_AFTER if select_first else STAGES
     graph = None
     with torch.cuda.stream(stream):
         for c in range(warmup):
@@ -365,7 +384,7 @@ def main():
     copies = make_copies(steps, 10_000)
     gref = ctypes.byref(runner.geom)
     rgs = [rb.struct() for rb in runner.batches]
-    stage_calls = {s: [[] for _ in range(L)] for s in STAGES}
+    stage_calls = {s: [[] for _ in range(L)] for s in STAGES + STAGES_AFTER}
     topk_calls = [[] for _ in range(L)]   # the selection half alone, for its own time
     keep = []
     # The attention is timed as the launch cb_blend_layer makes: the plan
@@ -410,6 +429,11 @@ def main():
                 (lib.cb_fuse_scatter, (gref, k_ptr, v_ptr, x["k_new_c"].data_ptr(),
                                        x["v_new_c"].data_ptr(), sl.data_ptr(), sg.data_ptr(),
                                        rb.n_sel, h)))
+            stage_calls["rerotate_fuse"][l].append(
+                (lib.cb_rerotate_fuse, (gref, k_ptr, v_ptr, x["k_new_c"].data_ptr(),
+                                        x["v_new_c"].data_ptr(), x["delta"].data_ptr(),
+                                        sl.data_ptr(), sg.data_ptr(), rb.n_sel, wl.n_tokens,
+                                        wl.rope_theta, B.ROPE_HALF, h)))
             plan, pws_ptr, pws_bytes = attn_plans[l]
             stage_calls["partial_attn"][l].append(
                 (lib.cb_partial_attn_with_plan,
@@ -421,7 +445,7 @@ def main():
     with torch.cuda.stream(stream):
         torch.cuda.synchronize()
         for l in range(L):
-            for s in STAGES:
+            for s in stages:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
                 for fn, args in stage_calls[s][l]:
@@ -441,13 +465,13 @@ def main():
             events[(l, "topk")] = (e0, e1)
         torch.cuda.synchronize()
     stage_ms = {s: sum(events[(l, s)][0].elapsed_time(events[(l, s)][1]) for l in range(L))
-                for s in STAGES}
+                for s in stages}
     launches = steps * L
     work = algorithmic_work(wl, runner, selected, 2 if a.dev_source == "kv" else 1)
     # every layer of every step was launched once
-    stage_work = {s: steps * sum(w[s] for w in work) for s in STAGES}
+    stage_work = {s: steps * sum(w[s] for w in work) for s in stages}
     kernels = {}
-    for s in STAGES:
+    for s in stages:
         avg_us = stage_ms[s] * 1e3 / launches
         if s == "partial_attn":
             rate = stage_work[s] / (stage_ms[s] * 1e-3) / 1e12
@@ -460,7 +484,7 @@ def main():
     # each class against its published peak and, when measured, the attainable one
     # (MFMA probe for the attention, streaming-read probe for the HBM stages)
     flop_peak_t = BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
-    for s in STAGES:
+    for s in stages:
         kk = kernels[s]
         if "tflops" in kk:
             kk["frac"] = round(kk["tflops"] / flop_peak_t, 5)
@@ -472,7 +496,7 @@ def main():
                 kk["frac_attainable"] = round(kk["gbs"] / peaks["read_gbs"], 5)
     topk_ms = sum(events[(l, "topk")][0].elapsed_time(events[(l, "topk")][1]) for l in range(L))
     kernels["topk"] = {"avg_us": round(topk_ms * 1e3 / launches, 3), "bound": "latency"}
-    dominant = max(STAGES, key=lambda s: stage_ms[s])
+    dominant = max(stages, key=lambda s: stage_ms[s])
     if dominant == "partial_attn":
         bf16 = wl.dtype == "bf16"
         peak = BF16_PEAK_TFLOPS if bf16 else FP32_PEAK_TFLOPS
@@ -528,6 +552,8 @@ def main():
                    "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "selection": ratio,
                    "hkvd_pct": wl.hkvd_pct, "schedule": a.schedule,
                    "dev_source": a.dev_source,
+                   "order": f"{a.order}: " + ("select, then rotate-or-replace" if select_first
+                                              else "rotate, select, fuse"),
                    "launch": "hip graph replay" if a.graph else "stream launches"},
         "roofline": roof,
         "step_roofline": step_roofline,

@@ -181,6 +181,31 @@ cb_status cb_fuse_scatter(const cb_geom *geom, void *k_fused, void *v_fused,
                           int64_t k_total, void *stream);
 
 /*
+ * cb_rerotate_fuse -- cb_rerotate (one layer, in place) followed by
+ * cb_fuse_scatter, in one pass after the selection: the rows of S take the
+ * recomputed K and V rows, and only the other rows' K is re-rotated.
+ * [Derivations, "形式化"]: a token outside S keeps its cached row and a token
+ * in S takes its recomputed row, so the rotation of [Derivations,
+ * "CacheBlend 中的应用"] is wasted on the rows of S.  For row t:
+ *   k[t] = t in S ? k_new_c[sel_local[s]] : R_{delta[t]} k[t]  (s: sel_global[s] = t)
+ *   v[t] = t in S ? v_new_c[sel_local[s]] : v[t]
+ * The result is bit for bit that of cb_rerotate then cb_fuse_scatter.
+ *   k, v           : [n_tok][n_kv_heads][head_dim], in/out
+ *   k_new_c, v_new_c : [M][n_kv_heads][head_dim]
+ *   delta          : [n_tok] p_new - p_old (not NULL when n_tok > 0)
+ *   sel_local, sel_global : [k_total]; sel_global strictly ascending over the
+ *                    whole packed batch (as cb_deviation_topk writes it), not
+ *                    checked on the host.
+ * Errors: those of cb_rerotate and cb_fuse_scatter; INVALID_ARG if
+ * k_total > n_tok.
+ */
+cb_status cb_rerotate_fuse(const cb_geom *geom, void *k, void *v, const void *k_new_c,
+                           const void *v_new_c, const int32_t *delta,
+                           const int32_t *sel_local, const int32_t *sel_global,
+                           int64_t k_total, int64_t n_tok, double rope_theta,
+                           int32_t rope_style, void *stream);
+
+/*
  * cb_partial_attn -- causal GQA attention of the selected rows only.
  * [Derivations, "形式化"]: Attention(Q, K_fused, V_fused); [KV-blog, "阶段二：
  * 注意力分数计算阶段"]: every query row is computed independently;
@@ -279,6 +304,24 @@ cb_status cb_partial_attn_with_plan(const cb_geom *geom, const cb_ragged *rg,
                                     void *workspace, size_t workspace_bytes,
                                     uint32_t flags, void *stream);
 
+/* Order of the steps in cb_blend_layer.
+ *   CB_ORDER_ROTATE_FIRST : re-rotate, score, select, fuse; the re-rotation
+ *       and a V deviation share one launch.
+ *   CB_ORDER_SELECT_FIRST : score (V only), select, then cb_rerotate_fuse:
+ *       the rows of S are written once and never re-rotated.
+ *   CB_ORDER_AUTO : select first for a V deviation when the layer's K cache
+ *       (n_tok rows) is at most CB_SELECT_FIRST_MAX_BYTES, or when the shared
+ *       launch does not cover the geometry; rotate first otherwise.  Where
+ *       the re-rotation is long it hides the deviation in the shared launch;
+ *       where it is short, saving the bytes of S and a smaller first launch
+ *       win.  Either order gives the same results bit for bit. */
+typedef enum {
+  CB_ORDER_AUTO = 0,
+  CB_ORDER_ROTATE_FIRST = 1,
+  CB_ORDER_SELECT_FIRST = 2
+} cb_order;
+#define CB_SELECT_FIRST_MAX_BYTES (16u << 20)
+
 /* Every argument of one layer of the blend. */
 typedef struct cb_layer_args {
   cb_geom geom;
@@ -300,16 +343,26 @@ typedef struct cb_layer_args {
   void *workspace;      /* optional attention workspace (see cb_partial_attn) */
   size_t workspace_bytes;
   int32_t dev_source;   /* cb_dev_source; CB_DEV_V is the score of [Derivations] */
+  int32_t order;        /* a cb_order value; 0 is CB_ORDER_AUTO */
 } cb_layer_args;
 
 /*
  * cb_blend_layer -- one layer: cb_rerotate (in place, when delta != NULL) ->
  * cb_kv_deviation_topk (keys scored after their re-rotation) ->
- * cb_fuse_scatter -> cb_partial_attn, all on `stream`.
+ * cb_fuse_scatter -> cb_partial_attn, all on `stream`.  With the order
+ * CB_ORDER_SELECT_FIRST (or CB_ORDER_AUTO choosing it): cb_kv_deviation_topk
+ * (V) -> cb_rerotate_fuse -> cb_partial_attn, with the same results bit for
+ * bit (INVALID_ARG for CB_ORDER_SELECT_FIRST with a key deviation source,
+ * which needs the keys re-rotated before it).
  * [KV-blog, "渐进式过滤机制"]: the caller runs it per layer, passing all
  * tokens as candidates at layer 1 and the surviving rows afterwards.
  */
 cb_status cb_blend_layer(const cb_layer_args *args, void *stream);
+
+/* The order cb_blend_layer follows for these arguments
+ * (CB_ORDER_ROTATE_FIRST or CB_ORDER_SELECT_FIRST), after the same checks of
+ * the order field; host only, enqueues nothing. */
+cb_status cb_blend_layer_order(const cb_layer_args *args, int32_t *order);
 
 /* Static description of a status code. */
 const char *cb_status_str(cb_status status);
@@ -318,7 +371,7 @@ const char *cb_last_error(void);
 /* ABI revision of this header (bumped on any incompatible change). */
 int32_t cb_abi_version(void);
 
-#define CB_ABI_VERSION 5
+#define CB_ABI_VERSION 6
 
 #ifdef __cplusplus
 }

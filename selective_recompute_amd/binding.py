@@ -22,6 +22,9 @@ CB_DTYPE_F32, CB_DTYPE_BF16 = 0, 1
 ROPE_HALF, ROPE_INTERLEAVED = 0, 1
 CB_DEV_V, CB_DEV_K, CB_DEV_KV = 0, 1, 2
 CB_ATTN_COUNTERS_ZERO = 1
+CB_ORDER_AUTO, CB_ORDER_ROTATE_FIRST, CB_ORDER_SELECT_FIRST = 0, 1, 2
+ORDERS = {"auto": CB_ORDER_AUTO, "rotate-first": CB_ORDER_ROTATE_FIRST,
+          "select-first": CB_ORDER_SELECT_FIRST}
 DEV_SOURCES = {"v": CB_DEV_V, "k": CB_DEV_K, "kv": CB_DEV_KV}
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -49,7 +52,7 @@ class LayerArgs(ctypes.Structure):
                 ("dev", ctypes.c_void_p), ("sel_local", ctypes.c_void_p),
                 ("sel_global", ctypes.c_void_p), ("out", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("dev_source", ctypes.c_int32)]
+                ("dev_source", ctypes.c_int32), ("order", ctypes.c_int32)]
 
 
 class AttnPlan(ctypes.Structure):
@@ -83,6 +86,10 @@ _SIGNATURES = {
     "cb_fuse_scatter": [ctypes.POINTER(Geom), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                         ctypes.c_void_p],
+    "cb_rerotate_fuse": [ctypes.POINTER(Geom), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                         ctypes.c_int64, ctypes.c_int64, ctypes.c_double, ctypes.c_int32,
+                         ctypes.c_void_p],
     "cb_partial_attn": [ctypes.POINTER(Geom), ctypes.POINTER(Ragged), ctypes.c_void_p,
                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                         ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t,
@@ -99,6 +106,7 @@ _SIGNATURES = {
                                   ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
                                   ctypes.c_size_t, ctypes.c_uint32, ctypes.c_void_p],
     "cb_blend_layer": [ctypes.POINTER(LayerArgs), ctypes.c_void_p],
+    "cb_blend_layer_order": [ctypes.POINTER(LayerArgs), ctypes.POINTER(ctypes.c_int32)],
 }
 
 
@@ -232,6 +240,14 @@ def fuse_scatter(g: Geom, k_fused, v_fused, k_new_c, v_new_c, sel_local, sel_glo
                                 _dev(sel_global, torch.int32), k_total, _stream(stream)))
 
 
+def rerotate_fuse(g: Geom, k, v, k_new_c, v_new_c, delta, sel_local, sel_global, k_total: int,
+                  n_tok: int, rope_theta: float, rope_style: int = ROPE_HALF, stream=None):
+    check(lib().cb_rerotate_fuse(ctypes.byref(g), _dev(k), _dev(v), _dev(k_new_c), _dev(v_new_c),
+                                 _dev(delta, torch.int32), _dev(sel_local, torch.int32),
+                                 _dev(sel_global, torch.int32), k_total, n_tok, rope_theta,
+                                 rope_style, _stream(stream)))
+
+
 def attn_workspace_bytes(g: Geom, rb: RaggedBatch) -> int:
     """Workspace with which cb_partial_attn may split long rows (0 = none)."""
     n = ctypes.c_size_t(0)
@@ -302,12 +318,12 @@ def partial_attn_with_plan(g: Geom, rb: RaggedBatch, plan: dict, out, q_c, sel_l
 def blend_layer(g: Geom, rb: RaggedBatch, *, k, v, k_new_c, v_new_c, q_c, delta, cand_idx,
                 rope_theta: float, rope_style: int, softmax_scale: float, dev, sel_local,
                 sel_global, out, workspace: Optional[torch.Tensor] = None,
-                dev_source: int = CB_DEV_V, stream=None):
+                dev_source: int = CB_DEV_V, order: int = CB_ORDER_AUTO, stream=None):
     args = LayerArgs(g, rb.struct(), _dev(k), _dev(v), _dev(k_new_c), _dev(v_new_c), _dev(q_c),
                      _dev(delta, torch.int32), _dev(cand_idx, torch.int32), rope_theta,
                      rope_style, softmax_scale, _dev(dev, torch.float32),
                      _dev(sel_local, torch.int32), _dev(sel_global, torch.int32), _dev(out),
-                     *_ws(workspace), dev_source)
+                     *_ws(workspace), dev_source, order)
     check(lib().cb_blend_layer(ctypes.byref(args), _stream(stream)))
 
 
@@ -317,15 +333,22 @@ class PreparedLayer:
 
     def __init__(self, g: Geom, rb: RaggedBatch, *, k, v, k_new_c, v_new_c, q_c, delta,
                  cand_idx, rope_theta, rope_style, softmax_scale, dev, sel_local, sel_global,
-                 out, workspace: Optional[torch.Tensor] = None, dev_source: int = CB_DEV_V):
+                 out, workspace: Optional[torch.Tensor] = None, dev_source: int = CB_DEV_V,
+                 order: int = CB_ORDER_AUTO):
         self._keep = (rb, k, v, k_new_c, v_new_c, q_c, delta, cand_idx, dev, sel_local,
                       sel_global, out, workspace)
         self.args = LayerArgs(g, rb.struct(), _dev(k), _dev(v), _dev(k_new_c), _dev(v_new_c),
                               _dev(q_c), _dev(delta, torch.int32), _dev(cand_idx, torch.int32),
                               rope_theta, rope_style, softmax_scale, _dev(dev, torch.float32),
                               _dev(sel_local, torch.int32), _dev(sel_global, torch.int32),
-                              _dev(out), *_ws(workspace), dev_source)
+                              _dev(out), *_ws(workspace), dev_source, order)
         self.ref = ctypes.byref(self.args)
+
+    def resolved_order(self) -> int:
+        """CB_ORDER_ROTATE_FIRST or CB_ORDER_SELECT_FIRST, as cb_blend_layer runs it."""
+        o = ctypes.c_int32(-1)
+        check(lib().cb_blend_layer_order(self.ref, ctypes.byref(o)))
+        return o.value
 
     def launch(self, stream_handle: int):
         st = lib().cb_blend_layer(self.ref, stream_handle)

@@ -547,6 +547,27 @@ CB_EXPORT cb_status cb_fuse_scatter(const cb_geom *geom, void *k_fused, void *v_
                     "fuse_scatter");
 }
 
+CB_EXPORT cb_status cb_rerotate_fuse(const cb_geom *geom, void *k, void *v, const void *k_new_c,
+                                     const void *v_new_c, const int32_t *delta,
+                                     const int32_t *sel_local, const int32_t *sel_global,
+                                     int64_t k_total, int64_t n_tok, double rope_theta,
+                                     int32_t rope_style, void *stream) {
+  g_last_error.clear();
+  CB_TRY(validate_rerotate(geom, k, k, delta, n_tok, 1, rope_theta, rope_style));
+  CB_TRY(validate_fuse(geom, k, v, k_new_c, v_new_c, sel_local, sel_global, k_total));
+  CB_TRY(need_ptr(v, "v", n_tok > 0));
+  if (k_total > n_tok)
+    return fail(CB_ERR_INVALID_ARG, "k_total %lld exceeds n_tok %lld", (long long)k_total,
+                (long long)n_tok);
+  if (n_tok == 0) return CB_OK;
+  return hip_status(cb::launch_rerotate_fuse(geom->dtype, rope_style, k, v, k_new_c, v_new_c,
+                                             delta, sel_local, sel_global, k_total, n_tok,
+                                             geom->n_kv_heads, geom->head_dim,
+                                             rope_table(geom->head_dim, rope_theta), nullptr, 0,
+                                             (hipStream_t)stream),
+                    "rerotate_fuse");
+}
+
 CB_EXPORT cb_status cb_partial_attn(const cb_geom *geom, const cb_ragged *rg, void *out,
                                     const void *q_c, const int32_t *sel_local,
                                     const int32_t *sel_global, const void *k_fused,
@@ -634,6 +655,45 @@ CB_EXPORT cb_status cb_partial_attn_describe_plan(const cb_geom *geom, const cb_
   return CB_OK;
 }
 
+namespace {
+// The order of cb_blend_layer's steps (see cb_order): select_first is set
+// when the V deviation and the top-k run before a rotate-or-replace launch.
+// Without a re-rotation both orders are the same three steps (reported as
+// rotate first).
+cb_status resolve_order(const cb_layer_args *a, int64_t n_tok, bool &select_first) {
+  if (a->order < CB_ORDER_AUTO || a->order > CB_ORDER_SELECT_FIRST)
+    return fail(CB_ERR_INVALID_ARG, "order %d is not a cb_order", a->order);
+  if (a->order == CB_ORDER_SELECT_FIRST && a->dev_source != CB_DEV_V)
+    return fail(CB_ERR_INVALID_ARG,
+                "CB_ORDER_SELECT_FIRST needs dev_source CB_DEV_V (a key deviation reads the "
+                "re-rotated keys)");
+  const bool rotate = a->delta && n_tok > 0;
+  if (!rotate || a->order == CB_ORDER_ROTATE_FIRST || a->dev_source != CB_DEV_V) {
+    select_first = false;
+  } else if (a->order == CB_ORDER_SELECT_FIRST) {
+    select_first = true;
+  } else {
+    const cb_geom *g = &a->geom;
+    const int64_t cache = n_tok * row_elems(g) * elem_size(g->dtype);
+    select_first = cache <= (int64_t)CB_SELECT_FIRST_MAX_BYTES ||
+                   !cb::rerotate_deviation_fits(g->dtype, g->n_kv_heads, g->head_dim);
+  }
+  return CB_OK;
+}
+}  // namespace
+
+CB_EXPORT cb_status cb_blend_layer_order(const cb_layer_args *a, int32_t *order) {
+  g_last_error.clear();
+  if (!a) return fail(CB_ERR_INVALID_ARG, "args is NULL");
+  if (!order) return fail(CB_ERR_INVALID_ARG, "order is NULL");
+  CB_TRY(check_geom(&a->geom));
+  CB_TRY(check_ragged(&a->rg, true, false, false));
+  bool after = false;
+  CB_TRY(resolve_order(a, a->rg.h_tok_off[a->rg.n_req], after));
+  *order = after ? CB_ORDER_SELECT_FIRST : CB_ORDER_ROTATE_FIRST;
+  return CB_OK;
+}
+
 CB_EXPORT cb_status cb_blend_layer(const cb_layer_args *a, void *stream) {
   g_last_error.clear();
   if (!a) return fail(CB_ERR_INVALID_ARG, "args is NULL");
@@ -652,10 +712,18 @@ CB_EXPORT cb_status cb_blend_layer(const cb_layer_args *a, void *stream) {
   CB_TRY(validate_attn(geom, rg, a->out, a->q_c, a->sel_local, a->sel_global, a->k, a->v,
                        a->softmax_scale));
   CB_TRY(need_ptr(a->workspace, "workspace", a->workspace_bytes > 0));
+  bool after = false;
+  CB_TRY(resolve_order(a, n_tok, after));
   const hipStream_t s = (hipStream_t)stream;
   const int32_t m = rg->h_cand_off[rg->n_req];
-  if (a->dev_source == CB_DEV_V && a->delta && n_tok > 0 &&
-      cb::rerotate_deviation_fits(geom->dtype, geom->n_kv_heads, geom->head_dim)) {
+  const bool rotate = a->delta && n_tok > 0;
+  if (after) {
+    // the V deviation and the top-k first; the re-rotation joins the fuse
+    CB_TRY(hip_status(launch_dev_source(geom, CB_DEV_V, a->k_new_c, a->k, a->v_new_c, a->v,
+                                        a->cand_idx, a->dev, m, s),
+                      "deviation"));
+  } else if (a->dev_source == CB_DEV_V && rotate &&
+             cb::rerotate_deviation_fits(geom->dtype, geom->n_kv_heads, geom->head_dim)) {
     // independent K and V work in one launch (a key deviation instead reads
     // the re-rotated keys, so it follows the re-rotation)
     CB_TRY(hip_status(cb::launch_rerotate_deviation(
@@ -664,7 +732,7 @@ CB_EXPORT cb_status cb_blend_layer(const cb_layer_args *a, void *stream) {
                           a->v, a->cand_idx, a->dev, m, s),
                       "rerotate+deviation"));
   } else {
-    if (a->delta && n_tok > 0)
+    if (rotate)
       CB_TRY(hip_status(cb::launch_rerotate(geom->dtype, a->rope_style, a->k, a->k, a->delta,
                                             n_tok, 1, geom->n_kv_heads, geom->head_dim,
                                             rope_table(geom->head_dim, a->rope_theta), s),
@@ -673,19 +741,31 @@ CB_EXPORT cb_status cb_blend_layer(const cb_layer_args *a, void *stream) {
                                         a->cand_idx, a->dev, m, s),
                       "deviation"));
   }
-  if (k_total == 0) return CB_OK;
-  CB_TRY(hip_status(cb::launch_topk(rg->n_req, a->dev, a->cand_idx, rg->cand_off, rg->sel_off,
-                                    a->sel_local, a->sel_global, rg->h_cand_off, rg->h_sel_off, s),
-                    "topk"));
-  // The fuse launch also clears the attention's arrival counters.
+  if (k_total > 0)
+    CB_TRY(hip_status(cb::launch_topk(rg->n_req, a->dev, a->cand_idx, rg->cand_off, rg->sel_off,
+                                      a->sel_local, a->sel_global, rg->h_cand_off,
+                                      rg->h_sel_off, s),
+                      "topk"));
+  // The fuse launch (or the rotate-or-replace launch) also clears the
+  // attention's arrival counters.
   const cb::AttnPlan plan = plan_attn(geom, rg, a->workspace ? a->workspace_bytes : 0);
-  const bool clear = plan.rows_per_tile > 0 && plan.split;
-  CB_TRY(hip_status(
-      cb::launch_fuse(a->k, a->v, a->k_new_c, a->v_new_c, a->sel_local, a->sel_global, k_total,
-                      (int32_t)(row_elems(geom) * elem_size(geom->dtype)),
-                      clear ? (uint32_t *)((char *)a->workspace + plan.cnt_offset) : nullptr,
-                      clear ? plan.n_cnt : 0, s),
-      "fuse_scatter"));
+  const bool clear = k_total > 0 && plan.rows_per_tile > 0 && plan.split;
+  uint32_t *const cnt = clear ? (uint32_t *)((char *)a->workspace + plan.cnt_offset) : nullptr;
+  const int64_t n_cnt = clear ? plan.n_cnt : 0;
+  if (after && rotate) {
+    CB_TRY(hip_status(cb::launch_rerotate_fuse(geom->dtype, a->rope_style, a->k, a->v, a->k_new_c,
+                                               a->v_new_c, a->delta, a->sel_local, a->sel_global,
+                                               k_total, n_tok, geom->n_kv_heads, geom->head_dim,
+                                               rope_table(geom->head_dim, a->rope_theta), cnt,
+                                               n_cnt, s),
+                      "rerotate_fuse"));
+  } else if (k_total > 0) {
+    CB_TRY(hip_status(
+        cb::launch_fuse(a->k, a->v, a->k_new_c, a->v_new_c, a->sel_local, a->sel_global, k_total,
+                        (int32_t)(row_elems(geom) * elem_size(geom->dtype)), cnt, n_cnt, s),
+        "fuse_scatter"));
+  }
+  if (k_total == 0) return CB_OK;
   return run_attn(geom, rg, plan, a->out, a->q_c, a->sel_local, a->sel_global, a->k, a->v,
                   a->softmax_scale, a->workspace, clear, s);
 }

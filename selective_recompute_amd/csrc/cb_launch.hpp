@@ -52,6 +52,16 @@ hipError_t launch_fuse(void *k_fused, void *v_fused, const void *k_new_c,
                        int32_t row_bytes, uint32_t *clear, int64_t n_clear,
                        hipStream_t stream);
 
+// Rotate-or-replace after the selection (rows of S take the new K/V rows,
+// every other row's K is re-rotated by delta); also zeroes clear[0 .. n_clear).
+// sel_global ascending.
+hipError_t launch_rerotate_fuse(int dtype, int style, void *k, void *v, const void *k_new_c,
+                                const void *v_new_c, const int32_t *delta,
+                                const int32_t *sel_local, const int32_t *sel_global,
+                                int64_t k_total, int64_t n_tok, int32_t n_kv_heads,
+                                int32_t head_dim, const RopeTable &tab, uint32_t *clear,
+                                int64_t n_clear, hipStream_t stream);
+
 // Partial attention.
 struct AttnArgs {
   void *out;

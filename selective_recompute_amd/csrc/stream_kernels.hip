@@ -29,6 +29,70 @@ struct RotGeom {
   int32_t n_layers, head_dim, units_per_head, units_per_row, tok_per_iter, tok_per_block;
 };
 
+// cos / sin of a unit's VP pair angles for position delta d: the angle in
+// turns, d * rev[i], reduced to [-1/2, 1/2] in double precision.
+template <int VP>
+__device__ inline void unit_trig(int d, const double *rev, float *cs, float *sn) {
+#pragma unroll
+  for (int i = 0; i < VP; ++i) {
+    const double turns = (double)d * rev[i];
+    const float frac = (float)(turns - rint(turns));  // in [-1/2, 1/2]
+    sn[i] = __builtin_amdgcn_sinf(frac);
+    cs[i] = __builtin_amdgcn_cosf(frac);
+  }
+}
+
+// One unit of one row (head base pointers src / dst): load its VP pairs,
+// turn them by the 2x2 block (when `turn`), store.  dst == src allowed.
+template <typename T, int STYLE>
+__device__ inline void rotate_unit(T *dst, const T *src, int j0, int hd, const float *cs,
+                                   const float *sn, bool turn) {
+  constexpr int VP = Vec16<T>::N;
+  float a[VP], b[VP];
+  if (STYLE == 0) {  // pairs (j, j + D/2)
+    Vec16<T>::load(src + j0, a);
+    Vec16<T>::load(src + hd / 2 + j0, b);
+  } else {           // pairs (2j, 2j + 1)
+    float x0[VP], x1[VP];
+    Vec16<T>::load(src + 2 * j0, x0);
+    Vec16<T>::load(src + 2 * j0 + VP, x1);
+#pragma unroll
+    for (int i = 0; i < VP / 2; ++i) {
+      a[i] = x0[2 * i]; b[i] = x0[2 * i + 1];
+      a[VP / 2 + i] = x1[2 * i]; b[VP / 2 + i] = x1[2 * i + 1];
+    }
+  }
+  if (turn) {
+#pragma unroll
+    for (int i = 0; i < VP; ++i) {
+      const float x = a[i], y = b[i];
+      a[i] = fmaf(x, cs[i], -y * sn[i]);
+      b[i] = fmaf(x, sn[i], y * cs[i]);
+    }
+  }
+  if (STYLE == 0) {
+    Vec16<T>::store(dst + j0, a);
+    Vec16<T>::store(dst + hd / 2 + j0, b);
+  } else {
+    float x0[VP], x1[VP];
+#pragma unroll
+    for (int i = 0; i < VP / 2; ++i) {
+      x0[2 * i] = a[i]; x0[2 * i + 1] = b[i];
+      x1[2 * i] = a[VP / 2 + i]; x1[2 * i + 1] = b[VP / 2 + i];
+    }
+    Vec16<T>::store(dst + 2 * j0, x0);
+    Vec16<T>::store(dst + 2 * j0 + VP, x1);
+  }
+}
+
+// Element offsets, inside a head, of a unit's two 16-byte pieces.
+template <typename T, int STYLE>
+__device__ inline void unit_pieces(int j0, int hd, int &p0, int &p1) {
+  constexpr int VP = Vec16<T>::N;
+  p0 = STYLE == 0 ? j0 : 2 * j0;
+  p1 = STYLE == 0 ? hd / 2 + j0 : 2 * j0 + VP;
+}
+
 template <typename T, int STYLE>
 __device__ inline void rerotate_block(T *__restrict__ k_out, const T *__restrict__ k_in,
                                       const int32_t *__restrict__ delta, const RotGeom &gm,
@@ -57,53 +121,11 @@ __device__ inline void rerotate_block(T *__restrict__ k_out, const T *__restrict
     if (d == 0 && in_place) continue;  // R_0 = I
     if (d != cur && d != 0) {
       cur = d;
-#pragma unroll
-      for (int i = 0; i < VP; ++i) {
-        const double turns = (double)d * rev[i];
-        const float frac = (float)(turns - rint(turns));  // in [-1/2, 1/2]
-        sn[i] = __builtin_amdgcn_sinf(frac);
-        cs[i] = __builtin_amdgcn_cosf(frac);
-      }
+      unit_trig<VP>(d, rev, cs, sn);
     }
     for (int l = 0; l < gm.n_layers; ++l) {
       const int64_t off = ((int64_t)l * gm.n_tok + t) * row_elems + (int64_t)head * hd;
-      const T *src = k_in + off;
-      T *dst = k_out + off;
-      float a[VP], b[VP];
-      if (STYLE == 0) {  // pairs (j, j + D/2)
-        Vec16<T>::load(src + j0, a);
-        Vec16<T>::load(src + hd / 2 + j0, b);
-      } else {           // pairs (2j, 2j + 1)
-        float x0[VP], x1[VP];
-        Vec16<T>::load(src + 2 * j0, x0);
-        Vec16<T>::load(src + 2 * j0 + VP, x1);
-#pragma unroll
-        for (int i = 0; i < VP / 2; ++i) {
-          a[i] = x0[2 * i]; b[i] = x0[2 * i + 1];
-          a[VP / 2 + i] = x1[2 * i]; b[VP / 2 + i] = x1[2 * i + 1];
-        }
-      }
-      if (d != 0) {
-#pragma unroll
-        for (int i = 0; i < VP; ++i) {
-          const float x = a[i], y = b[i];
-          a[i] = fmaf(x, cs[i], -y * sn[i]);
-          b[i] = fmaf(x, sn[i], y * cs[i]);
-        }
-      }
-      if (STYLE == 0) {
-        Vec16<T>::store(dst + j0, a);
-        Vec16<T>::store(dst + hd / 2 + j0, b);
-      } else {
-        float x0[VP], x1[VP];
-#pragma unroll
-        for (int i = 0; i < VP / 2; ++i) {
-          x0[2 * i] = a[i]; x0[2 * i + 1] = b[i];
-          x1[2 * i] = a[VP / 2 + i]; x1[2 * i + 1] = b[VP / 2 + i];
-        }
-        Vec16<T>::store(dst + 2 * j0, x0);
-        Vec16<T>::store(dst + 2 * j0 + VP, x1);
-      }
+      rotate_unit<T, STYLE>(k_out + off, k_in + off, j0, hd, cs, sn, d != 0);
     }
   }
 }
@@ -524,6 +546,143 @@ hipError_t launch_fuse(void *k_fused, void *v_fused, const void *k_new_c, const 
                      (uint4 *)v_fused, (const uint4 *)k_new_c, (const uint4 *)v_new_c, sel_local,
                      sel_global, k_total, row_vec, clear, n_clear);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Rotate-or-replace: the re-rotation and the fuse in one pass after the
+// selection.  [Derivations, "形式化"] keeps the cached row of every token
+// outside S and takes the recomputed row for every token in S, so a row of
+// S need not be re-rotated ([Derivations, "CacheBlend 中的应用"]) first:
+//   K[t] = t in S ? K_new_c[local(t)] : R_delta(t) K[t],
+//   V[t] = t in S ? V_new_c[local(t)] : V[t].
+// The re-rotation's token ranges and units are reused.  A workgroup finds the
+// entries of S in its range with one 64-ary search of the ascending
+// sel_global by its first wave (a ballot per level), maps them in LDS, and
+// each unit then copies its two 16-byte pieces of a new K and V row, or
+// turns its pairs of a kept K row by the same arithmetic as rerotate_kernel.
+// Like the fuse launch it also zeroes clear[0 .. n_clear).
+// ---------------------------------------------------------------------------
+constexpr int kFuseMapMax = 4096;  // tokens per workgroup (rot_geom keeps <= 16 * 256)
+
+// First index i in [0, n) with a[i] >= key (n if none), for an ascending a.
+// Every lane of the calling wave takes part and gets the result.
+__device__ inline int64_t wave_lower_bound(const int32_t *__restrict__ a, int64_t n, int64_t key,
+                                           int lane) {
+  int64_t lo = 0, hi = n;  // the answer lies in [lo, hi]
+  while (hi - lo > 64) {
+    const int64_t step = (hi - lo + 63) / 64;
+    const int64_t p = lo + lane * step;
+    const int c = __popcll(__ballot(p < hi && (int64_t)a[p] < key));  // probes below key
+    if (c == 0) return lo;
+    const int64_t top = lo + (int64_t)c * step;
+    lo += (int64_t)(c - 1) * step + 1;
+    hi = top < hi ? top : hi;
+  }
+  const int64_t p = lo + lane;
+  return lo + __popcll(__ballot(p < hi && (int64_t)a[p] < key));
+}
+
+template <typename T, int STYLE>
+__global__ __launch_bounds__(1024) void rerotate_fuse_kernel(
+    T *__restrict__ k, T *__restrict__ v, const T *__restrict__ k_new_c,
+    const T *__restrict__ v_new_c, const int32_t *__restrict__ delta,
+    const int32_t *__restrict__ sel_local, const int32_t *__restrict__ sel_global,
+    int64_t k_total, RotGeom gm, RopeTable tab, uint32_t *__restrict__ clear, int64_t n_clear) {
+  constexpr int VP = Vec16<T>::N;
+  __shared__ int32_t sel_of[kFuseMapMax];
+  __shared__ int64_t s_first;
+  const int tid = threadIdx.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + tid; i < n_clear;
+       i += (int64_t)gridDim.x * blockDim.x)
+    clear[i] = 0;
+  const int64_t t_begin = (int64_t)blockIdx.x * gm.tok_per_block;
+  const int64_t t_end = t_begin + gm.tok_per_block < gm.n_tok ? t_begin + gm.tok_per_block : gm.n_tok;
+  const int n_rows = (int)(t_end - t_begin);
+  for (int i = tid; i < n_rows; i += blockDim.x) sel_of[i] = -1;
+  if (tid < 64) {
+    const int64_t first = wave_lower_bound(sel_global, k_total, t_begin, tid);
+    if (tid == 0) s_first = first;
+  }
+  __syncthreads();
+  // at most n_rows entries of S fall in [t_begin, t_end), all from s_first on
+  for (int i = tid; i < n_rows; i += blockDim.x) {
+    const int64_t e = s_first + i;
+    if (e < k_total) {
+      const int64_t g = sel_global[e];
+      if (g >= t_begin && g < t_end) sel_of[g - t_begin] = (int32_t)e;
+    }
+  }
+  __syncthreads();
+  if (tid >= gm.units_per_row * gm.tok_per_iter) return;
+  const int unit = tid % gm.units_per_row;
+  const int slot = tid / gm.units_per_row;
+  const int head = unit / gm.units_per_head;
+  const int j0 = (unit % gm.units_per_head) * VP;
+  const int hd = gm.head_dim;
+  const int64_t row_elems = (int64_t)(gm.units_per_row / gm.units_per_head) * hd;
+  int p0, p1;
+  unit_pieces<T, STYLE>(j0, hd, p0, p1);
+
+  double rev[VP];
+#pragma unroll
+  for (int i = 0; i < VP; ++i) rev[i] = tab.rev_per_pos[j0 + i];
+  float cs[VP], sn[VP];
+  int cur = INT_MIN;
+  for (int64_t t = t_begin + slot; t < t_end; t += gm.tok_per_iter) {
+    const int64_t off = t * row_elems + (int64_t)head * hd;
+    const int32_t e = sel_of[t - t_begin];
+    if (e >= 0) {  // a row of S: the recomputed K and V, bit for bit
+      const int64_t src = (int64_t)sel_local[e] * row_elems + (int64_t)head * hd;
+      const uint4 k0 = *reinterpret_cast<const uint4 *>(k_new_c + src + p0);
+      const uint4 k1 = *reinterpret_cast<const uint4 *>(k_new_c + src + p1);
+      const uint4 v0 = *reinterpret_cast<const uint4 *>(v_new_c + src + p0);
+      const uint4 v1 = *reinterpret_cast<const uint4 *>(v_new_c + src + p1);
+      *reinterpret_cast<uint4 *>(k + off + p0) = k0;
+      *reinterpret_cast<uint4 *>(k + off + p1) = k1;
+      *reinterpret_cast<uint4 *>(v + off + p0) = v0;
+      *reinterpret_cast<uint4 *>(v + off + p1) = v1;
+      continue;
+    }
+    const int d = delta[t];
+    if (d == 0) continue;  // R_0 = I
+    if (d != cur) {
+      cur = d;
+      unit_trig<VP>(d, rev, cs, sn);
+    }
+    rotate_unit<T, STYLE>(k + off, k + off, j0, hd, cs, sn, true);
+  }
+}
+
+template <typename T, int STYLE>
+static hipError_t rerotate_fuse_typed(void *k, void *v, const void *k_new_c, const void *v_new_c,
+                                      const int32_t *delta, const int32_t *sel_local,
+                                      const int32_t *sel_global, int64_t k_total, int64_t n_tok,
+                                      int32_t n_kv_heads, int32_t head_dim, const RopeTable &tab,
+                                      uint32_t *clear, int64_t n_clear, hipStream_t stream) {
+  int64_t blocks;
+  const RotGeom gm = rot_geom<T>(n_tok, 1, n_kv_heads, head_dim, blocks);
+  if (blocks == 0) return hipSuccess;
+  const int threads = gm.units_per_row * gm.tok_per_iter;
+  // the LDS map covers a workgroup's tokens; its first wave searches S
+  if (gm.tok_per_block > kFuseMapMax || threads < 64 || threads > 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((rerotate_fuse_kernel<T, STYLE>), dim3((unsigned)blocks), dim3(threads), 0,
+                     stream, (T *)k, (T *)v, (const T *)k_new_c, (const T *)v_new_c, delta,
+                     sel_local, sel_global, k_total, gm, tab, clear, n_clear);
+  return hipGetLastError();
+}
+
+hipError_t launch_rerotate_fuse(int dtype, int style, void *k, void *v, const void *k_new_c,
+                                const void *v_new_c, const int32_t *delta,
+                                const int32_t *sel_local, const int32_t *sel_global,
+                                int64_t k_total, int64_t n_tok, int32_t n_kv_heads,
+                                int32_t head_dim, const RopeTable &tab, uint32_t *clear,
+                                int64_t n_clear, hipStream_t stream) {
+#define CB_RF(T, S)                                                                          \
+  rerotate_fuse_typed<T, S>(k, v, k_new_c, v_new_c, delta, sel_local, sel_global, k_total, \
+                            n_tok, n_kv_heads, head_dim, tab, clear, n_clear, stream)
+  if (dtype == kBF16) return style == 0 ? CB_RF(bf16, 0) : CB_RF(bf16, 1);
+  return style == 0 ? CB_RF(float, 0) : CB_RF(float, 1);
+#undef CB_RF
 }
 
 }  // namespace cb

@@ -63,9 +63,10 @@ class BlendRunner:
     def __init__(self, n_q_heads: int, n_kv_heads: int, head_dim: int, dtype: torch.dtype,
                  request_lengths: Sequence[int], r1_pct: int, r2_pct: int, n_layers: int,
                  rope_theta: float, rope_style: int = B.ROPE_HALF, schedule: str = "pool",
-                 dev_source: str = "v", device="cuda"):
+                 dev_source: str = "v", device="cuda", order: str = "auto"):
         self.geom = B.geom(n_q_heads, n_kv_heads, head_dim, dtype)
         self.dev_source = B.DEV_SOURCES[dev_source]
+        self.order = B.ORDERS[order]
         self.filter = GradualFilter(request_lengths, r1_pct, r2_pct, schedule)
         self.n_layers, self.theta, self.style = n_layers, rope_theta, rope_style
         self.scale = 1.0 / math.sqrt(head_dim)
@@ -103,7 +104,8 @@ class BlendRunner:
                       rope_theta=self.theta, rope_style=self.style,
                       softmax_scale=self.scale, dev=o["dev"], sel_local=o["sel_local"],
                       sel_global=o["sel_global"], out=o["out"], workspace=self.workspace,
-                      dev_source=self.dev_source, stream=stream)
+                      dev_source=self.dev_source, order=self.order,
+                      stream=stream)
         return o
 
     def run(self, layers_inputs: Sequence[dict], stream=None):

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
             "cb_blend_layer"} <= declared
     for name in sorted(declared):
         assert hasattr(lib, name), name
-    assert lib.cb_abi_version() == 5
+    assert lib.cb_abi_version() == 6
 
 
 def test_status_strings(lib):
@@ -161,12 +161,77 @@ def test_blend_layer_validates_every_stage_first(lib):
     for field, value, status in [("out", None, 1), ("softmax_scale", -1.0, 1),
                                  ("rope_style", 3, 1), ("cand_idx", None, 1),
                                  ("workspace_bytes", 1024, 1), ("dev_source", 7, 1),
+                                 ("order", 3, 1), ("order", -1, 1),
                                  ("geom", B.Geom(32, 8, 128, 9), 2)]:
         args = dict(good)
         args[field] = value
         st = lib.cb_blend_layer(ctypes.byref(B.LayerArgs(**args)), None)
         assert st == status, field
     assert lib.cb_last_error() != b""
+    # the select-first order scores V only: the keys are re-rotated after it
+    for src in (B.CB_DEV_K, B.CB_DEV_KV):
+        args = dict(good, order=B.CB_ORDER_SELECT_FIRST, dev_source=src)
+        assert lib.cb_blend_layer(ctypes.byref(B.LayerArgs(**args)), None) == 1
+        assert b"CB_ORDER_SELECT_FIRST" in lib.cb_last_error()
+
+
+def test_blend_layer_order_choice(lib):
+    """CB_ORDER_AUTO selects first for a V deviation while the layer's K cache
+    is at most CB_SELECT_FIRST_MAX_BYTES (16 MiB), or when the shared
+    re-rotation + deviation launch does not cover the geometry."""
+    def order(n_tok, g=None, **kw):
+        rg, keep = _ragged([0, n_tok], [0, n_tok], [0, 1])
+        args = dict(geom=g or _geom(), rg=rg, k=P, v=P2, k_new_c=P, v_new_c=P, q_c=P, delta=P,
+                    cand_idx=P, rope_theta=1e4, rope_style=0, softmax_scale=0.1, dev=P,
+                    sel_local=P, sel_global=P, out=P, workspace=None, workspace_bytes=0)
+        args.update(kw)
+        o = ctypes.c_int32(-1)
+        st = lib.cb_blend_layer_order(ctypes.byref(B.LayerArgs(**args)), ctypes.byref(o))
+        return st, o.value
+    first, rot = (0, B.CB_ORDER_SELECT_FIRST), (0, B.CB_ORDER_ROTATE_FIRST)
+    # 2 KiB rows (8 KV heads x 128, bf16): 8192 rows = 16 MiB
+    assert order(2048) == first and order(6144) == first and order(8192) == first
+    assert order(8193) == rot and order(32768) == rot
+    assert order(32768, order=B.CB_ORDER_SELECT_FIRST) == first
+    assert order(2048, order=B.CB_ORDER_ROTATE_FIRST) == rot
+    assert order(2048, dev_source=B.CB_DEV_K) == rot and order(2048, dev_source=B.CB_DEV_KV) == rot
+    assert order(2048, delta=None) == rot                       # nothing to re-rotate
+    assert order(100000, g=_geom(64, 64, 128)) == first         # rows too wide for the shared launch
+    assert order(2048, order=5)[0] == 1
+    assert order(2048, order=B.CB_ORDER_SELECT_FIRST, dev_source=B.CB_DEV_K)[0] == 1
+    assert lib.cb_blend_layer_order(None, None) == 1
+
+
+def _rf(lib, g, k=P, v=P2, kn=P, vn=P2, delta=P, sl=P, sg=P, k_total=4, n_tok=16, theta=1e4,
+        style=0):
+    return lib.cb_rerotate_fuse(ctypes.byref(g), k, v, kn, vn, delta, sl, sg, k_total, n_tok,
+                                theta, style, None)
+
+
+def test_rerotate_fuse_errors(lib):
+    """cb_rerotate_fuse checks what cb_rerotate and cb_fuse_scatter check, and
+    that S fits the tokens (fake pointers: nothing may launch)."""
+    g = _geom()
+    for case, status, needle in [
+        (dict(k_total=17), 1, "exceeds n_tok"),
+        (dict(k_total=-1), 1, "k_total"),
+        (dict(n_tok=-1), 1, "n_tok"),
+        (dict(v=None), 1, "NULL"),
+        (dict(kn=MISALIGNED), 1, "aligned"),
+        (dict(delta=None), 1, "delta"),
+        (dict(sg=None), 1, "sel_global"),
+        (dict(sl=P + 2), 1, "4-byte"),
+        (dict(theta=-1.0), 1, "rope_theta"),
+        (dict(style=2), 1, "rope_style"),
+    ]:
+        assert _rf(lib, g, **case) == status, case
+        assert needle in lib.cb_last_error().decode(), (case, lib.cb_last_error())
+    assert _rf(lib, _geom(d=80)) == 2
+    assert _rf(lib, B.Geom(32, 8, 128, 5)) == 2
+    # nothing to do: no pointer is touched
+    assert _rf(lib, g, k=None, v=None, kn=None, vn=None, delta=None, sl=None, sg=None,
+               k_total=0, n_tok=0) == 0
+    assert lib.cb_last_error() == b""
 
 
 def test_zero_sized_calls_are_noops(lib):

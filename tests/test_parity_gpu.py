@@ -646,3 +646,107 @@ def test_topk_register_and_memory_paths(m, k):
     loc, glob = O.topk_select(dev.astype(np.float64), cand, k)
     assert np.array_equal(npi(sg), glob)
     assert np.array_equal(npi(sl), loc)
+
+
+# ------------------------------------------- rotate-or-replace after select --
+# cb_rerotate_fuse, and cb_blend_layer selecting first: the rows of S
+# take the recomputed K/V rows, every other row's K is re-rotated.  Bit for bit
+# the result of cb_rerotate followed by cb_fuse_scatter, and against the
+# oracle: kept rows to the K tolerance, replaced rows bit-exact.
+def _selection(kind, t_count, rng):
+    if kind == "none":
+        return np.zeros(0, np.int64)
+    if kind == "all":
+        return np.arange(t_count)
+    if kind == "runs":  # long runs across workgroup ranges, the first and last rows
+        rows = np.concatenate([np.arange(0, 70), np.arange(t_count // 2 - 90, t_count // 2 + 90),
+                               np.arange(t_count - 33, t_count)])
+        return np.unique(rows)
+    return np.sort(rng.choice(t_count, max(1, (15 * t_count + 99) // 100), replace=False))
+
+
+@pytest.mark.parametrize("kind", ["random", "runs", "none", "all"])
+@pytest.mark.parametrize("dtype,style,hkv,d", [
+    (torch.bfloat16, B.ROPE_HALF, 8, 128), (torch.bfloat16, B.ROPE_INTERLEAVED, 8, 128),
+    (torch.bfloat16, B.ROPE_HALF, 2, 16), (torch.bfloat16, B.ROPE_HALF, 16, 128),
+    (torch.float32, B.ROPE_HALF, 2, 16), (torch.float32, B.ROPE_INTERLEAVED, 3, 64),
+    (torch.bfloat16, B.ROPE_INTERLEAVED, 1, 32),
+    (torch.float32, B.ROPE_HALF, 32, 128)])     # 512 threads per workgroup
+def test_rerotate_fuse_matches_rotate_then_fuse(dtype, style, hkv, d, kind):
+    say(f"rerotate_fuse {dtype} style={style} hkv={hkv} d={d} {kind}")
+    rng = np.random.default_rng(hkv * 100 + d + style + len(kind))
+    chunks, starts = [37, 1000, 1500, 3, 1556], [0, 37, 60000, 101, 2540]
+    delta = np.concatenate([np.full(n, s) for n, s in zip(chunks, starts)]).astype(np.int32)
+    t_count, m = len(delta), len(delta) + 50
+    glob = _selection(kind, t_count, rng).astype(np.int32)
+    k_total = len(glob)
+    loc = rng.choice(m, k_total, replace=False).astype(np.int32)  # any distinct compact rows
+    gen = torch.Generator().manual_seed(int(k_total) + d)
+    k0 = torch.randn(t_count, hkv, d, generator=gen).to(dtype)
+    v0 = torch.randn(t_count, hkv, d, generator=gen).to(dtype)
+    kn = torch.randn(m, hkv, d, generator=gen).to(dtype)
+    vn = torch.randn(m, hkv, d, generator=gen).to(dtype)
+    g = B.geom(hkv, hkv, d, dtype)
+    dl, sl, sg = (torch.from_numpy(a).to(DEV) for a in (delta, loc, glob))
+    kng, vng = kn.to(DEV), vn.to(DEV)
+    # two launches: rotate every row, then overwrite the rows of S
+    ka, va = k0.to(DEV), v0.to(DEV)
+    B.rerotate(g, ka, ka, dl, t_count, 1, 10000.0, style)
+    B.fuse_scatter(g, ka, va, kng, vng, sl, sg, k_total)
+    # one launch
+    kb, vb = k0.to(DEV), v0.to(DEV)
+    B.rerotate_fuse(g, kb, vb, kng, vng, dl, sl, sg, k_total, t_count, 10000.0, style)
+    torch.cuda.synchronize()
+    assert torch.equal(ka, kb) and torch.equal(va, vb)
+    # against the oracle: kept rows re-rotated, rows of S replaced bit for bit
+    kf, vf = np64(kb), np64(vb)
+    keep = np.ones(t_count, bool)
+    keep[glob] = False
+    ref = O.rerotate(np64(k0), delta, 10000.0, style)
+    assert_k_close(kf[keep], ref[keep], dtype, "kept K")
+    assert np.array_equal(kf[glob], np64(kn)[loc]) and np.array_equal(vf[glob], np64(vn)[loc])
+    assert np.array_equal(vf[keep], np64(v0)[keep])
+    # delta 0 rows that stay keep their bits
+    same = keep & (delta == 0)
+    assert np.array_equal(kf[same], np64(k0)[same])
+
+
+@pytest.mark.parametrize("name,layer,use_ws", [("tiny", 0, True), ("mistral7b-layer", 0, True),
+                                               ("mistral7b-layer", 0, False),
+                                               ("7b-32layer-6k", 0, True),
+                                               ("7b-32layer-6k", 1, True)])
+def test_blend_layer_orders_are_bit_identical(name, layer, use_ws):
+    """cb_blend_layer in both orders (and as CB_ORDER_AUTO chooses) on the same
+    inputs: fused K/V, deviations, selections and attention outputs equal bit
+    for bit (the split attention's counters cleared by the rotate-or-replace
+    launch instead of the fuse)."""
+    say(f"blend orders {name} layer {layer} workspace={use_ws}")
+    wl = W.make_workload(name)
+    sets = W.PlantedSets(wl)
+    counts = PL.GradualFilter(wl.request_lengths, wl.r1_pct, wl.r2_pct).counts(layer)
+    res = []
+    for order in (B.CB_ORDER_ROTATE_FIRST, B.CB_ORDER_SELECT_FIRST, B.CB_ORDER_AUTO):
+        x = {k: (v.to(DEV) if torch.is_tensor(v) else v)
+             for k, v in W.layer_inputs(wl, sets, layer).items()}
+        g = B.geom(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.torch_dtype)
+        rb = B.RaggedBatch(x["h_tok_off"], x["h_cand_off"], PL.offsets(counts), DEV)
+        ws = B.workspace_tensor(B.attn_workspace_bytes(g, rb), DEV) if use_ws else None
+        if ws is not None:
+            ws.fill_(0xFF)                       # garbage counters: the launch must clear them
+        dev = torch.empty(rb.n_cand, dtype=torch.float32, device=DEV)
+        sl = torch.empty(rb.n_sel, dtype=torch.int32, device=DEV)
+        sg = torch.empty(rb.n_sel, dtype=torch.int32, device=DEV)
+        out = torch.full((rb.n_sel, wl.n_q_heads, wl.head_dim), float("nan"),
+                         dtype=wl.torch_dtype, device=DEV)
+        B.blend_layer(g, rb, k=x["k_old"], v=x["v_old"], k_new_c=x["k_new_c"],
+                      v_new_c=x["v_new_c"], q_c=x["q_c"], delta=x["delta"],
+                      cand_idx=x["cand_idx"], rope_theta=wl.rope_theta, rope_style=B.ROPE_HALF,
+                      softmax_scale=1.0 / math.sqrt(wl.head_dim), dev=dev, sel_local=sl,
+                      sel_global=sg, out=out, workspace=ws, order=order)
+        torch.cuda.synchronize()
+        res.append([t.cpu() for t in (x["k_old"], x["v_old"], dev, sl, sg, out)])
+        assert np.array_equal(npi(sg), x["planted"])
+    for other in res[1:]:
+        for a, b in zip(res[0], other):
+            assert torch.equal(a, b)
+    assert torch.isfinite(res[1][5].float()).all()
