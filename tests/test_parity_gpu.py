@@ -714,7 +714,8 @@ def test_rerotate_fuse_matches_rotate_then_fuse(dtype, style, hkv, d, kind):
 @pytest.mark.parametrize("name,layer,use_ws", [("tiny", 0, True), ("mistral7b-layer", 0, True),
                                                ("mistral7b-layer", 0, False),
                                                ("7b-32layer-6k", 0, True),
-                                               ("7b-32layer-6k", 1, True)])
+                                               ("7b-32layer-6k", 1, True),
+                                               ("70b-80layer-8req", 1, True)])
 def test_blend_layer_orders_are_bit_identical(name, layer, use_ws):
     """cb_blend_layer in both orders (and as CB_ORDER_AUTO chooses) on the same
     inputs: fused K/V, deviations, selections and attention outputs equal bit
@@ -727,7 +728,7 @@ def test_blend_layer_orders_are_bit_identical(name, layer, use_ws):
     res = []
     for order in (B.CB_ORDER_ROTATE_FIRST, B.CB_ORDER_SELECT_FIRST, B.CB_ORDER_AUTO):
         x = {k: (v.to(DEV) if torch.is_tensor(v) else v)
-             for k, v in W.layer_inputs(wl, sets, layer).items()}
+             for k, v in W.layer_inputs(wl, sets, layer, device=_gen_device(wl)).items()}
         g = B.geom(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.torch_dtype)
         rb = B.RaggedBatch(x["h_tok_off"], x["h_cand_off"], PL.offsets(counts), DEV)
         ws = B.workspace_tensor(B.attn_workspace_bytes(g, rb), DEV) if use_ws else None
