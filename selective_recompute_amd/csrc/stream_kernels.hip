@@ -565,10 +565,22 @@ hipError_t launch_fuse(void *k_fused, void *v_fused, const void *k_new_c, const 
 constexpr int kFuseMapMax = 4096;  // tokens per workgroup (rot_geom keeps <= 16 * 256)
 
 // First index i in [0, n) with a[i] >= key (n if none), for an ascending a.
-// Every lane of the calling wave takes part and gets the result.
+// Every lane of the calling wave takes part and gets the result.  The first
+// probe reads the 64 entries around `guess`; when the answer lies inside
+// them (the usual case when the entries spread evenly and guess interpolates)
+// that single load settles it, otherwise it narrows [lo, hi] for the 64-ary
+// search.
 __device__ inline int64_t wave_lower_bound(const int32_t *__restrict__ a, int64_t n, int64_t key,
-                                           int lane) {
+                                           int64_t guess, int lane) {
   int64_t lo = 0, hi = n;  // the answer lies in [lo, hi]
+  if (n > 64) {
+    int64_t w0 = guess - 32;
+    w0 = w0 < 0 ? 0 : (w0 > n - 64 ? n - 64 : w0);
+    const int c = __popcll(__ballot((int64_t)a[w0 + lane] < key));  // a prefix of the window
+    if (c < 64 && (c > 0 || w0 == 0)) return w0 + c;
+    if (c == 64) lo = w0 + 64;
+    else hi = w0;
+  }
   while (hi - lo > 64) {
     const int64_t step = (hi - lo + 63) / 64;
     const int64_t p = lo + lane * step;
@@ -600,7 +612,8 @@ __global__ __launch_bounds__(1024) void rerotate_fuse_kernel(
   const int n_rows = (int)(t_end - t_begin);
   for (int i = tid; i < n_rows; i += blockDim.x) sel_of[i] = -1;
   if (tid < 64) {
-    const int64_t first = wave_lower_bound(sel_global, k_total, t_begin, tid);
+    const int64_t first =
+        wave_lower_bound(sel_global, k_total, t_begin, t_begin * k_total / gm.n_tok, tid);
     if (tid == 0) s_first = first;
   }
   __syncthreads();
