@@ -4,9 +4,16 @@
 A step is one pass of the whole hot path -- for every layer of the workload:
 re-rotate the cached keys, score and select the candidates, fuse the
 recomputed rows, and run the selected rows' causal GQA attention -- over one
-batch of seeded synthetic input already resident in HBM.  Every step gets its
-own copy of the inputs (the blend works in place), so nothing is restored
-inside the timed region and no step is served from the 256 MB Infinity Cache.
+batch of seeded synthetic input already resident in HBM.  The blend works in
+place on the cached K/V, so the run keeps one pristine and one working copy
+of every layer's K/V: before each step (untimed) the working copy is restored
+from the pristine one and the 256 MB Infinity Cache is flushed by writing
+512 MiB, so no step reads another step's results or starts from a warm MALL.
+Each step's L-layer loop is timed with its own pair of HIP events on the
+launch stream; ms_per_step is the median over the timed steps.
+
+Default workload: the batched 70B-layer blend (8 ragged requests, 67 100
+tokens, 80 layers, 64 Q / 8 KV heads), the largest single-GPU configuration.
 
 Metric: blended context tokens per second per layer = tokens * layers / time.
 
@@ -26,6 +33,8 @@ import ctypes
 import json
 import math
 import os
+import statistics
+import subprocess
 import sys
 import time
 
@@ -36,16 +45,19 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3       # fp32 vector
-DEFAULT_STEPS = {"tiny": (200, 20), "mistral7b-layer": (200, 20), "7b-32layer-6k": (20, 3),
-                 "7b-32layer-32k": (4, 1), "70b-80layer-8req": (2, 1)}
+DEFAULT_WORKLOAD = "70b-80layer-8req"
+DEFAULT_STEPS = {"tiny": (200, 20), "mistral7b-layer": (200, 20), "7b-32layer-6k": (20, 5),
+                 "7b-32layer-32k": (20, 5), "70b-80layer-8req": (20, 5)}
 STAGES = ("rerotate", "deviation_topk", "fuse_scatter", "partial_attn")
 # the order that scores and selects first, then rotates-or-replaces in one pass
 STAGES_AFTER = ("deviation_topk", "rerotate_fuse", "partial_attn")
 PROFILES = os.path.join(ROOT, "profiles")
+FLUSH_BYTES = 512 << 20        # twice the Infinity Cache
+CPU_WORKERS_MAX = 16           # host CPU share of one GPU
 
 
 def source_fingerprint():
-    """sha256 over the library's sources (its compiled files, their headers and
+    """sha256 over the library sources (its compiled files, their headers and
     the public header): a recorded byte count is only valid for the kernels it
     was measured on."""
     import hashlib
@@ -64,7 +76,6 @@ def source_fingerprint():
 def attainable_peaks():
     """Run the in-tree probe (built next to the library) in a child process
     before this process touches the GPU; None if it is not built."""
-    import subprocess
     from selective_recompute_amd import build as BLD
     if not os.path.exists(BLD.PEAKS):
         return None
@@ -92,12 +103,13 @@ def recorded_traffic(stage, workload):
     return float(rec["hbm_bytes_per_launch"])
 
 
-def parse_args():
+def parse_args(argv=None):
+    from selective_recompute_amd import workloads as W
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="mistral7b-layer", choices=list(DEFAULT_STEPS))
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(W.WORKLOADS))
     ap.add_argument("--schedule", default="pool", choices=["pool", "chain"])
     ap.add_argument("--dev-source", default="v", choices=["v", "k", "kv"],
                     help="what the token deviation measures: V (default), K at the new "
@@ -106,14 +118,17 @@ def parse_args():
                     help="step order of cb_blend_layer: select-first scores V and selects "
                          "first, then one launch writes the rows of S and re-rotates only the "
                          "others; auto lets the library choose")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="budget of the CPU oracle baseline (0 disables it)")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="rough budget of the CPU oracle baseline (0 disables it)")
     ap.add_argument("--attainable", type=int, default=1,
                     help="1: measure attainable MFMA / HBM peaks first and report "
                          "fractions against them too")
     ap.add_argument("--graph", type=int, default=0,
-                    help="1: capture the timed steps' launches in one HIP graph and "
-                         "time its replay (same kernels, no host launch cost)")
+                    help="1: capture one step's launches in a HIP graph and time its "
+                         "replay (same kernels, no host launch cost)")
+    ap.add_argument("--attribution", type=int, default=1,
+                    help="1: also time every entry point on its own (per-kernel figures "
+                         "and the roofline entry)")
     ap.add_argument("--prefill", action="store_true",
                     help="instead of the blend step: dense causal attention of every "
                          "row (layer-1 full prefill) at the workload's shape")
@@ -122,7 +137,9 @@ def parse_args():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the run, copy this many MiB device to device once (a "
                          "plain copy of known size that calibrates byte counters)")
-    return ap.parse_args()
+    ap.add_argument("--cpu-baseline-only", action="store_true",
+                    help=argparse.SUPPRESS)  # the child process that times the oracle
+    return ap.parse_args(argv)
 
 
 def log(msg):
@@ -160,60 +177,126 @@ def algorithmic_work(wl, runner, selected_per_layer, dev_tensors=1):
     return work
 
 
-def cpu_baseline(wl, seconds, dev_source="v"):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload."""
+# --------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on a bounded sample of the workload.
+# It runs in a child process started before this process touches the GPU.
+# --------------------------------------------------------------------------
+_POOL_ARGS = None
+
+
+def _pool_init(args):
+    global _POOL_ARGS
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)          # one thread per process: the pool is the parallelism
+    _POOL_ARGS = args
+
+
+def _pool_rows(rows):
+    from oracle import cacheblend_oracle as O
+    a = _POOL_ARGS
+    O.attention_rows(a["q_c"], a["sel_local"][rows], a["sel_global"][rows], a["row_start"][rows],
+                     a["k_fused"], a["v_fused"], a["n_q_heads"], a["n_kv_heads"], a["scale"])
+    return len(rows)
+
+
+def _oracle_layer_time(wl, sets, layer, frac, workers, dev_source):
+    """Seconds the oracle takes for one layer: every step but the attention in
+    full (plain numpy, one thread), the attention on every frac-th selected
+    row over a pool of `workers` processes, its wall time scaled by frac."""
+    import multiprocessing as mp
+
     import numpy as np
     import torch
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_limits
 
     from oracle import cacheblend_oracle as O
     from selective_recompute_amd import workloads as W
 
-    sets = W.PlantedSets(wl)
-    x = W.layer_inputs(wl, sets, 0, device="cpu")
+    x = W.layer_inputs(wl, sets, layer, device="cpu")
     f64 = lambda t: t.to(torch.float64).numpy()
+    pct = wl.r1_pct if layer == 0 else wl.r2_pct
     args = dict(k_old=f64(x["k_old"]), v_old=f64(x["v_old"]), delta=wl.delta(),
                 k_new_c=f64(x["k_new_c"]), v_new_c=f64(x["v_new_c"]), q_c=f64(x["q_c"]),
                 cand_idx=x["cand_idx"].numpy(), tok_off=wl.tok_off, cand_off=x["h_cand_off"],
-                sel_counts=[(wl.r1_pct * n + 99) // 100 for n in wl.request_lengths],
+                sel_counts=[(pct * n + 99) // 100 for n in wl.request_lengths],
                 n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads, theta=wl.rope_theta,
                 scale=1.0 / math.sqrt(wl.head_dim))
-    # Large layers: time re-rotation/deviation/top-k/fuse in full and the
-    # attention on an evenly spaced 1/frac of the selected rows, then scale.
-    frac = 1 if wl.n_tokens <= 8192 else 16
-    reps, t_total = 0, 0.0
-    t_start = time.perf_counter()
-    while True:
+    del x
+    with threadpool_limits(1):
+        # repeated while short (about 1 s), so one cold pass does not decide it
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            res = O.blend_layer(**args, attend=False, dev_source=dev_source)
+            reps += 1
+            if time.perf_counter() - t0 >= 1.0:
+                break
+        t_steps = (time.perf_counter() - t0) / reps
+    n_sel = len(res["sel_global"])
+    rows = np.arange(0, n_sel, frac)
+    blocks = [b for b in np.array_split(rows, max(1, min(len(rows), workers * 8))) if len(b)]
+    pool_args = dict(q_c=args["q_c"], sel_local=res["sel_local"], sel_global=res["sel_global"],
+                     row_start=res["row_start"], k_fused=res["k_fused"], v_fused=res["v_fused"],
+                     n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads, scale=args["scale"])
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers, initializer=_pool_init, initargs=(pool_args,)) as pool:
         t0 = time.perf_counter()
-        res = O.blend_layer(**args, attend=(frac == 1), dev_source=dev_source)
-        t1 = time.perf_counter()
-        t_layer = t1 - t0
-        if frac > 1:
-            rows = np.arange(0, len(res["sel_global"]), frac)
-            O.attention_rows(args["q_c"], res["sel_local"][rows], res["sel_global"][rows],
-                             res["row_start"][rows], res["k_fused"], res["v_fused"],
-                             wl.n_q_heads, wl.n_kv_heads, args["scale"])
-            t_layer += (time.perf_counter() - t1) * frac
-        t_total += t_layer
-        reps += 1
-        if time.perf_counter() - t_start >= seconds:
-            break
-    blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
-    cores = max(blas) if blas else 1
-    sample = (f"layer 1 of {wl.name} ({wl.n_tokens} tokens, {sum(args['sel_counts'])} selected), "
-              f"{reps} repetition(s) of the full oracle pipeline in float64 numpy")
-    if frac > 1:
-        sample += f"; attention timed on every {frac}th selected row and scaled by {frac}"
-    sample += "; element-wise numpy runs on one thread, matrix-vector products on the BLAS pool"
-    return {"value": wl.n_tokens * reps / t_total, "unit": "tokens/s/layer", "cores": cores,
-            "kind": "oracle", "sample": sample}
+        done = sum(pool.map(_pool_rows, blocks, chunksize=1))
+        t_attn = time.perf_counter() - t0
+    assert done == len(rows)
+    return t_steps + t_attn * frac, t_steps, t_attn, n_sel, len(rows)
+
+
+def cpu_baseline(wl, seconds, dev_source="v"):
+    """Oracle tokens/s per layer on this host: layer 1 (every token a
+    candidate) and, for multi-layer workloads, layer 2 (the later layers'
+    shape), extrapolated to the whole stack."""
+    workers = max(1, min(CPU_WORKERS_MAX, len(os.sched_getaffinity(0))))
+    from selective_recompute_amd import workloads as W
+    sets = W.PlantedSets(wl)
+    # attention sample: aim at about `seconds` of attention work on the pool
+    # (about 4 s per 64 heads of the 32k-token rows and 1k sampled rows)
+    k1 = sum((wl.r1_pct * n + 99) // 100 for n in wl.request_lengths)
+    avg_keys = sum(n * n / 2 for n in wl.request_lengths) / max(1, wl.n_tokens)
+    est_per_row = 2.0e-9 * wl.n_q_heads * avg_keys * wl.head_dim + 2e-5 * wl.n_q_heads
+    frac = max(1, int(math.ceil(k1 * est_per_row / workers / max(seconds, 1.0) * 2)))
+    layers = [0] if wl.n_layers == 1 else [0, 1]
+    times, parts = [], []
+    for layer in layers:
+        t, t_steps, t_attn, n_sel, n_rows = _oracle_layer_time(wl, sets, layer, frac, workers,
+                                                               dev_source)
+        times.append(t)
+        parts.append(f"layer {layer + 1}: {n_sel} selected rows, re-rotation/deviation/"
+                     f"top-k/fuse {t_steps:.2f} s on one thread, attention of {n_rows} rows "
+                     f"(every {frac}th) {t_attn:.2f} s on {workers} processes")
+    total = times[0] + (wl.n_layers - 1) * (times[1] if len(times) > 1 else times[0])
+    sample = (f"{wl.name}, the unchanged float64 numpy oracle; " + "; ".join(parts)
+              + (f"; attention wall time scaled by {frac}" if frac > 1 else ""))
+    if wl.n_layers > 1:
+        sample += (f"; stack time = layer 1 + {wl.n_layers - 1} x layer 2 (later layers share "
+                   "layer 2's candidate and selection counts)")
+    return {"value": wl.n_tokens * wl.n_layers / total, "unit": "tokens/s/layer",
+            "cores": workers, "kind": "oracle", "sample": sample}
+
+
+def run_cpu_baseline_child(a):
+    """The CPU baseline in a child process (started before this process
+    initialises the GPU); None if it fails."""
+    cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-only", "--workload",
+           a.workload, "--cpu-seconds", str(a.cpu_seconds), "--dev-source", a.dev_source]
+    log("[bench] timing the CPU oracle")
+    res = subprocess.run(cmd, capture_output=True, text=True, timeout=900)
+    if res.returncode != 0:
+        log(f"[bench] CPU baseline failed: {res.stderr.strip()[-2000:]}")
+        return None
+    out = json.loads(res.stdout.strip().splitlines()[-1])
+    log(f"[bench] CPU oracle: {out['value']:.4g} tokens/s/layer on {out['cores']} processes")
+    return out
 
 
 def prefill_main(a, peaks):
     """Layer-1 full prefill: every row of every request attends causally over
     its request, through the same cb_partial_attn entry point (all rows
     selected).  Prints one JSON line in TFLOP/s."""
-    import numpy as np
     import torch
 
     from selective_recompute_amd import binding as B
@@ -269,18 +352,60 @@ def prefill_main(a, peaks):
         "roofline": roof, "attainable": peaks}), flush=True)
 
 
+class Inputs:
+    """Every layer's inputs on the device, generated once.  K and V of all
+    layers live in one working and one pristine tensor each: restore() copies
+    the pristine caches over the working ones and then writes FLUSH_BYTES so
+    that nothing of the previous step stays in the Infinity Cache."""
+
+    def __init__(self, wl, sets):
+        import torch
+
+        from selective_recompute_amd import workloads as W
+        L, T = wl.n_layers, wl.n_tokens
+        shape = (L, T, wl.n_kv_heads, wl.head_dim)
+        dt = wl.torch_dtype
+        self.k_work = torch.empty(shape, dtype=dt, device="cuda")
+        self.v_work = torch.empty(shape, dtype=dt, device="cuda")
+        self.k_pristine = torch.empty(shape, dtype=dt, device="cuda")
+        self.v_pristine = torch.empty(shape, dtype=dt, device="cuda")
+        self.layers = []
+        for layer in range(L):
+            x = W.layer_inputs(wl, sets, layer, device="cuda")
+            self.k_pristine[layer].copy_(x.pop("k_old"))
+            self.v_pristine[layer].copy_(x.pop("v_old"))
+            x["k_old"], x["v_old"] = self.k_work[layer], self.v_work[layer]
+            self.layers.append(x)
+        self.flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        self._n = 0
+
+    def restore(self):
+        self.k_work.copy_(self.k_pristine)
+        self.v_work.copy_(self.v_pristine)
+        self._n += 1
+        self.flush.fill_(self._n & 0xFF)
+
+
 def main():
     a = parse_args()
     if a.print_source_sha:
         print(source_fingerprint())
         return
     if a.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {a.gpus} is not supported (the library "
-              "has no multi-GPU path).", file=sys.stderr)
+        print(f"bench.py measures one GPU: --gpus {a.gpus} is not supported (this build runs "
+              "on one GPU only and has no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
+    if a.cpu_baseline_only:
+        from selective_recompute_amd import workloads as W
+        print(json.dumps(cpu_baseline(W.make_workload(a.workload), a.cpu_seconds, a.dev_source)),
+              flush=True)
+        return
+    # child processes first: nothing below them has touched the GPU yet
     peaks = attainable_peaks() if a.attainable else None
     if a.prefill:
         return prefill_main(a, peaks)
+    cpu = run_cpu_baseline_child(a) if a.cpu_seconds > 0 else None
+
     import numpy as np
     import torch
 
@@ -295,6 +420,8 @@ def main():
     steps, warmup = DEFAULT_STEPS[wl.name]
     steps = a.steps if a.steps is not None else steps
     warmup = a.warmup if a.warmup is not None else warmup
+    if steps < 1:
+        raise SystemExit("--steps must be >= 1")
     L = wl.n_layers
     sets = W.PlantedSets(wl, a.schedule)
     runner = PL.BlendRunner(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.torch_dtype,
@@ -307,67 +434,62 @@ def main():
     stream = torch.cuda.Stream()
     h = stream.cuda_stream
 
-    def make_copies(n, first_draw):
-        cps = []
-        for c in range(n):
-            cps.append([W.layer_inputs(wl, sets, l, device="cuda", draw=first_draw + c)
-                        for l in range(L)])
-        torch.cuda.synchronize()
-        return cps
-
-    # ---- timed pass: whole layers through cb_blend_layer --------------------
-    log(f"[bench] {wl.name}: generating {steps + warmup} input copies")
-    copies = make_copies(steps + warmup, 0)
+    log(f"[bench] {wl.name}: generating the inputs of {L} layer(s)")
+    inp = Inputs(wl, sets)
+    torch.cuda.synchronize()
     prepared = []
-    for cp in copies:
-        row = []
-        for l, x in enumerate(cp):
-            o = runner.outs[l]
-            row.append(B.PreparedLayer(runner.geom, runner.batches[l], k=x["k_old"], v=x["v_old"],
-                                       k_new_c=x["k_new_c"], v_new_c=x["v_new_c"], q_c=x["q_c"],
-                                       delta=x["delta"], cand_idx=runner.candidates(l),
-                                       rope_theta=wl.rope_theta, rope_style=B.ROPE_HALF,
-                                       softmax_scale=runner.scale, dev=o["dev"],
-                                       sel_local=o["sel_local"], sel_global=o["sel_global"],
-                                       out=o["out"], workspace=runner.workspace,
-                                       dev_source=runner.dev_source,
-                                       order=runner.order))
-        prepared.append(row)
+    for l, x in enumerate(inp.layers):
+        o = runner.outs[l]
+        prepared.append(B.PreparedLayer(runner.geom, runner.batches[l], k=x["k_old"],
+                                        v=x["v_old"], k_new_c=x["k_new_c"], v_new_c=x["v_new_c"],
+                                        q_c=x["q_c"], delta=x["delta"],
+                                        cand_idx=runner.candidates(l), rope_theta=wl.rope_theta,
+                                        rope_style=B.ROPE_HALF, softmax_scale=runner.scale,
+                                        dev=o["dev"], sel_local=o["sel_local"],
+                                        sel_global=o["sel_global"], out=o["out"],
+                                        workspace=runner.workspace, dev_source=runner.dev_source,
+                                        order=runner.order))
     # the attribution pass times the entry points of the order the library runs
     # (the same for every layer: it depends on the cache size and the source)
-    select_first = prepared[0][0].resolved_order() == B.CB_ORDER_SELECT_FIRST
+    select_first = prepared[0].resolved_order() == B.CB_ORDER_SELECT_FIRST
     stages = STAGES_AFTER if select_first else STAGES
+
+    def launch_step():
+        for p in prepared:
+            p.launch(h)
+
+    # ---- timed pass: whole layers through cb_blend_layer --------------------
     graph = None
+    step_events = []
     with torch.cuda.stream(stream):
-        for c in range(warmup):
-            for p in prepared[c]:
-                p.launch(h)
+        for _ in range(warmup):
+            inp.restore()
+            launch_step()
         torch.cuda.synchronize()
         if a.graph:
-            # capture records the launches without running them: the timed
-            # copies are still pristine when the graph is replayed
+            # capture records the launches without running them
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph, stream=stream):
-                for c in range(warmup, warmup + steps):
-                    for p in prepared[c]:
-                        p.launch(h)
+                launch_step()
             torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
-        ev0.record(stream)
-        if graph is not None:
-            graph.replay()
-        else:
-            for c in range(warmup, warmup + steps):
-                for p in prepared[c]:
-                    p.launch(h)
-        ev1.record(stream)
+        for _ in range(steps):
+            inp.restore()                                   # untimed: outside the events
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            if graph is not None:
+                graph.replay()
+            else:
+                launch_step()
+            e1.record(stream)
+            step_events.append((e0, e1))
         torch.cuda.synchronize()
         t1 = time.perf_counter()
     del graph
-    ms_per_step = ev0.elapsed_time(ev1) / steps
-    wall_ms_per_step = (t1 - t0) * 1e3 / steps
-    log(f"[bench] timed {steps} steps: {ms_per_step:.4f} ms/step (wall {wall_ms_per_step:.4f})")
+    step_ms = [e0.elapsed_time(e1) for e0, e1 in step_events]
+    ms_per_step = statistics.median(step_ms)
+    log(f"[bench] timed {steps} steps: median {ms_per_step:.4f} ms/step (min {min(step_ms):.4f}, "
+        f"max {max(step_ms):.4f}); timed region with restores {t1 - t0:.2f} s")
     # The inputs plant the deviation tiers in V: a V score must select the
     # planted rows.  K-based scores select other rows; the attention work is
     # then counted on the last step's selection.
@@ -376,147 +498,12 @@ def main():
         for l in range(L):
             if not np.array_equal(selected[l], sets.layer(l).planted):
                 raise RuntimeError(f"layer {l}: selection differs from the planted set")
-    del prepared, copies
-    torch.cuda.empty_cache()
-
-    # ---- attribution pass: each entry point timed over all its launches -----
-    lib = B.lib()
-    copies = make_copies(steps, 10_000)
-    gref = ctypes.byref(runner.geom)
-    rgs = [rb.struct() for rb in runner.batches]
-    stage_calls = {s: [[] for _ in range(L)] for s in STAGES + STAGES_AFTER}
-    topk_calls = [[] for _ in range(L)]   # the selection half alone, for its own time
-    keep = []
-    # The attention is timed as the launch cb_blend_layer makes: the plan
-    # cb_partial_attn chooses, pinned, on a workspace zero-filled once per
-    # distinct plan (every call leaves its counters at zero), so no call
-    # needs the launch that clears them.
-    ws_bytes = 0 if runner.workspace is None else runner.workspace.numel()
-    attn_plans, plan_ws = [], {}
-    for l in range(L):
-        pd = B.attn_plan(runner.geom, runner.batches[l], ws_bytes)
-        key = (pd["mfma"], pd["key_split"], pd["key_chunk"])
-        if key not in plan_ws:
-            plan_ws[key] = B.workspace_tensor(pd["workspace_bytes"], "cuda")
-            if plan_ws[key] is not None:
-                plan_ws[key].zero_()
-        attn_plans.append((B.AttnPlan(key[0], key[1], 0, key[2], 0, 0, 0),
-                           *B._ws(plan_ws[key])))
-    for cp in copies:
-        sels = []
-        for l, x in enumerate(cp):
-            rb = runner.batches[l]
-            dev_t = torch.empty(rb.n_cand, dtype=torch.float32, device="cuda")
-            sl = torch.empty(rb.n_sel, dtype=torch.int32, device="cuda")
-            sg = torch.empty(rb.n_sel, dtype=torch.int32, device="cuda")
-            sels.append(sg)
-            src = runner.filter.cand_source(l)
-            cand = runner.all_tokens if src is None else sels[src]
-            keep += [dev_t, sl, sg]
-            k_ptr, v_ptr = x["k_old"].data_ptr(), x["v_old"].data_ptr()
-            stage_calls["rerotate"][l].append(
-                (lib.cb_rerotate, (gref, k_ptr, k_ptr, x["delta"].data_ptr(), wl.n_tokens, 1,
-                                   wl.rope_theta, B.ROPE_HALF, h)))
-            stage_calls["deviation_topk"][l].append(
-                (lib.cb_kv_deviation_topk, (gref, ctypes.byref(rgs[l]), runner.dev_source,
-                                            x["k_new_c"].data_ptr(), k_ptr,
-                                            x["v_new_c"].data_ptr(), v_ptr, cand.data_ptr(),
-                                            dev_t.data_ptr(), sl.data_ptr(), sg.data_ptr(), h)))
-            topk_calls[l].append(
-                (lib.cb_topk, (ctypes.byref(rgs[l]), dev_t.data_ptr(), cand.data_ptr(),
-                               sl.data_ptr(), sg.data_ptr(), h)))
-            stage_calls["fuse_scatter"][l].append(
-                (lib.cb_fuse_scatter, (gref, k_ptr, v_ptr, x["k_new_c"].data_ptr(),
-                                       x["v_new_c"].data_ptr(), sl.data_ptr(), sg.data_ptr(),
-                                       rb.n_sel, h)))
-            stage_calls["rerotate_fuse"][l].append(
-                (lib.cb_rerotate_fuse, (gref, k_ptr, v_ptr, x["k_new_c"].data_ptr(),
-                                        x["v_new_c"].data_ptr(), x["delta"].data_ptr(),
-                                        sl.data_ptr(), sg.data_ptr(), rb.n_sel, wl.n_tokens,
-                                        wl.rope_theta, B.ROPE_HALF, h)))
-            plan, pws_ptr, pws_bytes = attn_plans[l]
-            stage_calls["partial_attn"][l].append(
-                (lib.cb_partial_attn_with_plan,
-                 (gref, ctypes.byref(rgs[l]), ctypes.byref(plan),
-                  runner.outs[l]["out"].data_ptr(), x["q_c"].data_ptr(), sl.data_ptr(),
-                  sg.data_ptr(), k_ptr, v_ptr, runner.scale, pws_ptr, pws_bytes,
-                  B.CB_ATTN_COUNTERS_ZERO, h)))
-    events = {}
-    with torch.cuda.stream(stream):
-        torch.cuda.synchronize()
-        for l in range(L):
-            for s in stages:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                for fn, args in stage_calls[s][l]:
-                    st = fn(*args)
-                    if st != 0:
-                        B.check(st)
-                e1.record(stream)
-                events[(l, s)] = (e0, e1)
-            # the top-k again on the scores just computed (same outputs)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for fn, args in topk_calls[l]:
-                st = fn(*args)
-                if st != 0:
-                    B.check(st)
-            e1.record(stream)
-            events[(l, "topk")] = (e0, e1)
-        torch.cuda.synchronize()
-    stage_ms = {s: sum(events[(l, s)][0].elapsed_time(events[(l, s)][1]) for l in range(L))
-                for s in stages}
-    launches = steps * L
     work = algorithmic_work(wl, runner, selected, 2 if a.dev_source == "kv" else 1)
-    # every layer of every step was launched once
-    stage_work = {s: steps * sum(w[s] for w in work) for s in stages}
-    kernels = {}
-    for s in stages:
-        avg_us = stage_ms[s] * 1e3 / launches
-        if s == "partial_attn":
-            rate = stage_work[s] / (stage_ms[s] * 1e-3) / 1e12
-            kernels[s] = {"avg_us": round(avg_us, 3), "tflops": round(rate, 3),
-                          "gflop_per_launch": round(stage_work[s] / launches / 1e9, 4)}
-        else:
-            rate = stage_work[s] / (stage_ms[s] * 1e-3) / 1e9
-            kernels[s] = {"avg_us": round(avg_us, 3), "gbs": round(rate, 1),
-                          "mb_per_launch": round(stage_work[s] / launches / 1e6, 4)}
-    # each class against its published peak and, when measured, the attainable one
-    # (MFMA probe for the attention, streaming-read probe for the HBM stages)
-    flop_peak_t = BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
-    for s in stages:
-        kk = kernels[s]
-        if "tflops" in kk:
-            kk["frac"] = round(kk["tflops"] / flop_peak_t, 5)
-            if peaks and wl.dtype == "bf16":
-                kk["frac_attainable"] = round(kk["tflops"] / peaks["mfma_bf16_32x32x16_tflops"], 5)
-        else:
-            kk["frac"] = round(kk["gbs"] / HBM_PEAK_GBS, 5)
-            if peaks:
-                kk["frac_attainable"] = round(kk["gbs"] / peaks["read_gbs"], 5)
-    topk_ms = sum(events[(l, "topk")][0].elapsed_time(events[(l, "topk")][1]) for l in range(L))
-    kernels["topk"] = {"avg_us": round(topk_ms * 1e3 / launches, 3), "bound": "latency"}
-    dominant = max(stages, key=lambda s: stage_ms[s])
-    if dominant == "partial_attn":
-        bf16 = wl.dtype == "bf16"
-        peak = BF16_PEAK_TFLOPS if bf16 else FP32_PEAK_TFLOPS
-        achieved = kernels[dominant]["tflops"]
-        roof = {"kernel": "partial_attn", "bound": "mfma" if bf16 else "alu",
-                "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 5),
-                "traffic": recorded_traffic(dominant, wl.name)}
-    else:
-        achieved = kernels[dominant]["gbs"]
-        roof = {"kernel": dominant, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
-                "traffic": recorded_traffic(dominant, wl.name)}
-    if peaks:
-        att = peaks["mfma_bf16_32x32x16_tflops"] if roof["unit"] == "TFLOP/s" else peaks["read_gbs"]
-        if roof["bound"] in ("mfma", "hbm"):
-            roof["attainable_peak"] = att
-            roof["frac_attainable"] = round(roof["achieved"] / att, 5)
-    del stage_calls, copies, keep
-    torch.cuda.empty_cache()
+
+    kernels, roof = {}, None
+    if a.attribution:
+        kernels, roof = attribution_pass(a, wl, runner, inp, stream, stages, steps, warmup, work,
+                                         peaks)
 
     if a.copy_probe_mib > 0:
         n = a.copy_probe_mib << 20
@@ -526,11 +513,6 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-
-    cpu = None
-    if a.cpu_seconds > 0:
-        log("[bench] timing the CPU oracle")
-        cpu = cpu_baseline(wl, a.cpu_seconds, a.dev_source)
 
     value = wl.n_tokens * L / (ms_per_step * 1e-3)
     # whole-step roofline: streaming bytes at the HBM peak plus attention flops
@@ -554,15 +536,164 @@ def main():
                    "dev_source": a.dev_source,
                    "order": f"{a.order}: " + ("select, then rotate-or-replace" if select_first
                                               else "rotate, select, fuse"),
-                   "launch": "hip graph replay" if a.graph else "stream launches"},
+                   "launch": "hip graph replay" if a.graph else "stream launches",
+                   "step_timing": "median of per-step HIP event pairs; K/V restored from a "
+                                  "pristine copy and 512 MiB written (MALL flush) before each "
+                                  "step, outside the events"},
         "roofline": roof,
         "step_roofline": step_roofline,
         "attainable": peaks,
         "cpu_baseline": cpu,
         "kernels": kernels,
-        "wall_ms_per_step": round(wall_ms_per_step, 5),
+        "step_ms": {"median": round(ms_per_step, 5), "mean": round(statistics.mean(step_ms), 5),
+                    "min": round(min(step_ms), 5), "max": round(max(step_ms), 5)},
+        "timed_region_s": round(t1 - t0, 3),
     }
     print(json.dumps(line), flush=True)
+
+
+def attribution_pass(a, wl, runner, inp, stream, stages, steps, warmup, work, peaks):
+    """Each entry point of the step timed on its own, layer by layer, over as
+    many restored steps as the timed pass; returns (kernels, roofline entry of
+    the dominant one)."""
+    import torch
+
+    from selective_recompute_amd import binding as B
+
+    L = wl.n_layers
+    h = stream.cuda_stream
+    lib = B.lib()
+    gref = ctypes.byref(runner.geom)
+    rgs = [rb.struct() for rb in runner.batches]
+    stage_calls = {s: [None] * L for s in STAGES + STAGES_AFTER}
+    topk_calls = [None] * L   # the selection half alone, for its own time
+    # The attention is timed as the launch cb_blend_layer makes: the plan
+    # cb_partial_attn chooses, pinned, on a workspace zero-filled once per
+    # distinct plan (every call leaves its counters at zero), so no call
+    # needs the launch that clears them.
+    ws_bytes = 0 if runner.workspace is None else runner.workspace.numel()
+    plan_ws, keep = {}, []
+    for l, x in enumerate(inp.layers):
+        rb, o = runner.batches[l], runner.outs[l]
+        pd = B.attn_plan(runner.geom, rb, ws_bytes)
+        key = (pd["mfma"], pd["key_split"], pd["key_chunk"])
+        if key not in plan_ws:
+            plan_ws[key] = B.workspace_tensor(pd["workspace_bytes"], "cuda")
+            if plan_ws[key] is not None:
+                plan_ws[key].zero_()
+        plan = B.AttnPlan(key[0], key[1], 0, key[2], 0, 0, 0)
+        keep.append(plan)
+        pws_ptr, pws_bytes = B._ws(plan_ws[key])
+        cand = runner.candidates(l)
+        dev_t, sl, sg = o["dev"], o["sel_local"], o["sel_global"]
+        k_ptr, v_ptr = x["k_old"].data_ptr(), x["v_old"].data_ptr()
+        stage_calls["rerotate"][l] = (lib.cb_rerotate, (gref, k_ptr, k_ptr, x["delta"].data_ptr(),
+                                                         wl.n_tokens, 1, wl.rope_theta,
+                                                         B.ROPE_HALF, h))
+        stage_calls["deviation_topk"][l] = (
+            lib.cb_kv_deviation_topk, (gref, ctypes.byref(rgs[l]), runner.dev_source,
+                                       x["k_new_c"].data_ptr(), k_ptr, x["v_new_c"].data_ptr(),
+                                       v_ptr, cand.data_ptr(), dev_t.data_ptr(), sl.data_ptr(),
+                                       sg.data_ptr(), h))
+        topk_calls[l] = (lib.cb_topk, (ctypes.byref(rgs[l]), dev_t.data_ptr(), cand.data_ptr(),
+                                       sl.data_ptr(), sg.data_ptr(), h))
+        stage_calls["fuse_scatter"][l] = (
+            lib.cb_fuse_scatter, (gref, k_ptr, v_ptr, x["k_new_c"].data_ptr(),
+                                  x["v_new_c"].data_ptr(), sl.data_ptr(), sg.data_ptr(), rb.n_sel,
+                                  h))
+        stage_calls["rerotate_fuse"][l] = (
+            lib.cb_rerotate_fuse, (gref, k_ptr, v_ptr, x["k_new_c"].data_ptr(),
+                                   x["v_new_c"].data_ptr(), x["delta"].data_ptr(), sl.data_ptr(),
+                                   sg.data_ptr(), rb.n_sel, wl.n_tokens, wl.rope_theta,
+                                   B.ROPE_HALF, h))
+        stage_calls["partial_attn"][l] = (
+            lib.cb_partial_attn_with_plan,
+            (gref, ctypes.byref(rgs[l]), ctypes.byref(plan), o["out"].data_ptr(),
+             x["q_c"].data_ptr(), sl.data_ptr(), sg.data_ptr(), k_ptr, v_ptr, runner.scale,
+             pws_ptr, pws_bytes, B.CB_ATTN_COUNTERS_ZERO, h))
+
+    def call(fn_args):
+        fn, args = fn_args
+        st = fn(*args)
+        if st != 0:
+            B.check(st)
+
+    totals = {s: 0.0 for s in stages}
+    topk_ms = 0.0
+    with torch.cuda.stream(stream):
+        for step in range(warmup + steps):
+            inp.restore()
+            evs = []
+            for l in range(L):
+                for s in stages:
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    call(stage_calls[s][l])
+                    e1.record(stream)
+                    evs.append((s, e0, e1))
+                # the top-k again on the scores just computed (same outputs)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                call(topk_calls[l])
+                e1.record(stream)
+                evs.append(("topk", e0, e1))
+            torch.cuda.synchronize()
+            if step < warmup:
+                continue
+            for s, e0, e1 in evs:
+                if s == "topk":
+                    topk_ms += e0.elapsed_time(e1)
+                else:
+                    totals[s] += e0.elapsed_time(e1)
+    launches = steps * L
+    stage_work = {s: steps * sum(w[s] for w in work) for s in stages}
+    kernels = {}
+    for s in stages:
+        avg_us = totals[s] * 1e3 / launches
+        if s == "partial_attn":
+            rate = stage_work[s] / (totals[s] * 1e-3) / 1e12
+            kernels[s] = {"avg_us": round(avg_us, 3), "tflops": round(rate, 3),
+                          "gflop_per_launch": round(stage_work[s] / launches / 1e9, 4)}
+        else:
+            rate = stage_work[s] / (totals[s] * 1e-3) / 1e9
+            kernels[s] = {"avg_us": round(avg_us, 3), "gbs": round(rate, 1),
+                          "mb_per_launch": round(stage_work[s] / launches / 1e6, 4)}
+    # each class against its published peak and, when measured, the attainable one
+    # (MFMA probe for the attention, streaming-read probe for the HBM stages)
+    flop_peak_t = BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
+    for s in stages:
+        kk = kernels[s]
+        if "tflops" in kk:
+            kk["frac"] = round(kk["tflops"] / flop_peak_t, 5)
+            if peaks and wl.dtype == "bf16":
+                kk["frac_attainable"] = round(kk["tflops"] / peaks["mfma_bf16_32x32x16_tflops"], 5)
+        else:
+            kk["frac"] = round(kk["gbs"] / HBM_PEAK_GBS, 5)
+            if peaks:
+                kk["frac_attainable"] = round(kk["gbs"] / peaks["read_gbs"], 5)
+    kernels["topk"] = {"avg_us": round(topk_ms * 1e3 / launches, 3), "bound": "latency"}
+    dominant = max(stages, key=lambda s: totals[s])
+    if dominant == "partial_attn":
+        bf16 = wl.dtype == "bf16"
+        peak = BF16_PEAK_TFLOPS if bf16 else FP32_PEAK_TFLOPS
+        achieved = kernels[dominant]["tflops"]
+        roof = {"kernel": "partial_attn", "bound": "mfma" if bf16 else "alu",
+                "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 5),
+                "traffic": recorded_traffic(dominant, wl.name)}
+    else:
+        achieved = kernels[dominant]["gbs"]
+        roof = {"kernel": dominant, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
+                "traffic": recorded_traffic(dominant, wl.name)}
+    if peaks:
+        att = peaks["mfma_bf16_32x32x16_tflops"] if roof["unit"] == "TFLOP/s" else peaks["read_gbs"]
+        if roof["bound"] in ("mfma", "hbm"):
+            roof["attainable_peak"] = att
+            roof["frac_attainable"] = round(roof["achieved"] / att, 5)
+    del stage_calls, keep, plan_ws
+    torch.cuda.empty_cache()
+    return kernels, roof
 
 
 if __name__ == "__main__":
