@@ -16,6 +16,7 @@ import numpy as np
 import pytest
 import torch
 
+import needles as N
 from oracle import cacheblend_oracle as O
 from selective_recompute_amd import binding as B
 from selective_recompute_amd import pipeline as PL
@@ -322,10 +323,12 @@ def _counters(ws, plan, hkv):
     return ws[end - 4 * n:end].view(torch.int32)
 
 
-def _attention_case(case, use_ws, seed, max_rows=None, plan=None):
+def _attention_case(case, use_ws, seed, max_rows=None, plan=None, family="random"):
     """Run cb_partial_attn (or, given `plan`, cb_partial_attn_with_plan) on a
     seeded case; compare every row (or a sample of max_rows plus each
-    request's first and last) with the oracle."""
+    request's first and last) with the oracle.  family: "random" (iid
+    N(0,1) inputs), "needle" or "peaked" (tests/needles.py: outputs O(1) at
+    any row length)."""
     dtype, hq, hkv, d, lens, ks = case
     rng = np.random.default_rng(seed)
     t_count = sum(lens)
@@ -349,6 +352,10 @@ def _attention_case(case, use_ws, seed, max_rows=None, plan=None):
     q = torch.randn(m, hq, d, generator=gen).to(dtype)
     kf = torch.randn(t_count, hkv, d, generator=gen).to(dtype)
     vf = torch.randn(t_count, hkv, d, generator=gen).to(dtype)
+    if family == "needle":
+        q, kf, vf = N.plant_in_cache(q, kf, vf, N.needle_rows(sel_g, tok_off, sel_off), seed)
+    elif family == "peaked":
+        q = N.peak_queries(q)
     rb = B.RaggedBatch(tok_off, tok_off, sel_off, DEV)
     g = B.geom(hq, hkv, d, dtype)
     ws = None
@@ -360,9 +367,17 @@ def _attention_case(case, use_ws, seed, max_rows=None, plan=None):
     elif use_ws:
         nbytes = B.attn_workspace_bytes(g, rb)
         if nbytes == 0:
-            pytest.skip("the planner does not split this case")
-        ws = B.workspace_tensor(nbytes, DEV)
-        ws.fill_(0xFF)                                        # NaN garbage: must be overwritten
+            # the planner keeps every row whole: the geometry runs the plain
+            # kernel (no split at all), or no request with selected rows is
+            # longer than the shortest key chunk (256 keys); the call then
+            # takes no workspace and the parity below checks that path
+            chosen = B.attn_plan(g, rb)
+            assert chosen["key_chunk"] == 0 and chosen["workspace_bytes"] == 0
+            longest = max(n for n, k in zip(lens, ks) if k)
+            assert chosen["mfma"] == 0 or longest <= 256, (chosen, longest)
+        else:
+            ws = B.workspace_tensor(nbytes, DEV)
+            ws.fill_(0xFF)                                    # NaN garbage: must be overwritten
     out = torch.full((rb.n_sel, hq, d), float("nan"), dtype=dtype, device=DEV)
     scale = 1.0 / math.sqrt(d)
     args = (out, q.to(DEV), torch.from_numpy(sel_l).to(DEV), torch.from_numpy(sel_g).to(DEV),
@@ -372,7 +387,7 @@ def _attention_case(case, use_ws, seed, max_rows=None, plan=None):
     else:
         B.partial_attn(g, rb, *args, workspace=ws)
     torch.cuda.synchronize()
-    used = full if plan is not None else (B.attn_plan(g, rb, ws.numel()) if use_ws else None)
+    used = full if plan is not None else (B.attn_plan(g, rb, ws.numel()) if ws is not None else None)
     if used is not None and used["key_chunk"]:
         # every merging workgroup sets its arrival counter back to zero
         assert not _counters(ws, used, hkv).any()
@@ -398,13 +413,19 @@ def _attention_case(case, use_ws, seed, max_rows=None, plan=None):
                            np64(vf), hq, hkv, scale)
     err = np.abs(got[rows] - ref)
     assert err.max() <= ATTN_ABS, f"max err {err.max()}"
+    if family != "random":
+        assert np.abs(ref).max() > 0.2                         # O(1) outputs
 
 
+FAMILIES = ["random", "needle", "peaked"]
+
+
+@pytest.mark.parametrize("family", FAMILIES)
 @pytest.mark.parametrize("use_ws", [False, True], ids=["direct", "split"])
 @pytest.mark.parametrize("case", ATTN_CASES, ids=[f"a{i}" for i in range(len(ATTN_CASES))])
-def test_partial_attention_parity(case, use_ws):
-    say(f"attention {case} workspace={use_ws}")
-    _attention_case(case, use_ws, sum(case[4]) + case[1])
+def test_partial_attention_parity(case, use_ws, family):
+    say(f"attention {case} workspace={use_ws} {family}")
+    _attention_case(case, use_ws, sum(case[4]) + case[1], family=family)
 
 
 def _random_case(i):
@@ -440,19 +461,20 @@ PINNED_PLANS = [dict(mfma=0), dict(mfma=1, key_split=1, key_chunk=0),
 PINNED_GEOMS = [(32, 8, 128), (8, 2, 64), (16, 1, 32), (8, 8, 128)]
 
 
+@pytest.mark.parametrize("family", FAMILIES)
 @pytest.mark.parametrize("plan", PINNED_PLANS,
                          ids=["plain", "ks1", "ks1c256", "ks1c576", "ks2", "ks2c384", "ks2c1024"])
 @pytest.mark.parametrize("geo", PINNED_GEOMS, ids=[f"h{a}-{b}-d{c}" for a, b, c in PINNED_GEOMS])
-def test_attention_pinned_plans(geo, plan):
+def test_attention_pinned_plans(geo, plan, family):
     hq, hkv, d = geo
     case = (torch.bfloat16, hq, hkv, d, [1500, 700, 33], [230, 100, 33])
-    say(f"attention pinned plan {plan} geometry {geo}")
+    say(f"attention pinned plan {plan} geometry {geo} {family}")
     full = B.describe_plan(B.geom(hq, hkv, d, torch.bfloat16),
                            B.RaggedBatch(PL.offsets(case[4]), PL.offsets(case[4]),
                                          PL.offsets(case[5]), DEV), **plan)
     if plan.get("key_chunk"):
         assert full["key_chunk"] == plan["key_chunk"] and full["workspace_bytes"] > 0
-    _attention_case(case, False, 4242 + d + hq, max_rows=120, plan=plan)
+    _attention_case(case, False, 4242 + d + hq, max_rows=120, plan=plan, family=family)
 
 
 DENSE = [(32, 8, 128, [2048], 64), (64, 8, 128, [700, 1300], 48), (8, 8, 64, [333], None)]
@@ -514,17 +536,43 @@ def _oracle_layer(wl, x, cand, counts, attend_rows=None):
                 v_fused=v_fused, out=out, rows=rows)
 
 
-E2E = [("tiny", [0], None, "pool", True), ("mistral7b-layer", [0], None, "pool", True),
-       ("mistral7b-layer", [0], None, "pool", False), ("7b-32layer-6k", [0, 1, 2], 96, "pool", True),
-       ("7b-32layer-6k", [0, 1], 96, "pool", False), ("7b-32layer-6k", [0, 1, 2, 3], 96, "chain", True),
-       ("7b-32layer-32k", [0, 1], 24, "pool", True), ("70b-80layer-8req", [0, 1], 24, "pool", True)]
+E2E = [("tiny", [0], None, "pool", True, False), ("mistral7b-layer", [0], None, "pool", True, False),
+       ("mistral7b-layer", [0], None, "pool", False, False),
+       ("mistral7b-layer", [0], None, "pool", True, True),
+       ("7b-32layer-6k", [0, 1, 2], 96, "pool", True, False),
+       ("7b-32layer-6k", [0, 1], 96, "pool", False, False),
+       ("7b-32layer-6k", [0, 1, 2, 3], 96, "chain", True, False),
+       ("7b-32layer-6k", [0, 1, 2], 64, "pool", True, True),
+       ("7b-32layer-32k", [0, 1], 24, "pool", True, False),
+       ("7b-32layer-32k", [0, 1], 16, "pool", True, True),
+       ("70b-80layer-8req", [0, 1], 24, "pool", True, False),
+       ("70b-80layer-8req", [0, 1], 16, "pool", True, True)]
 
 
-@pytest.mark.parametrize("name,layers,n_rows,schedule,use_ws", E2E,
-                         ids=[f"{e[0]}-{e[3]}{'' if e[4] else '-noworkspace'}" for e in E2E])
-def test_blend_layers_end_to_end(name, layers, n_rows, schedule, use_ws):
+def _oracle_schedule(wl, layer, first_sel, prev_sel, schedule):
+    """[KV-blog, "渐进式过滤机制"] per request, from the oracle: the selected
+    count of this layer and its packed candidate rows, built from the
+    oracle's own selections of layer 1 and of the previous layer
+    (request-local rows, one array per request)."""
+    counts, cands = [], []
+    for r, n in enumerate(wl.request_lengths):
+        counts.append(O.layer_plan(layer + 1, n, wl.r1_pct, wl.r2_pct)[1])
+        c = O.candidates_for_layer(layer + 1, n, None if first_sel is None else first_sel[r],
+                                   None if prev_sel is None else prev_sel[r], schedule)
+        cands.append(c + wl.tok_off[r])
+    return counts, np.concatenate(cands)
+
+
+@pytest.mark.parametrize("name,layers,n_rows,schedule,use_ws,needles", E2E,
+                         ids=[f"{e[0]}-{e[3]}{'' if e[4] else '-noworkspace'}{'-needles' if e[5] else ''}"
+                              for e in E2E])
+def test_blend_layers_end_to_end(name, layers, n_rows, schedule, use_ws, needles):
     """Whole layers through cb_blend_layer against the oracle; without a
-    workspace the attention runs unsplit."""
+    workspace the attention runs unsplit.  Each layer's selected counts and
+    candidate rows come from the oracle's own schedule over its own previous
+    selections, and must equal what the host driver passes to the library.
+    With needles (tests/needles.py) the attention outputs are O(1) on every
+    row, so a lost key chunk, tile or diagonal fails the bar."""
     wl = W.make_workload(name)
     sets = W.PlantedSets(wl, schedule)
     gen_dev = "cpu" if wl.n_tokens <= 8192 else DEV
@@ -533,22 +581,26 @@ def test_blend_layers_end_to_end(name, layers, n_rows, schedule, use_ws):
                             wl.rope_theta, schedule=schedule)
     if not use_ws:
         runner.workspace = None
+    first_sel = prev_sel = None                      # the oracle's, request-local
     for layer in layers:
-        say(f"blend {name} layer {layer}")
+        say(f"blend {name} layer {layer}{' needles' if needles else ''}")
+        counts, cand = _oracle_schedule(wl, layer, first_sel, prev_sel, schedule)
+        assert counts == runner.filter.counts(layer)
+        assert np.array_equal(cand, npi(runner.candidates(layer)))
         x = W.layer_inputs(wl, sets, layer, device=gen_dev)
+        assert np.array_equal(npi(x["cand_idx"]), cand)   # the compact rows follow it
+        if needles:
+            planted_off = x["planted_off"]
+            pins = N.needle_rows(x["planted"], wl.tok_off, planted_off)
+            x = N.plant_in_blend(x, pins, cand, seed=1000 + layer)
         xg = {k: (v.to(DEV) if torch.is_tensor(v) else v) for k, v in x.items()}
         k_pristine = x["k_old"].cpu() if gen_dev == "cpu" else x["k_old"].clone().cpu()
         x_cpu = dict(x)
         x_cpu["k_old"], x_cpu["v_old"] = k_pristine, x["v_old"].clone().cpu()
         x_cpu["v_new_c"], x_cpu["k_new_c"] = x["v_new_c"].cpu(), x["k_new_c"].cpu()
         x_cpu["q_c"] = x["q_c"].cpu()
-        if layer > 0:
-            # the device keeps the source layer's selection as this layer's candidates
-            assert np.array_equal(npi(runner.candidates(layer)), npi(x["cand_idx"]))
         o = runner.run_layer(layer, xg)
         torch.cuda.synchronize()
-        counts = runner.filter.counts(layer)
-        cand = npi(x["cand_idx"])
         n_sel = int(np.sum(counts))
         rows = None
         if n_rows is not None and n_rows < n_sel:
@@ -570,19 +622,33 @@ def test_blend_layers_end_to_end(name, layers, n_rows, schedule, use_ws):
         got = np64(o["out"])[ref["rows"]]
         err = np.abs(got - ref["out"])
         assert err.max() <= ATTN_ABS, f"attention max err {err.max()}"
+        if needles:
+            assert np.abs(ref["out"]).max() > 0.2        # O(1) outputs: the bar has power
+        # the oracle's own selection feeds its schedule of the next layer
+        sel_loc = [ref["sel_global"][(ref["sel_global"] >= wl.tok_off[r]) &
+                                     (ref["sel_global"] < wl.tok_off[r + 1])] - wl.tok_off[r]
+                   for r in range(wl.n_requests)]
+        if layer == 0:
+            first_sel = sel_loc
+        prev_sel = sel_loc
 
 
-def test_blend_layer_128k_token_request():
+@pytest.mark.parametrize("needles", [False, True], ids=["random", "needles"])
+def test_blend_layer_128k_token_request(needles):
     """One request of 131072 tokens (16 chunks of 8192; deltas up to 122880),
     1% selected: the top-k runs its memory path (128 scores per thread), the
     attention rows reach 131072 keys and the split plan sees its longest rows.
     Exact selection, deviations to 1e-4, fused rows and sampled attention rows
-    against the oracle."""
-    say("blend 128k-token request")
+    against the oracle; with needles the sampled outputs are O(1), so a lost
+    key chunk of these rows fails the bar."""
+    say(f"blend 128k-token request{' needles' if needles else ''}")
     wl = W.Workload("long-128k", 1, ((8192,) * 16,), 32, 8, 128, 10000.0, "bf16", 1, 1, 1, 80,
                     0xCB10, "one request of 131072 tokens")
     sets = W.PlantedSets(wl)
     x = W.layer_inputs(wl, sets, 0, device=DEV)
+    if needles:
+        pins = N.needle_rows(x["planted"], wl.tok_off, x["planted_off"])
+        x = N.plant_in_blend(x, pins, npi(x["cand_idx"]), seed=128)
     x_cpu = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in x.items()}
     runner = PL.BlendRunner(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.torch_dtype,
                             wl.request_lengths, wl.r1_pct, wl.r2_pct, 1, wl.rope_theta)
@@ -608,6 +674,8 @@ def test_blend_layer_128k_token_request():
     assert_k_close(kf[probe], ref["k_rot"][probe], wl.torch_dtype, "fused K")
     err = np.abs(np64(o["out"])[ref["rows"]] - ref["out"])
     assert err.max() <= ATTN_ABS, f"attention max err {err.max()}"
+    if needles:
+        assert np.abs(ref["out"]).max() > 0.2
 
 
 def test_blend_is_deterministic():

@@ -47,7 +47,8 @@ def test_generation_is_deterministic():
     assert not torch.equal(a["k_old"], c["k_old"])
 
 
-@pytest.mark.parametrize("name,layers", [("tiny", [0]), ("mistral7b-layer", [0]), ("7b-32layer-6k", [0, 1, 2, 5])])
+@pytest.mark.parametrize("name,layers", [("tiny", [0]), ("mistral7b-layer", [0]), ("7b-32layer-6k", [0, 1, 2, 5]),
+                                         ("7b-32layer-32k", [0, 1]), ("70b-80layer-8req", [0, 1])])
 @pytest.mark.parametrize("schedule", ["pool", "chain"])
 def test_planted_selection_has_gap(name, layers, schedule):
     wl = W.make_workload(name)
