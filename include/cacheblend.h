@@ -26,7 +26,8 @@
  *     cand_off[r+1]), packed row numbers in ascending order; the recomputed
  *     tensors (k_new_c, v_new_c, q_c) hold one row per candidate in that order.
  *   - Ownership: the caller allocates and frees every buffer.  The library
- *     never allocates, frees or synchronizes, and keeps no mutable global state.
+ *     never allocates, frees or synchronizes, and keeps no mutable global
+ *     state, except the static device scratch of cb_blend_layer_noalloc.
  *   - Ordering: every call enqueues its kernels on `stream` (a hipStream_t;
  *     NULL = the default stream) and returns without waiting.  Calls are
  *     thread-safe.
@@ -363,6 +364,29 @@ cb_status cb_blend_layer(const cb_layer_args *args, void *stream);
  * (CB_ORDER_ROTATE_FIRST or CB_ORDER_SELECT_FIRST), after the same checks of
  * the order field; host only, enqueues nothing. */
 cb_status cb_blend_layer_order(const cb_layer_args *args, int32_t *order);
+
+/*
+ * cb_blend_layer_noalloc -- cb_blend_layer for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, steps and results as
+ * cb_blend_layer, except that args->workspace must be NULL and
+ * args->workspace_bytes 0 (else CB_ERR_INVALID_ARG): the attention's split
+ * partials and arrival counters live in a static device array of the library
+ * of CB_NOALLOC_SCRATCH_BYTES, one per GPU, held from the library's first use
+ * on that GPU until the process ends.  Long rows are split only by plans
+ * that fit in it (where cb_blend_layer with a larger workspace would split
+ * further, this call keeps the best plan that fits, or none; outputs then
+ * agree to rounding, selections and fused rows bit for bit); a plan larger
+ * than the array is refused with CB_ERR_UNSUPPORTED before anything is
+ * enqueued.  The call allocates and frees nothing; its first call on a GPU
+ * looks up the array's device address there (a HIP symbol query).
+ * The array keeps the last call's contents; each call clears the counters it
+ * uses in its own fuse launch.  Every call in a process shares the GPU's one
+ * array, so calls that may overlap on one GPU (different streams or host
+ * threads) race: order them, e.g. on one stream.
+ */
+#define CB_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+cb_status cb_blend_layer_noalloc(const cb_layer_args *args, void *stream);
 
 /* Static description of a status code. */
 const char *cb_status_str(cb_status status);

@@ -106,6 +106,7 @@ _SIGNATURES = {
                                   ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
                                   ctypes.c_size_t, ctypes.c_uint32, ctypes.c_void_p],
     "cb_blend_layer": [ctypes.POINTER(LayerArgs), ctypes.c_void_p],
+    "cb_blend_layer_noalloc": [ctypes.POINTER(LayerArgs), ctypes.c_void_p],
     "cb_blend_layer_order": [ctypes.POINTER(LayerArgs), ctypes.POINTER(ctypes.c_int32)],
 }
 
@@ -325,6 +326,20 @@ def blend_layer(g: Geom, rb: RaggedBatch, *, k, v, k_new_c, v_new_c, q_c, delta,
                      _dev(sel_local, torch.int32), _dev(sel_global, torch.int32), _dev(out),
                      *_ws(workspace), dev_source, order)
     check(lib().cb_blend_layer(ctypes.byref(args), _stream(stream)))
+
+
+def blend_layer_noalloc(g: Geom, rb: RaggedBatch, *, k, v, k_new_c, v_new_c, q_c, delta,
+                        cand_idx, rope_theta: float, rope_style: int, softmax_scale: float, dev,
+                        sel_local, sel_global, out, dev_source: int = CB_DEV_V,
+                        order: int = CB_ORDER_AUTO, stream=None):
+    """cb_blend_layer_noalloc: the attention workspace is the library's static
+    device scratch (no workspace argument)."""
+    args = LayerArgs(g, rb.struct(), _dev(k), _dev(v), _dev(k_new_c), _dev(v_new_c), _dev(q_c),
+                     _dev(delta, torch.int32), _dev(cand_idx, torch.int32), rope_theta,
+                     rope_style, softmax_scale, _dev(dev, torch.float32),
+                     _dev(sel_local, torch.int32), _dev(sel_global, torch.int32), _dev(out),
+                     None, 0, dev_source, order)
+    check(lib().cb_blend_layer_noalloc(ctypes.byref(args), _stream(stream)))
 
 
 class PreparedLayer:

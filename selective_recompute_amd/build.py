@@ -17,7 +17,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcacheblend.so")
 PEAKS = os.path.join(PKG, "cb_peaks")    # attainable-peak probe run by bench.py
 
-SOURCES = ["api.cpp", "stream_kernels.hip", "attn_kernels.hip"]
+SOURCES = ["api.cpp", "stream_kernels.hip", "attn_kernels.hip", "scratch.hip"]
 ARCH = "gfx950"
 
 

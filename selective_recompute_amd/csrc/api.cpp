@@ -694,12 +694,13 @@ CB_EXPORT cb_status cb_blend_layer_order(const cb_layer_args *a, int32_t *order)
   return CB_OK;
 }
 
-CB_EXPORT cb_status cb_blend_layer(const cb_layer_args *a, void *stream) {
-  g_last_error.clear();
+namespace {
+// Every check of cb_blend_layer's arguments but the workspace's, before any
+// HIP call; `after` receives the step order.
+cb_status validate_blend(const cb_layer_args *a, bool &after) {
   if (!a) return fail(CB_ERR_INVALID_ARG, "args is NULL");
   const cb_geom *geom = &a->geom;
   const cb_ragged *rg = &a->rg;
-  // Validate every stage before enqueuing any of them.
   CB_TRY(check_ragged(rg, true, true, true));
   const int64_t n_tok = rg->h_tok_off[rg->n_req];
   if (a->delta)
@@ -711,12 +712,25 @@ CB_EXPORT cb_status cb_blend_layer(const cb_layer_args *a, void *stream) {
                        k_total));
   CB_TRY(validate_attn(geom, rg, a->out, a->q_c, a->sel_local, a->sel_global, a->k, a->v,
                        a->softmax_scale));
-  CB_TRY(need_ptr(a->workspace, "workspace", a->workspace_bytes > 0));
-  bool after = false;
-  CB_TRY(resolve_order(a, n_tok, after));
-  const hipStream_t s = (hipStream_t)stream;
+  return resolve_order(a, n_tok, after);
+}
+
+// The launches of one validated layer; the attention's split partials and
+// arrival counters go to `ws` (ws_bytes; NULL / 0: no split).
+cb_status launch_blend(const cb_layer_args *a, bool after, void *ws, size_t ws_bytes,
+                       hipStream_t s) {
+  const cb_geom *geom = &a->geom;
+  const cb_ragged *rg = &a->rg;
+  const int64_t n_tok = rg->h_tok_off[rg->n_req];
+  const int32_t k_total = rg->h_sel_off[rg->n_req];
   const int32_t m = rg->h_cand_off[rg->n_req];
   const bool rotate = a->delta && n_tok > 0;
+  // The plan first: it only reads host mirrors, and a plan that would not fit
+  // the workspace must stop the call before anything is enqueued.
+  const cb::AttnPlan plan = plan_attn(geom, rg, ws ? ws_bytes : 0);
+  if (plan.split && plan.ws_bytes > ws_bytes)
+    return fail(CB_ERR_UNSUPPORTED, "the attention split needs %zu bytes of workspace, more than "
+                "the %zu available", plan.ws_bytes, ws_bytes);
   if (after) {
     // the V deviation and the top-k first; the re-rotation joins the fuse
     CB_TRY(hip_status(launch_dev_source(geom, CB_DEV_V, a->k_new_c, a->k, a->v_new_c, a->v,
@@ -748,9 +762,8 @@ CB_EXPORT cb_status cb_blend_layer(const cb_layer_args *a, void *stream) {
                       "topk"));
   // The fuse launch (or the rotate-or-replace launch) also clears the
   // attention's arrival counters.
-  const cb::AttnPlan plan = plan_attn(geom, rg, a->workspace ? a->workspace_bytes : 0);
   const bool clear = k_total > 0 && plan.rows_per_tile > 0 && plan.split;
-  uint32_t *const cnt = clear ? (uint32_t *)((char *)a->workspace + plan.cnt_offset) : nullptr;
+  uint32_t *const cnt = clear ? (uint32_t *)((char *)ws + plan.cnt_offset) : nullptr;
   const int64_t n_cnt = clear ? plan.n_cnt : 0;
   if (after && rotate) {
     CB_TRY(hip_status(cb::launch_rerotate_fuse(geom->dtype, a->rope_style, a->k, a->v, a->k_new_c,
@@ -767,7 +780,33 @@ CB_EXPORT cb_status cb_blend_layer(const cb_layer_args *a, void *stream) {
   }
   if (k_total == 0) return CB_OK;
   return run_attn(geom, rg, plan, a->out, a->q_c, a->sel_local, a->sel_global, a->k, a->v,
-                  a->softmax_scale, a->workspace, clear, s);
+                  a->softmax_scale, ws, clear, s);
+}
+}  // namespace
+
+CB_EXPORT cb_status cb_blend_layer(const cb_layer_args *a, void *stream) {
+  g_last_error.clear();
+  // Validate every stage before enqueuing any of them.
+  bool after = false;
+  CB_TRY(validate_blend(a, after));
+  CB_TRY(need_ptr(a->workspace, "workspace", a->workspace_bytes > 0));
+  return launch_blend(a, after, a->workspace, a->workspace ? a->workspace_bytes : 0,
+                      (hipStream_t)stream);
+}
+
+static_assert(CB_NOALLOC_SCRATCH_BYTES == cb::kNoAllocScratchBytes,
+              "the header states the static scratch's size");
+
+CB_EXPORT cb_status cb_blend_layer_noalloc(const cb_layer_args *a, void *stream) {
+  g_last_error.clear();
+  bool after = false;
+  CB_TRY(validate_blend(a, after));
+  if (a->workspace || a->workspace_bytes)
+    return fail(CB_ERR_INVALID_ARG, "cb_blend_layer_noalloc takes no workspace (it uses the "
+                "library's static scratch): pass workspace NULL and workspace_bytes 0");
+  void *scratch = nullptr;
+  CB_TRY(hip_status(cb::noalloc_scratch(&scratch), "static scratch address"));
+  return launch_blend(a, after, scratch, cb::kNoAllocScratchBytes, (hipStream_t)stream);
 }
 
 CB_EXPORT const char *cb_status_str(cb_status status) {

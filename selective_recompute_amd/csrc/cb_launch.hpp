@@ -110,4 +110,10 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &plan, bool counte
 
 hipError_t launch_attn_simple(int dtype, const AttnArgs &a, hipStream_t stream);
 
+// The library's own device scratch (scratch.hip): the attention workspace of
+// cb_blend_layer_noalloc.  noalloc_scratch() gives its address on the
+// current device (looked up once per device); it allocates nothing.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_scratch(void **ptr);
+
 }  // namespace cb

@@ -175,6 +175,26 @@ def test_blend_layer_validates_every_stage_first(lib):
         assert b"CB_ORDER_SELECT_FIRST" in lib.cb_last_error()
 
 
+def test_blend_layer_noalloc_validates_and_refuses_a_workspace(lib):
+    """cb_blend_layer_noalloc checks every stage as cb_blend_layer does and
+    refuses a workspace (it brings its own static scratch), all before any
+    HIP call, so nothing here touches a device."""
+    assert lib.cb_blend_layer_noalloc(None, None) == 1
+    rg, keep = _ragged([0, 10], [0, 10], [0, 3])
+    good = dict(geom=_geom(), rg=rg, k=P, v=P2, k_new_c=P, v_new_c=P, q_c=P, delta=P,
+                cand_idx=P, rope_theta=1e4, rope_style=0, softmax_scale=0.1, dev=P,
+                sel_local=P, sel_global=P, out=P, workspace=None, workspace_bytes=0)
+    for field, value, status, text in [("workspace", P, 1, b"static scratch"),
+                                       ("workspace_bytes", 1024, 1, b"static scratch"),
+                                       ("out", None, 1, b"out"),
+                                       ("order", 3, 1, b"order"),
+                                       ("geom", B.Geom(32, 8, 128, 9), 2, b"dtype")]:
+        args = dict(good)
+        args[field] = value
+        assert lib.cb_blend_layer_noalloc(ctypes.byref(B.LayerArgs(**args)), None) == status, field
+        assert text in lib.cb_last_error(), field
+
+
 def test_blend_layer_order_choice(lib):
     """CB_ORDER_AUTO selects first for a V deviation while the layer's K cache
     is at most CB_SELECT_FIRST_MAX_BYTES (16 MiB), or when the shared
