@@ -42,7 +42,8 @@ namespace cb {
 //    so that the two read patterns below are free of bank conflicts.
 //  * S^T = K Q^T (keys on the M side, queries on the N side) in 32-key
 //    blocks: a lane's scores all belong to one query column, so the
-//    online-softmax statistics stay in the lane and its partner l^32, and the
+//    online-softmax statistics stay in the lane and its partner l^32 (pair
+//    exchange through v_permlane32_swap), and the
 //    probabilities of 16 consecutive keys are 8 consecutive accumulator
 //    registers -- already the B operand of the second product.
 //  * O^T += V^T P^T in 32-dim blocks.  The A operand (8 keys of one head
@@ -189,6 +190,21 @@ template <typename T> __device__ inline void store_agent(T *p, T v) {
 }
 template <typename T> __device__ inline T load_agent(const T *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Lanes l and l ^ 32 hold the two halves of one query column.  gfx950's
+// v_permlane32_swap trades the upper 32 lanes of one register with the lower
+// 32 lanes of another; swapping x with itself leaves each lane holding, in
+// the two results, x of itself and x of lane l ^ 32 -- no LDS round trip
+// (a shuffle through ds_bpermute costs one on the path from the scores to
+// the exponentials of every tile).
+__device__ inline float lane_pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float lane_pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ inline uint32_t lds_addr(const bf16 *p) {
@@ -362,6 +378,17 @@ void attn_mfma_kernel(const AttnParams p) {
         sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[st], sacc[sb], 0, 0, 0);
       }
     }
+    // Keep four K fragments in flight ahead of the products: left alone, the
+    // compiler reads each fragment right before its product and every
+    // product waits out an LDS latency (measured: 2-4% of the launch at the
+    // 6k to 70B-batch shapes).
+#pragma unroll
+    for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < NKS * NSB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
 
     if (kg0 + 32 * NSB - 1 > p_first) {  // causal mask (key blocks past the first row)
 #pragma unroll
@@ -375,7 +402,7 @@ void attn_mfma_kernel(const AttnParams p) {
     for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[sb][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    mx = lane_pair_max(mx);
     const float mxs = mx * p.scale_log2;
     const bool raise = mxs > m_run + kRescaleSlack;
     if (__any(raise)) {
@@ -420,7 +447,7 @@ void attn_mfma_kernel(const AttnParams p) {
     }
   }
 
-  float l = l_run + __shfl_xor(l_run, 32, kWave);
+  float l = lane_pair_sum(l_run);
   if constexpr (KS == 2) {
     // Key group 1 hands (running max, running sum, O) of its query vectors to
     // group 0 through LDS (the stage buffers are free once every wave is past
@@ -487,7 +514,7 @@ void attn_mfma_kernel(const AttnParams p) {
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(o[dt][e]));
-      amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+      amax = lane_pair_max(amax);
       const float inv_amax = amax > 0.f ? 1.f / amax : 0.f;
       uint64_t *wo = reinterpret_cast<uint64_t *>(w);
 #pragma unroll

@@ -320,18 +320,22 @@ hipError_t launch_rerotate_deviation(int dtype, int style, void *k, const int32_
 
 // ---------------------------------------------------------------------------
 // Top-k, [Derivations, "近似解"] (greedy TopK of the deviation) with ties to
-// the lower index and NaN above +inf.  One 1024-thread workgroup per request;
-// thread t owns the contiguous candidate segment [t*seg, (t+1)*seg), held in
-// registers when seg <= KPT (KPT = 0: re-read from memory every pass).
+// the lower index and NaN above +inf.  One 1024-thread workgroup per request.
+// Wave w owns the contiguous candidate range [w cw, (w + 1) cw) of its
+// request (cw = ceil(m / 16) rounded up to 64), and in round i its lane l holds
+// candidate w cw + 64 i + l: every load is one coalesced 256-byte run, and the
+// scores stay in registers for up to KPT rounds (KPT = 0: re-read every pass).
 //   1. MSB-first radix select over the order-preserving uint32 key of each
-//      fp32 score, 8 bits per pass with an LDS histogram.  Histogram updates
-//      are aggregated per wave (one atomic per distinct bin and wave), since
-//      most scores share their leading bits.  The select stops at the first
+//      fp32 score, 8 bits per pass with an LDS histogram (one atomic per wave
+//      for each of its first two distinct bins, then one per lane).  The select
+//      stops at the first
 //      pass whose boundary bin holds exactly the keys still missing: then the
 //      whole bin is selected.
 //   2. An ordered compaction emits, in candidate order (= ascending packed
 //      row), every key above the boundary bin and the first `keep_eq` keys
-//      inside it (ties to the lower index).
+//      inside it (ties to the lower index): one scan over the 16 waves' counts
+//      gives each wave's bases, and inside a round the ballot of the same
+//      predicate orders the lanes (its bits below the lane).
 // ---------------------------------------------------------------------------
 __device__ inline uint32_t order_key(float x) {
   uint32_t u = __float_as_uint(x);
@@ -343,29 +347,27 @@ __device__ inline uint32_t order_key(float x) {
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / kWave;
 
-// Exclusive block-wide prefix of two per-thread counts.
-__device__ inline void block_excl_scan2(uint32_t a, uint32_t b, uint32_t &a_excl, uint32_t &b_excl,
-                                        uint32_t (*wave_tot)[kTopkWaves]) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int ai = wave_incl_scan((int)a), bi = wave_incl_scan((int)b);
-  if (lane == kWave - 1) { wave_tot[0][wave] = ai; wave_tot[1][wave] = bi; }
-  __syncthreads();
-  uint32_t a_before = 0, b_before = 0;
-  for (int w = 0; w < wave; ++w) { a_before += wave_tot[0][w]; b_before += wave_tot[1][w]; }
-  a_excl = a_before + ai - a;
-  b_excl = b_before + bi - b;
+// Rounds of 64 candidates per wave for a request of m candidates.
+__host__ __device__ constexpr int topk_rounds(int m) {
+  return ((m + kTopkWaves - 1) / kTopkWaves + kWave - 1) / kWave;
 }
 
-// hist[bin] += 1 for every lane with bin >= 0, one atomic per distinct bin.
+// hist[bin] += 1 for every lane with bin >= 0: one atomic per bin for the
+// first two distinct bins of the wave (most scores share their leading bits,
+// so in the first passes a wave seldom spans more), then one per lane.
 __device__ inline void wave_hist_add(uint32_t *hist, int bin) {
+  const int lane = (int)(threadIdx.x & (kWave - 1));
   uint64_t pending = __ballot(bin >= 0);
-  while (pending) {
+#pragma unroll
+  for (int round = 0; round < 2; ++round) {
+    if (!pending) return;
     const int leader = __builtin_ctzll(pending);
     const int lb = __builtin_amdgcn_readlane(bin, leader);
     const uint64_t same = __ballot(bin == lb);
-    if ((int)(threadIdx.x & (kWave - 1)) == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(same));
+    if (lane == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(same));
     pending &= ~same;
   }
+  if ((pending >> lane) & 1ull) atomicAdd(&hist[bin], 1u);
 }
 
 // one_m / one_k: for a single request, its candidate and selected counts
@@ -387,7 +389,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   const int m = one ? one_m : cand_off[r + 1] - c0;
   const int s0 = one ? 0 : sel_off[r];
   const int k = one ? one_k : sel_off[r + 1] - s0;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   if (k <= 0) return;
   if (k >= m) {  // every candidate is selected
     for (int j = tid; j < m; j += kTopkThreads) {
@@ -396,34 +398,37 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     }
     return;
   }
-  const int seg = (m + kTopkThreads - 1) / kTopkThreads;
-  const int jb = tid * seg < m ? tid * seg : m;
-  const int n_my = (jb + seg < m ? jb + seg : m) - jb;
+  const int rounds = topk_rounds(m);
+  const int wb = wave * rounds * kWave;                  // first candidate of this wave
+  const int n_w = max(0, min(m - wb, rounds * kWave));   // candidates of this wave
+  const float *dw = dev + c0 + wb + lane;
+  const int32_t *cw = cand_idx + c0 + wb + lane;
   uint32_t keys[KPT > 0 ? KPT : 1];
   int32_t cands[KPT > 0 ? KPT : 1];  // loaded with the scores: no load left at the end
   if (KPT > 0) {
 #pragma unroll
     for (int i = 0; i < (KPT > 0 ? KPT : 1); ++i) {
-      keys[i] = i < n_my ? order_key(dev[c0 + jb + i]) : 0u;
-      cands[i] = i < n_my ? cand_idx[c0 + jb + i] : 0;
+      const bool ok = kWave * i + lane < n_w;
+      keys[i] = ok ? order_key(dw[kWave * i]) : 0u;
+      cands[i] = ok ? cw[kWave * i] : 0;
     }
   }
-  auto key_at = [&](int i) -> uint32_t {
+  auto key_at = [&](int i) -> uint32_t {  // only for candidates of this wave
     if (KPT > 0) return keys[i];
-    return order_key(dev[c0 + jb + i]);
+    return order_key(dw[kWave * i]);
   };
-  const int iters = KPT > 0 ? KPT : seg;  // uniform over the workgroup
+  const int iters = KPT > 0 ? KPT : rounds;  // uniform over the workgroup
   constexpr int kUnroll = KPT > 0 ? KPT : 1;  // register path: fully unrolled
 
   uint32_t prefix = 0, mask = 0, krem = (uint32_t)k;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     if (tid < 256) hist[tid] = 0;
-    __syncthreads();
+    __syncthreads();  // also: every thread has read the previous pass's sh_*
 #pragma unroll kUnroll
     for (int i = 0; i < iters; ++i) {
       int bin = -1;
-      if (i < n_my) {
+      if (kWave * i + lane < n_w) {
         const uint32_t key = key_at(i);
         if ((key & mask) == prefix) bin = (int)((key >> shift) & 255u);
       }
@@ -453,36 +458,52 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     prefix |= sh_digit << shift;
     mask |= 255u << shift;
     krem -= sh_above;
-    const uint32_t cnt = sh_count;
-    __syncthreads();  // every thread has read sh_* before the next pass
-    if (cnt == krem) break;  // the whole boundary bin is selected
+    if (sh_count == krem) break;  // the whole boundary bin is selected
   }
   const uint32_t keep_eq = krem;  // keys of the boundary bin to keep, lowest index first
 
+  // keys above the boundary bin (gt) and inside it (eq), per wave
   uint32_t n_gt = 0, n_eq = 0;
 #pragma unroll kUnroll
   for (int i = 0; i < iters; ++i) {
-    if (i < n_my) {
+    bool gt = false, eq = false;
+    if (kWave * i + lane < n_w) {
       const uint32_t km = key_at(i) & mask;
-      n_gt += km > prefix;
-      n_eq += km == prefix;
+      gt = km > prefix;
+      eq = km == prefix;
     }
+    n_gt += __popcll(__ballot(gt));
+    n_eq += __popcll(__ballot(eq));
   }
-  uint32_t gt_before, eq_before;
-  block_excl_scan2(n_gt, n_eq, gt_before, eq_before, wave_tot);
+  if (lane == 0) {
+    wave_tot[0][wave] = n_gt;
+    wave_tot[1][wave] = n_eq;
+  }
+  __syncthreads();
+  uint32_t gt_before = 0, eq_before = 0;  // of the waves before this one
+  for (int w = 0; w < wave; ++w) {
+    gt_before += wave_tot[0][w];
+    eq_before += wave_tot[1][w];
+  }
+  const uint64_t below = (1ull << lane) - 1ull;  // lanes before this one
 #pragma unroll kUnroll
   for (int i = 0; i < iters; ++i) {
-    if (i < n_my) {
+    bool gt = false, eq = false;
+    if (kWave * i + lane < n_w) {
       const uint32_t km = key_at(i) & mask;
-      const bool gt = km > prefix, eq = km == prefix;
-      if (gt || (eq && eq_before < keep_eq)) {
-        const uint32_t pos = gt_before + (eq_before < keep_eq ? eq_before : keep_eq);
-        sel_local[s0 + pos] = c0 + jb + i;
-        sel_global[s0 + pos] = KPT > 0 ? cands[i] : cand_idx[c0 + jb + i];
-      }
-      gt_before += gt;
-      eq_before += eq;
+      gt = km > prefix;
+      eq = km == prefix;
     }
+    const uint64_t bg = __ballot(gt), be = __ballot(eq);
+    const uint32_t g_pos = gt_before + (uint32_t)__popcll(bg & below);
+    const uint32_t e_pos = eq_before + (uint32_t)__popcll(be & below);
+    if (gt || (eq && e_pos < keep_eq)) {
+      const uint32_t pos = g_pos + (e_pos < keep_eq ? e_pos : keep_eq);
+      sel_local[s0 + pos] = c0 + wb + kWave * i + lane;
+      sel_global[s0 + pos] = KPT > 0 ? cands[i] : cw[kWave * i];
+    }
+    gt_before += (uint32_t)__popcll(bg);
+    eq_before += (uint32_t)__popcll(be);
   }
 }
 
@@ -495,16 +516,16 @@ hipError_t launch_topk(int32_t n_req, const float *dev, const int32_t *cand_idx,
   for (int32_t r = 0; r < n_req; ++r) max_m = std::max(max_m, h_cand_off[r + 1] - h_cand_off[r]);
   const int32_t one_m = n_req == 1 ? h_cand_off[1] : -1;
   const int32_t one_k = n_req == 1 ? h_sel_off[1] : -1;
-  const int seg = (max_m + kTopkThreads - 1) / kTopkThreads;
+  const int rounds = topk_rounds(max_m);
 #define CB_TOPK(K)                                                                            \
   hipLaunchKernelGGL(topk_kernel<K>, dim3(n_req), dim3(kTopkThreads), 0, stream, dev, cand_idx, \
                      cand_off, sel_off, sel_local, sel_global, one_m, one_k)
-  if (seg <= 1) CB_TOPK(1);
-  else if (seg <= 2) CB_TOPK(2);
-  else if (seg <= 4) CB_TOPK(4);
-  else if (seg <= 8) CB_TOPK(8);
-  else if (seg <= 16) CB_TOPK(16);
-  else if (seg <= 32) CB_TOPK(32);
+  if (rounds <= 1) CB_TOPK(1);
+  else if (rounds <= 2) CB_TOPK(2);
+  else if (rounds <= 4) CB_TOPK(4);
+  else if (rounds <= 8) CB_TOPK(8);
+  else if (rounds <= 16) CB_TOPK(16);
+  else if (rounds <= 32) CB_TOPK(32);
   else CB_TOPK(0);
 #undef CB_TOPK
   return hipGetLastError();
