@@ -23,7 +23,8 @@ HIP events on the launch stream, against the published peak and against the
 peak measured by the in-tree probe `cb_peaks`), the whole-step roofline
 fraction (streaming bytes at 8 TB/s plus attention flops at the MFMA peak,
 over the step time), per-kernel figures (each stage's rate and its fraction of
-the published and the measured peak; the top-k also timed on its own) and the
+the published and the measured peak; the top-k also timed on its own), the
+selection objective of the deviation top-k against random selections, and the
 CPU oracle timed on the host as a reported baseline.
 """
 from __future__ import annotations
@@ -129,6 +130,9 @@ def parse_args(argv=None):
     ap.add_argument("--attribution", type=int, default=1,
                     help="1: also time every entry point on its own (per-kernel figures "
                          "and the roofline entry)")
+    ap.add_argument("--objective", type=int, default=1,
+                    help="1: also report the selection objective of the deviation top-k "
+                         "against random selections (library kernels, c1's shape)")
     ap.add_argument("--prefill", action="store_true",
                     help="instead of the blend step: dense causal attention of every "
                          "row (layer-1 full prefill) at the workload's shape")
@@ -352,6 +356,80 @@ def prefill_main(a, peaks):
         "roofline": roof, "attainable": peaks}), flush=True)
 
 
+def selection_objective():
+    """[Derivations, "形式化"] objective at the Mistral-7B-shaped layer (4 chunks
+    of 512 tokens, 32 / 8 heads, bf16), through the library only: the norm of
+    the difference between every row's attention over the fused cache and
+    over full recompute, for the deviation top-k ([Derivations, "近似解"]), for
+    8 random selections of the same size, for no recompute and for the top-k
+    over a cache that is not re-rotated.  Keys: one content rotated (by the
+    library) to chunk-local cached and global recomputed positions; values
+    deviate strongly on 15% of the tokens."""
+    import torch
+
+    from selective_recompute_amd import binding as B
+    from selective_recompute_amd import pipeline as PL
+
+    hq, hkv, d, theta, chunk, n_chunks = 32, 8, 128, 10000.0, 512, 4
+    t = chunk * n_chunks
+    k_sel = PL.select_count(15, t)
+    gen = torch.Generator(device="cuda").manual_seed(0xCB0E)
+    rnd = lambda *shape: torch.randn(*shape, generator=gen, device="cuda")
+    p_old = torch.arange(chunk, dtype=torch.int32, device="cuda").repeat(n_chunks)
+    p_new = torch.arange(t, dtype=torch.int32, device="cuda")
+    g_kv, g_q, g = B.geom(hkv, hkv, d, torch.bfloat16), B.geom(hq, hq, d, torch.bfloat16), \
+        B.geom(hq, hkv, d, torch.bfloat16)
+
+    def rotated(x, pos, geom):
+        out = torch.empty_like(x)
+        B.rerotate(geom, out, x, pos, t, 1, theta)
+        return out
+
+    k_base = rnd(t, hkv, d)
+    k_old = rotated(k_base.to(torch.bfloat16), p_old, g_kv)
+    k_new = rotated((k_base + 0.01 * rnd(t, hkv, d)).to(torch.bfloat16), p_new, g_kv)
+    q = rotated(rnd(t, hq, d).to(torch.bfloat16), p_new, g_q)
+    v_old = rnd(t, hkv, d).to(torch.bfloat16)
+    hot = torch.randperm(t, generator=gen, device="cuda")[:k_sel]
+    sigma = torch.full((t, 1, 1), 0.01, device="cuda")
+    sigma[hot] = 1.0
+    v_new = (v_old.float() + sigma * rnd(t, hkv, d)).to(torch.bfloat16)
+    delta = p_new - p_old
+    every = torch.arange(t, dtype=torch.int32, device="cuda")
+    rb_all = B.RaggedBatch([0, t], [0, t], [0, t], "cuda")
+    ws = B.workspace_tensor(B.attn_workspace_bytes(g, rb_all))
+    scale = 1.0 / math.sqrt(d)
+
+    def attend(keys, vals):
+        out = torch.empty((t, hq, d), dtype=torch.bfloat16, device="cuda")
+        B.partial_attn(g, rb_all, out, q, every, every, keys, vals, scale, ws)
+        return out
+
+    full = attend(k_new, v_new).float()
+
+    def error(sel, rerotate_cache=True):
+        sel = torch.sort(sel.to(torch.int32)).values
+        keys, vals = k_old.clone(), v_old.clone()
+        if rerotate_cache:
+            B.rerotate(g_kv, keys, keys, delta, t, 1, theta)
+        B.fuse_scatter(g, keys, vals, k_new, v_new, sel, sel, len(sel))
+        return float(torch.linalg.vector_norm(attend(keys, vals).float() - full))
+
+    rb = B.RaggedBatch([0, t], [0, t], [0, k_sel], "cuda")
+    dev = torch.empty(t, dtype=torch.float32, device="cuda")
+    sl = torch.empty(k_sel, dtype=torch.int32, device="cuda")
+    sg = torch.empty(k_sel, dtype=torch.int32, device="cuda")
+    B.deviation_topk(g, rb, v_new, v_old, every, dev, sl, sg)
+    e_rand = [error(torch.randperm(t, generator=gen, device="cuda")[:k_sel]) for _ in range(8)]
+    return {"objective": "||Attn(Q,K_fused,V_fused) - Attn(Q,K_new,V_new)|| over every row",
+            "shape": "4x512 tokens, 32/8 heads, head_dim 128, bf16, 15% selected",
+            "hkvd_topk": round(error(sg), 4),
+            "random_min": round(min(e_rand), 4), "random_mean": round(sum(e_rand) / 8, 4),
+            "random_max": round(max(e_rand), 4), "random_draws": 8,
+            "no_recompute": round(error(sg[:0]), 4),
+            "hkvd_topk_cache_not_rerotated": round(error(sg, rerotate_cache=False), 4)}
+
+
 class Inputs:
     """Every layer's inputs on the device, generated once.  K and V of all
     layers live in one working and one pristine tensor each: restore() copies
@@ -505,6 +583,8 @@ def main():
         kernels, roof = attribution_pass(a, wl, runner, inp, stream, stages, steps, warmup, work,
                                          peaks)
 
+    objective = selection_objective() if a.objective else None
+
     if a.copy_probe_mib > 0:
         n = a.copy_probe_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
@@ -545,6 +625,7 @@ def main():
         "attainable": peaks,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "selection_objective": objective,
         "step_ms": {"median": round(ms_per_step, 5), "mean": round(statistics.mean(step_ms), 5),
                     "min": round(min(step_ms), 5), "max": round(max(step_ms), 5)},
         "timed_region_s": round(t1 - t0, 3),

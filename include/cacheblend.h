@@ -357,6 +357,12 @@ typedef struct cb_layer_args {
  * which needs the keys re-rotated before it).
  * [KV-blog, "渐进式过滤机制"]: the caller runs it per layer, passing all
  * tokens as candidates at layer 1 and the surviving rows afterwards.
+ * Precondition (not checked on the host): cand_idx is ascending within each
+ * request and the requests' rows follow each other, so that the selection
+ * (cand_idx[sel_local]) is strictly ascending over the whole batch, as the
+ * rotate-or-replace pass of CB_ORDER_SELECT_FIRST requires.  With candidates
+ * out of order that pass may turn a selected row instead of replacing it;
+ * the selection written by a previous layer's call always qualifies.
  */
 cb_status cb_blend_layer(const cb_layer_args *args, void *stream);
 

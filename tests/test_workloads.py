@@ -105,3 +105,29 @@ def test_tied_keys_carry_the_planted_gap(name, layer, source):
         assert np.array_equal(glob, x["planted"][x["planted_off"][r]:x["planted_off"][r + 1]])
         srt = np.sort(d_r)[::-1]
         assert (srt[k - 1] - srt[k]) / srt[k - 1] > 1e-3
+
+
+@pytest.mark.parametrize("schedule", ["pool", "chain"])
+def test_candidates_and_selections_ascend_over_the_batch(schedule):
+    """cb_blend_layer's rotate-or-replace pass needs the selection strictly
+    ascending over the whole packed batch; it is, whenever each request's
+    candidates ascend inside the request's rows: the oracle's top-k emits each
+    request's selection in ascending order, and the requests' rows follow
+    each other.  Checked on the ragged 8-request workload, layers 1-3."""
+    wl = W.make_workload("70b-80layer-8req")
+    sets = W.PlantedSets(wl, schedule)
+    for layer in range(3):
+        s = sets.layer(layer)
+        assert np.all(np.diff(s.cand_idx) > 0)
+        for r in range(wl.n_requests):
+            c = s.cand_idx[s.cand_off[r]:s.cand_off[r + 1]]
+            assert c.min() >= wl.tok_off[r] and c.max() < wl.tok_off[r + 1]
+        rng = np.random.default_rng(layer)
+        dev = rng.random(len(s.cand_idx))
+        sel = []
+        for r in range(wl.n_requests):
+            c0, c1 = s.cand_off[r], s.cand_off[r + 1]
+            k = O.layer_plan(layer + 1, wl.request_lengths[r], wl.r1_pct, wl.r2_pct)[1]
+            sel.append(O.topk_select(dev[c0:c1], s.cand_idx[c0:c1], min(k, c1 - c0))[1])
+        assert np.all(np.diff(np.concatenate(sel)) > 0)
+        assert np.all(np.diff(s.planted) > 0)
