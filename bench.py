@@ -7,8 +7,10 @@ recomputed rows, and run the selected rows' causal GQA attention -- over one
 batch of seeded synthetic input already resident in HBM.  The blend works in
 place on the cached K/V, so the run keeps one pristine and one working copy
 of every layer's K/V: before each step (untimed) the working copy is restored
-from the pristine one and the 256 MB Infinity Cache is flushed by writing
-512 MiB, so no step reads another step's results or starts from a warm MALL.
+from the pristine one and the 256 MB Infinity Cache is flushed by reading
+512 MiB, so no step reads another step's results or starts from a warm MALL;
+then a bounded spin kernel keeps the GPU busy while the host enqueues the
+step, so the events time the GPU's work rather than the host's launch rate.
 Each step's L-layer loop is timed with its own pair of HIP events on the
 launch stream; ms_per_step is the median over the timed steps.
 
@@ -85,6 +87,13 @@ def attainable_peaks():
         log(f"[bench] peak probe failed: {res.stderr.strip()}")
         return None
     return json.loads(res.stdout.strip().splitlines()[-1])
+
+
+def mfma_attainable(peaks):
+    """The attainable bf16 MFMA rate for real data: the probe's figure on
+    pseudo-random operands (the chip clocks lower when more operand bits
+    toggle), or its smooth-operand figure where an older probe lacks it."""
+    return peaks.get("mfma_bf16_32x32x16_random_tflops") or peaks["mfma_bf16_32x32x16_tflops"]
 
 
 def recorded_traffic(stage, workload):
@@ -343,8 +352,8 @@ def prefill_main(a, peaks):
             "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 5),
             "traffic": None}
     if peaks:
-        roof["attainable_peak"] = peaks["mfma_bf16_32x32x16_tflops"]
-        roof["frac_attainable"] = round(tf / peaks["mfma_bf16_32x32x16_tflops"], 5)
+        roof["attainable_peak"] = mfma_attainable(peaks)
+        roof["frac_attainable"] = round(tf / mfma_attainable(peaks), 5)
     print(json.dumps({
         "metric": "dense causal attention TFLOP/s (layer-1 full prefill)", "value": round(tf, 3),
         "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
@@ -433,8 +442,11 @@ def selection_objective():
 class Inputs:
     """Every layer's inputs on the device, generated once.  K and V of all
     layers live in one working and one pristine tensor each: restore() copies
-    the pristine caches over the working ones and then writes FLUSH_BYTES so
-    that nothing of the previous step stays in the Infinity Cache."""
+    the pristine caches over the working ones and then reads FLUSH_BYTES of
+    an unrelated buffer, so that nothing of the previous step (nor of the
+    restore) stays in L2 or the Infinity Cache.  A read evicts with clean
+    lines: a written flush would leave dirty lines whose write-back lands
+    inside the next step."""
 
     def __init__(self, wl, sets):
         import torch
@@ -454,14 +466,49 @@ class Inputs:
             self.v_pristine[layer].copy_(x.pop("v_old"))
             x["k_old"], x["v_old"] = self.k_work[layer], self.v_work[layer]
             self.layers.append(x)
-        self.flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
-        self._n = 0
+        self.flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+        self.flush_sum = torch.zeros((), dtype=torch.int64, device="cuda")
+        self._sum = torch.sum
+        self._i64 = torch.int64
 
     def restore(self):
         self.k_work.copy_(self.k_pristine)
         self.v_work.copy_(self.v_pristine)
-        self._n += 1
-        self.flush.fill_(self._n & 0xFF)
+        self._sum(self.flush, dim=0, dtype=self._i64, out=self.flush_sum)
+
+
+class HeadStart:
+    """Keeps the GPU busy while the host enqueues a step, so that the events
+    around the step (or around each launch of the attribution pass) time the
+    GPU's work and not the rate at which the host can launch.  Before each
+    step, outside the events, it enqueues torch's bounded spin kernel
+    (torch.cuda._sleep) for 1.5x the host's enqueue time of the previous
+    step, at least 100 us and at most 50 ms."""
+
+    MIN_US, MAX_US = 100.0, 50000.0
+
+    def __init__(self, torch, stream):
+        self._sleep = torch.cuda._sleep
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            self._sleep(1000)
+            e0.record(stream)
+            self._sleep(1 << 21)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        self.cycles_per_us = (1 << 21) / max(e0.elapsed_time(e1) * 1e3, 1.0)
+        self.us = self.MIN_US
+        self._t = None
+
+    def __call__(self):
+        """Enqueue the spin, then start the host clock of the step."""
+        self._sleep(int(self.us * self.cycles_per_us))
+        self._t = time.perf_counter()
+
+    def done(self):
+        """The step is enqueued: size the next spin to the host's time."""
+        host_us = (time.perf_counter() - self._t) * 1e6
+        self.us = min(self.MAX_US, max(self.MIN_US, 1.5 * host_us))
 
 
 def main():
@@ -539,10 +586,13 @@ def main():
     # ---- timed pass: whole layers through cb_blend_layer --------------------
     graph = None
     step_events = []
+    head = HeadStart(torch, stream)
     with torch.cuda.stream(stream):
         for _ in range(warmup):
             inp.restore()
+            head()
             launch_step()
+            head.done()
         torch.cuda.synchronize()
         if a.graph:
             # capture records the launches without running them
@@ -553,6 +603,7 @@ def main():
         t0 = time.perf_counter()
         for _ in range(steps):
             inp.restore()                                   # untimed: outside the events
+            head()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             if graph is not None:
@@ -560,6 +611,7 @@ def main():
             else:
                 launch_step()
             e1.record(stream)
+            head.done()
             step_events.append((e0, e1))
         torch.cuda.synchronize()
         t1 = time.perf_counter()
@@ -618,7 +670,8 @@ def main():
                                               else "rotate, select, fuse"),
                    "launch": "hip graph replay" if a.graph else "stream launches",
                    "step_timing": "median of per-step HIP event pairs; K/V restored from a "
-                                  "pristine copy and 512 MiB written (MALL flush) before each "
+                                  "pristine copy, 512 MiB read (L2 and MALL flush) and a spin "
+                                  "that outlasts the host's enqueue of the step, before each "
                                   "step, outside the events"},
         "roofline": roof,
         "step_roofline": step_roofline,
@@ -701,9 +754,11 @@ def attribution_pass(a, wl, runner, inp, stream, stages, steps, warmup, work, pe
 
     totals = {s: 0.0 for s in stages}
     topk_ms = 0.0
+    head = HeadStart(torch, stream)
     with torch.cuda.stream(stream):
         for step in range(warmup + steps):
             inp.restore()
+            head()
             evs = []
             for l in range(L):
                 for s in stages:
@@ -718,6 +773,7 @@ def attribution_pass(a, wl, runner, inp, stream, stages, steps, warmup, work, pe
                 call(topk_calls[l])
                 e1.record(stream)
                 evs.append(("topk", e0, e1))
+            head.done()
             torch.cuda.synchronize()
             if step < warmup:
                 continue
@@ -747,7 +803,7 @@ def attribution_pass(a, wl, runner, inp, stream, stages, steps, warmup, work, pe
         if "tflops" in kk:
             kk["frac"] = round(kk["tflops"] / flop_peak_t, 5)
             if peaks and wl.dtype == "bf16":
-                kk["frac_attainable"] = round(kk["tflops"] / peaks["mfma_bf16_32x32x16_tflops"], 5)
+                kk["frac_attainable"] = round(kk["tflops"] / mfma_attainable(peaks), 5)
         else:
             kk["frac"] = round(kk["gbs"] / HBM_PEAK_GBS, 5)
             if peaks:
@@ -768,7 +824,7 @@ def attribution_pass(a, wl, runner, inp, stream, stages, steps, warmup, work, pe
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
                 "traffic": recorded_traffic(dominant, wl.name)}
     if peaks:
-        att = peaks["mfma_bf16_32x32x16_tflops"] if roof["unit"] == "TFLOP/s" else peaks["read_gbs"]
+        att = mfma_attainable(peaks) if roof["unit"] == "TFLOP/s" else peaks["read_gbs"]
         if roof["bound"] in ("mfma", "hbm"):
             roof["attainable_peak"] = att
             roof["frac_attainable"] = round(roof["achieved"] / att, 5)

@@ -1,6 +1,7 @@
 // Attainable peaks of one MI355X, measured rather than quoted: dense bf16
 // MFMA throughput of v_mfma_f32_32x32x16_bf16 (the instruction the attention
-// uses) with independent accumulators, and the HBM bandwidth of a plain
+// uses) with independent accumulators, on slowly varying and on
+// pseudo-random operands, and the HBM bandwidth of a plain
 // 16-byte copy and of a streaming read over buffers far larger than the
 // 256 MB Infinity Cache.  Prints one JSON object on stdout.
 #include <hip/hip_runtime.h>
@@ -21,14 +22,35 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
   } while (0)
 
 constexpr int kAcc = 8;  // independent accumulators per wave
+constexpr int kOps = 4;  // distinct A and B operands per wave
 
+// Value in [-1, 1) from a 32-bit integer hash (splitmix-style finaliser).
+__device__ inline float hash_unit(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return (float)(x >> 8) * (1.0f / 8388608.0f) - 1.0f;
+}
+
+// SMOOTH = 1: slowly varying operands (few bits toggle between MFMAs);
+// SMOOTH = 0: pseudo-random operands, rotated every product like the K/V
+// fragments of the attention -- the rate that real data sees, since the
+// chip lowers its clock when more bits toggle.
+template <int SMOOTH>
 __global__ __launch_bounds__(256) void mfma_loop(float *sink, int iters) {
-  bf16x8 a, b;
+  bf16x8 a[kOps], b[kOps];
+  const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    a[i] = (__bf16)(0.001f * (float)(threadIdx.x + i));
-    b[i] = (__bf16)(0.002f * (float)i);
-  }
+  for (int o = 0; o < kOps; ++o)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      a[o][i] = SMOOTH ? (__bf16)(0.001f * (float)(threadIdx.x + i))
+                       : (__bf16)hash_unit(t * 64u + (uint32_t)(o * 8 + i));
+      b[o][i] = SMOOTH ? (__bf16)(0.002f * (float)i)
+                       : (__bf16)hash_unit(t * 64u + 32u + (uint32_t)(o * 8 + i));
+    }
   f32x16 c[kAcc];
 #pragma unroll
   for (int j = 0; j < kAcc; ++j)
@@ -36,7 +58,8 @@ __global__ __launch_bounds__(256) void mfma_loop(float *sink, int iters) {
     for (int e = 0; e < 16; ++e) c[j][e] = 0.f;
   for (int it = 0; it < iters; ++it)
 #pragma unroll
-    for (int j = 0; j < kAcc; ++j) c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[j], 0, 0, 0);
+    for (int j = 0; j < kAcc; ++j)
+      c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j % kOps], b[(j / 2) % kOps], c[j], 0, 0, 0);
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < kAcc; ++j) s += c[j][0];
@@ -91,7 +114,10 @@ int main() {
   const int mblocks = cus * 4, iters = 4096;
   CHECK(hipMalloc(&sink, (size_t)mblocks * 256 * sizeof(float)));
   const float mfma_ms = best_ms([&] {
-    hipLaunchKernelGGL(mfma_loop, dim3(mblocks), dim3(256), 0, 0, sink, iters);
+    hipLaunchKernelGGL(mfma_loop<1>, dim3(mblocks), dim3(256), 0, 0, sink, iters);
+  }, 3);
+  const float mfma_rnd_ms = best_ms([&] {
+    hipLaunchKernelGGL(mfma_loop<0>, dim3(mblocks), dim3(256), 0, 0, sink, iters);
   }, 3);
   const double mfma_flops = (double)mblocks * 4 * iters * kAcc * (2.0 * 32 * 32 * 16);
 
@@ -110,8 +136,9 @@ int main() {
     hipLaunchKernelGGL(read16, dim3(sblocks), dim3(256), 0, 0, a, n, (uint32_t *)sink);
   }, 5);
   printf("{\"device\": \"%s\", \"cus\": %d, \"mfma_bf16_32x32x16_tflops\": %.1f, "
-         "\"copy_gbs\": %.1f, \"read_gbs\": %.1f}\n",
+         "\"mfma_bf16_32x32x16_random_tflops\": %.1f, \"copy_gbs\": %.1f, \"read_gbs\": %.1f}\n",
          prop.gcnArchName, cus, mfma_flops / (mfma_ms * 1e-3) / 1e12,
+         mfma_flops / (mfma_rnd_ms * 1e-3) / 1e12,
          2.0 * bytes / (copy_ms * 1e-3) / 1e9, (double)bytes / (read_ms * 1e-3) / 1e9);
   CHECK(hipFree(a));
   CHECK(hipFree(b));
