@@ -326,8 +326,9 @@ hipError_t launch_rerotate_deviation(int dtype, int style, void *k, const int32_
 // candidate w cw + 64 i + l: every load is one coalesced 256-byte run, and the
 // scores stay in registers for up to KPT rounds (KPT = 0: re-read every pass).
 //   1. MSB-first radix select over the order-preserving uint32 key of each
-//      fp32 score, 8 bits per pass with an LDS histogram (one atomic per wave
-//      for each of its first two distinct bins, then one per lane).  The select
+//      fp32 score, 8 bits per pass with an LDS histogram (a wave counts its
+//      first two distinct bins in registers over all its rounds and adds them
+//      once per pass; other bins one atomic per lane).  The select
 //      stops at the first
 //      pass whose boundary bin holds exactly the keys still missing: then the
 //      whole bin is selected.
@@ -352,23 +353,40 @@ __host__ __device__ constexpr int topk_rounds(int m) {
   return ((m + kTopkWaves - 1) / kTopkWaves + kWave - 1) / kWave;
 }
 
-// hist[bin] += 1 for every lane with bin >= 0: one atomic per bin for the
-// first two distinct bins of the wave (most scores share their leading bits,
-// so in the first passes a wave seldom spans more), then one per lane.
-__device__ inline void wave_hist_add(uint32_t *hist, int bin) {
-  const int lane = (int)(threadIdx.x & (kWave - 1));
-  uint64_t pending = __ballot(bin >= 0);
+// A wave's contribution to the LDS histogram of one radix pass.  Most scores
+// share their leading bits (the deviation tiers), so a wave's keys fall into
+// very few bins: the first two distinct bins it meets are counted in
+// registers over all of its rounds and added with one atomic each when the
+// pass ends (flush); keys in any other bin add one atomic per lane.  Atomics
+// of 16 waves on the same one or two LDS words, one per wave and round,
+// serialised the pass before (26.6k of the 66k cycles at 32k candidates).
+struct WaveHist {
+  int bin[2] = {-1, -1};
+  uint32_t cnt[2] = {0u, 0u};
+
+  __device__ void add(uint32_t *hist, int b) {
+    const int lane = (int)(threadIdx.x & (kWave - 1));
+    uint64_t pending = __ballot(b >= 0);
 #pragma unroll
-  for (int round = 0; round < 2; ++round) {
-    if (!pending) return;
-    const int leader = __builtin_ctzll(pending);
-    const int lb = __builtin_amdgcn_readlane(bin, leader);
-    const uint64_t same = __ballot(bin == lb);
-    if (lane == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(same));
-    pending &= ~same;
+    for (int j = 0; j < 2; ++j) {
+      if (!pending) return;
+      if (bin[j] < 0) {  // first use of this slot: the lowest pending lane's bin
+        bin[j] = __builtin_amdgcn_readlane(b, __builtin_ctzll(pending));
+      }
+      const uint64_t same = __ballot(b == bin[j]);
+      cnt[j] += (uint32_t)__popcll(same);
+      pending &= ~same;
+    }
+    if ((pending >> lane) & 1ull) atomicAdd(&hist[b], 1u);
   }
-  if ((pending >> lane) & 1ull) atomicAdd(&hist[bin], 1u);
-}
+  __device__ void flush(uint32_t *hist) const {
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (bin[j] >= 0 && cnt[j]) atomicAdd(&hist[bin[j]], cnt[j]);
+    }
+  }
+};
 
 // one_m / one_k: for a single request, its candidate and selected counts
 // (known on the host), so the scores are loaded without first waiting for
@@ -425,6 +443,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     const int shift = 24 - 8 * pass;
     if (tid < 256) hist[tid] = 0;
     __syncthreads();  // also: every thread has read the previous pass's sh_*
+    WaveHist wh;
 #pragma unroll kUnroll
     for (int i = 0; i < iters; ++i) {
       int bin = -1;
@@ -432,8 +451,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
         const uint32_t key = key_at(i);
         if ((key & mask) == prefix) bin = (int)((key >> shift) & 255u);
       }
-      wave_hist_add(hist, bin);
+      wh.add(hist, bin);
     }
+    wh.flush(hist);
     __syncthreads();
     if (tid < kWave) {
       uint32_t h[4];
