@@ -128,6 +128,9 @@ def parse_args(argv=None):
                     help="step order of cb_blend_layer: select-first scores V and selects "
                          "first, then one launch writes the rows of S and re-rotates only the "
                          "others; auto lets the library choose")
+    ap.add_argument("--select-in-launch", type=int, default=0,
+                    help="1: the top-k runs inside the deviation launch (a zero-filled "
+                         "workspace, CB_LAYER_WORKSPACE_ZEROED); 0: its own launch")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="rough budget of the CPU oracle baseline (0 disables it)")
     ap.add_argument("--attainable", type=int, default=1,
@@ -552,7 +555,7 @@ def main():
     runner = PL.BlendRunner(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.torch_dtype,
                             wl.request_lengths, wl.r1_pct, wl.r2_pct, L, wl.rope_theta,
                             schedule=a.schedule, dev_source=a.dev_source, device="cuda",
-                            order=a.order)
+                            order=a.order, in_launch_select=bool(a.select_in_launch))
     if a.order == "select-first" and a.dev_source != "v":
         raise SystemExit("--order select-first scores V only (a key deviation reads the "
                          "re-rotated keys)")
@@ -573,7 +576,7 @@ def main():
                                         dev=o["dev"], sel_local=o["sel_local"],
                                         sel_global=o["sel_global"], out=o["out"],
                                         workspace=runner.workspace, dev_source=runner.dev_source,
-                                        order=runner.order))
+                                        order=runner.order, flags=runner.flags))
     # the attribution pass times the entry points of the order the library runs
     # (the same for every layer: it depends on the cache size and the source)
     select_first = prepared[0].resolved_order() == B.CB_ORDER_SELECT_FIRST
@@ -669,6 +672,8 @@ def main():
                    "order": f"{a.order}: " + ("select, then rotate-or-replace" if select_first
                                               else "rotate, select, fuse"),
                    "launch": "hip graph replay" if a.graph else "stream launches",
+                   "select": ("top-k inside the deviation launch" if runner.flags
+                              else "top-k in its own launch"),
                    "step_timing": "median of per-step HIP event pairs; K/V restored from a "
                                   "pristine copy, 512 MiB read (L2 and MALL flush) and a spin "
                                   "that outlasts the host's enqueue of the step, before each "

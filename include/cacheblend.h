@@ -345,12 +345,28 @@ typedef struct cb_layer_args {
   size_t workspace_bytes;
   int32_t dev_source;   /* cb_dev_source; CB_DEV_V is the score of [Derivations] */
   int32_t order;        /* a cb_order value; 0 is CB_ORDER_AUTO */
+  uint32_t flags;       /* 0 or CB_LAYER_WORKSPACE_ZEROED (other bits: INVALID_ARG) */
 } cb_layer_args;
+
+/* cb_layer_args.flags: the caller filled the workspace with zeros before its
+ * first use by cb_blend_layer and has used it since only for cb_blend_layer
+ * calls.  The last CB_SELECT_COUNTER_BYTES of the workspace then hold one
+ * arrival counter per request, which every call leaves at zero, and for a V
+ * deviation with at most CB_SELECT_COUNTER_BYTES / 4 requests the top-k runs
+ * inside the deviation launch (the workgroup that scores a request's last
+ * candidates selects its rows): one launch fewer per layer, the same results
+ * bit for bit.  The attention then uses the workspace without those bytes.
+ * Ignored with a workspace smaller than CB_SELECT_COUNTER_BYTES.  Counters
+ * that are not zero give wrong selections (a request selected before all of
+ * its scores are written, or never); nothing waits on them, so nothing hangs. */
+#define CB_LAYER_WORKSPACE_ZEROED 1u
+#define CB_SELECT_COUNTER_BYTES 4096u
 
 /*
  * cb_blend_layer -- one layer: cb_rerotate (in place, when delta != NULL) ->
  * cb_kv_deviation_topk (keys scored after their re-rotation) ->
- * cb_fuse_scatter -> cb_partial_attn, all on `stream`.  With the order
+ * cb_fuse_scatter -> cb_partial_attn, all on `stream` (with
+ * CB_LAYER_WORKSPACE_ZEROED the deviation and the top-k share one launch).  With the order
  * CB_ORDER_SELECT_FIRST (or CB_ORDER_AUTO choosing it): cb_kv_deviation_topk
  * (V) -> cb_rerotate_fuse -> cb_partial_attn, with the same results bit for
  * bit (INVALID_ARG for CB_ORDER_SELECT_FIRST with a key deviation source,
@@ -380,14 +396,18 @@ cb_status cb_blend_layer_order(const cb_layer_args *args, int32_t *order);
  * partials and arrival counters live in a static device array of the library
  * of CB_NOALLOC_SCRATCH_BYTES, one per GPU, held from the library's first use
  * on that GPU until the process ends.  Long rows are split only by plans
- * that fit in it (where cb_blend_layer with a larger workspace would split
+ * that fit in it, less its last CB_SELECT_COUNTER_BYTES (where cb_blend_layer with a larger workspace would split
  * further, this call keeps the best plan that fits, or none; outputs then
  * agree to rounding, selections and fused rows bit for bit); a plan larger
  * than the array is refused with CB_ERR_UNSUPPORTED before anything is
- * enqueued.  The call allocates and frees nothing; its first call on a GPU
+ * enqueued.  The array starts zero-filled, so the call always runs the top-k
+ * inside the deviation launch as CB_LAYER_WORKSPACE_ZEROED describes (its
+ * last CB_SELECT_COUNTER_BYTES hold those counters; args->flags may be 0 or
+ * that flag).  The call allocates and frees nothing; its first call on a GPU
  * looks up the array's device address there (a HIP symbol query).
- * The array keeps the last call's contents; each call clears the counters it
- * uses in its own fuse launch.  Every call in a process shares the GPU's one
+ * The array keeps the last call's contents; each call clears the attention
+ * counters it uses in its own fuse launch and leaves the selection counters
+ * at zero.  Every call in a process shares the GPU's one
  * array, so calls that may overlap on one GPU (different streams or host
  * threads) race: order them, e.g. on one stream.
  */
@@ -401,7 +421,7 @@ const char *cb_last_error(void);
 /* ABI revision of this header (bumped on any incompatible change). */
 int32_t cb_abi_version(void);
 
-#define CB_ABI_VERSION 6
+#define CB_ABI_VERSION 7
 
 #ifdef __cplusplus
 }

@@ -22,6 +22,8 @@ CB_DTYPE_F32, CB_DTYPE_BF16 = 0, 1
 ROPE_HALF, ROPE_INTERLEAVED = 0, 1
 CB_DEV_V, CB_DEV_K, CB_DEV_KV = 0, 1, 2
 CB_ATTN_COUNTERS_ZERO = 1
+CB_LAYER_WORKSPACE_ZEROED = 1
+CB_SELECT_COUNTER_BYTES = 4096
 CB_ORDER_AUTO, CB_ORDER_ROTATE_FIRST, CB_ORDER_SELECT_FIRST = 0, 1, 2
 ORDERS = {"auto": CB_ORDER_AUTO, "rotate-first": CB_ORDER_ROTATE_FIRST,
           "select-first": CB_ORDER_SELECT_FIRST}
@@ -52,7 +54,8 @@ class LayerArgs(ctypes.Structure):
                 ("dev", ctypes.c_void_p), ("sel_local", ctypes.c_void_p),
                 ("sel_global", ctypes.c_void_p), ("out", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("dev_source", ctypes.c_int32), ("order", ctypes.c_int32)]
+                ("dev_source", ctypes.c_int32), ("order", ctypes.c_int32),
+                ("flags", ctypes.c_uint32)]
 
 
 class AttnPlan(ctypes.Structure):
@@ -278,10 +281,12 @@ def describe_plan(g: Geom, rb: RaggedBatch, mfma: int = 1, key_split: int = 1,
 
 
 def workspace_tensor(nbytes: int, device="cuda") -> Optional[torch.Tensor]:
-    """A device buffer of at least nbytes (16-byte aligned), or None for 0."""
+    """A device buffer of at least nbytes (16-byte aligned), zero-filled, or
+    None for 0.  Zero-filled, it may be passed to cb_blend_layer with
+    CB_LAYER_WORKSPACE_ZEROED."""
     if nbytes <= 0:
         return None
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
 def _ws(ws: Optional[torch.Tensor]):
@@ -319,12 +324,15 @@ def partial_attn_with_plan(g: Geom, rb: RaggedBatch, plan: dict, out, q_c, sel_l
 def blend_layer(g: Geom, rb: RaggedBatch, *, k, v, k_new_c, v_new_c, q_c, delta, cand_idx,
                 rope_theta: float, rope_style: int, softmax_scale: float, dev, sel_local,
                 sel_global, out, workspace: Optional[torch.Tensor] = None,
-                dev_source: int = CB_DEV_V, order: int = CB_ORDER_AUTO, stream=None):
+                dev_source: int = CB_DEV_V, order: int = CB_ORDER_AUTO, flags: int = 0,
+                stream=None):
+    """cb_blend_layer.  flags: CB_LAYER_WORKSPACE_ZEROED when the workspace was
+    zero-filled (workspace_tensor) and used since only by cb_blend_layer."""
     args = LayerArgs(g, rb.struct(), _dev(k), _dev(v), _dev(k_new_c), _dev(v_new_c), _dev(q_c),
                      _dev(delta, torch.int32), _dev(cand_idx, torch.int32), rope_theta,
                      rope_style, softmax_scale, _dev(dev, torch.float32),
                      _dev(sel_local, torch.int32), _dev(sel_global, torch.int32), _dev(out),
-                     *_ws(workspace), dev_source, order)
+                     *_ws(workspace), dev_source, order, flags)
     check(lib().cb_blend_layer(ctypes.byref(args), _stream(stream)))
 
 
@@ -338,7 +346,7 @@ def blend_layer_noalloc(g: Geom, rb: RaggedBatch, *, k, v, k_new_c, v_new_c, q_c
                      _dev(delta, torch.int32), _dev(cand_idx, torch.int32), rope_theta,
                      rope_style, softmax_scale, _dev(dev, torch.float32),
                      _dev(sel_local, torch.int32), _dev(sel_global, torch.int32), _dev(out),
-                     None, 0, dev_source, order)
+                     None, 0, dev_source, order, 0)
     check(lib().cb_blend_layer_noalloc(ctypes.byref(args), _stream(stream)))
 
 
@@ -349,14 +357,14 @@ class PreparedLayer:
     def __init__(self, g: Geom, rb: RaggedBatch, *, k, v, k_new_c, v_new_c, q_c, delta,
                  cand_idx, rope_theta, rope_style, softmax_scale, dev, sel_local, sel_global,
                  out, workspace: Optional[torch.Tensor] = None, dev_source: int = CB_DEV_V,
-                 order: int = CB_ORDER_AUTO):
+                 order: int = CB_ORDER_AUTO, flags: int = 0):
         self._keep = (rb, k, v, k_new_c, v_new_c, q_c, delta, cand_idx, dev, sel_local,
                       sel_global, out, workspace)
         self.args = LayerArgs(g, rb.struct(), _dev(k), _dev(v), _dev(k_new_c), _dev(v_new_c),
                               _dev(q_c), _dev(delta, torch.int32), _dev(cand_idx, torch.int32),
                               rope_theta, rope_style, softmax_scale, _dev(dev, torch.float32),
                               _dev(sel_local, torch.int32), _dev(sel_global, torch.int32),
-                              _dev(out), *_ws(workspace), dev_source, order)
+                              _dev(out), *_ws(workspace), dev_source, order, flags)
         self.ref = ctypes.byref(self.args)
 
     def resolved_order(self) -> int:

@@ -699,6 +699,9 @@ namespace {
 // HIP call; `after` receives the step order.
 cb_status validate_blend(const cb_layer_args *a, bool &after) {
   if (!a) return fail(CB_ERR_INVALID_ARG, "args is NULL");
+  if (a->flags & ~CB_LAYER_WORKSPACE_ZEROED)
+    return fail(CB_ERR_INVALID_ARG, "flags 0x%x: only CB_LAYER_WORKSPACE_ZEROED is defined",
+                a->flags);
   const cb_geom *geom = &a->geom;
   const cb_ragged *rg = &a->rg;
   CB_TRY(check_ragged(rg, true, true, true));
@@ -716,28 +719,46 @@ cb_status validate_blend(const cb_layer_args *a, bool &after) {
 }
 
 // The launches of one validated layer; the attention's split partials and
-// arrival counters go to `ws` (ws_bytes; NULL / 0: no split).
+// arrival counters go to `ws` (ws_bytes; NULL / 0: no split).  sel_cnt: the
+// selection's per-request arrival counters, all zero (NULL: the top-k is its
+// own launch); used for a V deviation with at most kSelectMaxRequests
+// requests.
 cb_status launch_blend(const cb_layer_args *a, bool after, void *ws, size_t ws_bytes,
-                       hipStream_t s) {
+                       unsigned *sel_cnt, hipStream_t s) {
   const cb_geom *geom = &a->geom;
   const cb_ragged *rg = &a->rg;
   const int64_t n_tok = rg->h_tok_off[rg->n_req];
   const int32_t k_total = rg->h_sel_off[rg->n_req];
   const int32_t m = rg->h_cand_off[rg->n_req];
   const bool rotate = a->delta && n_tok > 0;
+  const bool fits_shared = cb::rerotate_deviation_fits(geom->dtype, geom->n_kv_heads,
+                                                       geom->head_dim);
+  // the top-k inside the deviation launch: a V score, counters to count
+  // arrivals in, and a re-rotation (if any) that can share the launch
+  const bool in_launch = sel_cnt && a->dev_source == CB_DEV_V && m > 0 &&
+                         rg->n_req <= cb::kSelectMaxRequests && (after || !rotate || fits_shared);
   // The plan first: it only reads host mirrors, and a plan that would not fit
   // the workspace must stop the call before anything is enqueued.
   const cb::AttnPlan plan = plan_attn(geom, rg, ws ? ws_bytes : 0);
   if (plan.split && plan.ws_bytes > ws_bytes)
     return fail(CB_ERR_UNSUPPORTED, "the attention split needs %zu bytes of workspace, more than "
                 "the %zu available", plan.ws_bytes, ws_bytes);
-  if (after) {
+  if (in_launch) {
+    // score and select in one launch; rotate first: the re-rotation shares it
+    const bool rot_here = rotate && !after;
+    CB_TRY(hip_status(cb::launch_deviation_select(
+                          geom->dtype, a->rope_style, rot_here ? a->k : nullptr, a->delta, n_tok,
+                          geom->n_kv_heads, geom->head_dim,
+                          rope_table(geom->head_dim, a->rope_theta), a->v_new_c, a->v,
+                          a->cand_idx, a->dev, rg->n_req, rg->cand_off, rg->sel_off,
+                          rg->h_cand_off, a->sel_local, a->sel_global, sel_cnt, s),
+                      rot_here ? "rerotate+deviation+topk" : "deviation+topk"));
+  } else if (after) {
     // the V deviation and the top-k first; the re-rotation joins the fuse
     CB_TRY(hip_status(launch_dev_source(geom, CB_DEV_V, a->k_new_c, a->k, a->v_new_c, a->v,
                                         a->cand_idx, a->dev, m, s),
                       "deviation"));
-  } else if (a->dev_source == CB_DEV_V && rotate &&
-             cb::rerotate_deviation_fits(geom->dtype, geom->n_kv_heads, geom->head_dim)) {
+  } else if (a->dev_source == CB_DEV_V && rotate && fits_shared) {
     // independent K and V work in one launch (a key deviation instead reads
     // the re-rotated keys, so it follows the re-rotation)
     CB_TRY(hip_status(cb::launch_rerotate_deviation(
@@ -755,7 +776,7 @@ cb_status launch_blend(const cb_layer_args *a, bool after, void *ws, size_t ws_b
                                         a->cand_idx, a->dev, m, s),
                       "deviation"));
   }
-  if (k_total > 0)
+  if (k_total > 0 && !in_launch)
     CB_TRY(hip_status(cb::launch_topk(rg->n_req, a->dev, a->cand_idx, rg->cand_off, rg->sel_off,
                                       a->sel_local, a->sel_global, rg->h_cand_off,
                                       rg->h_sel_off, s),
@@ -782,6 +803,18 @@ cb_status launch_blend(const cb_layer_args *a, bool after, void *ws, size_t ws_b
   return run_attn(geom, rg, plan, a->out, a->q_c, a->sel_local, a->sel_global, a->k, a->v,
                   a->softmax_scale, ws, clear, s);
 }
+
+// The selection counters at the end of a workspace of `bytes` (the region
+// CB_SELECT_COUNTER_BYTES long, 256-byte aligned); the bytes before them
+// stay for the attention.
+unsigned *select_counters(void *ws, size_t &bytes) {
+  if (!ws || bytes < CB_SELECT_COUNTER_BYTES + 256) return nullptr;
+  const size_t off = (bytes - CB_SELECT_COUNTER_BYTES) & ~(size_t)255;
+  bytes = off;
+  return reinterpret_cast<unsigned *>(static_cast<char *>(ws) + off);
+}
+static_assert(CB_SELECT_COUNTER_BYTES / 4 == cb::kSelectMaxRequests,
+              "one selection counter per request");
 }  // namespace
 
 CB_EXPORT cb_status cb_blend_layer(const cb_layer_args *a, void *stream) {
@@ -790,8 +823,11 @@ CB_EXPORT cb_status cb_blend_layer(const cb_layer_args *a, void *stream) {
   bool after = false;
   CB_TRY(validate_blend(a, after));
   CB_TRY(need_ptr(a->workspace, "workspace", a->workspace_bytes > 0));
-  return launch_blend(a, after, a->workspace, a->workspace ? a->workspace_bytes : 0,
-                      (hipStream_t)stream);
+  void *ws = a->workspace;
+  size_t ws_bytes = ws ? a->workspace_bytes : 0;
+  unsigned *sel_cnt =
+      (a->flags & CB_LAYER_WORKSPACE_ZEROED) ? select_counters(ws, ws_bytes) : nullptr;
+  return launch_blend(a, after, ws, ws_bytes, sel_cnt, (hipStream_t)stream);
 }
 
 static_assert(CB_NOALLOC_SCRATCH_BYTES == cb::kNoAllocScratchBytes,
@@ -806,7 +842,10 @@ CB_EXPORT cb_status cb_blend_layer_noalloc(const cb_layer_args *a, void *stream)
                 "library's static scratch): pass workspace NULL and workspace_bytes 0");
   void *scratch = nullptr;
   CB_TRY(hip_status(cb::noalloc_scratch(&scratch), "static scratch address"));
-  return launch_blend(a, after, scratch, cb::kNoAllocScratchBytes, (hipStream_t)stream);
+  // the array starts zero-filled and every call leaves its selection counters at zero
+  size_t bytes = cb::kNoAllocScratchBytes;
+  unsigned *sel_cnt = select_counters(scratch, bytes);
+  return launch_blend(a, after, scratch, bytes, sel_cnt, (hipStream_t)stream);
 }
 
 CB_EXPORT const char *cb_status_str(cb_status status) {

@@ -159,9 +159,8 @@ __device__ inline bool locate_unit(const AttnParams &p, int u, UnitPos &up) {
   return false;
 }
 
-// Wave-count encodings of s_waitcnt (gfx9): vmcnt(n) with the LGKM and EXP
-// counters left free, and lgkmcnt(0) with the VM counter left free.
-__device__ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// s_waitcnt operand for lgkmcnt(0) with the VM counter left free (gfx9
+// encoding; vmcnt(n) is waitcnt_vm).
 constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
 
 // 16 bytes per lane from global memory straight into LDS: lane l writes
@@ -180,17 +179,11 @@ __device__ inline void dma16(const char *base, uint32_t off, uint32_t lds_byte) 
 #pragma clang diagnostic pop
 
 // Split partials pass between workgroups on different XCDs, whose L2 caches
-// are not coherent with each other.  They are stored and loaded only as
-// relaxed agent-scope atomics, which the hardware performs at the coherence
-// point all XCDs share; the arrival counter is such an atomic too.  So no
-// fence has to write back or invalidate a whole L2 (an agent-scope fence
-// does both, and in every workgroup it tripled the launch time).
-template <typename T> __device__ inline void store_agent(T *p, T v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <typename T> __device__ inline T load_agent(const T *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// are not coherent with each other.  They are stored and loaded only with
+// store_agent / load_agent (relaxed agent-scope atomics, performed at the
+// coherence point all XCDs share); the arrival counter is such an atomic too.
+// So no fence has to write back or invalidate a whole L2 (an agent-scope
+// fence does both, and in every workgroup it tripled the launch time).
 
 // Lanes l and l ^ 32 hold the two halves of one query column.  gfx950's
 // v_permlane32_swap trades the upper 32 lanes of one register with the lower

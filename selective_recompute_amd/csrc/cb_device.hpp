@@ -13,6 +13,21 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
+// Relaxed accesses at agent scope: performed at the coherence point that
+// all XCDs share, so a workgroup on another XCD of the same launch sees them
+// (the XCDs' L2 caches are not coherent with each other).
+template <typename T> __device__ inline void store_agent(T *p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T> __device__ inline T load_agent(const T *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// s_waitcnt operand that waits until at most n vector-memory operations of
+// the wave are outstanding (loads, stores and copies to LDS; gfx9 encoding,
+// the other counters left alone).
+__device__ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 // 16-byte vector of storage elements, converted to/from fp32.
 template <typename T> struct Vec16;
 

@@ -44,6 +44,19 @@ hipError_t launch_topk(int32_t n_req, const float *dev, const int32_t *cand_idx,
                        int32_t *sel_global, const int32_t *h_cand_off, const int32_t *h_sel_off,
                        hipStream_t stream);
 
+// V deviation and top-k in one launch; with k != NULL the same launch also
+// re-rotates K in place (only where rerotate_deviation_fits).  cnt: one
+// arrival counter per request, zero before the launch and left at zero by
+// it.  h_cand_off: host mirror (grid and register-path sizing).
+constexpr int kSelectMaxRequests = 1024;  // counters in CB_SELECT_COUNTER_BYTES
+hipError_t launch_deviation_select(int dtype, int style, void *k, const int32_t *delta,
+                                   int64_t n_tok, int32_t n_kv_heads, int32_t head_dim,
+                                   const RopeTable &tab, const void *v_new_c, const void *v_old,
+                                   const int32_t *cand_idx, float *dev, int32_t n_req,
+                                   const int32_t *cand_off, const int32_t *sel_off,
+                                   const int32_t *h_cand_off, int32_t *sel_local,
+                                   int32_t *sel_global, unsigned *cnt, hipStream_t stream);
+
 // Also sets clear[0 .. n_clear) to zero (the attention's arrival counters;
 // clear may be NULL when n_clear is 0).
 hipError_t launch_fuse(void *k_fused, void *v_fused, const void *k_new_c,

@@ -93,12 +93,12 @@ __device__ inline void unit_pieces(int j0, int hd, int &p0, int &p1) {
   p1 = STYLE == 0 ? hd / 2 + j0 : 2 * j0 + VP;
 }
 
+// tid: the thread's index among the block's units_per_row * tok_per_iter threads.
 template <typename T, int STYLE>
 __device__ inline void rerotate_block(T *__restrict__ k_out, const T *__restrict__ k_in,
                                       const int32_t *__restrict__ delta, const RotGeom &gm,
-                                      const RopeTable &tab, int block) {
+                                      const RopeTable &tab, int64_t block, int tid) {
   constexpr int VP = Vec16<T>::N;  // pairs per unit
-  const int tid = threadIdx.x;
   if (tid >= gm.units_per_row * gm.tok_per_iter) return;
   const int unit = tid % gm.units_per_row;
   const int slot = tid / gm.units_per_row;
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(1024) void rerotate_kernel(T *__restrict__ k_out,
                                                         const T *__restrict__ k_in,
                                                         const int32_t *__restrict__ delta,
                                                         RotGeom gm, RopeTable tab) {
-  rerotate_block<T, STYLE>(k_out, k_in, delta, gm, tab, blockIdx.x);
+  rerotate_block<T, STYLE>(k_out, k_in, delta, gm, tab, blockIdx.x, threadIdx.x);
 }
 
 template <typename T, int STYLE>
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(256) void rerotate_deviation_kernel(
     int64_t rot_blocks, const T *__restrict__ v_new_c, const T *__restrict__ v_old,
     const int32_t *__restrict__ cand_idx, float *__restrict__ dev, int64_t m, int32_t row_elems) {
   if ((int64_t)blockIdx.x < rot_blocks)
-    rerotate_block<T, STYLE>(k, k, delta, gm, tab, blockIdx.x);
+    rerotate_block<T, STYLE>(k, k, delta, gm, tab, blockIdx.x, threadIdx.x);
   else
     deviation_block<T, 1>(v_new_c, v_old, nullptr, nullptr, cand_idx, dev, m, row_elems,
                           blockIdx.x - rot_blocks, gridDim.x - rot_blocks);
@@ -388,25 +388,23 @@ struct WaveHist {
   }
 };
 
-// one_m / one_k: for a single request, its candidate and selected counts
-// (known on the host), so the scores are loaded without first waiting for
-// the offsets; -1 with several requests.
-template <int KPT>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(
-    const float *__restrict__ dev, const int32_t *__restrict__ cand_idx,
-    const int32_t *__restrict__ cand_off, const int32_t *__restrict__ sel_off,
-    int32_t *__restrict__ sel_local, int32_t *__restrict__ sel_global, int32_t one_m,
-    int32_t one_k) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t sh_digit, sh_above, sh_count;
-  __shared__ uint32_t wave_tot[2][kTopkWaves];
+// Shared memory of one workgroup's top-k.
+struct TopkShared {
+  uint32_t hist[256];
+  uint32_t digit, above, count;
+  uint32_t wave_tot[2][kTopkWaves];
+};
 
-  const int r = blockIdx.x;
-  const bool one = one_m >= 0;
-  const int c0 = one ? 0 : cand_off[r];
-  const int m = one ? one_m : cand_off[r + 1] - c0;
-  const int s0 = one ? 0 : sel_off[r];
-  const int k = one ? one_k : sel_off[r + 1] - s0;
+// Selects k of the m scores dev[c0 .. c0 + m) of one request (candidates
+// cand_idx[c0 ..]) into sel_local / sel_global [s0 .. s0 + k), ascending,
+// with the whole 1024-thread workgroup.  AGENT: the scores were written by
+// other workgroups of the same launch and are read at agent scope.  May be
+// called again by the same workgroup for another request.
+template <int KPT, bool AGENT>
+__device__ __attribute__((always_inline)) void topk_select(TopkShared &sh, const float *__restrict__ dev,
+                            const int32_t *__restrict__ cand_idx, int c0, int m, int s0, int k,
+                            int32_t *__restrict__ sel_local, int32_t *__restrict__ sel_global) {
+  __syncthreads();  // a previous call's readers of sh are done
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   if (k <= 0) return;
   if (k >= m) {  // every candidate is selected
@@ -420,6 +418,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   const int wb = wave * rounds * kWave;                  // first candidate of this wave
   const int n_w = max(0, min(m - wb, rounds * kWave));   // candidates of this wave
   const float *dw = dev + c0 + wb + lane;
+  auto score = [&](int off) -> float {  // scores another workgroup may have written: agent scope
+    return AGENT ? __uint_as_float(load_agent(reinterpret_cast<const uint32_t *>(dw + off)))
+                 : dw[off];
+  };
   const int32_t *cw = cand_idx + c0 + wb + lane;
   uint32_t keys[KPT > 0 ? KPT : 1];
   int32_t cands[KPT > 0 ? KPT : 1];  // loaded with the scores: no load left at the end
@@ -427,13 +429,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
 #pragma unroll
     for (int i = 0; i < (KPT > 0 ? KPT : 1); ++i) {
       const bool ok = kWave * i + lane < n_w;
-      keys[i] = ok ? order_key(dw[kWave * i]) : 0u;
+      keys[i] = ok ? order_key(score(kWave * i)) : 0u;
       cands[i] = ok ? cw[kWave * i] : 0;
     }
   }
   auto key_at = [&](int i) -> uint32_t {  // only for candidates of this wave
     if (KPT > 0) return keys[i];
-    return order_key(dw[kWave * i]);
+    return order_key(score(kWave * i));
   };
   const int iters = KPT > 0 ? KPT : rounds;  // uniform over the workgroup
   constexpr int kUnroll = KPT > 0 ? KPT : 1;  // register path: fully unrolled
@@ -441,7 +443,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   uint32_t prefix = 0, mask = 0, krem = (uint32_t)k;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    if (tid < 256) hist[tid] = 0;
+    if (tid < 256) sh.hist[tid] = 0;
     __syncthreads();  // also: every thread has read the previous pass's sh_*
     WaveHist wh;
 #pragma unroll kUnroll
@@ -451,14 +453,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
         const uint32_t key = key_at(i);
         if ((key & mask) == prefix) bin = (int)((key >> shift) & 255u);
       }
-      wh.add(hist, bin);
+      wh.add(sh.hist, bin);
     }
-    wh.flush(hist);
+    wh.flush(sh.hist);
     __syncthreads();
     if (tid < kWave) {
       uint32_t h[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) h[q] = hist[4 * tid + q];
+      for (int q = 0; q < 4; ++q) h[q] = sh.hist[4 * tid + q];
       const uint32_t tot = h[0] + h[1] + h[2] + h[3];
       uint32_t suf = tot;  // sum over this lane's bins and every higher lane's
 #pragma unroll
@@ -469,16 +471,16 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
       uint32_t above = suf - tot;
       if (above < krem && suf >= krem) {
         for (int q = 3; q >= 0; --q) {
-          if (above + h[q] >= krem) { sh_digit = 4 * tid + q; sh_above = above; sh_count = h[q]; break; }
+          if (above + h[q] >= krem) { sh.digit = 4 * tid + q; sh.above = above; sh.count = h[q]; break; }
           above += h[q];
         }
       }
     }
     __syncthreads();
-    prefix |= sh_digit << shift;
+    prefix |= sh.digit << shift;
     mask |= 255u << shift;
-    krem -= sh_above;
-    if (sh_count == krem) break;  // the whole boundary bin is selected
+    krem -= sh.above;
+    if (sh.count == krem) break;  // the whole boundary bin is selected
   }
   const uint32_t keep_eq = krem;  // keys of the boundary bin to keep, lowest index first
 
@@ -496,14 +498,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     n_eq += __popcll(__ballot(eq));
   }
   if (lane == 0) {
-    wave_tot[0][wave] = n_gt;
-    wave_tot[1][wave] = n_eq;
+    sh.wave_tot[0][wave] = n_gt;
+    sh.wave_tot[1][wave] = n_eq;
   }
   __syncthreads();
   uint32_t gt_before = 0, eq_before = 0;  // of the waves before this one
   for (int w = 0; w < wave; ++w) {
-    gt_before += wave_tot[0][w];
-    eq_before += wave_tot[1][w];
+    gt_before += sh.wave_tot[0][w];
+    eq_before += sh.wave_tot[1][w];
   }
   const uint64_t below = (1ull << lane) - 1ull;  // lanes before this one
 #pragma unroll kUnroll
@@ -527,6 +529,25 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   }
 }
 
+// one_m / one_k: for a single request, its candidate and selected counts
+// (known on the host), so the scores are loaded without first waiting for
+// the offsets; -1 with several requests.
+template <int KPT>
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(
+    const float *__restrict__ dev, const int32_t *__restrict__ cand_idx,
+    const int32_t *__restrict__ cand_off, const int32_t *__restrict__ sel_off,
+    int32_t *__restrict__ sel_local, int32_t *__restrict__ sel_global, int32_t one_m,
+    int32_t one_k) {
+  __shared__ TopkShared sh;
+  const int r = blockIdx.x;
+  const bool one = one_m >= 0;
+  const int c0 = one ? 0 : cand_off[r];
+  const int m = one ? one_m : cand_off[r + 1] - c0;
+  const int s0 = one ? 0 : sel_off[r];
+  const int k = one ? one_k : sel_off[r + 1] - s0;
+  topk_select<KPT, false>(sh, dev, cand_idx, c0, m, s0, k, sel_local, sel_global);
+}
+
 hipError_t launch_topk(int32_t n_req, const float *dev, const int32_t *cand_idx,
                        const int32_t *cand_off, const int32_t *sel_off, int32_t *sel_local,
                        int32_t *sel_global, const int32_t *h_cand_off, const int32_t *h_sel_off,
@@ -548,6 +569,128 @@ hipError_t launch_topk(int32_t n_req, const float *dev, const int32_t *cand_idx,
   else if (rounds <= 32) CB_TOPK(32);
   else CB_TOPK(0);
 #undef CB_TOPK
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// V deviation and top-k in one launch (cb_blend_layer on a workspace that
+// started zero-filled).  Workgroup b scores candidates [16 b, 16 b + 16), one
+// wave per row ([Derivations, "近似解"] score, as deviation_kernel), and
+// stores each score at agent scope.  Once those stores have completed it
+// adds 1 to the arrival counter of every request its rows belong to; the
+// workgroup that completes a request's count sets the counter back to zero
+// and selects that request's rows itself (topk_select), so the selection
+// needs no launch of its own and every launch leaves its counters at zero.
+// ROT: the same launch re-rotates K in place ([Derivations, "CacheBlend 中的
+// 应用"]) in the workgroups after the scoring ones, four 256-thread
+// re-rotation blocks each; the selections then run while the longer
+// re-rotation still streams.
+// ---------------------------------------------------------------------------
+constexpr int kSelRows = kTopkWaves;  // candidates scored per workgroup
+
+template <typename T, int KPT, int ROT, int STYLE>
+__global__ __launch_bounds__(kTopkThreads) void deviation_select_kernel(
+    const T *__restrict__ v_new_c, const T *__restrict__ v_old,
+    const int32_t *__restrict__ cand_idx, float *__restrict__ dev, int64_t m, int32_t row_elems,
+    const int32_t *__restrict__ cand_off, const int32_t *__restrict__ sel_off, int32_t n_req,
+    int32_t *__restrict__ sel_local, int32_t *__restrict__ sel_global, unsigned *__restrict__ cnt,
+    int64_t dev_blocks, T *__restrict__ k, const int32_t *__restrict__ delta, RotGeom gm,
+    RopeTable tab, int64_t rot_blocks) {
+  if (ROT && (int64_t)blockIdx.x >= dev_blocks) {  // uniform
+    const int64_t rb = ((int64_t)blockIdx.x - dev_blocks) * 4 + threadIdx.x / 256;
+    if (rb < rot_blocks) rerotate_block<T, STYLE>(k, k, delta, gm, tab, rb, threadIdx.x & 255);
+    return;
+  }
+  __shared__ TopkShared sh;
+  __shared__ int s_req[kSelRows];  // requests this workgroup completes (at most one per row)
+  __shared__ int s_n;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int64_t j0 = (int64_t)blockIdx.x * kSelRows;
+  const int64_t j1 = j0 + kSelRows < m ? j0 + kSelRows : m;
+  const int64_t j = j0 + wave;
+  if (j < m) {
+    const int64_t c = cand_idx[j];
+    float acc = sq_dist_share(v_new_c + j * row_elems, v_old + c * row_elems, lane,
+                              row_elems / Vec16<T>::N, 0.f);
+    acc = wave_sum(acc);
+    if (lane == 0) store_agent(reinterpret_cast<uint32_t *>(dev + j), __float_as_uint(acc));
+  }
+  if (threadIdx.x == 0) s_n = 0;
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's score has reached the coherence point
+  __syncthreads();
+  for (int r = threadIdx.x; r < n_req; r += kTopkThreads) {
+    const int c0 = cand_off[r], c1 = cand_off[r + 1];
+    if (c1 > c0 && c0 < j1 && c1 > j0) {
+      const unsigned need = (unsigned)((c1 - 1) / kSelRows - c0 / kSelRows + 1);
+      const unsigned prev =
+          __hip_atomic_fetch_add(cnt + r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (prev == need - 1) {
+        store_agent(cnt + r, 0u);
+        s_req[atomicAdd(&s_n, 1)] = r;
+      }
+    }
+  }
+  __syncthreads();
+  const int n_done = s_n;
+  for (int i = 0; i < n_done; ++i) {
+    const int r = s_req[i];
+    const int c0 = cand_off[r], s0 = sel_off[r];
+    topk_select<KPT, true>(sh, dev, cand_idx, c0, cand_off[r + 1] - c0, s0, sel_off[r + 1] - s0,
+                           sel_local, sel_global);
+  }
+}
+
+template <typename T, int KPT>
+static void deviation_select_typed(int style, void *k, const int32_t *delta, int64_t n_tok,
+                                   int32_t n_kv_heads, int32_t head_dim, const RopeTable &tab,
+                                   const void *v_new_c, const void *v_old,
+                                   const int32_t *cand_idx, float *dev, int64_t m,
+                                   int32_t n_req, const int32_t *cand_off,
+                                   const int32_t *sel_off, int32_t *sel_local,
+                                   int32_t *sel_global, unsigned *cnt, hipStream_t stream) {
+  const int64_t dev_blocks = (m + kSelRows - 1) / kSelRows;
+  const int32_t row_elems = n_kv_heads * head_dim;
+  int64_t rot_blocks = 0;
+  RotGeom gm{};
+  if (k) gm = rot_geom<T>(n_tok, 1, n_kv_heads, head_dim, rot_blocks);
+  const int64_t blocks = dev_blocks + (rot_blocks + 3) / 4;
+  if (blocks == 0) return;
+#define CB_DS(R, S)                                                                                \
+  hipLaunchKernelGGL((deviation_select_kernel<T, KPT, R, S>), dim3((unsigned)blocks),                \
+                     dim3(kTopkThreads), 0, stream, (const T *)v_new_c, (const T *)v_old, cand_idx, \
+                     dev, m, row_elems, cand_off, sel_off, n_req, sel_local, sel_global, cnt,     \
+                     dev_blocks, (T *)k, delta, gm, tab, rot_blocks)
+  if (!k) CB_DS(0, 0);
+  else if (style == 0) CB_DS(1, 0);
+  else CB_DS(1, 1);
+#undef CB_DS
+}
+
+hipError_t launch_deviation_select(int dtype, int style, void *k, const int32_t *delta,
+                                   int64_t n_tok, int32_t n_kv_heads, int32_t head_dim,
+                                   const RopeTable &tab, const void *v_new_c, const void *v_old,
+                                   const int32_t *cand_idx, float *dev, int32_t n_req,
+                                   const int32_t *cand_off, const int32_t *sel_off,
+                                   const int32_t *h_cand_off, int32_t *sel_local,
+                                   int32_t *sel_global, unsigned *cnt, hipStream_t stream) {
+  int32_t max_m = 0;
+  for (int32_t r = 0; r < n_req; ++r) max_m = std::max(max_m, h_cand_off[r + 1] - h_cand_off[r]);
+  const int64_t m = h_cand_off[n_req];
+  const int rounds = topk_rounds(max_m);
+#define CB_DSEL(K)                                                                            \
+  deviation_select_typed<T, K>(style, k, delta, n_tok, n_kv_heads, head_dim, tab, v_new_c,   \
+                               v_old, cand_idx, dev, m, n_req, cand_off, sel_off, sel_local, \
+                               sel_global, cnt, stream)
+  auto run = [&](auto tag) {
+    using T = decltype(tag);
+    if (rounds <= 2) CB_DSEL(2);
+    else if (rounds <= 8) CB_DSEL(8);
+    else if (rounds <= 32) CB_DSEL(32);
+    else CB_DSEL(0);
+  };
+#undef CB_DSEL
+  if (dtype == kBF16) run(bf16{});
+  else run(float{});
   return hipGetLastError();
 }
 

@@ -58,15 +58,23 @@ def offsets(counts: Sequence[int]) -> np.ndarray:
 
 
 class BlendRunner:
-    """Runs L layers of the blend on one stream with preallocated outputs."""
+    """Runs L layers of the blend on one stream with preallocated outputs.
+
+    The layers share one zero-filled workspace (the attention's split partials
+    and counters).  in_launch_select=True also reserves the selection's
+    arrival counters at its end and passes CB_LAYER_WORKSPACE_ZEROED, so each
+    call selects inside the deviation launch; by default the top-k is a launch
+    of its own, which measured as fast or faster on every workload."""
 
     def __init__(self, n_q_heads: int, n_kv_heads: int, head_dim: int, dtype: torch.dtype,
                  request_lengths: Sequence[int], r1_pct: int, r2_pct: int, n_layers: int,
                  rope_theta: float, rope_style: int = B.ROPE_HALF, schedule: str = "pool",
-                 dev_source: str = "v", device="cuda", order: str = "auto"):
+                 dev_source: str = "v", device="cuda", order: str = "auto",
+                 in_launch_select: bool = False):
         self.geom = B.geom(n_q_heads, n_kv_heads, head_dim, dtype)
         self.dev_source = B.DEV_SOURCES[dev_source]
         self.order = B.ORDERS[order]
+        self.flags = B.CB_LAYER_WORKSPACE_ZEROED if in_launch_select else 0
         self.filter = GradualFilter(request_lengths, r1_pct, r2_pct, schedule)
         self.n_layers, self.theta, self.style = n_layers, rope_theta, rope_style
         self.scale = 1.0 / math.sqrt(head_dim)
@@ -87,8 +95,11 @@ class BlendRunner:
                 sel_local=torch.empty(k, dtype=torch.int32, device=device),
                 sel_global=torch.empty(k, dtype=torch.int32, device=device),
                 out=torch.empty((k, n_q_heads, head_dim), dtype=dtype, device=device)))
-        # one attention workspace, sized for the largest layer, shared in stream order
+        # one workspace, sized for the largest layer's attention plus the
+        # selection counters, zero-filled once and shared in stream order
         ws = max(B.attn_workspace_bytes(self.geom, rb) for rb in self.batches)
+        if in_launch_select:
+            ws += B.CB_SELECT_COUNTER_BYTES + 256
         self.workspace = B.workspace_tensor(ws, device)
 
     def candidates(self, layer: int) -> torch.Tensor:
@@ -104,7 +115,7 @@ class BlendRunner:
                       rope_theta=self.theta, rope_style=self.style,
                       softmax_scale=self.scale, dev=o["dev"], sel_local=o["sel_local"],
                       sel_global=o["sel_global"], out=o["out"], workspace=self.workspace,
-                      dev_source=self.dev_source, order=self.order,
+                      dev_source=self.dev_source, order=self.order, flags=self.flags,
                       stream=stream)
         return o
 

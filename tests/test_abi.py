@@ -35,7 +35,34 @@ def test_exports_every_declared_symbol(lib):
             "cb_blend_layer"} <= declared
     for name in sorted(declared):
         assert hasattr(lib, name), name
-    assert lib.cb_abi_version() == 6
+    assert lib.cb_abi_version() == 7
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """The binding's ctypes structs have the sizes and field offsets a C
+    compiler gives the header's structs (gcc, host only)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no host C compiler")
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stddef.h>\n#include <stdio.h>\n#include "cacheblend.h"\n'
+        'int main(void) {\n'
+        '  printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(cb_layer_args),\n'
+        '         offsetof(cb_layer_args, workspace_bytes), offsetof(cb_layer_args, order),\n'
+        '         offsetof(cb_layer_args, flags), sizeof(cb_attn_plan), sizeof(cb_ragged),\n'
+        '         sizeof(cb_geom));\n'
+        '  return 0;\n}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
+                   check=True, capture_output=True)
+    got = [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    want = [ctypes.sizeof(B.LayerArgs), B.LayerArgs.workspace_bytes.offset,
+            B.LayerArgs.order.offset, B.LayerArgs.flags.offset, ctypes.sizeof(B.AttnPlan),
+            ctypes.sizeof(B.Ragged), ctypes.sizeof(B.Geom)]
+    assert got == want
 
 
 def test_status_strings(lib):
@@ -161,7 +188,8 @@ def test_blend_layer_validates_every_stage_first(lib):
     for field, value, status in [("out", None, 1), ("softmax_scale", -1.0, 1),
                                  ("rope_style", 3, 1), ("cand_idx", None, 1),
                                  ("workspace_bytes", 1024, 1), ("dev_source", 7, 1),
-                                 ("order", 3, 1), ("order", -1, 1),
+                                 ("order", 3, 1), ("order", -1, 1), ("flags", 2, 1),
+                                 ("flags", 0x80000000, 1),
                                  ("geom", B.Geom(32, 8, 128, 9), 2)]:
         args = dict(good)
         args[field] = value
@@ -188,6 +216,7 @@ def test_blend_layer_noalloc_validates_and_refuses_a_workspace(lib):
                                        ("workspace_bytes", 1024, 1, b"static scratch"),
                                        ("out", None, 1, b"out"),
                                        ("order", 3, 1, b"order"),
+                                       ("flags", 4, 1, b"flags"),
                                        ("geom", B.Geom(32, 8, 128, 9), 2, b"dtype")]:
         args = dict(good)
         args[field] = value

@@ -18,15 +18,20 @@ def say(msg):
     print(f"[graph-test] {msg}", flush=True)
 
 
-@pytest.mark.parametrize("name,source", [("mistral7b-layer", "v"), ("tiny", "v"),
-                                         ("mistral7b-layer", "kv")])
-def test_blend_layer_graph_replays_match_eager(name, source):
-    say(f"graph replay {name} deviation source {source}")
+@pytest.mark.parametrize("name,source,in_launch", [("mistral7b-layer", "v", False),
+                                                   ("tiny", "v", False),
+                                                   ("mistral7b-layer", "kv", False),
+                                                   ("mistral7b-layer", "v", True),
+                                                   ("70b-80layer-8req", "v", True)])
+def test_blend_layer_graph_replays_match_eager(name, source, in_launch):
+    """in_launch: the top-k inside the deviation launch, whose arrival counters
+    every replay leaves at zero for the next (no memset in the graph)."""
+    say(f"graph replay {name} deviation source {source} select in launch {in_launch}")
     wl = W.make_workload(name)
     sets = W.PlantedSets(wl)
     runner = PL.BlendRunner(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.torch_dtype,
                             wl.request_lengths, wl.r1_pct, wl.r2_pct, 1, wl.rope_theta,
-                            dev_source=source, device=DEV)
+                            dev_source=source, device=DEV, in_launch_select=in_launch)
     x = W.layer_inputs(wl, sets, 0, device=DEV)
     k0, v0 = x["k_old"].clone(), x["v_old"].clone()
     o = runner.outs[0]
@@ -36,7 +41,7 @@ def test_blend_layer_graph_replays_match_eager(name, source):
                            rope_theta=wl.rope_theta, rope_style=B.ROPE_HALF,
                            softmax_scale=runner.scale, dev=o["dev"], sel_local=o["sel_local"],
                            sel_global=o["sel_global"], out=o["out"], workspace=runner.workspace,
-                           dev_source=runner.dev_source)
+                           dev_source=runner.dev_source, flags=runner.flags)
     outs = [o["dev"], o["sel_local"], o["sel_global"], o["out"], x["k_old"], x["v_old"]]
     stream = torch.cuda.Stream()
 
