@@ -711,16 +711,16 @@ def attribution_pass(a, wl, runner, inp, stream, stages, steps, warmup, work, pe
     # distinct plan (every call leaves its counters at zero), so no call
     # needs the launch that clears them.
     ws_bytes = 0 if runner.workspace is None else runner.workspace.numel()
+    if runner.flags & B.CB_LAYER_WORKSPACE_ZEROED and ws_bytes >= B.CB_SELECT_COUNTER_BYTES + 256:
+        ws_bytes = (ws_bytes - B.CB_SELECT_COUNTER_BYTES) & ~255   # what the attention gets
     plan_ws, keep = {}, []
     for l, x in enumerate(inp.layers):
         rb, o = runner.batches[l], runner.outs[l]
         pd = B.attn_plan(runner.geom, rb, ws_bytes)
-        key = (pd["mfma"], pd["key_split"], pd["key_chunk"])
+        key = (pd["mfma"], pd["key_split"], pd["key_chunk"], pd["stream_spans"])
         if key not in plan_ws:
             plan_ws[key] = B.workspace_tensor(pd["workspace_bytes"], "cuda")
-            if plan_ws[key] is not None:
-                plan_ws[key].zero_()
-        plan = B.AttnPlan(key[0], key[1], 0, key[2], 0, 0, 0)
+        plan = B.AttnPlan(key[0], key[1], 0, key[2], 0, 0, 0, key[3])
         keep.append(plan)
         pws_ptr, pws_bytes = B._ws(plan_ws[key])
         cand = runner.candidates(l)

@@ -255,6 +255,15 @@ typedef struct cb_attn_plan {
   int64_t tiles;          /* MFMA: query tiles over all requests */
   int64_t workgroups;     /* workgroups of the attention launch */
   size_t workspace_bytes; /* workspace the plan uses (<= the size passed in) */
+  int32_t stream_spans;   /* MFMA, key split 1: > 0 = balanced decomposition --
+                             the 64-key tiles of all query tiles of a KV head,
+                             laid end to end, are cut into this many equal
+                             spans, one workgroup each; a query tile cut by a
+                             span's end is computed in pieces whose partials
+                             merge as key chunks do.  0: (query tile, key
+                             chunk) workgroups.  cb_partial_attn never chooses
+                             it (slower on the shapes measured); a pinned plan
+                             may. */
 } cb_attn_plan;
 
 /* The plan cb_partial_attn follows with `workspace_bytes` of workspace
@@ -275,13 +284,16 @@ cb_status cb_partial_attn_describe_plan(const cb_geom *geom, const cb_ragged *rg
  * cb_partial_attn_with_plan -- cb_partial_attn with the decomposition pinned
  * by the caller instead of chosen by the cost model (tuning, reproducible
  * launch shapes).  Same operation, arguments and result as cb_partial_attn.
- * Of *plan only three fields are read:
+ * Of *plan only four fields are read:
  *   mfma      : 0 = plain kernel (any geometry), 1 = MFMA query tiles;
  *   key_split : 1 or 2 (MFMA); UNSUPPORTED if the group size does not
  *               divide the 256 / key_split query vectors of a tile;
  *   key_chunk : 0 = no split over keys, else a positive multiple of
  *               64 * key_split that splits no request with selected rows
- *               into more than 8 chunks (INVALID_ARG otherwise).
+ *               into more than 8 chunks (INVALID_ARG otherwise);
+ *   stream_spans : 0, or 1 .. 65536 spans of the balanced decomposition
+ *               (key_split 1 and key_chunk 0, else INVALID_ARG; at most
+ *               1024 requests and 2048 query tiles, else UNSUPPORTED).
  * A split needs the workspace that cb_partial_attn_describe_plan() reports
  * for the same fields (INVALID_ARG if workspace_bytes is smaller).
  *

@@ -62,7 +62,7 @@ class AttnPlan(ctypes.Structure):
     _fields_ = [("mfma", ctypes.c_int32), ("key_split", ctypes.c_int32),
                 ("rows_per_tile", ctypes.c_int32), ("key_chunk", ctypes.c_int32),
                 ("tiles", ctypes.c_int64), ("workgroups", ctypes.c_int64),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("stream_spans", ctypes.c_int32)]
 
 
 class CbError(RuntimeError):
@@ -271,9 +271,9 @@ def attn_plan(g: Geom, rb: RaggedBatch, workspace_bytes: Optional[int] = None) -
 
 
 def describe_plan(g: Geom, rb: RaggedBatch, mfma: int = 1, key_split: int = 1,
-                  key_chunk: int = 0) -> dict:
+                  key_chunk: int = 0, stream_spans: int = 0) -> dict:
     """A pinned plan with its derived fields (cb_partial_attn_describe_plan)."""
-    plan = AttnPlan(mfma, key_split, 0, key_chunk, 0, 0, 0)
+    plan = AttnPlan(mfma, key_split, 0, key_chunk, 0, 0, 0, stream_spans)
     rg = rb.struct()
     check(lib().cb_partial_attn_describe_plan(ctypes.byref(g), ctypes.byref(rg),
                                               ctypes.byref(plan)))
@@ -310,7 +310,8 @@ def partial_attn_with_plan(g: Geom, rb: RaggedBatch, plan: dict, out, q_c, sel_l
     """cb_partial_attn with a pinned plan (a dict with mfma, key_split, key_chunk).
     counters_zero: pass CB_ATTN_COUNTERS_ZERO (the workspace was zero-filled and
     has since been used only with this plan)."""
-    p = AttnPlan(plan["mfma"], plan.get("key_split", 1), 0, plan.get("key_chunk", 0), 0, 0, 0)
+    p = AttnPlan(plan["mfma"], plan.get("key_split", 1), 0, plan.get("key_chunk", 0), 0, 0, 0,
+                 plan.get("stream_spans", 0))
     rg = rb.struct()
     ws_ptr, ws_bytes = _ws(workspace)
     flags = CB_ATTN_COUNTERS_ZERO if counters_zero else 0

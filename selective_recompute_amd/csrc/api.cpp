@@ -318,12 +318,31 @@ size_t split_ws_bytes(const cb_geom *g, int ks, int64_t units, int64_t tiles,
   return off + (size_t)tiles * g->n_kv_heads * sizeof(uint32_t);
 }
 
+// Workspace of the balanced decomposition: two partial slots per workgroup,
+// then (256-byte aligned) one arrival counter per (query tile, KV head).
+size_t stream_ws_bytes(const cb_geom *g, int spans, int64_t tiles, size_t *cnt_offset = nullptr) {
+  const size_t partials =
+      (size_t)spans * g->n_kv_heads * 2 * cb::attn_unit_bytes(g->head_dim, 1);
+  const size_t off = (partials + 255) / 256 * 256;
+  if (cnt_offset) *cnt_offset = off;
+  return off + (size_t)tiles * g->n_kv_heads * sizeof(uint32_t);
+}
+
 // Fills the counts of an MFMA plan whose key split, rows per tile and key
-// chunk are set: tiles, units, split, counters, workspace.
+// chunk (or spans) are set: tiles, units, split, counters, workspace.
 void finish_plan(const cb_geom *g, const cb_ragged *rg, cb::AttnPlan &pl) {
   const int rows = pl.rows_per_tile;
   pl.tiles = pl.units = 0;
   pl.split = false;
+  if (pl.spans > 0) {
+    for (int32_t r = 0; r < rg->n_req; ++r)
+      pl.tiles += (rg->h_sel_off[r + 1] - rg->h_sel_off[r] + rows - 1) / rows;
+    pl.units = pl.spans;
+    pl.split = pl.tiles > 0;
+    pl.n_cnt = pl.split ? pl.tiles * g->n_kv_heads : 0;
+    pl.ws_bytes = pl.split ? stream_ws_bytes(g, pl.spans, pl.tiles, &pl.cnt_offset) : 0;
+    return;
+  }
   for (int32_t r = 0; r < rg->n_req; ++r) {
     const int64_t kr = rg->h_sel_off[r + 1] - rg->h_sel_off[r];
     const int64_t n = rg->h_tok_off[r + 1] - rg->h_tok_off[r];
@@ -338,7 +357,9 @@ void finish_plan(const cb_geom *g, const cb_ragged *rg, cb::AttnPlan &pl) {
   pl.ws_bytes = pl.split ? split_ws_bytes(g, pl.key_split, pl.units, pl.tiles, &pl.cnt_offset) : 0;
 }
 
-// Decomposition of the MFMA attention, from host mirrors only.  When the
+// Decomposition of the MFMA attention, from host mirrors only (never the
+// balanced decomposition, which only a pinned plan selects: on the shapes
+// measured its cut pieces cost more than its balance gains).  When the
 // query tiles of 256 query vectors give 1024 workgroups or more, that is the
 // plan.  Otherwise the cost model above picks, among the plans whose
 // workspace fits in `ws_avail`, the shortest of: key split 1 or 2 (2 only
@@ -417,8 +438,8 @@ cb::AttnPlan plan_attn(const cb_geom *g, const cb_ragged *rg, size_t ws_avail) {
   return pl;
 }
 
-// A plan the caller pins (cb_partial_attn_with_plan): only mfma, key_split
-// and key_chunk are read; the rest is derived as for a chosen plan.
+// A plan the caller pins (cb_partial_attn_with_plan): only mfma, key_split,
+// key_chunk and stream_spans are read; the rest is derived as for a chosen plan.
 cb_status pinned_plan(const cb_geom *g, const cb_ragged *rg, const cb_attn_plan *in,
                       size_t ws_avail, cb::AttnPlan &pl) {
   pl = cb::AttnPlan{};
@@ -440,6 +461,24 @@ cb_status pinned_plan(const cb_geom *g, const cb_ragged *rg, const cb_attn_plan 
   if (in->key_chunk < 0 || in->key_chunk % tile_keys != 0)
     return fail(CB_ERR_INVALID_ARG, "plan.key_chunk %d must be 0 or a positive multiple of %d",
                 in->key_chunk, tile_keys);
+  if (in->stream_spans < 0 || in->stream_spans > 65536)
+    return fail(CB_ERR_INVALID_ARG, "plan.stream_spans %d must be in [0, 65536]",
+                in->stream_spans);
+  if (in->stream_spans > 0) {
+    if (pl.key_split != 1 || in->key_chunk != 0)
+      return fail(CB_ERR_INVALID_ARG,
+                  "plan.stream_spans needs key_split 1 and key_chunk 0");
+    pl.spans = in->stream_spans;
+    finish_plan(g, rg, pl);
+    if (!cb::attn_stream_fits(rg->n_req, pl.tiles))
+      return fail(CB_ERR_UNSUPPORTED, "the balanced decomposition takes at most 1024 requests "
+                  "and 2048 query tiles (%d requests, %lld tiles)", (int)rg->n_req,
+                  (long long)pl.tiles);
+    if (pl.ws_bytes > ws_avail)
+      return fail(CB_ERR_INVALID_ARG, "workspace_bytes %zu is smaller than the plan's %zu",
+                  ws_avail, pl.ws_bytes);
+    return CB_OK;
+  }
   if (in->key_chunk > 0) {
     pl.key_chunk = in->key_chunk;
     for (int32_t r = 0; r < rg->n_req; ++r) {
@@ -625,7 +664,8 @@ void export_plan(const cb_geom *geom, const cb_ragged *rg, const cb::AttnPlan &p
   plan->mfma = 1;
   plan->key_split = pl.key_split;
   plan->rows_per_tile = pl.rows_per_tile;
-  plan->key_chunk = pl.split ? pl.key_chunk : 0;
+  plan->key_chunk = pl.split && pl.spans == 0 ? pl.key_chunk : 0;
+  plan->stream_spans = pl.spans;
   plan->tiles = pl.tiles;
   plan->workgroups = pl.units * geom->n_kv_heads;
   plan->workspace_bytes = pl.ws_bytes;

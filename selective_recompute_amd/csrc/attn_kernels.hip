@@ -80,6 +80,7 @@ struct AttnParams {
   unsigned char *ws;     // split partials, one per workgroup of the launch
   unsigned *cnt;         // arrival counter per (query tile, KV head); zero at launch and at exit
   int32_t n_req, hq, hkv, group, rows_per_tile, key_chunk;
+  int32_t spans;         // > 0: balanced decomposition over this many workgroups per KV head
   float scale_log2;
 };
 
@@ -216,43 +217,55 @@ __device__ inline void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int HD, int KS>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
-void attn_mfma_kernel(const AttnParams p) {
+// Compile-time shape of one MFMA attention workgroup.
+template <int HD, int KS> struct AttnCfg {
   static_assert(KS == 1 || KS == 2, "key split of 1 or 2 groups");
-  constexpr int QT = kQT / KS;            // query vectors per unit
-  constexpr int WPG = kWaves / KS;        // waves per key group
-  constexpr int KT = kKeyTile * KS;       // keys per tile: 64 per key group
-  constexpr int STAGES = kStages / KS;    // tiles resident in LDS (the same bytes)
-  constexpr int NSB = 2;                  // 32-key blocks per wave and tile
-  constexpr int NKS = HD / 16;            // 16-wide contraction steps of S over head_dim
-  constexpr int NDT = HD / 32;            // 32-dim output blocks
-  constexpr int CPR = HD / 8;             // 16-byte chunks per key row
-  constexpr int TILE = KT * HD;           // elements per tensor per stage
-  constexpr int NI = TILE / 512;          // 1 KiB DMA instructions per tensor per tile
-  constexpr int DMA_WAVES = NI < kWaves ? NI : kWaves;
-  constexpr int IPW = NI / DMA_WAVES;     // per issuing wave and tensor
-  constexpr int PER_TILE = 2 * IPW;       // vector-memory ops per tile and issuing wave
-  __shared__ __attribute__((aligned(1024))) bf16 kst[STAGES][TILE];
-  __shared__ __attribute__((aligned(1024))) bf16 vst[STAGES][TILE];
+  static constexpr int QT = kQT / KS;            // query vectors per unit
+  static constexpr int WPG = kWaves / KS;        // waves per key group
+  static constexpr int KT = kKeyTile * KS;       // keys per tile: 64 per key group
+  static constexpr int STAGES = kStages / KS;    // tiles resident in LDS (the same bytes)
+  static constexpr int NSB = 2;                  // 32-key blocks per wave and tile
+  static constexpr int NKS = HD / 16;            // 16-wide contraction steps of S over head_dim
+  static constexpr int NDT = HD / 32;            // 32-dim output blocks
+  static constexpr int CPR = HD / 8;             // 16-byte chunks per key row
+  static constexpr int TILE = KT * HD;           // elements per tensor per stage
+  static constexpr int NI = TILE / 512;          // 1 KiB DMA instructions per tensor per tile
+  static constexpr int DMA_WAVES = NI < kWaves ? NI : kWaves;
+  static constexpr int IPW = NI / DMA_WAVES;     // per issuing wave and tensor
+  static constexpr int PER_TILE = 2 * IPW;       // vector-memory ops per tile and issuing wave
+};
 
+// One piece of attention work: query tile `tile` of request `r` (KV head g)
+// over the keys [k_begin, k_end), k_end <= p_last + 1.  With n_active == 1 the
+// piece covers the tile's whole row and writes the output; otherwise it
+// stores its partial at `own`, and the last of the tile's n_active pieces to
+// arrive (counter `item` of head g) merges all of them, in piece order, and
+// writes the output.  Piece c's partial: part0 for c == 0, else
+// part1 + (c - 1) * part_stride.
+struct Piece {
+  int r, tile, s0, ns, lo, p_first, p_last, k_begin, k_end, n_active;
+  int64_t item;
+  unsigned char *own;
+  const unsigned char *part0, *part1;
+  int64_t part_stride;
+};
+
+template <int HD, int KS>
+__device__ __attribute__((always_inline)) void attn_piece(
+    const AttnParams &p, const int g, const Piece &pc,
+    bf16 (*kst)[AttnCfg<HD, KS>::TILE], bf16 (*vst)[AttnCfg<HD, KS>::TILE], int &s_last) {
+  using C = AttnCfg<HD, KS>;
+  constexpr int QT = C::QT, WPG = C::WPG, KT = C::KT, STAGES = C::STAGES, NSB = C::NSB;
+  constexpr int NKS = C::NKS, NDT = C::NDT, CPR = C::CPR, TILE = C::TILE;
+  constexpr int DMA_WAVES = C::DMA_WAVES, IPW = C::IPW, PER_TILE = C::PER_TILE;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
   const int kg = wave / WPG;              // key group: keys 64kg .. 64kg+63 of each tile
-  const int g = blockIdx.x % p.hkv;
-  UnitPos up;
-  if (!locate_unit(p, (int)(blockIdx.x / p.hkv), up)) return;
-  const int r = up.r, tile = up.tile, chunk = up.chunk;
-  const int s0 = p.sel_off[r] + tile * p.rows_per_tile;
-  const int ns = min(p.rows_per_tile, p.sel_off[r + 1] - s0);
-  const int lo = p.tok_off[r];
-  const int p_first = p.sel_global[s0];
-  const int p_last = p.sel_global[s0 + ns - 1];
-  const int64_t kb = (int64_t)lo + (int64_t)chunk * p.key_chunk;
-  if (kb > p_last) return;  // whole chunk after the tile's last row (uniform)
-  const int k_begin = (int)kb;
-  const int k_end = (int)min((int64_t)p_last + 1, kb + p.key_chunk);
+  const int s0 = pc.s0, ns = pc.ns, lo = pc.lo, p_first = pc.p_first, p_last = pc.p_last;
+  const int k_begin = pc.k_begin, k_end = pc.k_end;
   const int n_kt = (k_end - k_begin + KT - 1) / KT;
+  (void)lo;
+  phase_barrier();  // a previous piece of this workgroup is done with the LDS stages
 
   // DMA slots of this wave: instruction i writes 64 consecutive 16-byte chunks
   // of the tile; lane -> (row, physical chunk) -> logical chunk.  Rows past
@@ -483,7 +496,7 @@ void attn_mfma_kernel(const AttnParams p) {
   // Split over keys: every working chunk of the tile stores its partial;
   // the last to arrive merges all of them and writes the output.  A tile
   // whose rows all lie in its first chunk has one working unit and no merge.
-  const int n_active = (int)((p_last - lo) / p.key_chunk) + 1;
+  const int n_active = pc.n_active;
   // The merge of a split tile: with key split 2 both wave groups take part,
   // each on half of the dim blocks of its query vectors (one dim block:
   // group 0 alone); with key split 1 every wave on its own vectors.
@@ -501,7 +514,7 @@ void attn_mfma_kernel(const AttnParams p) {
       // query vector's O is divided by its largest |O| (the two lanes l and
       // l ^ 32 hold its dims), so fp16 keeps 11 significant bits of every
       // value whatever the scale of V; the merge multiplies it back.
-      unsigned char *w = p.ws + (int64_t)blockIdx.x * UNIT;
+      unsigned char *w = pc.own;
       float amax = 0.f;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
@@ -531,11 +544,10 @@ void attn_mfma_kernel(const AttnParams p) {
     // that brings the count to n_active goes on.  It is the last to touch
     // the counter in this launch, so it sets it back to zero: every launch
     // leaves its counters as it needs to find them.
-    __shared__ int s_last;
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     phase_barrier();
     if (tid == 0) {
-      unsigned *const cnt = p.cnt + (up.tbase + tile) * p.hkv + g;
+      unsigned *const cnt = p.cnt + pc.item * p.hkv + g;
       const unsigned prev =
           __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_last = prev == (unsigned)(n_active - 1);
@@ -544,13 +556,12 @@ void attn_mfma_kernel(const AttnParams p) {
     phase_barrier();
     if (!s_last) return;  // uniform
     merged = true;
-    // Merge every working chunk's stored partial, this one's included, in
-    // chunk order: the result does not depend on which chunk arrived last.
-    // Unit of (tile, chunk c): ubase + c * tr + (tr - 1 - tile).
+    // Merge every piece's stored partial, this one's included, in piece
+    // order: the result does not depend on which piece arrived last.
     if (merging) {
-      const unsigned char *w0 =
-          p.ws + ((up.ubase + (int64_t)(up.tr - 1 - tile)) * p.hkv + g) * UNIT;
-      const int64_t ustride = (int64_t)up.tr * p.hkv * UNIT;
+      auto part = [&](int c) -> const unsigned char * {
+        return c == 0 ? pc.part0 : pc.part1 + (int64_t)(c - 1) * pc.part_stride;
+      };
       const int fw = wave - kg * WPG;  // query block of this wave in the fragment order
       // One round of loads for up to MCH chunks: the running max, running
       // sum and largest |O| of every chunk, then the first MCH chunks' O
@@ -567,7 +578,7 @@ void attn_mfma_kernel(const AttnParams p) {
           lc[c] = ac[c] = 0.f;
           if (c < n_active) {
             const uint32_t *mt =
-                reinterpret_cast<const uint32_t *>(w0 + c * ustride + QT * HD * 2);
+                reinterpret_cast<const uint32_t *>(part(c) + QT * HD * 2);
             mc[c] = __builtin_bit_cast(float, load_agent(mt + qv));
             lc[c] = __builtin_bit_cast(float, load_agent(mt + QT + qv));
             ac[c] = __builtin_bit_cast(float, load_agent(mt + 2 * QT + qv));
@@ -578,7 +589,7 @@ void attn_mfma_kernel(const AttnParams p) {
 #pragma unroll
           for (int j = 0; j < MCH; ++j) {
             if (c0 + j < n_active) {
-              const uint64_t *src = reinterpret_cast<const uint64_t *>(w0 + (c0 + j) * ustride);
+              const uint64_t *src = reinterpret_cast<const uint64_t *>(part(c0 + j));
 #pragma unroll
               for (int dl = 0; dl < MDT; ++dl)
 #pragma unroll
@@ -667,6 +678,188 @@ void attn_mfma_kernel(const AttnParams p) {
   }
 }
 
+// Tables of the balanced decomposition: tiles per request, then each query
+// tile's 64-key tiles laid end to end (exclusive prefix sums), in LDS.
+constexpr int kStreamMaxRequests = 1024;
+constexpr int kStreamMaxTiles = 2048;
+
+// Exclusive prefix sum of a[0 .. n) in place (n <= 4 * 512), a[n] = total;
+// every thread of the 512-thread workgroup takes part (the entries may have
+// been written by any thread just before).  tmp: kWaves words.
+__device__ inline void block_scan_exclusive(uint32_t *a, int n, uint32_t *tmp) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  __syncthreads();  // every thread's writes of a are visible
+  uint32_t v[4], s = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = 4 * t + q;
+    v[q] = i < n ? a[i] : 0u;
+    s += v[q];
+  }
+  uint32_t x = s;  // inclusive scan over the wave's lanes
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) tmp[wave] = x;  // tmp's readers of a previous scan passed its last barrier
+  __syncthreads();
+  uint32_t run = x - s, total = 0;
+  for (int w = 0; w < kWaves; ++w) {
+    if (w < wave) run += tmp[w];
+    total += tmp[w];
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = 4 * t + q;
+    if (i < n) a[i] = run;
+    run += v[q];
+  }
+  if (t == 0) a[n] = total;
+  __syncthreads();
+}
+
+// Largest i in [0, n) with a[i] <= x, for an ascending a with a[0] <= x.
+__device__ inline int upper_index(const uint32_t *a, int n, uint32_t x) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a[mid] <= x) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Balanced decomposition (key split 1): the 64-key tiles of all query tiles
+// of KV head g, laid end to end in request and tile order, are cut into
+// p.spans equal spans of S tiles, one per workgroup (S at least a seventh of
+// the longest row, so a row is cut into at most 8 pieces).  A workgroup
+// computes the layout itself (one selected-row position per query tile) and
+// runs each piece of its span: query tiles inside the span whole, the ones
+// cut by its ends as pieces whose partials merge like key chunks.  Partial
+// slots: two per workgroup, slot 1 for the piece of a tile that starts inside
+// the span, slot 0 for the first piece.
+template <int HD>
+__device__ __attribute__((always_inline)) void attn_stream(
+    const AttnParams &p, const int g, bf16 (*kst)[AttnCfg<HD, 1>::TILE],
+    bf16 (*vst)[AttnCfg<HD, 1>::TILE], int &s_last, uint32_t *tb, uint32_t *gt, uint32_t *tmp,
+    uint32_t &s_maxn) {
+  const int tid = threadIdx.x;
+  const int rpt = p.rows_per_tile, n_req = p.n_req;
+  const uint32_t w = blockIdx.x / p.hkv, n_spans = (uint32_t)p.spans;
+  if (n_req > kStreamMaxRequests) return;  // uniform; the host plans within the tables
+  // query tiles per request -> tb (exclusive prefix), tb[n_req] = all tiles
+  for (int r = tid; r < n_req; r += 64 * kWaves) {
+    const int kr = p.sel_off[r + 1] - p.sel_off[r];
+    tb[r] = (uint32_t)((kr + rpt - 1) / rpt);
+  }
+  if (tid == 0) s_maxn = 0;
+  block_scan_exclusive(tb, n_req, tmp);
+  const int n_items = (int)tb[n_req];
+  if (n_items > kStreamMaxTiles) return;  // uniform; the host plans within the tables
+  // 64-key tiles of each query tile: its last selected row's position in the request
+  // (the request of tile i: the last r with tb[r] <= i, so requests without
+  // selected rows, which repeat the previous tb value, are passed over)
+  for (int i = tid; i < n_items; i += 64 * kWaves) {
+    const int r = upper_index(tb, n_req, (uint32_t)i);
+    const int tile = i - (int)tb[r];
+    const int s0 = p.sel_off[r], kr = p.sel_off[r + 1] - s0;
+    if (tile < 0 || tile * rpt >= kr) {  // cannot happen with the table above; never read outside
+      gt[i] = 1;
+      continue;
+    }
+    const int last = s0 + min((tile + 1) * rpt, kr) - 1;
+    const uint32_t n = (uint32_t)((p.sel_global[last] - p.tok_off[r]) / kKeyTile + 1);
+    gt[i] = n;
+    atomicMax(&s_maxn, n);
+  }
+  block_scan_exclusive(gt, n_items, tmp);
+  const uint32_t total = gt[n_items], maxn = s_maxn;
+  const uint32_t span = max((total + n_spans - 1) / n_spans, (maxn + 6) / 7);
+  const uint32_t t0 = w * span, t1 = min(total, t0 + span);
+  if (t0 >= t1) return;  // uniform: nothing left for this span
+  constexpr int64_t UNIT = partial_bytes<HD, kQT>();
+  auto slot = [&](uint32_t ww, int sl) {
+    return p.ws + (((int64_t)ww * p.hkv + g) * 2 + sl) * UNIT;
+  };
+  for (int i = upper_index(gt, n_items, t0); i < n_items && gt[i] < t1; ++i) {
+    const uint32_t gi = gt[i], ni = gt[i + 1] - gi;
+    const uint32_t a = max(t0, gi) - gi, b = min(t1, gi + ni) - gi;
+    const int r = upper_index(tb, n_req, (uint32_t)i);
+    Piece pc;
+    pc.r = r;
+    pc.tile = i - (int)tb[r];
+    pc.s0 = p.sel_off[r] + pc.tile * rpt;
+    pc.ns = min(rpt, p.sel_off[r + 1] - pc.s0);
+    pc.lo = p.tok_off[r];
+    pc.p_first = p.sel_global[pc.s0];
+    pc.p_last = p.sel_global[pc.s0 + pc.ns - 1];
+    pc.k_begin = pc.lo + kKeyTile * (int)a;
+    pc.k_end = min(pc.p_last + 1, pc.lo + kKeyTile * (int)b);
+    const uint32_t wa = gi / span, wb = (gi + ni - 1) / span;
+    // (wb < n_spans and at most kMaxChunks pieces follow from the layout above;
+    // the check keeps every partial slot and merge inside the workspace)
+    if (wb >= n_spans || wb - wa >= (uint32_t)kMaxChunks) return;  // uniform
+    pc.n_active = (int)(wb - wa + 1);
+    pc.item = i;
+    pc.own = pc.n_active > 1 ? slot(w, t0 < gi ? 1 : 0) : nullptr;
+    pc.part0 = pc.n_active > 1 ? slot(wa, wa * span < gi ? 1 : 0) : nullptr;
+    pc.part1 = pc.n_active > 1 ? slot(wa + 1, 0) : nullptr;
+    pc.part_stride = (int64_t)p.hkv * 2 * UNIT;
+    attn_piece<HD, 1>(p, g, pc, kst, vst, s_last);
+  }
+}
+
+template <int HD, int KS>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_mfma_kernel(const AttnParams p) {
+  using C = AttnCfg<HD, KS>;
+  __shared__ __attribute__((aligned(1024))) bf16 kst[C::STAGES][C::TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 vst[C::STAGES][C::TILE];
+  __shared__ int s_last;
+  const int g = blockIdx.x % p.hkv;
+  // (query tile, key chunk) units
+  UnitPos up;
+  if (!locate_unit(p, (int)(blockIdx.x / p.hkv), up)) return;
+  Piece pc;
+  pc.r = up.r;
+  pc.tile = up.tile;
+  pc.s0 = p.sel_off[pc.r] + pc.tile * p.rows_per_tile;
+  pc.ns = min(p.rows_per_tile, p.sel_off[pc.r + 1] - pc.s0);
+  pc.lo = p.tok_off[pc.r];
+  pc.p_first = p.sel_global[pc.s0];
+  pc.p_last = p.sel_global[pc.s0 + pc.ns - 1];
+  const int64_t kb = (int64_t)pc.lo + (int64_t)up.chunk * p.key_chunk;
+  if (kb > pc.p_last) return;  // whole chunk after the tile's last row (uniform)
+  pc.k_begin = (int)kb;
+  pc.k_end = (int)min((int64_t)pc.p_last + 1, kb + p.key_chunk);
+  pc.n_active = (int)((pc.p_last - pc.lo) / p.key_chunk) + 1;
+  pc.item = up.tbase + pc.tile;
+  constexpr int64_t UNIT = partial_bytes<HD, C::QT>();
+  // unit of (tile, chunk c): ubase + c * tr + (tr - 1 - tile)
+  const int64_t ustride = (int64_t)up.tr * p.hkv * UNIT;
+  pc.own = pc.n_active > 1 ? p.ws + (int64_t)blockIdx.x * UNIT : nullptr;
+  pc.part0 = pc.n_active > 1
+                 ? p.ws + ((up.ubase + (int64_t)(up.tr - 1 - pc.tile)) * p.hkv + g) * UNIT
+                 : nullptr;
+  pc.part1 = pc.n_active > 1 ? pc.part0 + ustride : nullptr;
+  pc.part_stride = ustride;
+  attn_piece<HD, KS>(p, g, pc, kst, vst, s_last);
+}
+
+// The balanced decomposition (p.spans workgroups per KV head, key split 1).
+template <int HD>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_stream_kernel(const AttnParams p) {
+  using C = AttnCfg<HD, 1>;
+  __shared__ __attribute__((aligned(1024))) bf16 kst[C::STAGES][C::TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 vst[C::STAGES][C::TILE];
+  __shared__ int s_last;
+  __shared__ uint32_t tb[kStreamMaxRequests + 1], gt[kStreamMaxTiles + 1], tmp[kWaves];
+  __shared__ uint32_t s_maxn;
+  attn_stream<HD>(p, (int)(blockIdx.x % p.hkv), kst, vst, s_last, tb, gt, tmp, s_maxn);
+}
+
 // Arrival counters of a split launch set to zero before it (standalone calls
 // on a workspace of unknown contents; inside cb_blend_layer the fuse launch
 // clears them).
@@ -692,10 +885,20 @@ size_t attn_unit_bytes(int32_t head_dim, int key_split) {
 
 int attn_max_chunks() { return kMaxChunks; }
 
+bool attn_stream_fits(int32_t n_req, int64_t tiles) {
+  return n_req <= kStreamMaxRequests && tiles <= kStreamMaxTiles;
+}
+
 template <int HD, int KS>
 static hipError_t launch_hd(const AttnParams &p, const AttnPlan &plan, int n_kv_heads,
                             hipStream_t stream) {
   const dim3 grid((unsigned)(plan.units * n_kv_heads)), block(64 * kWaves);
+  if constexpr (KS == 1) {
+    if (plan.spans > 0) {
+      hipLaunchKernelGGL((attn_stream_kernel<HD>), grid, block, 0, stream, p);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((attn_mfma_kernel<HD, KS>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
@@ -720,8 +923,12 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &plan, bool counte
   p.group = a.n_q_heads / a.n_kv_heads;
   p.rows_per_tile = plan.rows_per_tile;
   p.key_chunk = plan.key_chunk;
+  p.spans = plan.spans;
   p.scale_log2 = a.softmax_scale * 1.4426950408889634f;
   if (plan.key_chunk % (kKeyTile * plan.key_split) != 0) return hipErrorInvalidValue;
+  if (plan.spans > 0 && (plan.key_split != 1 || a.n_req > kStreamMaxRequests ||
+                         plan.tiles > kStreamMaxTiles))
+    return hipErrorInvalidValue;
   if (plan.split && !counters_zero) {
     const int blocks = (int)std::min<int64_t>((plan.n_cnt + 255) / 256, 64);
     hipLaunchKernelGGL(attn_clear_kernel, dim3(blocks), dim3(256), 0, stream, p.cnt,

@@ -105,6 +105,9 @@ struct AttnPlan {
   size_t cnt_offset;   // split: byte offset of the arrival counters in the workspace
   int64_t n_cnt;       // split: arrival counters, one per (tile, KV head)
   size_t ws_bytes;     // workspace the split needs: partials, then counters
+  int spans;           // > 0: balanced decomposition (key split 1): the 64-key tiles of
+                       // all query tiles of a KV head cut into `spans` equal spans, one
+                       // workgroup each (units = spans); 0: (tile, key chunk) units
 };
 
 // Selected rows per MFMA query tile (256 / key_split query vectors), or 0 if
@@ -115,6 +118,8 @@ int attn_mfma_rows_per_tile(int dtype, int32_t n_q_heads, int32_t n_kv_heads,
 size_t attn_unit_bytes(int32_t head_dim, int key_split);
 // Most key chunks one row may be split into.
 int attn_max_chunks();
+// Whether a batch fits the balanced decomposition's tables (requests, query tiles).
+bool attn_stream_fits(int32_t n_req, int64_t tiles);
 
 // counters_zero: the split's arrival counters are already zero (cleared by
 // the preceding fuse launch); otherwise a clear launch goes first.

@@ -307,6 +307,12 @@ def _split_ws(ks, workgroups, tiles, hkv, d=128):
     return -(-workgroups * _unit(ks, d) // 256) * 256 + 4 * tiles * hkv
 
 
+def _stream_ws(spans, tiles, hkv, d=128):
+    """The balanced decomposition's workspace: two partial slots per
+    workgroup, then (256-byte aligned) one arrival counter per (tile, KV head)."""
+    return _split_ws(1, 2 * spans * hkv, tiles, hkv, d)
+
+
 def _plan(lib, g, tok, sel, ws=SIZE_MAX):
     rg, keep = _ragged(tok, tok, sel)
     p = B.AttnPlan()
@@ -382,6 +388,7 @@ def test_workspace_plan_properties(lib):
         tiles1 = sum(-(-k // (256 // (hq // hkv))) for k in ks)
         if tiles1 * hkv >= 1024:
             assert (p.key_split, p.key_chunk, p.workspace_bytes) == (1, 0, 0)
+        assert p.stream_spans == 0              # only a pinned plan is balanced
         seen.add((p.key_split, p.key_chunk > 0))
         if p.key_chunk == 0:
             assert p.workgroups == p.tiles * hkv and p.workspace_bytes == 0
@@ -397,6 +404,46 @@ def test_workspace_plan_properties(lib):
         q = _plan(lib, g, tok, sel, ws=p.workspace_bytes - 1)
         assert q.workspace_bytes <= p.workspace_bytes - 1
     assert seen == {(1, False), (1, True), (2, False), (2, True)}
+
+
+def test_pinned_balanced_plans(lib):
+    """The balanced decomposition, pinned: stream_spans workgroups per KV head,
+    two partial slots each and a counter per (query tile, KV head); key split
+    1 and no key chunk only; at most 1024 requests and 2048 query tiles."""
+    tok, sel = [0, 3000, 3100, 9000], [0, 450, 470, 1000]
+    rg, keep = _ragged(tok, tok, sel)
+    g = _geom()
+
+    def describe(ks, kc, spans, r=None):
+        p = B.AttnPlan(1, ks, 0, kc, 0, 0, 0, spans)
+        st = lib.cb_partial_attn_describe_plan(ctypes.byref(g), ctypes.byref(r or rg), ctypes.byref(p))
+        return st, p
+
+    tiles = -(-450 // 64) + -(-20 // 64) + -(-530 // 64)
+    for spans in (1, 7, 32, 300):
+        st, p = describe(1, 0, spans)
+        assert st == 0 and p.stream_spans == spans and p.key_chunk == 0
+        assert (p.tiles, p.workgroups) == (tiles, spans * 8)
+        assert p.workspace_bytes == _stream_ws(spans, tiles, 8)
+    for ks, kc, spans, status in [(2, 0, 8, 1), (1, 512, 8, 1), (1, 0, -1, 1), (1, 0, 65537, 1)]:
+        st, p = describe(ks, kc, spans)
+        assert st == status, (ks, kc, spans)
+    assert b"stream_spans" in lib.cb_last_error()
+    # more than 1024 requests, or more than 2048 query tiles
+    n = 1100
+    many, keep2 = _ragged(list(range(0, 10 * n + 1, 10)), list(range(0, 10 * n + 1, 10)),
+                          list(range(0, n + 1)))
+    assert describe(1, 0, 8, many)[0] == 2
+    big, keep3 = _ragged([0, 200000], [0, 200000], [0, 2049 * 64])
+    assert describe(1, 0, 8, big)[0] == 2
+    assert b"2048" in lib.cb_last_error()
+    # a workspace smaller than the plan's is refused before anything launches
+    st, p = describe(1, 0, 32)
+    P = ctypes.c_void_p(1 << 40)
+    args = [ctypes.byref(g), ctypes.byref(rg), ctypes.byref(p), P, P, P, P, P, P, 0.1, P,
+            p.workspace_bytes - 1, 0, None]
+    assert lib.cb_partial_attn_with_plan(*args) == 1
+    assert b"workspace" in lib.cb_last_error()
 
 
 def test_pinned_plans(lib):

@@ -64,6 +64,9 @@ def _plans(lens, ks_list=(1, 2)):
             kc = -(-kc // (64 * ks)) * (64 * ks)
             if kc < max_n:
                 plans.append(dict(mfma=1, key_split=ks, key_chunk=kc))
+    # the balanced decomposition: a span per CU, and coarse spans (fewer
+    # cuts, so longer rows end in different spans' pieces)
+    plans += [dict(mfma=1, key_split=1, stream_spans=32), dict(mfma=1, key_split=1, stream_spans=5)]
     return plans
 
 

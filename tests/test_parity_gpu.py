@@ -457,13 +457,17 @@ def test_attention_random_ragged_batches(case, use_ws):
 PINNED_PLANS = [dict(mfma=0), dict(mfma=1, key_split=1, key_chunk=0),
                 dict(mfma=1, key_split=1, key_chunk=256), dict(mfma=1, key_split=1, key_chunk=576),
                 dict(mfma=1, key_split=2, key_chunk=0), dict(mfma=1, key_split=2, key_chunk=384),
-                dict(mfma=1, key_split=2, key_chunk=1024)]
+                dict(mfma=1, key_split=2, key_chunk=1024),
+                dict(mfma=1, key_split=1, stream_spans=1), dict(mfma=1, key_split=1, stream_spans=3),
+                dict(mfma=1, key_split=1, stream_spans=32),
+                dict(mfma=1, key_split=1, stream_spans=500)]
 PINNED_GEOMS = [(32, 8, 128), (8, 2, 64), (16, 1, 32), (8, 8, 128)]
 
 
 @pytest.mark.parametrize("family", FAMILIES)
 @pytest.mark.parametrize("plan", PINNED_PLANS,
-                         ids=["plain", "ks1", "ks1c256", "ks1c576", "ks2", "ks2c384", "ks2c1024"])
+                         ids=["plain", "ks1", "ks1c256", "ks1c576", "ks2", "ks2c384", "ks2c1024",
+                              "bal1", "bal3", "bal32", "bal500"])
 @pytest.mark.parametrize("geo", PINNED_GEOMS, ids=[f"h{a}-{b}-d{c}" for a, b, c in PINNED_GEOMS])
 def test_attention_pinned_plans(geo, plan, family):
     hq, hkv, d = geo
@@ -474,6 +478,9 @@ def test_attention_pinned_plans(geo, plan, family):
                                          PL.offsets(case[5]), DEV), **plan)
     if plan.get("key_chunk"):
         assert full["key_chunk"] == plan["key_chunk"] and full["workspace_bytes"] > 0
+    if plan.get("stream_spans"):
+        assert full["stream_spans"] == plan["stream_spans"] and full["workspace_bytes"] > 0
+        assert full["workgroups"] == plan["stream_spans"] * hkv
     _attention_case(case, False, 4242 + d + hq, max_rows=120, plan=plan, family=family)
 
 
