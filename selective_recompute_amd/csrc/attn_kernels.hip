@@ -981,10 +981,16 @@ __global__ __launch_bounds__(64) void attn_simple_kernel(
   for (int u0 = lo; u0 <= hi; u0 += 64) {
     const int u = u0 + lane;
     float sc = -INFINITY;
-    if (u <= hi) {
+    if (u <= hi) {  // this lane's key row in 16-byte pieces (head_dim is a multiple of 8)
       const T *kr = k_fused + ((int64_t)u * hkv + g) * hd;
+      constexpr int VN = Vec16<T>::N;
       float dot = 0.f;
-      for (int d = 0; d < hd; ++d) dot = fmaf(qs[d], ld(kr + d), dot);
+      for (int d0 = 0; d0 < hd; d0 += VN) {
+        float kv[VN];
+        Vec16<T>::load(kr + d0, kv);
+#pragma unroll
+        for (int i = 0; i < VN; ++i) dot = fmaf(qs[d0 + i], kv[i], dot);
+      }
       sc = dot * scale;
     }
     const float m_new = fmaxf(m_run, wave_max(sc));
@@ -996,9 +1002,27 @@ __global__ __launch_bounds__(64) void attn_simple_kernel(
     __syncthreads();
     acc0 *= alpha;
     acc1 *= alpha;
+    // O += P V over this step's keys, eight V rows loaded before their products
     const int nk = min(64, hi - u0 + 1);
-    for (int kk = 0; kk < nk; ++kk) {
-      const T *vr = v_fused + ((int64_t)(u0 + kk) * hkv + g) * hd;
+    const T *vb = v_fused + ((int64_t)u0 * hkv + g) * hd;
+    const int64_t vstride = (int64_t)hkv * hd;
+    int kk = 0;
+    for (; kk + 8 <= nk; kk += 8) {
+      float v0[8], v1[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const T *vr = vb + (kk + j) * vstride;
+        v0[j] = lane < hd ? ld(vr + lane) : 0.f;
+        v1[j] = lane + 64 < hd ? ld(vr + lane + 64) : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        acc0 = fmaf(ps[kk + j], v0[j], acc0);
+        acc1 = fmaf(ps[kk + j], v1[j], acc1);
+      }
+    }
+    for (; kk < nk; ++kk) {
+      const T *vr = vb + kk * vstride;
       const float pk = ps[kk];
       if (lane < hd) acc0 = fmaf(pk, ld(vr + lane), acc0);
       if (lane + 64 < hd) acc1 = fmaf(pk, ld(vr + lane + 64), acc1);
