@@ -426,6 +426,42 @@ cb_status cb_blend_layer_order(const cb_layer_args *args, int32_t *order);
 #define CB_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 cb_status cb_blend_layer_noalloc(const cb_layer_args *args, void *stream);
 
+/*
+ * cb_check_indices -- checks on the device the index preconditions that the
+ * other calls do not check on the host (they would cost a device read):
+ *   CB_CHECK_CAND_RANGE    1  a cand_idx entry of request r lies outside
+ *                             [tok_off[r], tok_off[r+1])
+ *   CB_CHECK_CAND_ORDER    2  cand_idx does not ascend strictly within a request
+ *   CB_CHECK_SEL_RANGE     4  a sel_global entry lies outside its request's rows
+ *   CB_CHECK_SEL_ORDER     8  sel_global does not ascend strictly over the whole
+ *                             batch (cb_rerotate_fuse and CB_ORDER_SELECT_FIRST
+ *                             rely on it; a previous layer's selection always
+ *                             qualifies)
+ *   CB_CHECK_LOCAL_RANGE  16  a sel_local entry lies outside its request's
+ *                             candidate range
+ *   CB_CHECK_LOCAL_MISMATCH 32  cand_idx[sel_local[s]] != sel_global[s]
+ *
+ *   rg          : the ragged batch (tok_off, cand_off, sel_off on the device
+ *                 and their host mirrors; cand_off may be NULL when cand_idx
+ *                 and sel_local are)
+ *   cand_idx    : [M] or NULL (its checks skipped)
+ *   sel_local, sel_global : [K] or NULL (their checks skipped)
+ *   flags       : device int32, written with the OR of the violations found
+ *                 (0: every check passed); no clearing needed beforehand.
+ * One workgroup, stream-ordered, no allocation: a debugging aid, also safe
+ * under graph capture.  Errors: INVALID_ARG for a NULL flags or invalid
+ * offsets, before any HIP call.
+ */
+#define CB_CHECK_CAND_RANGE 1
+#define CB_CHECK_CAND_ORDER 2
+#define CB_CHECK_SEL_RANGE 4
+#define CB_CHECK_SEL_ORDER 8
+#define CB_CHECK_LOCAL_RANGE 16
+#define CB_CHECK_LOCAL_MISMATCH 32
+cb_status cb_check_indices(const cb_ragged *rg, const int32_t *cand_idx,
+                           const int32_t *sel_local, const int32_t *sel_global, int32_t *flags,
+                           void *stream);
+
 /* Static description of a status code. */
 const char *cb_status_str(cb_status status);
 /* Detail text of the calling thread's last failing call ("" if none). */

@@ -24,6 +24,8 @@ CB_DEV_V, CB_DEV_K, CB_DEV_KV = 0, 1, 2
 CB_ATTN_COUNTERS_ZERO = 1
 CB_LAYER_WORKSPACE_ZEROED = 1
 CB_SELECT_COUNTER_BYTES = 4096
+CB_CHECK_CAND_RANGE, CB_CHECK_CAND_ORDER, CB_CHECK_SEL_RANGE = 1, 2, 4
+CB_CHECK_SEL_ORDER, CB_CHECK_LOCAL_RANGE, CB_CHECK_LOCAL_MISMATCH = 8, 16, 32
 CB_ORDER_AUTO, CB_ORDER_ROTATE_FIRST, CB_ORDER_SELECT_FIRST = 0, 1, 2
 ORDERS = {"auto": CB_ORDER_AUTO, "rotate-first": CB_ORDER_ROTATE_FIRST,
           "select-first": CB_ORDER_SELECT_FIRST}
@@ -89,6 +91,8 @@ _SIGNATURES = {
     "cb_fuse_scatter": [ctypes.POINTER(Geom), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                         ctypes.c_void_p],
+    "cb_check_indices": [ctypes.POINTER(Ragged), ctypes.c_void_p, ctypes.c_void_p,
+                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p],
     "cb_rerotate_fuse": [ctypes.POINTER(Geom), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                          ctypes.c_int64, ctypes.c_int64, ctypes.c_double, ctypes.c_int32,
@@ -242,6 +246,17 @@ def fuse_scatter(g: Geom, k_fused, v_fused, k_new_c, v_new_c, sel_local, sel_glo
     check(lib().cb_fuse_scatter(ctypes.byref(g), _dev(k_fused), _dev(v_fused), _dev(k_new_c),
                                 _dev(v_new_c), _dev(sel_local, torch.int32),
                                 _dev(sel_global, torch.int32), k_total, _stream(stream)))
+
+
+def check_indices(rb: RaggedBatch, cand_idx=None, sel_local=None, sel_global=None,
+                  stream=None) -> torch.Tensor:
+    """cb_check_indices: a device int32 tensor with the OR of the violated
+    preconditions (0: all hold); the caller reads it when it wants to."""
+    flags = torch.empty(1, dtype=torch.int32, device=rb.tok.device)
+    check(lib().cb_check_indices(ctypes.byref(rb.struct()), _dev(cand_idx, torch.int32),
+                                 _dev(sel_local, torch.int32), _dev(sel_global, torch.int32),
+                                 _dev(flags, torch.int32), _stream(stream)))
+    return flags
 
 
 def rerotate_fuse(g: Geom, k, v, k_new_c, v_new_c, delta, sel_local, sel_global, k_total: int,

@@ -573,6 +573,19 @@ CB_EXPORT cb_status cb_topk(const cb_ragged *rg, const float *dev, const int32_t
                     "topk");
 }
 
+CB_EXPORT cb_status cb_check_indices(const cb_ragged *rg, const int32_t *cand_idx,
+                                     const int32_t *sel_local, const int32_t *sel_global,
+                                     int32_t *flags, void *stream) {
+  g_last_error.clear();
+  if (!flags) return fail(CB_ERR_INVALID_ARG, "flags is NULL");
+  const bool cands = cand_idx || sel_local;
+  CB_TRY(check_ragged(rg, true, cands, sel_local || sel_global));
+  return hip_status(cb::launch_check_indices(rg->tok_off, cands ? rg->cand_off : nullptr,
+                                             rg->sel_off, rg->n_req, cand_idx, sel_local,
+                                             sel_global, flags, (hipStream_t)stream),
+                    "check_indices");
+}
+
 CB_EXPORT cb_status cb_fuse_scatter(const cb_geom *geom, void *k_fused, void *v_fused,
                                     const void *k_new_c, const void *v_new_c,
                                     const int32_t *sel_local, const int32_t *sel_global,

@@ -57,6 +57,13 @@ hipError_t launch_deviation_select(int dtype, int style, void *k, const int32_t 
                                    const int32_t *h_cand_off, int32_t *sel_local,
                                    int32_t *sel_global, unsigned *cnt, hipStream_t stream);
 
+// Device-side check of the index preconditions (one workgroup); writes the
+// violation bits to *flags.  cand_idx / sel_local / sel_global may be NULL.
+hipError_t launch_check_indices(const int32_t *tok_off, const int32_t *cand_off,
+                                const int32_t *sel_off, int32_t n_req, const int32_t *cand_idx,
+                                const int32_t *sel_local, const int32_t *sel_global,
+                                int32_t *flags, hipStream_t stream);
+
 // Also sets clear[0 .. n_clear) to zero (the attention's arrival counters;
 // clear may be NULL when n_clear is 0).
 hipError_t launch_fuse(void *k_fused, void *v_fused, const void *k_new_c,

@@ -695,6 +695,62 @@ hipError_t launch_deviation_select(int dtype, int style, void *k, const int32_t 
 }
 
 // ---------------------------------------------------------------------------
+// Index preconditions, checked on the device (cb_check_indices): one
+// 1024-thread workgroup walks every request's candidates and selections and
+// ORs the violations it finds; the workgroup's OR is written to *flags, so
+// the word needs no clearing beforehand.  Reads only the arrays it is given.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void check_indices_kernel(
+    const int32_t *__restrict__ tok_off, const int32_t *__restrict__ cand_off,
+    const int32_t *__restrict__ sel_off, int32_t n_req, const int32_t *__restrict__ cand_idx,
+    const int32_t *__restrict__ sel_local, const int32_t *__restrict__ sel_global,
+    int32_t *__restrict__ flags) {
+  __shared__ int32_t s_flags;
+  if (threadIdx.x == 0) s_flags = 0;
+  __syncthreads();
+  int32_t f = 0;
+  for (int32_t r = 0; r < n_req; ++r) {
+    const int32_t t0 = tok_off[r], t1 = tok_off[r + 1];
+    if (cand_idx) {
+      const int32_t c0 = cand_off[r], c1 = cand_off[r + 1];
+      for (int32_t j = c0 + (int32_t)threadIdx.x; j < c1; j += kTopkThreads) {
+        const int32_t c = cand_idx[j];
+        if (c < t0 || c >= t1) f |= 1;                       // CB_CHECK_CAND_RANGE
+        if (j > c0 && cand_idx[j - 1] >= c) f |= 2;          // CB_CHECK_CAND_ORDER
+      }
+    }
+    if (sel_global || sel_local) {
+      const int32_t s0 = sel_off[r], s1 = sel_off[r + 1];
+      const int32_t c0 = cand_off ? cand_off[r] : 0, c1 = cand_off ? cand_off[r + 1] : 0;
+      for (int32_t j = s0 + (int32_t)threadIdx.x; j < s1; j += kTopkThreads) {
+        const int32_t gsel = sel_global ? sel_global[j] : 0;
+        if (sel_global) {
+          if (gsel < t0 || gsel >= t1) f |= 4;                // CB_CHECK_SEL_RANGE
+          if (j > 0 && sel_global[j - 1] >= gsel) f |= 8;     // CB_CHECK_SEL_ORDER (whole batch)
+        }
+        if (sel_local) {
+          const int32_t l = sel_local[j];
+          if (l < c0 || l >= c1) f |= 16;                     // CB_CHECK_LOCAL_RANGE
+          else if (cand_idx && sel_global && cand_idx[l] != gsel) f |= 32;  // CB_CHECK_LOCAL_MISMATCH
+        }
+      }
+    }
+  }
+  if (f) atomicOr(&s_flags, f);
+  __syncthreads();
+  if (threadIdx.x == 0) *flags = s_flags;
+}
+
+hipError_t launch_check_indices(const int32_t *tok_off, const int32_t *cand_off,
+                                const int32_t *sel_off, int32_t n_req, const int32_t *cand_idx,
+                                const int32_t *sel_local, const int32_t *sel_global,
+                                int32_t *flags, hipStream_t stream) {
+  hipLaunchKernelGGL(check_indices_kernel, dim3(1), dim3(kTopkThreads), 0, stream, tok_off,
+                     cand_off, sel_off, n_req, cand_idx, sel_local, sel_global, flags);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Fuse, [Derivations, "形式化"]: row sel_global[s] of K/V takes row
 // sel_local[s] of the recomputed tensors.  16-byte copies; a row is covered
 // by consecutive threads so every access is a contiguous run.

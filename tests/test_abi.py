@@ -65,6 +65,15 @@ def test_struct_layouts_match_the_header(tmp_path):
     assert got == want
 
 
+def test_check_indices_validates_on_the_host(lib):
+    rg, keep = _ragged([0, 10, 25], [0, 6, 13], [0, 2, 5])
+    assert lib.cb_check_indices(ctypes.byref(rg), P, P, P, None, None) == 1
+    assert b"flags" in lib.cb_last_error()
+    assert lib.cb_check_indices(None, P, P, P, P, None) == 1
+    bad, keep2 = _ragged([0, 10, 5], [0, 6, 13], [0, 2, 5])   # offsets that go down
+    assert lib.cb_check_indices(ctypes.byref(bad), P, P, P, P, None) == 1
+
+
 def test_status_strings(lib):
     assert lib.cb_status_str(0) == b"CB_OK"
     assert lib.cb_status_str(1) == b"CB_ERR_INVALID_ARG"
