@@ -507,6 +507,7 @@ cb_status run_attn(const cb_geom *geom, const cb_ragged *rg, const cb::AttnPlan 
   cb::AttnArgs a;
   a.out = out; a.q_c = q_c; a.sel_local = sel_local; a.sel_global = sel_global;
   a.k_fused = k_fused; a.v_fused = v_fused; a.tok_off = rg->tok_off; a.sel_off = rg->sel_off;
+  a.h_tok_off = rg->h_tok_off; a.h_sel_off = rg->h_sel_off;
   a.workspace = workspace;
   a.n_req = rg->n_req; a.k_total = rg->h_sel_off[rg->n_req];
   a.n_q_heads = geom->n_q_heads; a.n_kv_heads = geom->n_kv_heads; a.head_dim = geom->head_dim;

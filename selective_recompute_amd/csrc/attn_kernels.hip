@@ -84,6 +84,13 @@ struct AttnParams {
   float scale_log2;
 };
 
+// Launch order of whole-row units, passed by value (kernel arguments: the
+// table needs no device memory and is captured with the launch).
+constexpr int kMaxOrder = 960;
+struct AttnOrder {
+  uint32_t e[kMaxOrder];  // (request << 16) | query tile
+};
+
 constexpr int kKeyTile = 64;
 constexpr int kWaves = 8;              // waves per workgroup, two per SIMD
 constexpr int kQT = 32 * kWaves;       // query vectors per unit
@@ -847,6 +854,38 @@ void attn_mfma_kernel(const AttnParams p) {
   attn_piece<HD, KS>(p, g, pc, kst, vst, s_last);
 }
 
+// Whole-row units in a launch order chosen on the host: unit u of the launch
+// is query tile ord.e[u] & 0xFFFF of request ord.e[u] >> 16.  The hardware
+// hands out workgroups in launch order, so listing the longest rows first
+// leaves the short ones to fill the end of the launch (list scheduling,
+// longest first) instead of a long row of the last request.
+template <int HD, int KS>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_ordered_kernel(const AttnParams p, const AttnOrder ord) {
+  using C = AttnCfg<HD, KS>;
+  __shared__ __attribute__((aligned(1024))) bf16 kst[C::STAGES][C::TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 vst[C::STAGES][C::TILE];
+  __shared__ int s_last;
+  const int g = blockIdx.x % p.hkv;
+  const uint32_t e = ord.e[blockIdx.x / p.hkv];
+  Piece pc;
+  pc.r = (int)(e >> 16);
+  pc.tile = (int)(e & 0xFFFFu);
+  pc.s0 = p.sel_off[pc.r] + pc.tile * p.rows_per_tile;
+  pc.ns = min(p.rows_per_tile, p.sel_off[pc.r + 1] - pc.s0);
+  pc.lo = p.tok_off[pc.r];
+  pc.p_first = p.sel_global[pc.s0];
+  pc.p_last = p.sel_global[pc.s0 + pc.ns - 1];
+  pc.k_begin = pc.lo;
+  pc.k_end = pc.p_last + 1;
+  pc.n_active = 1;
+  pc.item = 0;
+  pc.own = nullptr;
+  pc.part0 = pc.part1 = nullptr;
+  pc.part_stride = 0;
+  attn_piece<HD, KS>(p, g, pc, kst, vst, s_last);
+}
+
 // The balanced decomposition (p.spans workgroups per KV head, key split 1).
 template <int HD>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
@@ -891,8 +930,12 @@ bool attn_stream_fits(int32_t n_req, int64_t tiles) {
 
 template <int HD, int KS>
 static hipError_t launch_hd(const AttnParams &p, const AttnPlan &plan, int n_kv_heads,
-                            hipStream_t stream) {
+                            const AttnOrder *ord, hipStream_t stream) {
   const dim3 grid((unsigned)(plan.units * n_kv_heads)), block(64 * kWaves);
+  if (ord) {
+    hipLaunchKernelGGL((attn_ordered_kernel<HD, KS>), grid, block, 0, stream, p, *ord);
+    return hipGetLastError();
+  }
   if constexpr (KS == 1) {
     if (plan.spans > 0) {
       hipLaunchKernelGGL((attn_stream_kernel<HD>), grid, block, 0, stream, p);
@@ -901,6 +944,39 @@ static hipError_t launch_hd(const AttnParams &p, const AttnPlan &plan, int n_kv_
   }
   hipLaunchKernelGGL((attn_mfma_kernel<HD, KS>), grid, block, 0, stream, p);
   return hipGetLastError();
+}
+
+// Longest-first launch order of a whole-row plan over several requests, or
+// false where the default order stands (one request: its tiles already run
+// last tile first; split or balanced plans; more units than the table
+// holds).  A tile's row ends at its last selected row's position, which only
+// the device knows; the host estimates it as if request r's k_r selected
+// rows were spread evenly over its n_r tokens: rows_end * n_r / k_r.
+static bool build_order(const AttnArgs &a, const AttnPlan &plan, AttnOrder &ord) {
+  if (plan.split || plan.spans > 0 || a.n_req < 2 || plan.units > kMaxOrder) return false;
+  if (!a.h_tok_off || !a.h_sel_off) return false;
+  struct Item { double est; int32_t r, tile; };
+  Item items[kMaxOrder];
+  int n = 0;
+  const int rows = plan.rows_per_tile;
+  for (int32_t r = 0; r < a.n_req; ++r) {
+    const int64_t kr = (int64_t)a.h_sel_off[r + 1] - a.h_sel_off[r];
+    const int64_t nr = (int64_t)a.h_tok_off[r + 1] - a.h_tok_off[r];
+    const int64_t tr = (kr + rows - 1) / rows;
+    if (r > 0xFFFF || tr > 0x10000 || n + tr > kMaxOrder) return false;
+    for (int64_t t = 0; t < tr; ++t) {
+      const int64_t end = std::min<int64_t>(kr, (t + 1) * rows);
+      items[n++] = {(double)end * (double)nr / (double)kr, r, (int32_t)t};
+    }
+  }
+  if (n != plan.units) return false;
+  std::sort(items, items + n, [](const Item &x, const Item &y) {
+    if (x.est != y.est) return x.est > y.est;
+    if (x.r != y.r) return x.r < y.r;
+    return x.tile > y.tile;
+  });
+  for (int i = 0; i < n; ++i) ord.e[i] = ((uint32_t)items[i].r << 16) | (uint32_t)items[i].tile;
+  return true;
 }
 
 hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &plan, bool counters_zero,
@@ -937,17 +1013,19 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &plan, bool counte
     if (e != hipSuccess) return e;
   }
   const int h = a.n_kv_heads;
+  static thread_local AttnOrder order;
+  const AttnOrder *ord = build_order(a, plan, order) ? &order : nullptr;
   if (plan.key_split == 2) {
     switch (a.head_dim) {
-      case 32: return launch_hd<32, 2>(p, plan, h, stream);
-      case 64: return launch_hd<64, 2>(p, plan, h, stream);
-      default: return launch_hd<128, 2>(p, plan, h, stream);
+      case 32: return launch_hd<32, 2>(p, plan, h, ord, stream);
+      case 64: return launch_hd<64, 2>(p, plan, h, ord, stream);
+      default: return launch_hd<128, 2>(p, plan, h, ord, stream);
     }
   }
   switch (a.head_dim) {
-    case 32: return launch_hd<32, 1>(p, plan, h, stream);
-    case 64: return launch_hd<64, 1>(p, plan, h, stream);
-    default: return launch_hd<128, 1>(p, plan, h, stream);
+    case 32: return launch_hd<32, 1>(p, plan, h, ord, stream);
+    case 64: return launch_hd<64, 1>(p, plan, h, ord, stream);
+    default: return launch_hd<128, 1>(p, plan, h, ord, stream);
   }
 }
 

@@ -92,6 +92,8 @@ struct AttnArgs {
   const void *v_fused;
   const int32_t *tok_off;
   const int32_t *sel_off;
+  const int32_t *h_tok_off;  // host mirrors of tok_off / sel_off (launch order)
+  const int32_t *h_sel_off;
   void *workspace;
   int32_t n_req;
   int32_t k_total;
