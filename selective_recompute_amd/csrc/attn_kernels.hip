@@ -84,11 +84,14 @@ struct AttnParams {
   float scale_log2;
 };
 
-// Launch order of whole-row units, passed by value (kernel arguments: the
-// table needs no device memory and is captured with the launch).
-constexpr int kMaxOrder = 960;
+// Launch order of the units, passed by value (kernel arguments: the table
+// needs no device memory and is captured with the launch).  Sized to the
+// launch: kernel arguments travel to the device with every launch, and a
+// short launch feels 4 KB of them.
+constexpr int kMaxOrder = kAttnMaxOrder;
+template <int N>
 struct AttnOrder {
-  uint32_t e[kMaxOrder];  // (request << 16) | query tile
+  uint32_t e[N];  // units, by their index in the kernel's own order
 };
 
 constexpr int kKeyTile = 64;
@@ -817,17 +820,16 @@ __device__ __attribute__((always_inline)) void attn_stream(
   }
 }
 
+// Unit u of the (query tile, key chunk) decomposition, KV head g.  Unit
+// ubase + c * tr + (tr - 1 - tile) of a request is chunk c of its query tile
+// `tile`; its partial (when the tile is split) sits in slot u * hkv + g.
 template <int HD, int KS>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
-void attn_mfma_kernel(const AttnParams p) {
+__device__ __attribute__((always_inline)) void attn_unit(
+    const AttnParams &p, const int u, const int g, bf16 (*kst)[AttnCfg<HD, KS>::TILE],
+    bf16 (*vst)[AttnCfg<HD, KS>::TILE], int &s_last) {
   using C = AttnCfg<HD, KS>;
-  __shared__ __attribute__((aligned(1024))) bf16 kst[C::STAGES][C::TILE];
-  __shared__ __attribute__((aligned(1024))) bf16 vst[C::STAGES][C::TILE];
-  __shared__ int s_last;
-  const int g = blockIdx.x % p.hkv;
-  // (query tile, key chunk) units
   UnitPos up;
-  if (!locate_unit(p, (int)(blockIdx.x / p.hkv), up)) return;
+  if (!locate_unit(p, u, up)) return;
   Piece pc;
   pc.r = up.r;
   pc.tile = up.tile;
@@ -843,9 +845,8 @@ void attn_mfma_kernel(const AttnParams p) {
   pc.n_active = (int)((pc.p_last - pc.lo) / p.key_chunk) + 1;
   pc.item = up.tbase + pc.tile;
   constexpr int64_t UNIT = partial_bytes<HD, C::QT>();
-  // unit of (tile, chunk c): ubase + c * tr + (tr - 1 - tile)
   const int64_t ustride = (int64_t)up.tr * p.hkv * UNIT;
-  pc.own = pc.n_active > 1 ? p.ws + (int64_t)blockIdx.x * UNIT : nullptr;
+  pc.own = pc.n_active > 1 ? p.ws + ((int64_t)u * p.hkv + g) * UNIT : nullptr;
   pc.part0 = pc.n_active > 1
                  ? p.ws + ((up.ubase + (int64_t)(up.tr - 1 - pc.tile)) * p.hkv + g) * UNIT
                  : nullptr;
@@ -854,36 +855,33 @@ void attn_mfma_kernel(const AttnParams p) {
   attn_piece<HD, KS>(p, g, pc, kst, vst, s_last);
 }
 
-// Whole-row units in a launch order chosen on the host: unit u of the launch
-// is query tile ord.e[u] & 0xFFFF of request ord.e[u] >> 16.  The hardware
-// hands out workgroups in launch order, so listing the longest rows first
-// leaves the short ones to fill the end of the launch (list scheduling,
-// longest first) instead of a long row of the last request.
+// Units in their own order: workgroup b runs unit b / hkv of KV head b % hkv
+// (within a request chunk by chunk, each chunk from its last query tile to
+// its first).
 template <int HD, int KS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
-void attn_ordered_kernel(const AttnParams p, const AttnOrder ord) {
+void attn_mfma_kernel(const AttnParams p) {
   using C = AttnCfg<HD, KS>;
   __shared__ __attribute__((aligned(1024))) bf16 kst[C::STAGES][C::TILE];
   __shared__ __attribute__((aligned(1024))) bf16 vst[C::STAGES][C::TILE];
   __shared__ int s_last;
-  const int g = blockIdx.x % p.hkv;
-  const uint32_t e = ord.e[blockIdx.x / p.hkv];
-  Piece pc;
-  pc.r = (int)(e >> 16);
-  pc.tile = (int)(e & 0xFFFFu);
-  pc.s0 = p.sel_off[pc.r] + pc.tile * p.rows_per_tile;
-  pc.ns = min(p.rows_per_tile, p.sel_off[pc.r + 1] - pc.s0);
-  pc.lo = p.tok_off[pc.r];
-  pc.p_first = p.sel_global[pc.s0];
-  pc.p_last = p.sel_global[pc.s0 + pc.ns - 1];
-  pc.k_begin = pc.lo;
-  pc.k_end = pc.p_last + 1;
-  pc.n_active = 1;
-  pc.item = 0;
-  pc.own = nullptr;
-  pc.part0 = pc.part1 = nullptr;
-  pc.part_stride = 0;
-  attn_piece<HD, KS>(p, g, pc, kst, vst, s_last);
+  attn_unit<HD, KS>(p, (int)(blockIdx.x / p.hkv), (int)(blockIdx.x % p.hkv), kst, vst, s_last);
+}
+
+// Units in a launch order chosen on the host: workgroup b runs unit
+// ord.e[b / hkv] of KV head b % hkv.  The hardware hands out workgroups in
+// launch order, so listing the longest pieces first leaves the short ones to
+// fill the end of the launch (list scheduling, longest first) instead of a
+// long row of the last request or the last key chunk of a long row.
+template <int HD, int KS, int N>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_ordered_kernel(const AttnParams p, const AttnOrder<N> ord) {
+  using C = AttnCfg<HD, KS>;
+  __shared__ __attribute__((aligned(1024))) bf16 kst[C::STAGES][C::TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 vst[C::STAGES][C::TILE];
+  __shared__ int s_last;
+  attn_unit<HD, KS>(p, (int)ord.e[blockIdx.x / p.hkv], (int)(blockIdx.x % p.hkv), kst, vst,
+                    s_last);
 }
 
 // The balanced decomposition (p.spans workgroups per KV head, key split 1).
@@ -928,13 +926,23 @@ bool attn_stream_fits(int32_t n_req, int64_t tiles) {
   return n_req <= kStreamMaxRequests && tiles <= kStreamMaxTiles;
 }
 
+template <int HD, int KS, int N>
+static hipError_t launch_ordered(const AttnParams &p, const dim3 grid, const uint32_t *ord,
+                                 int64_t n, hipStream_t stream) {
+  AttnOrder<N> o;
+  std::copy(ord, ord + n, o.e);
+  hipLaunchKernelGGL((attn_ordered_kernel<HD, KS, N>), grid, dim3(64 * kWaves), 0, stream, p, o);
+  return hipGetLastError();
+}
+
 template <int HD, int KS>
 static hipError_t launch_hd(const AttnParams &p, const AttnPlan &plan, int n_kv_heads,
-                            const AttnOrder *ord, hipStream_t stream) {
+                            const uint32_t *ord, hipStream_t stream) {
   const dim3 grid((unsigned)(plan.units * n_kv_heads)), block(64 * kWaves);
   if (ord) {
-    hipLaunchKernelGGL((attn_ordered_kernel<HD, KS>), grid, block, 0, stream, p, *ord);
-    return hipGetLastError();
+    if (plan.units <= 64) return launch_ordered<HD, KS, 64>(p, grid, ord, plan.units, stream);
+    if (plan.units <= 256) return launch_ordered<HD, KS, 256>(p, grid, ord, plan.units, stream);
+    return launch_ordered<HD, KS, kMaxOrder>(p, grid, ord, plan.units, stream);
   }
   if constexpr (KS == 1) {
     if (plan.spans > 0) {
@@ -946,36 +954,41 @@ static hipError_t launch_hd(const AttnParams &p, const AttnPlan &plan, int n_kv_
   return hipGetLastError();
 }
 
-// Longest-first launch order of a whole-row plan over several requests, or
-// false where the default order stands (one request: its tiles already run
-// last tile first; split or balanced plans; more units than the table
-// holds).  A tile's row ends at its last selected row's position, which only
-// the device knows; the host estimates it as if request r's k_r selected
-// rows were spread evenly over its n_r tokens: rows_end * n_r / k_r.
-static bool build_order(const AttnArgs &a, const AttnPlan &plan, AttnOrder &ord) {
-  if (plan.split || plan.spans > 0 || a.n_req < 2 || plan.units > kMaxOrder) return false;
+// Longest-first launch order of a plan's units, or false where the kernel's
+// own order stands (the balanced decomposition; one request unsplit, whose
+// tiles already run last tile first; more units than the table holds).  A
+// tile's row ends at its last selected row's position, which only the device
+// knows; the host estimates it as if request r's k_r selected rows were
+// spread evenly over its n_r tokens (rows_end * n_r / k_r) and ranks units by
+// the keys of their chunk before that end.
+static bool attn_launch_order(const AttnArgs &a, const AttnPlan &plan, uint32_t *ord) {
+  if (plan.spans > 0 || (a.n_req < 2 && !plan.split) || plan.units > kMaxOrder) return false;
   if (!a.h_tok_off || !a.h_sel_off) return false;
-  struct Item { double est; int32_t r, tile; };
+  struct Item { int64_t keys; uint32_t u; };
   Item items[kMaxOrder];
-  int n = 0;
+  int64_t n = 0, ubase = 0;
   const int rows = plan.rows_per_tile;
+  const int64_t kc = plan.key_chunk;
   for (int32_t r = 0; r < a.n_req; ++r) {
     const int64_t kr = (int64_t)a.h_sel_off[r + 1] - a.h_sel_off[r];
     const int64_t nr = (int64_t)a.h_tok_off[r + 1] - a.h_tok_off[r];
     const int64_t tr = (kr + rows - 1) / rows;
-    if (r > 0xFFFF || tr > 0x10000 || n + tr > kMaxOrder) return false;
-    for (int64_t t = 0; t < tr; ++t) {
-      const int64_t end = std::min<int64_t>(kr, (t + 1) * rows);
-      items[n++] = {(double)end * (double)nr / (double)kr, r, (int32_t)t};
-    }
+    const int64_t cr = (nr + kc - 1) / kc;
+    if (n + tr * cr > kMaxOrder) return false;
+    for (int64_t c = 0; c < cr; ++c)
+      for (int64_t t = 0; t < tr; ++t) {
+        const int64_t end = (std::min<int64_t>(kr, (t + 1) * rows) * nr + kr - 1) / kr;
+        const int64_t keys = std::max<int64_t>(0, std::min(end, (c + 1) * kc) - c * kc);
+        items[n++] = {keys, (uint32_t)(ubase + c * tr + (tr - 1 - t))};
+      }
+    ubase += tr * cr;
   }
   if (n != plan.units) return false;
+  if (!ord) return true;
   std::sort(items, items + n, [](const Item &x, const Item &y) {
-    if (x.est != y.est) return x.est > y.est;
-    if (x.r != y.r) return x.r < y.r;
-    return x.tile > y.tile;
+    return x.keys != y.keys ? x.keys > y.keys : x.u < y.u;
   });
-  for (int i = 0; i < n; ++i) ord.e[i] = ((uint32_t)items[i].r << 16) | (uint32_t)items[i].tile;
+  for (int64_t i = 0; i < n; ++i) ord[i] = items[i].u;
   return true;
 }
 
@@ -1013,8 +1026,8 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &plan, bool counte
     if (e != hipSuccess) return e;
   }
   const int h = a.n_kv_heads;
-  static thread_local AttnOrder order;
-  const AttnOrder *ord = build_order(a, plan, order) ? &order : nullptr;
+  static thread_local uint32_t order[kMaxOrder];
+  const uint32_t *ord = attn_launch_order(a, plan, order) ? order : nullptr;
   if (plan.key_split == 2) {
     switch (a.head_dim) {
       case 32: return launch_hd<32, 2>(p, plan, h, ord, stream);

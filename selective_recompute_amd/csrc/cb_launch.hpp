@@ -130,6 +130,11 @@ int attn_max_chunks();
 // Whether a batch fits the balanced decomposition's tables (requests, query tiles).
 bool attn_stream_fits(int32_t n_req, int64_t tiles);
 
+// Most units whose launch order the host can choose (a table in the kernel
+// arguments); plans with more units, or of the balanced decomposition, or
+// of one unsplit request run in the kernel's own order.
+constexpr int kAttnMaxOrder = 960;
+
 // counters_zero: the split's arrival counters are already zero (cleared by
 // the preceding fuse launch); otherwise a clear launch goes first.
 hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &plan, bool counters_zero,

@@ -1,15 +1,18 @@
-"""The launch order of whole-row attention units does not change results.
+"""The launch order of attention units does not change results.
 
-A plan whose units are whole rows over several requests launches its query
-tiles longest row first, in an order the host estimates from the request
-sizes; a single request keeps the default order.  Every unit computes the
-same numbers wherever it sits in the launch, so each request's rows of a
-batched launch must equal, bit for bit, those of a launch over that request
-alone ([Derivations, "形式化"]: each selected row attends over its own
-request's keys only).  Cases: the 70B-shaped batch's ragged requests with
-rows spread at random, many small requests (some with nothing selected), and
-more query tiles than the order table holds (the default order).  The batched
-outputs are also checked against the oracle on sampled rows.
+Plans over several requests, and split plans, launch their units longest
+piece first, in an order the host estimates from the request sizes (a single
+unsplit request keeps the kernel's own order, which is already that).  Every
+unit computes the same numbers wherever it sits in the launch, and a split
+tile merges its pieces in piece order whichever arrives last, so each
+request's rows of a batched launch must equal, bit for bit, those of a
+launch over that request alone ([Derivations, "形式化"]: each selected row
+attends over its own request's keys only) -- a launch whose units come in
+another order.  Cases: the 70B-shaped batch's ragged requests with rows
+spread at random, many small requests (some with nothing selected), and more
+units than the order table holds (the kernel's own order); whole rows, and
+rows split over key chunks with either key split.  The batched outputs are
+also checked against the oracle on sampled rows.
 """
 import math
 
@@ -50,11 +53,23 @@ def _case(name):
     raise KeyError(name)
 
 
-@pytest.mark.parametrize("name", ["70b-8req", "40-small", "1000-tiles"])
-def test_batched_rows_equal_single_request_launches(name):
+SPLIT_KS1 = dict(mfma=1, key_split=1, key_chunk=512)
+SPLIT_KS2 = dict(mfma=1, key_split=2, key_chunk=768)
+SPLIT_6K = dict(mfma=1, key_split=1, key_chunk=6144)
+
+
+def _ws(geo, rb, plan):
+    n = B.describe_plan(geo, rb, **plan)["workspace_bytes"]
+    return B.workspace_tensor(max(n, 256), DEV)
+
+
+@pytest.mark.parametrize("name,plan", [("70b-8req", WHOLE_ROWS), ("70b-8req", SPLIT_6K),
+                                       ("40-small", WHOLE_ROWS), ("40-small", SPLIT_KS1),
+                                       ("40-small", SPLIT_KS2), ("1000-tiles", WHOLE_ROWS)])
+def test_batched_rows_equal_single_request_launches(name, plan):
     hq, hkv, lens, ks = _case(name)
     d = 128
-    say(f"{name}: {len(lens)} requests, {sum(lens)} tokens, {sum(ks)} rows")
+    say(f"{name}: {len(lens)} requests, {sum(lens)} tokens, {sum(ks)} rows, plan {plan}")
     rng = np.random.default_rng(11)
     tok_off, sel_off = PL.offsets(lens), PL.offsets(ks)
     sel = np.concatenate([np.sort(rng.choice(n, k, replace=False)) + tok_off[r]
@@ -70,7 +85,8 @@ def test_batched_rows_equal_single_request_launches(name):
     sl = torch.arange(n_sel, dtype=torch.int32, device=DEV)
     sg = torch.from_numpy(sel).to(DEV)
     out = torch.full((n_sel, hq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
-    B.partial_attn_with_plan(geo, rb, WHOLE_ROWS, out, q, sl, sg, k, v, scale)
+    B.partial_attn_with_plan(geo, rb, plan, out, q, sl, sg, k, v, scale,
+                             workspace=_ws(geo, rb, plan))
     torch.cuda.synchronize()
     assert not torch.isnan(out).any(), "a row of the batched launch was not written"
 
@@ -80,9 +96,10 @@ def test_batched_rows_equal_single_request_launches(name):
         lo, s0, s1 = int(tok_off[r]), int(sel_off[r]), int(sel_off[r + 1])
         rb1 = B.RaggedBatch(np.array([0, n]), np.array([0, n]), np.array([0, kr]), DEV)
         out1 = torch.full((kr, hq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
-        B.partial_attn_with_plan(geo, rb1, WHOLE_ROWS, out1, q[s0:s1],
+        B.partial_attn_with_plan(geo, rb1, plan, out1, q[s0:s1],
                                  torch.arange(kr, dtype=torch.int32, device=DEV),
-                                 sg[s0:s1] - lo, k[lo:lo + n], v[lo:lo + n], scale)
+                                 sg[s0:s1] - lo, k[lo:lo + n], v[lo:lo + n], scale,
+                                 workspace=_ws(geo, rb1, plan))
         torch.cuda.synchronize()
         assert torch.equal(out[s0:s1], out1), f"request {r}: batched rows differ from its own launch"
 
