@@ -1026,7 +1026,7 @@ hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &plan, bool counte
     if (e != hipSuccess) return e;
   }
   const int h = a.n_kv_heads;
-  static thread_local uint32_t order[kMaxOrder];
+  uint32_t order[kMaxOrder];  // on the stack: the library keeps no state between calls
   const uint32_t *ord = attn_launch_order(a, plan, order) ? order : nullptr;
   if (plan.key_split == 2) {
     switch (a.head_dim) {
