@@ -241,15 +241,17 @@ cb_status validate_attn(const cb_geom *geom, const cb_ragged *rg, void *out, con
 constexpr int kNoSplit = 1 << 30;
 
 // Cost model of one MFMA attention launch, for choosing the key split and
-// the key chunk.  The figures were measured on MI355X at head_dim 128 (they
-// scale with head_dim): 64 keys of a 256-query unit take ~2.1 us with every
-// CU busy, and kKeySplitTile of that for a 128-query unit whose 128-key
-// tiles are split over two wave groups; a workgroup spends ~3.6 us before
-// its first tile (three dependent loads: request offsets, selected rows, Q)
-// and, when split, ~1 us storing its partial; the last working unit of a
-// split tile then spends kMergeUs arriving (fences and the counter) plus
+// the key chunk.  The figures are in microseconds at head_dim 128 (they
+// scale with head_dim), fitted on MI355X to the measured best plans of the
+// 2k-, 6k- and 32k-token single-request shapes over key splits and chunk
+// sizes: 64 keys of a 256-query unit take ~1.6 us on a lightly loaded chip,
+// and kKeySplitTile of that for a 128-query unit whose 128-key tiles are
+// split over two wave groups; a workgroup spends ~3.6 us before its first
+// tile (three dependent loads: request offsets, selected rows, Q) and, when
+// split, ~5 us storing its partial at the coherence point and signalling;
+// the last working unit of a split tile then spends kMergeUs arriving plus
 // kMergePairUs per two other partials it loads and merges.
-constexpr double kTileUs = 2.1, kSetupUs = 3.6, kPartialUs = 1.0;
+constexpr double kTileUs = 1.6, kSetupUs = 3.6, kPartialUs = 5.0;
 constexpr double kKeySplitTile = 0.55;
 constexpr double kMergeUs = 1.0, kMergePairUs = 1.0;
 // CUs the simulated dispatch fills: 240 of the 256, a margin against plans
@@ -260,30 +262,33 @@ constexpr int kSimCUs = 240;
 // rows per tile and key chunk `kc` (kNoSplit: none), and the number of units
 // that do work.  The selected rows of a request are taken as evenly spread
 // over its tokens, so query tile t ends near position min(k, (t+1) rows) n / k.
-// Units are dispatched in the kernel's order (request by request, chunk by
-// chunk, longest tile first), each to the earliest free group of CUs; the
-// n_kv_heads workgroups of a unit run side by side, so one "slot" stands for
-// n_kv_heads CUs.  A split tile ends when its last unit has merged.
+// Units are dispatched in launch order, each to the earliest free group of
+// CUs: longest unit first where cb::launch_attn_mfma orders the launch
+// (split plans and several requests, up to cb::kAttnMaxOrder units), else
+// the kernel's own order (request by request, chunk by chunk, longest tile
+// first).  The n_kv_heads workgroups of a unit run side by side, so one
+// "slot" stands for n_kv_heads CUs.  A split tile ends when its last unit
+// has merged.
 double estimate_attn_us(const cb_geom *g, const cb_ragged *rg, int ks, int rows, int64_t kc,
                         int64_t *active) {
   const int n_slots = std::max(1, kSimCUs / g->n_kv_heads);
   const double tile_us = kTileUs * g->head_dim / 128.0 * (ks == 2 ? kKeySplitTile : 1.0);
   const double partial_us = kPartialUs / ks;
   const int64_t kt = 64 * ks;  // keys per tile
-  std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
-  for (int i = 0; i < n_slots; ++i) free_at.push(0.0);
-  int64_t busy = 0;
-  double makespan = 0.0;
-  std::vector<double> tile_end;
+  struct Unit { double us; int64_t tile; };  // tile: index over all requests
+  std::vector<Unit> units;
   std::vector<int> tile_units;
+  int64_t tbase = 0, all_units = 0;
+  bool split = false;
   for (int32_t r = 0; r < rg->n_req; ++r) {
     const int64_t k = rg->h_sel_off[r + 1] - rg->h_sel_off[r];
     const int64_t n = rg->h_tok_off[r + 1] - rg->h_tok_off[r];
     if (k == 0) continue;
     const int64_t tiles = (k + rows - 1) / rows;
     const int64_t chunks = (n + kc - 1) / kc;
-    tile_end.assign((size_t)tiles, 0.0);
-    tile_units.assign((size_t)tiles, 0);
+    all_units += tiles * chunks;
+    if (chunks > 1) split = true;
+    tile_units.resize((size_t)(tbase + tiles), 0);
     for (int64_t c = 0; c < chunks; ++c)
       for (int64_t t = tiles - 1; t >= 0; --t) {
         const int64_t end = (std::min(k, (t + 1) * rows) * n + k - 1) / k;
@@ -291,20 +296,30 @@ double estimate_attn_us(const cb_geom *g, const cb_ragged *rg, int ks, int rows,
         if (hi <= lo) continue;
         const double us = kSetupUs + (double)((hi - lo + kt - 1) / kt * ks) * tile_us +
                           (chunks > 1 ? partial_us : 0.0);
-        const double start = free_at.top();
-        free_at.pop();
-        free_at.push(start + us);
-        tile_end[(size_t)t] = std::max(tile_end[(size_t)t], start + us);
-        ++tile_units[(size_t)t];
-        ++busy;
+        units.push_back({us, tbase + t});
+        ++tile_units[(size_t)(tbase + t)];
       }
-    for (int64_t t = 0; t < tiles; ++t) {
-      const int u = tile_units[(size_t)t];
-      const double merge = u > 1 ? kMergeUs + (double)(u / 2) * kMergePairUs : 0.0;
-      makespan = std::max(makespan, tile_end[(size_t)t] + merge);
-    }
+    tbase += tiles;
   }
-  *active = busy;
+  if ((split || rg->n_req > 1) && all_units <= cb::kAttnMaxOrder)
+    std::stable_sort(units.begin(), units.end(),
+                     [](const Unit &x, const Unit &y) { return x.us > y.us; });
+  std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
+  for (int i = 0; i < n_slots; ++i) free_at.push(0.0);
+  std::vector<double> tile_end((size_t)tbase, 0.0);
+  for (const Unit &u : units) {
+    const double start = free_at.top();
+    free_at.pop();
+    free_at.push(start + u.us);
+    tile_end[(size_t)u.tile] = std::max(tile_end[(size_t)u.tile], start + u.us);
+  }
+  double makespan = 0.0;
+  for (int64_t t = 0; t < tbase; ++t) {
+    const int u = tile_units[(size_t)t];
+    const double merge = u > 1 ? kMergeUs + (double)(u / 2) * kMergePairUs : 0.0;
+    makespan = std::max(makespan, tile_end[(size_t)t] + merge);
+  }
+  *active = (int64_t)units.size();
   return makespan;
 }
 

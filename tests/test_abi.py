@@ -357,9 +357,11 @@ def test_attention_plan_choices(lib):
     # 2.88 ms against 2.92 with key split 2 in two chunks of 3072 keys)
     p = _plan(lib, _geom(), [0, 6144], [0, 922])
     assert fields(p) == (1, 1, 64, 2048, 15, 360) and p.workspace_bytes == _split_ws(1, 360, 15, 8)
-    # 3277 of 32768 rows: 52 tiles, unsplit (978 us against 1027 with key split 2)
+    # 3277 of 32768 rows: 52 tiles over four chunks of 8192 keys, launched
+    # longest piece first (858 us against 912 unsplit and 867-889 for the
+    # other chunkings, attention alone, one box)
     p = _plan(lib, _geom(), [0, 32768], [0, 3277])
-    assert fields(p) == (1, 1, 64, 0, 52, 416)
+    assert fields(p) == (1, 1, 64, 8192, 52, 1664)
     # 1024 workgroups or more: always key split 1 unsplit
     p = _plan(lib, _geom(), [0, 65536], [0, 16384])
     assert fields(p) == (1, 1, 64, 0, 256, 2048) and p.workspace_bytes == 0
