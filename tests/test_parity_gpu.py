@@ -367,14 +367,13 @@ def _attention_case(case, use_ws, seed, max_rows=None, plan=None, family="random
     elif use_ws:
         nbytes = B.attn_workspace_bytes(g, rb)
         if nbytes == 0:
-            # the planner keeps every row whole: the geometry runs the plain
-            # kernel (no split at all), or no request with selected rows is
-            # longer than the shortest key chunk (256 keys); the call then
-            # takes no workspace and the parity below checks that path
+            # the planner keeps every row whole (the plain kernel, rows no
+            # longer than the shortest key chunk, or rows short enough that
+            # its cost model prices a partial and a merge above the split's
+            # gain -- its choices are pinned on the host in test_abi.py); the
+            # call then takes no workspace and the parity below checks that path
             chosen = B.attn_plan(g, rb)
             assert chosen["key_chunk"] == 0 and chosen["workspace_bytes"] == 0
-            longest = max(n for n, k in zip(lens, ks) if k)
-            assert chosen["mfma"] == 0 or longest <= 256, (chosen, longest)
         else:
             ws = B.workspace_tensor(nbytes, DEV)
             ws.fill_(0xFF)                                    # NaN garbage: must be overwritten
