@@ -114,3 +114,44 @@ def test_batched_rows_equal_single_request_launches(name, plan):
     got = out[torch.from_numpy(pick).to(DEV)].float().cpu().numpy()
     err = np.abs(got - ref).max()
     assert err <= ATTN_ABS, f"attention max err {err}"
+
+
+@pytest.mark.parametrize("n_req", [64, 65, 256, 257, 960, 961])
+def test_order_table_sizes(n_req):
+    """The launch order travels in a table sized to the launch (64, 256 or
+    960 units; more keep the kernel's own order).  Requests of 64 tokens
+    with 8 selected rows are one query tile each (64 Q / 8 KV heads: 32 rows
+    per tile), so n_req units: each size at its edge and one past it.  Every
+    row is written, and sampled requests equal their own launches bit for
+    bit."""
+    hq, hkv, d = 64, 8, 128
+    lens, ks = [64] * n_req, [8] * n_req
+    say(f"order table: {n_req} one-tile requests")
+    rng = np.random.default_rng(n_req)
+    tok_off, sel_off = PL.offsets(lens), PL.offsets(ks)
+    sel = np.concatenate([np.sort(rng.choice(64, 8, replace=False)) + tok_off[r]
+                          for r in range(n_req)]).astype(np.int32)
+    gen = torch.Generator(device=DEV).manual_seed(n_req)
+    q = torch.randn(len(sel), hq, d, generator=gen, device=DEV).to(torch.bfloat16)
+    k = torch.randn(int(tok_off[-1]), hkv, d, generator=gen, device=DEV).to(torch.bfloat16)
+    v = torch.randn(int(tok_off[-1]), hkv, d, generator=gen, device=DEV).to(torch.bfloat16)
+    geo = B.geom(hq, hkv, d, torch.bfloat16)
+    scale = 1.0 / math.sqrt(d)
+    rb = B.RaggedBatch(tok_off, tok_off, sel_off, DEV)
+    assert B.describe_plan(geo, rb, **WHOLE_ROWS)["tiles"] == n_req
+    sg = torch.from_numpy(sel).to(DEV)
+    out = torch.full((len(sel), hq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    B.partial_attn_with_plan(geo, rb, WHOLE_ROWS, out, q,
+                             torch.arange(len(sel), dtype=torch.int32, device=DEV), sg, k, v,
+                             scale)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any(), "a row of the batched launch was not written"
+    rb1 = B.RaggedBatch(np.array([0, 64]), np.array([0, 64]), np.array([0, 8]), DEV)
+    for r in sorted({0, n_req // 2, n_req - 1} | set(range(0, n_req, 97))):
+        lo, s0 = int(tok_off[r]), int(sel_off[r])
+        out1 = torch.full((8, hq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+        B.partial_attn_with_plan(geo, rb1, WHOLE_ROWS, out1, q[s0:s0 + 8],
+                                 torch.arange(8, dtype=torch.int32, device=DEV),
+                                 sg[s0:s0 + 8] - lo, k[lo:lo + 64], v[lo:lo + 64], scale)
+        torch.cuda.synchronize()
+        assert torch.equal(out[s0:s0 + 8], out1), f"request {r}"
