@@ -929,7 +929,7 @@ bool attn_stream_fits(int32_t n_req, int64_t tiles) {
 template <int HD, int KS, int N>
 static hipError_t launch_ordered(const AttnParams &p, const dim3 grid, const uint32_t *ord,
                                  int64_t n, hipStream_t stream) {
-  AttnOrder<N> o;
+  AttnOrder<N> o{};  // entries past n are never read; zeroed all the same
   std::copy(ord, ord + n, o.e);
   hipLaunchKernelGGL((attn_ordered_kernel<HD, KS, N>), grid, dim3(64 * kWaves), 0, stream, p, o);
   return hipGetLastError();
