@@ -254,9 +254,9 @@ typedef struct cb_attn_plan {
                              keys (their partials go to the workspace); 0: no split */
   int64_t tiles;          /* MFMA: query tiles over all requests */
   int64_t workgroups;     /* workgroups of the attention launch (launched
-                             longest piece first when the plan is split or
-                             spans several requests and has at most 960
-                             units; the order never changes the result) */
+                             longest piece first when the plan is split and
+                             has at most 960 units; the order never changes
+                             the result) */
   size_t workspace_bytes; /* workspace the plan uses (<= the size passed in) */
   int32_t stream_spans;   /* MFMA, key split 1: > 0 = balanced decomposition --
                              the 64-key tiles of all query tiles of a KV head,

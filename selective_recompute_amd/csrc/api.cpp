@@ -264,9 +264,8 @@ constexpr int kSimCUs = 240;
 // over its tokens, so query tile t ends near position min(k, (t+1) rows) n / k.
 // Units are dispatched in launch order, each to the earliest free group of
 // CUs: longest unit first where cb::launch_attn_mfma orders the launch
-// (split plans and several requests, up to cb::kAttnMaxOrder units), else
-// the kernel's own order (request by request, chunk by chunk, longest tile
-// first).  The n_kv_heads workgroups of a unit run side by side, so one
+// (split plans of up to cb::kAttnMaxOrder units), else the kernel's own
+// order (request by request, chunk by chunk, longest tile first).  The n_kv_heads workgroups of a unit run side by side, so one
 // "slot" stands for n_kv_heads CUs.  A split tile ends when its last unit
 // has merged.
 double estimate_attn_us(const cb_geom *g, const cb_ragged *rg, int ks, int rows, int64_t kc,
@@ -301,7 +300,7 @@ double estimate_attn_us(const cb_geom *g, const cb_ragged *rg, int ks, int rows,
       }
     tbase += tiles;
   }
-  if ((split || rg->n_req > 1) && all_units <= cb::kAttnMaxOrder)
+  if (split && all_units <= cb::kAttnMaxOrder)
     std::stable_sort(units.begin(), units.end(),
                      [](const Unit &x, const Unit &y) { return x.us > y.us; });
   std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;

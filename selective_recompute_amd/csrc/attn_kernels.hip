@@ -871,8 +871,8 @@ void attn_mfma_kernel(const AttnParams p) {
 // Units in a launch order chosen on the host: workgroup b runs unit
 // ord.e[b / hkv] of KV head b % hkv.  The hardware hands out workgroups in
 // launch order, so listing the longest pieces first leaves the short ones to
-// fill the end of the launch (list scheduling, longest first) instead of a
-// long row of the last request or the last key chunk of a long row.
+// fill the end of the launch (list scheduling, longest first) instead of
+// the last key chunks of the long rows.
 template <int HD, int KS, int N>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_ordered_kernel(const AttnParams p, const AttnOrder<N> ord) {
@@ -954,15 +954,18 @@ static hipError_t launch_hd(const AttnParams &p, const AttnPlan &plan, int n_kv_
   return hipGetLastError();
 }
 
-// Longest-first launch order of a plan's units, or false where the kernel's
-// own order stands (the balanced decomposition; one request unsplit, whose
-// tiles already run last tile first; more units than the table holds).  A
-// tile's row ends at its last selected row's position, which only the device
-// knows; the host estimates it as if request r's k_r selected rows were
-// spread evenly over its n_r tokens (rows_end * n_r / k_r) and ranks units by
-// the keys of their chunk before that end.
+// Longest-first launch order of a split plan's units, or false where the
+// kernel's own order stands: unsplit plans (their units run request by
+// request, last tile first, so the workgroups side by side on an XCD share
+// one request's K/V rows in its L2 -- ordering them across requests bought
+// no time and tripled the L2 misses), the balanced decomposition, and more
+// units than the table holds.  A tile's row ends at its last selected row's
+// position, which only the device knows; the host estimates it as if
+// request r's k_r selected rows were spread evenly over its n_r tokens
+// (rows_end * n_r / k_r) and ranks units by the keys of their chunk before
+// that end.
 static bool attn_launch_order(const AttnArgs &a, const AttnPlan &plan, uint32_t *ord) {
-  if (plan.spans > 0 || (a.n_req < 2 && !plan.split) || plan.units > kMaxOrder) return false;
+  if (plan.spans > 0 || !plan.split || plan.units > kMaxOrder) return false;
   if (!a.h_tok_off || !a.h_sel_off) return false;
   struct Item { int64_t keys; uint32_t u; };
   Item items[kMaxOrder];

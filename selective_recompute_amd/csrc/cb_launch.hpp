@@ -131,8 +131,8 @@ int attn_max_chunks();
 bool attn_stream_fits(int32_t n_req, int64_t tiles);
 
 // Most units whose launch order the host can choose (a table in the kernel
-// arguments); plans with more units, or of the balanced decomposition, or
-// of one unsplit request run in the kernel's own order.
+// arguments); unsplit plans, plans with more units and the balanced
+// decomposition run in the kernel's own order.
 constexpr int kAttnMaxOrder = 960;
 
 // counters_zero: the split's arrival counters are already zero (cleared by

@@ -1,18 +1,18 @@
 """The launch order of attention units does not change results.
 
-Plans over several requests, and split plans, launch their units longest
-piece first, in an order the host estimates from the request sizes (a single
-unsplit request keeps the kernel's own order, which is already that).  Every
-unit computes the same numbers wherever it sits in the launch, and a split
-tile merges its pieces in piece order whichever arrives last, so each
-request's rows of a batched launch must equal, bit for bit, those of a
-launch over that request alone ([Derivations, "形式化"]: each selected row
-attends over its own request's keys only) -- a launch whose units come in
-another order.  Cases: the 70B-shaped batch's ragged requests with rows
-spread at random, many small requests (some with nothing selected), and more
-units than the order table holds (the kernel's own order); whole rows, and
-rows split over key chunks with either key split.  The batched outputs are
-also checked against the oracle on sampled rows.
+Split plans launch their units longest piece first, in an order the host
+estimates from the request sizes; unsplit plans keep the kernel's own order
+(request by request, last tile first).  Every unit computes the same numbers
+wherever it sits in the launch, and a split tile merges its pieces in piece
+order whichever arrives last, so each request's rows of a batched launch
+must equal, bit for bit, those of a launch over that request alone
+([Derivations, "形式化"]: each selected row attends over its own request's
+keys only) -- a launch whose units come in another order.  Cases: the
+70B-shaped batch's ragged requests with rows spread at random, many small
+requests (some with nothing selected), and more units than the order table
+holds (the kernel's own order); whole rows, and rows split over key chunks
+with either key split.  The batched outputs are also checked against the
+oracle on sampled rows.
 """
 import math
 
@@ -116,42 +116,49 @@ def test_batched_rows_equal_single_request_launches(name, plan):
     assert err <= ATTN_ABS, f"attention max err {err}"
 
 
-@pytest.mark.parametrize("n_req", [64, 65, 256, 257, 960, 961])
-def test_order_table_sizes(n_req):
+SPLIT_256 = dict(mfma=1, key_split=1, key_chunk=256)
+
+
+@pytest.mark.parametrize("units", [64, 65, 256, 257, 960, 961])
+def test_order_table_sizes(units):
     """The launch order travels in a table sized to the launch (64, 256 or
-    960 units; more keep the kernel's own order).  Requests of 64 tokens
-    with 8 selected rows are one query tile each (64 Q / 8 KV heads: 32 rows
-    per tile), so n_req units: each size at its edge and one past it.  Every
-    row is written, and sampled requests equal their own launches bit for
-    bit."""
+    960 units; more keep the kernel's own order).  Requests of 512 tokens
+    with 8 selected rows are one query tile (64 Q / 8 KV heads: 32 rows per
+    tile) in two key chunks of 256, one request of 256 tokens a single
+    chunk: units // 2 of the first and units % 2 of the second give each
+    table size at its edge and one past it.  Every row is written, and
+    sampled requests equal their own launches bit for bit."""
     hq, hkv, d = 64, 8, 128
-    lens, ks = [64] * n_req, [8] * n_req
-    say(f"order table: {n_req} one-tile requests")
-    rng = np.random.default_rng(n_req)
+    lens = [512] * (units // 2) + [256] * (units % 2)
+    n_req = len(lens)
+    ks = [8] * n_req
+    say(f"order table: {units} units over {n_req} requests")
+    rng = np.random.default_rng(units)
     tok_off, sel_off = PL.offsets(lens), PL.offsets(ks)
-    sel = np.concatenate([np.sort(rng.choice(64, 8, replace=False)) + tok_off[r]
-                          for r in range(n_req)]).astype(np.int32)
-    gen = torch.Generator(device=DEV).manual_seed(n_req)
+    sel = np.concatenate([np.sort(rng.choice(n, 8, replace=False)) + tok_off[r]
+                          for r, n in enumerate(lens)]).astype(np.int32)
+    gen = torch.Generator(device=DEV).manual_seed(units)
     q = torch.randn(len(sel), hq, d, generator=gen, device=DEV).to(torch.bfloat16)
     k = torch.randn(int(tok_off[-1]), hkv, d, generator=gen, device=DEV).to(torch.bfloat16)
     v = torch.randn(int(tok_off[-1]), hkv, d, generator=gen, device=DEV).to(torch.bfloat16)
     geo = B.geom(hq, hkv, d, torch.bfloat16)
     scale = 1.0 / math.sqrt(d)
     rb = B.RaggedBatch(tok_off, tok_off, sel_off, DEV)
-    assert B.describe_plan(geo, rb, **WHOLE_ROWS)["tiles"] == n_req
+    assert B.describe_plan(geo, rb, **SPLIT_256)["workgroups"] == units * hkv
     sg = torch.from_numpy(sel).to(DEV)
     out = torch.full((len(sel), hq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
-    B.partial_attn_with_plan(geo, rb, WHOLE_ROWS, out, q,
+    B.partial_attn_with_plan(geo, rb, SPLIT_256, out, q,
                              torch.arange(len(sel), dtype=torch.int32, device=DEV), sg, k, v,
-                             scale)
+                             scale, workspace=_ws(geo, rb, SPLIT_256))
     torch.cuda.synchronize()
     assert not torch.isnan(out).any(), "a row of the batched launch was not written"
-    rb1 = B.RaggedBatch(np.array([0, 64]), np.array([0, 64]), np.array([0, 8]), DEV)
     for r in sorted({0, n_req // 2, n_req - 1} | set(range(0, n_req, 97))):
-        lo, s0 = int(tok_off[r]), int(sel_off[r])
+        n, lo, s0 = lens[r], int(tok_off[r]), int(sel_off[r])
+        rb1 = B.RaggedBatch(np.array([0, n]), np.array([0, n]), np.array([0, 8]), DEV)
         out1 = torch.full((8, hq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
-        B.partial_attn_with_plan(geo, rb1, WHOLE_ROWS, out1, q[s0:s0 + 8],
+        B.partial_attn_with_plan(geo, rb1, SPLIT_256, out1, q[s0:s0 + 8],
                                  torch.arange(8, dtype=torch.int32, device=DEV),
-                                 sg[s0:s0 + 8] - lo, k[lo:lo + 64], v[lo:lo + 64], scale)
+                                 sg[s0:s0 + 8] - lo, k[lo:lo + n], v[lo:lo + n], scale,
+                                 workspace=_ws(geo, rb1, SPLIT_256))
         torch.cuda.synchronize()
         assert torch.equal(out[s0:s0 + 8], out1), f"request {r}"
