@@ -170,9 +170,6 @@ __device__ inline bool locate_unit(const AttnParams &p, int u, UnitPos &up) {
   return false;
 }
 
-// s_waitcnt operand for lgkmcnt(0) with the VM counter left free (gfx9
-// encoding; vmcnt(n) is waitcnt_vm).
-constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
 
 // 16 bytes per lane from global memory straight into LDS: lane l writes
 // lds_byte + 16 l (gfx950 global_load_lds_dwordx4, LDS base in M0).  Written
@@ -215,17 +212,6 @@ __device__ inline uint32_t lds_addr(const bf16 *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) bf16 *)p;
 }
 
-// Workgroup barrier between two tiles: LDS reads of this wave are complete,
-// and neither the compiler nor the scheduler moves work across it.  Global
-// loads into LDS stay in flight (their completion is waited for explicitly).
-__device__ inline void phase_barrier() {
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
 
 // Compile-time shape of one MFMA attention workgroup.
 template <int HD, int KS> struct AttnCfg {

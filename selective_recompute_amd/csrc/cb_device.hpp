@@ -28,6 +28,23 @@ template <typename T> __device__ inline T load_agent(const T *p) {
 // the other counters left alone).
 __device__ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
+// s_waitcnt operand for lgkmcnt(0) with the VM counter left free (gfx9
+// encoding; vmcnt(n) is waitcnt_vm).
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
+
+// Workgroup barrier after which every wave's LDS accesses before it are
+// complete; neither the compiler nor the scheduler moves work across it.
+// Global loads, and copies into LDS, stay in flight: their completion is
+// waited for where their data is used (__syncthreads waits for them too).
+__device__ inline void phase_barrier() {
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // 16-byte vector of storage elements, converted to/from fp32.
 template <typename T> struct Vec16;
 

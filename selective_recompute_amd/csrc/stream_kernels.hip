@@ -353,6 +353,23 @@ __host__ __device__ constexpr int topk_rounds(int m) {
   return ((m + kTopkWaves - 1) / kTopkWaves + kWave - 1) / kWave;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave, lane 0 first: shifted
+// adds inside each row of 16 lanes (DPP row_shr 1, 2, 4, 8, lanes shifted
+// in from outside the row reading 0), then the last lane of row 0 added to
+// row 1 and of row 2 to row 3 (row_bcast:15), then lane 31 to rows 2 and 3
+// (row_bcast:31) -- gfx9's cross-lane data paths, no LDS round trips.
+__device__ inline uint32_t wave_prefix_sum(uint32_t x) {
+  const int v = (int)x;
+  int s = v;
+  s += __builtin_amdgcn_update_dpp(0, s, 0x111, 0xf, 0xf, true);  // row_shr:1
+  s += __builtin_amdgcn_update_dpp(0, s, 0x112, 0xf, 0xf, true);  // row_shr:2
+  s += __builtin_amdgcn_update_dpp(0, s, 0x114, 0xf, 0xf, true);  // row_shr:4
+  s += __builtin_amdgcn_update_dpp(0, s, 0x118, 0xf, 0xf, true);  // row_shr:8
+  s += __builtin_amdgcn_update_dpp(0, s, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1, 3
+  s += __builtin_amdgcn_update_dpp(0, s, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2, 3
+  return (uint32_t)s;
+}
+
 // A wave's contribution to the LDS histogram of one radix pass.  Most scores
 // share their leading bits (the deviation tiers), so a wave's keys fall into
 // very few bins: the first two distinct bins it meets are counted in
@@ -414,6 +431,7 @@ __device__ __attribute__((always_inline)) void topk_select(TopkShared &sh, const
     }
     return;
   }
+  if (tid < 256) sh.hist[tid] = 0;  // the first pass's histogram, cleared while the scores load
   const int rounds = topk_rounds(m);
   const int wb = wave * rounds * kWave;                  // first candidate of this wave
   const int n_w = max(0, min(m - wb, rounds * kWave));   // candidates of this wave
@@ -443,8 +461,10 @@ __device__ __attribute__((always_inline)) void topk_select(TopkShared &sh, const
   uint32_t prefix = 0, mask = 0, krem = (uint32_t)k;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    if (tid < 256) sh.hist[tid] = 0;
-    __syncthreads();  // also: every thread has read the previous pass's sh_*
+    if (pass > 0 && tid < 256) sh.hist[tid] = 0;
+    // The zeros are visible, and every thread has read the previous pass's
+    // sh_*; the first pass's score loads may still be in flight.
+    phase_barrier();
     WaveHist wh;
 #pragma unroll kUnroll
     for (int i = 0; i < iters; ++i) {
@@ -458,20 +478,20 @@ __device__ __attribute__((always_inline)) void topk_select(TopkShared &sh, const
     wh.flush(sh.hist);
     __syncthreads();
     if (tid < kWave) {
+      // Lane l holds bins 255 - 4l down to 252 - 4l, so a prefix sum over
+      // the lanes counts every key in this lane's bins and the bins above.
       uint32_t h[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) h[q] = sh.hist[4 * tid + q];
+      for (int q = 0; q < 4; ++q) h[q] = sh.hist[255 - 4 * tid - q];
       const uint32_t tot = h[0] + h[1] + h[2] + h[3];
-      uint32_t suf = tot;  // sum over this lane's bins and every higher lane's
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t t = __shfl_down(suf, off, kWave);
-        if (tid + off < kWave) suf += t;
-      }
-      uint32_t above = suf - tot;
-      if (above < krem && suf >= krem) {
-        for (int q = 3; q >= 0; --q) {
-          if (above + h[q] >= krem) { sh.digit = 4 * tid + q; sh.above = above; sh.count = h[q]; break; }
+      const uint32_t incl = wave_prefix_sum(tot);
+      uint32_t above = incl - tot;
+      if (above < krem && incl >= krem) {
+        for (int q = 0; q < 4; ++q) {
+          if (above + h[q] >= krem) {
+            sh.digit = 255 - 4 * tid - q; sh.above = above; sh.count = h[q];
+            break;
+          }
           above += h[q];
         }
       }
@@ -519,8 +539,8 @@ __device__ __attribute__((always_inline)) void topk_select(TopkShared &sh, const
     const uint64_t bg = __ballot(gt), be = __ballot(eq);
     const uint32_t g_pos = gt_before + (uint32_t)__popcll(bg & below);
     const uint32_t e_pos = eq_before + (uint32_t)__popcll(be & below);
-    if (gt || (eq && e_pos < keep_eq)) {
-      const uint32_t pos = g_pos + (e_pos < keep_eq ? e_pos : keep_eq);
+    const uint32_t pos = g_pos + (e_pos < keep_eq ? e_pos : keep_eq);
+    if ((gt || (eq && e_pos < keep_eq)) && pos < (uint32_t)k) {  // pos < k always: a guard
       sel_local[s0 + pos] = c0 + wb + kWave * i + lane;
       sel_global[s0 + pos] = KPT > 0 ? cands[i] : cw[kWave * i];
     }
