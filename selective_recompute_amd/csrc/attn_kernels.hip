@@ -503,7 +503,6 @@ __device__ __attribute__((always_inline)) void attn_piece(
   const int dt_lo = MSPLIT == 2 ? kg * MDT : 0;
   bool merged = false;
   if (n_active > 1) {
-    constexpr int UNIT = partial_bytes<HD, QT>();
     if (kg == 0) {
       // Partial in fragment order: store (dt, q) of wave w writes 64 lanes x 8
       // contiguous bytes at fp16x4 index ((w*NDT + dt)*4 + q)*64 + lane.  Each
